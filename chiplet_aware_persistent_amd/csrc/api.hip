@@ -1,0 +1,446 @@
+// C ABI of libsgemm.so: validation, planning and launches.  See include/sgemm.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/sgemm.h"
+#include "launch.h"
+#include "stage_desc.h"
+
+using namespace sg;
+
+namespace {
+
+constexpr size_t kCtl = 256;            // control block: status word, done counter
+constexpr int kLdsMax = 64 * 1024;      // LDS budget of one workgroup
+constexpr size_t kMaxOperand = (size_t)1 << 31;  // buffer extents are 31-bit here
+constexpr int kWgPerXcd = 32;           // one workgroup per CU, 32 CUs per XCD
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Decomposition of one GEMM stage (see gemm_device.h for how it is executed).
+struct Geo {
+  int path = 0;        // 0 dot2, 1 MFMA
+  int M = 0, K = 0, N = 0;
+  int ta = 0, tb = 0;  // template parameters: dot2 (M, G); MFMA (MT, NT)
+  int waves = 8, TN = 0, CB = 0, Nx = 0, NB = 0, S = 1, KS = 0, steps = 0, items = 0;
+  int win = 0, xrow = 0, lds = 0;
+  int paired = 0, pair_off = 0;
+  size_t ctr_count = 0, part_floats = 0;
+  double est_us = 0.0;
+};
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return v && *v ? std::atoi(v) : dflt;
+}
+
+// Fill the derived fields of g for (path, template params, waves, S); returns
+// false when the candidate does not fit (LDS, registers, instantiations).
+bool shape_geo(Geo& g, int want_S) {
+  const int kstep = g.path == 0 ? kDot2KStep : kMfmaKStep;
+  g.TN = g.path == 0 ? g.tb : (g.paired ? 16 : 16 * g.tb);
+  g.CB = g.waves * g.TN;
+  g.Nx = (int)round_up((size_t)ceil_div(g.N, kXcds), 16);
+  g.NB = ceil_div(g.Nx, g.CB);
+  g.KS = (int)round_up((size_t)ceil_div(g.K, want_S), 8);
+  g.S = ceil_div(g.K, g.KS);
+  g.steps = ceil_div(g.KS, kstep);
+  g.win = g.steps * kstep;
+  const int rows = g.path == 0 ? g.M : 16 * g.ta;
+  g.xrow = g.path == 0 ? g.win : g.win + 8;
+  g.lds = rows * g.xrow * 2;
+  g.items = g.NB * g.S;
+  const int vals = g.path == 0 ? g.tb * g.M : g.tb * g.ta * 256;
+  g.ctr_count = (size_t)kXcds * g.NB * g.waves;
+  g.part_floats = g.S > 1 ? g.ctr_count * (size_t)g.S * vals : 0;
+  if (g.lds > kLdsMax) return false;
+  if (!gemm_variant_exists(g.path, g.ta, g.tb) && !g.paired) return false;
+  // Cost model (microseconds): streaming time of the busiest workgroup at the
+  // per-CU share of HBM bandwidth, plus per-item and split-K overheads.
+  const double bw_cu = 8.0e12 * 0.85 / 256.0;  // bytes/s per CU
+  const int rounds = ceil_div(g.items, kWgPerXcd);
+  const double item_bytes = (double)g.CB * g.KS * 2.0 * (g.paired ? 2.0 : 1.0);
+  const double part_bytes = g.S > 1 ? (double)g.CB * g.M * 4.0 * 2.0 : 0.0;
+  g.est_us = rounds * ((item_bytes + part_bytes) / bw_cu * 1e6 + 0.35) + (g.S > 1 ? 0.8 : 0.0);
+  return true;
+}
+
+bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, int s_o, int waves_o) {
+  bool found = false;
+  const int waves_opts[2] = {8, 4};
+  for (int wi = 0; wi < 2; ++wi) {
+    const int waves = waves_opts[wi];
+    if (waves_o && waves != waves_o) continue;
+    for (int tb = 1; tb <= 8; ++tb) {
+      Geo g;
+      g.path = path; g.M = M; g.K = K; g.N = N; g.waves = waves;
+      g.paired = paired;
+      if (path == 0) {
+        if (tb != 4 && tb != 8) continue;
+        if (tn_o && tb != tn_o) continue;
+        g.ta = M; g.tb = tb;
+      } else {
+        if (tb > 2) continue;
+        if (paired && tb != 2) continue;
+        if (tn_o && !paired && 16 * tb != tn_o) continue;
+        g.ta = (M + 15) / 16; g.tb = tb;
+      }
+      const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : 64;
+      for (int s = s_lo; s <= s_hi; ++s) {
+        if (s > 1 && (K + s - 1) / s < 8) break;
+        Geo c = g;
+        if (!shape_geo(c, s)) continue;
+        if (c.S != s && !s_o) continue;  // rounding collapsed it to another count
+        if (!found || c.est_us < best.est_us - 1e-9) { best = c; found = true; }
+      }
+    }
+  }
+  return found;
+}
+
+}  // namespace
+
+struct sgemm_plan_s {
+  sgemm_problem prob;
+  int device = 0;
+  unsigned w_aux = 2;
+  int sync = SYNC_AGENT;
+  int grid = 8 * kWgPerXcd;
+  Geo geo;                    // GEMM
+  Geo cg[kChainStages];       // chain stages
+  size_t ws_bytes = 0;
+  size_t off_ctr = 0, off_part = 0;                 // GEMM (and chain stage 0..3 bases below)
+  size_t c_ctr[kChainStages] = {0}, c_part[kChainStages] = {0};
+  size_t off_lctr = 0, off_gctr = 0, off_act = 0, off_stamps = 0;
+  size_t act_layer_elems = 0, a_h1 = 0, a_h2 = 0, a_a = 0, a_x = 0;
+  long long spin_ticks = 0;
+};
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int validate_gemm(const sgemm_problem& p) {
+  if (p.M < 1 || p.K < 8 || p.N < 1) return SGEMM_ERR_INVALID_ARG;
+  if (p.K % 8 != 0) return SGEMM_ERR_INVALID_ARG;
+  if (p.out_dtype != SGEMM_OUT_F32 && p.out_dtype != SGEMM_OUT_BF16) return SGEMM_ERR_INVALID_ARG;
+  if (p.M > 64) return SGEMM_ERR_UNSUPPORTED;
+  if ((size_t)p.N * p.K * 2 >= kMaxOperand || (size_t)p.M * p.K * 2 >= kMaxOperand ||
+      (size_t)p.M * p.N * 4 >= kMaxOperand)
+    return SGEMM_ERR_UNSUPPORTED;
+  return SGEMM_OK;
+}
+
+static int choose_path(const sgemm_problem& p) {
+  if (p.flags & SGEMM_F_FORCE_DOT2) return 0;
+  if (p.flags & SGEMM_F_FORCE_MFMA) return 1;
+  return p.M < 16 ? 0 : 1;
+}
+
+static void layout_stage_ws(size_t& cursor, const Geo& g, size_t& off_ctr, size_t& off_part) {
+  off_ctr = cursor;
+  cursor = round_up(cursor + g.ctr_count * 4, 256);
+  off_part = cursor;
+  cursor = round_up(cursor + g.part_floats * 4, 256);
+}
+
+extern "C" {
+
+int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
+                      size_t* workspace_bytes) {
+  if (!problem || !out || !workspace_bytes) return SGEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  const sgemm_problem& p = *problem;
+  if ((p.flags & SGEMM_F_FORCE_DOT2) && (p.flags & SGEMM_F_FORCE_MFMA)) return SGEMM_ERR_INVALID_ARG;
+  if (p.tn < 0 || p.splitk < 0 || p.waves < 0) return SGEMM_ERR_INVALID_ARG;
+  if (p.waves && p.waves != 4 && p.waves != 8) return SGEMM_ERR_INVALID_ARG;
+  if (p.splitk > 64) return SGEMM_ERR_UNSUPPORTED;
+  if (device < 0) return SGEMM_ERR_INVALID_ARG;
+
+  sgemm_plan_s* pl = new (std::nothrow) sgemm_plan_s();
+  if (!pl) return SGEMM_ERR_INVALID_ARG;
+  pl->prob = p;
+  pl->device = device;
+  pl->w_aux = (p.flags & SGEMM_F_W_CACHED) ? 0u : ((p.flags & SGEMM_F_W_SC1) ? 18u : 2u);
+  pl->sync = (p.flags & SGEMM_F_SYNC_AGENT) ? SYNC_AGENT : SYNC_XCD;
+  const int tn_o = p.tn ? p.tn : env_int("SGEMM_TN", 0);
+  const int s_o = p.splitk ? p.splitk : env_int("SGEMM_SPLITK", 0);
+  const int w_o = p.waves ? p.waves : env_int("SGEMM_WAVES", 0);
+
+  size_t cur = kCtl;
+  if (p.kind == SGEMM_KIND_GEMM) {
+    int rc = validate_gemm(p);
+    if (rc != SGEMM_OK) { delete pl; return rc; }
+    const int path = choose_path(p);
+    if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o)) {
+      delete pl;
+      return SGEMM_ERR_UNSUPPORTED;
+    }
+    layout_stage_ws(cur, pl->geo, pl->off_ctr, pl->off_part);
+  } else if (p.kind == SGEMM_KIND_LAYERCHAIN) {
+    if (p.M < 1 || p.n_layers < 1 || p.d_model < 8 || p.q_cols < 8 || p.d_ff < 8)
+      { delete pl; return SGEMM_ERR_INVALID_ARG; }
+    if (p.d_model % 8 || p.q_cols % 8 || p.d_ff % 8) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+    if (p.M > 64 || p.n_layers > kMaxLayers) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    if ((size_t)2 * p.d_ff * p.d_model * 2 >= kMaxOperand) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    // Stages: Q [d -> q], O [q -> d], gate_up paired [d -> dff], down [dff -> d].
+    // One block size and one n-tile width for the unpaired stages per launch.
+    const int Ks[4] = {p.d_model, p.q_cols, p.d_model, p.d_ff};
+    const int Ns[4] = {p.q_cols, p.d_model, p.d_ff, p.d_model};
+    double best = -1.0;
+    for (int waves = 8; waves >= 4; waves -= 4) {
+      if (w_o && waves != w_o) continue;
+      for (int nt = 1; nt <= 2; ++nt) {
+        if (tn_o && tn_o != 16 * nt) continue;
+        Geo c[kChainStages];
+        double tot = 0.0;
+        bool ok = chain_variant_exists((p.M + 15) / 16, nt, nt, nt);
+        for (int s = 0; s < kChainStages && ok; ++s) {
+          const int paired = s == 2;
+          ok = plan_geo(c[s], p.M, Ks[s], Ns[s], 1, paired, paired ? 0 : 16 * nt, s_o, waves);
+          if (ok && paired) c[s].pair_off = p.d_ff;
+          tot += ok ? c[s].est_us : 0.0;
+        }
+        if (ok && (best < 0.0 || tot < best)) {
+          best = tot;
+          for (int s = 0; s < kChainStages; ++s) pl->cg[s] = c[s];
+        }
+      }
+    }
+    if (best < 0.0) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    // Re-layout with the final geometries.
+    cur = kCtl;
+    for (int s = 0; s < kChainStages; ++s) layout_stage_ws(cur, pl->cg[s], pl->c_ctr[s], pl->c_part[s]);
+    const int events = kChainStages * p.n_layers;
+    pl->off_lctr = cur;
+    cur = round_up(cur + (size_t)kXcds * events * 4, 256);
+    pl->off_gctr = cur;
+    cur = round_up(cur + (size_t)events * 4, 256);
+    const size_t M = p.M;
+    pl->a_h1 = 0;
+    pl->a_h2 = round_up(M * p.q_cols, 128);
+    pl->a_a = pl->a_h2 + round_up(M * p.d_model, 128);
+    pl->a_x = pl->a_a + round_up(M * p.d_ff, 128);
+    pl->act_layer_elems = pl->a_x + round_up(M * p.d_model, 128);
+    pl->off_act = cur;
+    cur = round_up(cur + pl->act_layer_elems * 2 * p.n_layers, 256);
+    pl->off_stamps = cur;
+    if (p.flags & SGEMM_F_STAMPS) cur = round_up(cur + (size_t)pl->grid * events * 2 * 8, 256);
+    const double secs = std::atof(std::getenv("SGEMM_WATCHDOG_S") ? std::getenv("SGEMM_WATCHDOG_S") : "5");
+    pl->spin_ticks = (p.flags & SGEMM_F_WATCHDOG_TEST) ? 0 : (long long)(secs * 1.0e8);
+  } else {
+    delete pl;
+    return SGEMM_ERR_INVALID_ARG;
+  }
+  pl->ws_bytes = std::max(cur, (size_t)4096);
+  *workspace_bytes = pl->ws_bytes;
+  *out = pl;
+  return SGEMM_OK;
+}
+
+int sgemm_plan_destroy(sgemm_plan plan) {
+  delete plan;
+  return SGEMM_OK;
+}
+
+int sgemm_workspace_init(sgemm_plan plan, void* workspace, void* stream) {
+  if (!plan || !workspace || !aligned16(workspace)) return SGEMM_ERR_INVALID_ARG;
+  if (hipSetDevice(plan->device) != hipSuccess) return SGEMM_ERR_HIP;
+  return launch_fill_zero(workspace, plan->ws_bytes, (hipStream_t)stream) == hipSuccess ? SGEMM_OK
+                                                                                        : SGEMM_ERR_HIP;
+}
+
+static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
+  StageDesc d;
+  std::memset(&d, 0, sizeof d);
+  d.M = g.M; d.K = g.K; d.N = g.N;
+  d.Nx = g.Nx; d.TN = g.TN; d.CB = g.CB; d.NB = g.NB; d.S = g.S; d.KS = g.KS;
+  d.steps = g.steps; d.items = g.items; d.win = g.win; d.xrow = g.xrow;
+  d.pair_off = g.pair_off;
+  d.w_aux = w_aux;
+  d.sync = sync;
+  return d;
+}
+
+int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* workspace, void* stream) {
+  if (!plan || !X || !W || !Y || !workspace) return SGEMM_ERR_INVALID_ARG;
+  if (plan->prob.kind != SGEMM_KIND_GEMM) return SGEMM_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || !aligned16(workspace))
+    return SGEMM_ERR_INVALID_ARG;
+  const sgemm_problem& p = plan->prob;
+  const Geo& g = plan->geo;
+  StageDesc d = stage_desc(g, plan->w_aux, plan->sync);
+  char* ws = (char*)workspace;
+  d.X = (const uint16_t*)X;
+  d.W = (const uint16_t*)W;
+  d.Y = Y;
+  d.Y2 = nullptr;
+  d.ldx = p.K;
+  d.ldy = p.N;
+  d.mode = p.out_dtype == SGEMM_OUT_F32 ? OUT_F32 : OUT_BF16;
+  d.part = (float*)(ws + plan->off_part);
+  d.part_bytes = (unsigned)(g.part_floats * 4);
+  d.ctr = (unsigned*)(ws + plan->off_ctr);
+  d.x_bytes = (unsigned)((size_t)p.M * p.K * 2);
+  d.w_bytes = (unsigned)((size_t)p.N * p.K * 2);
+  d.y_bytes = (unsigned)((size_t)p.M * p.N * (p.out_dtype == SGEMM_OUT_F32 ? 4 : 2));
+  d.y2_bytes = 0;
+  if (hipSetDevice(plan->device) != hipSuccess) return SGEMM_ERR_HIP;
+  hipError_t e = launch_gemm(d, g.path, g.ta, g.tb, plan->grid, g.waves * 64, g.lds, (unsigned*)ws,
+                             (hipStream_t)stream);
+  return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
+}
+
+int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const void* const* Wo,
+                   const void* const* Wgu, const void* const* Wdown, float* Y_f32, void* Y_bf16,
+                   void* workspace, void* stream) {
+  if (!plan || !X0 || !Wq || !Wo || !Wgu || !Wdown || !Y_f32 || !workspace)
+    return SGEMM_ERR_INVALID_ARG;
+  const sgemm_problem& p = plan->prob;
+  if (p.kind != SGEMM_KIND_LAYERCHAIN) return SGEMM_ERR_INVALID_ARG;
+  if (!aligned16(X0) || !aligned16(Y_f32) || !aligned16(workspace) || (Y_bf16 && !aligned16(Y_bf16)))
+    return SGEMM_ERR_INVALID_ARG;
+  ChainArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int l = 0; l < p.n_layers; ++l) {
+    if (!Wq[l] || !Wo[l] || !Wgu[l] || !Wdown[l]) return SGEMM_ERR_INVALID_ARG;
+    if (!aligned16(Wq[l]) || !aligned16(Wo[l]) || !aligned16(Wgu[l]) || !aligned16(Wdown[l]))
+      return SGEMM_ERR_INVALID_ARG;
+    a.wq[l] = (const uint16_t*)Wq[l];
+    a.wo[l] = (const uint16_t*)Wo[l];
+    a.wgu[l] = (const uint16_t*)Wgu[l];
+    a.wdown[l] = (const uint16_t*)Wdown[l];
+  }
+  char* ws = (char*)workspace;
+  const int Ks[4] = {p.d_model, p.q_cols, p.d_model, p.d_ff};
+  const int Ns[4] = {p.q_cols, p.d_model, p.d_ff, p.d_model};
+  const int Wrows[4] = {p.q_cols, p.d_model, 2 * p.d_ff, p.d_model};
+  for (int s = 0; s < kChainStages; ++s) {
+    StageDesc d = stage_desc(plan->cg[s], plan->w_aux, plan->sync);
+    d.part = (float*)(ws + plan->c_part[s]);
+    d.part_bytes = (unsigned)(plan->cg[s].part_floats * 4);
+    d.ctr = (unsigned*)(ws + plan->c_ctr[s]);
+    d.ldx = Ks[s];
+    d.ldy = Ns[s];
+    d.x_bytes = (unsigned)((size_t)p.M * Ks[s] * 2);
+    d.w_bytes = (unsigned)((size_t)Wrows[s] * Ks[s] * 2);
+    d.y_bytes = (unsigned)((size_t)p.M * Ns[s] * 2);
+    d.mode = s == 2 ? OUT_SILU_BF16 : OUT_BF16;
+    d.y2_bytes = s == 3 ? (unsigned)((size_t)p.M * p.d_model * 4) : 0u;
+    a.st[s] = d;
+  }
+  a.x0 = (const uint16_t*)X0;
+  a.act = (uint16_t*)(ws + plan->off_act);
+  a.y_f32 = Y_f32;
+  a.y_bf16 = (uint16_t*)Y_bf16;
+  a.status = (unsigned*)ws;
+  a.done = (unsigned*)(ws + 64);
+  a.lctr = (unsigned*)(ws + plan->off_lctr);
+  a.gctr = (unsigned*)(ws + plan->off_gctr);
+  a.stamps = (p.flags & SGEMM_F_STAMPS) ? (unsigned long long*)(ws + plan->off_stamps) : nullptr;
+  a.n_layers = p.n_layers; a.M = p.M; a.d = p.d_model; a.q = p.q_cols; a.dff = p.d_ff;
+  a.act_layer_elems = plan->act_layer_elems;
+  a.off_h1 = plan->a_h1; a.off_h2 = plan->a_h2; a.off_a = plan->a_a; a.off_x = plan->a_x;
+  a.flat_sync = (p.flags & SGEMM_F_SYNC_FLAT) ? 1 : 0;
+  a.spin_ticks = plan->spin_ticks;
+  a.mt = plan->cg[0].ta;
+  a.nt_q = plan->cg[0].tb; a.nt_o = plan->cg[1].tb; a.nt_d = plan->cg[3].tb;
+  int lds = 0;
+  for (int s = 0; s < kChainStages; ++s) lds = std::max(lds, plan->cg[s].lds);
+  if (hipSetDevice(plan->device) != hipSuccess) return SGEMM_ERR_HIP;
+  hipError_t e = launch_chain(a, plan->grid, plan->cg[0].waves * 64, lds, (hipStream_t)stream);
+  if (e == hipSuccess && Y_bf16) {
+    const size_t off = plan->off_act + ((size_t)(p.n_layers - 1) * plan->act_layer_elems + plan->a_x) * 2;
+    e = hipMemcpyAsync(Y_bf16, ws + off, (size_t)p.M * p.d_model * 2, hipMemcpyDeviceToDevice,
+                       (hipStream_t)stream);
+  }
+  return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
+}
+
+int sgemm_chain_buffer(sgemm_plan plan, int layer, int which, size_t* offset, size_t* bytes) {
+  if (!plan || !offset || !bytes || plan->prob.kind != SGEMM_KIND_LAYERCHAIN) return SGEMM_ERR_INVALID_ARG;
+  const sgemm_problem& p = plan->prob;
+  if (layer < 0 || layer >= p.n_layers || which < 0 || which > 3) return SGEMM_ERR_INVALID_ARG;
+  const size_t offs[4] = {plan->a_h1, plan->a_h2, plan->a_a, plan->a_x};
+  const size_t cols[4] = {(size_t)p.q_cols, (size_t)p.d_model, (size_t)p.d_ff, (size_t)p.d_model};
+  *offset = plan->off_act + ((size_t)layer * plan->act_layer_elems + offs[which]) * 2;
+  *bytes = (size_t)p.M * cols[which] * 2;
+  return SGEMM_OK;
+}
+
+int sgemm_query_status(sgemm_plan plan, void* workspace, void* stream) {
+  if (!plan || !workspace) return SGEMM_ERR_INVALID_ARG;
+  if (hipSetDevice(plan->device) != hipSuccess) return SGEMM_ERR_HIP;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SGEMM_ERR_HIP;
+  unsigned st = 0;
+  if (hipMemcpy(&st, workspace, 4, hipMemcpyDeviceToHost) != hipSuccess) return SGEMM_ERR_HIP;
+  if (st) {
+    const unsigned zero = 0;
+    if (hipMemcpy(workspace, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return SGEMM_ERR_HIP;
+  }
+  if (st & 1u) return SGEMM_ERR_TIMEOUT;
+  if ((st & 2u) && plan->sync == SYNC_XCD) return SGEMM_ERR_TOPOLOGY;
+  return SGEMM_OK;
+}
+
+const char* sgemm_status_string(int status) {
+  switch (status) {
+    case SGEMM_OK: return "ok";
+    case SGEMM_ERR_INVALID_ARG: return "invalid argument";
+    case SGEMM_ERR_UNSUPPORTED: return "unsupported problem";
+    case SGEMM_ERR_HIP: return "HIP runtime error";
+    case SGEMM_ERR_TIMEOUT: return "device wait timed out";
+    case SGEMM_ERR_WORKSPACE: return "workspace error";
+    case SGEMM_ERR_TOPOLOGY: return "workgroup ran on an unexpected XCD";
+    default: return "unknown status";
+  }
+}
+
+static std::string geo_json(const Geo& g) {
+  char b[512];
+  std::snprintf(b, sizeof b,
+                "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,"
+                "\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,\"steps\":%d,"
+                "\"items\":%d,\"lds\":%d,\"paired\":%d,\"est_us\":%.3f}",
+                g.path == 0 ? "dot2" : "mfma", g.M, g.K, g.N, g.ta, g.tb, g.waves, g.TN, g.CB, g.Nx,
+                g.NB, g.S, g.KS, g.steps, g.items, g.lds, g.paired, g.est_us);
+  return b;
+}
+
+int sgemm_plan_describe(sgemm_plan plan, char* buf, size_t len) {
+  if (!plan) return SGEMM_ERR_INVALID_ARG;
+  std::string s = "{\"kind\":";
+  s += plan->prob.kind == SGEMM_KIND_GEMM ? "\"gemm\"" : "\"layerchain\"";
+  char b[256];
+  std::snprintf(b, sizeof b,
+                ",\"grid\":%d,\"workspace\":%zu,\"w_aux\":%u,\"sync\":\"%s\",\"stamps_offset\":%zu,",
+                plan->grid, plan->ws_bytes, plan->w_aux, plan->sync == SYNC_XCD ? "xcd" : "agent",
+                plan->off_stamps);
+  s += b;
+  if (plan->prob.kind == SGEMM_KIND_GEMM) {
+    s += "\"stage\":" + geo_json(plan->geo);
+  } else {
+    s += "\"stages\":[";
+    for (int i = 0; i < kChainStages; ++i) s += (i ? "," : "") + geo_json(plan->cg[i]);
+    s += "]";
+  }
+  s += "}";
+  if (buf && len) {
+    std::strncpy(buf, s.c_str(), len - 1);
+    buf[len - 1] = 0;
+  }
+  return (int)s.size() + 1;
+}
+
+int sgemm_topology_probe(int* xcc_out, int n_wg, void* stream) {
+  if (!xcc_out || n_wg < 1 || n_wg > 65536) return SGEMM_ERR_INVALID_ARG;
+  return launch_topology(xcc_out, n_wg, (hipStream_t)stream) == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+// Persistent layer chain: every projection of every layer in one launch.
+//
+// Per layer (Fleet reading note, sections 3f and 7b: gate and up are one
+// concatenated GEMM whose result is SiLU-gated; a decoder layer's projections
+// run back to back inside one persistent megakernel, section 2):
+//   event 4l+0  h1 = bf16(x . Wq^T)
+//   event 4l+1  h2 = bf16(h1 . Wo^T)
+//   event 4l+2  a  = bf16(silu(g) * u), [g|u] = h2 . Wgu^T  (gate column j and
+//               up column j are computed by the same wave, so the SiLU gate is
+//               applied in the epilogue and only a is written)
+//   event 4l+3  x' = bf16(a . Wdown^T)  (+ fp32 for the last layer)
+//
+// Completion of an event is published with two-level counters (Fleet reading
+// note, section 2b flowchart (b) and section 3d): every workgroup bumps its
+// XCD's counter L[x][e] (the 32 workgroups of an XCD share one L2, so no
+// write-back is needed between them); the workgroup that brings L[x][e] to 32
+// writes the XCD's L2 back (device-scope release) and bumps the global G[e].
+// Consumers wait for G[e] == 8.  With SGEMM_F_SYNC_FLAT every workgroup does
+// the release and bumps G[e] (target = grid), flowchart (a).
+//
+// Before waiting, a workgroup already has the first weight steps of the next
+// stage in flight (weights do not depend on the activations).  Every wait is
+// bounded by a wall-clock budget; on expiry the time-out bit is latched in
+// the status word and the workgroup stops, so a broken schedule ends the
+// launch instead of hanging it.  The last workgroup to finish resets every
+// counter for the next launch.
+#include <hip/hip_runtime.h>
+
+#include "gemm_device.h"
+#include "launch.h"
+
+namespace sg {
+
+constexpr int kChainRing = 2;
+
+__device__ __forceinline__ unsigned long long now_ticks() { return wall_clock64(); }
+
+struct ChainState {
+  const ChainArgs* a;
+  int* alive;       // LDS flag shared by the workgroup
+  int xcd, nslots;
+};
+
+// Wait until event e is complete (all producers published).  Executed by the
+// whole workgroup; returns false when the wait timed out (here or elsewhere).
+__device__ bool wait_event(const ChainArgs& a, int e, int* sh_alive) {
+  if (threadIdx.x == 0) {
+    const unsigned target = a.flat_sync ? gridDim.x : (unsigned)kXcds;
+    int ok = 1;
+    const unsigned long long t0 = now_ticks();
+    while (__hip_atomic_load(a.gctr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if ((long long)(now_ticks() - t0) > a.spin_ticks ||
+          (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout)) {
+        __hip_atomic_fetch_or(a.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *sh_alive = ok;
+  }
+  __syncthreads();
+  return *sh_alive != 0;
+}
+
+// Publish that this workgroup finished event e.
+__device__ void signal_event(const ChainArgs& a, int e, int xcd, int nslots) {
+  wait_vm0();  // this wave's stores are acknowledged by L2
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (a.flat_sync) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(a.gctr + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const int events = 4 * a.n_layers;
+      const unsigned old =
+          __hip_atomic_fetch_add(a.lctr + xcd * events + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == (unsigned)(nslots - 1)) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // write this XCD's L2 back
+        __hip_atomic_fetch_add(a.gctr + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+__device__ void stamp(const ChainArgs& a, int e, int which) {
+  if (a.stamps && threadIdx.x == 0) {
+    const int events = 4 * a.n_layers;
+    a.stamps[((size_t)blockIdx.x * events + e) * 2 + which] = now_ticks();
+  }
+}
+
+template <int MT, int NT>
+__global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  __shared__ int sh_alive;
+  __shared__ int sh_last;
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int nslots = gridDim.x >> 3;
+  check_topology(a.status);
+  bool alive = true;
+  for (int l = 0; l < a.n_layers && alive; ++l) {
+    uint16_t* act = a.act + (size_t)l * a.act_layer_elems;
+    const uint16_t* xin = l == 0 ? a.x0 : a.act + (size_t)(l - 1) * a.act_layer_elems + a.off_x;
+    for (int s = 0; s < kChainStages && alive; ++s) {
+      const int e = 4 * l + s;
+      StageDesc d = a.st[s];
+      if (s == 0) { d.X = xin; d.W = a.wq[l]; d.Y = act + a.off_h1; }
+      if (s == 1) { d.X = act + a.off_h1; d.W = a.wo[l]; d.Y = act + a.off_h2; }
+      if (s == 2) { d.X = act + a.off_h2; d.W = a.wgu[l]; d.Y = act + a.off_a; }
+      if (s == 3) {
+        d.X = act + a.off_a; d.W = a.wdown[l]; d.Y = act + a.off_x;
+        if (l == a.n_layers - 1) { d.mode = OUT_BF16_F32; d.Y2 = a.y_f32; }
+      }
+      auto hook = [&]() -> bool {
+        const bool ok = e == 0 ? true : wait_event(a, e - 1, &sh_alive);
+        stamp(a, e, 0);
+        return ok;
+      };
+      // A workgroup without items in this stage still waits (its next stage
+      // needs this one) and still publishes.
+      const int n_my = d.items > slot ? 1 : 0;
+      if (n_my == 0) {
+        alive = hook();
+      } else {
+        if (s == 2) {
+          mfma_stage<MT, 2, kChainRing, true>(d, lds, xcd, slot, nslots, hook);
+        } else {
+          mfma_stage<MT, NT, kChainRing, false>(d, lds, xcd, slot, nslots, hook);
+        }
+        alive = sh_alive != 0 || e == 0;
+      }
+      if (!alive) break;
+      stamp(a, e, 1);
+      signal_event(a, e, xcd, nslots);
+      __syncthreads();  // LDS window reuse by the next stage
+    }
+  }
+  // Finish: the last workgroup resets all counters for the next launch.
+  wait_vm0();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned old = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = old == gridDim.x - 1;
+    if (sh_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  if (sh_last) {
+    const int events = 4 * a.n_layers;
+    for (int i = threadIdx.x; i < events; i += blockDim.x) a.gctr[i] = 0u;
+    for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) a.lctr[i] = 0u;
+    for (int s = 0; s < kChainStages; ++s) {
+      const int n = kXcds * a.st[s].NB * (a.st[s].CB / (s == 2 ? 16 : a.st[s].TN));
+      for (int i = threadIdx.x; i < n; i += blockDim.x) a.st[s].ctr[i] = 0u;
+    }
+    wait_vm0();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+typedef void (*ChainKernel)(ChainArgs);
+
+static ChainKernel chain_kernel(int mt, int nt) {
+  switch (mt * 4 + nt) {
+    case 1 * 4 + 1: return k_chain<1, 1>;
+    case 1 * 4 + 2: return k_chain<1, 2>;
+    case 2 * 4 + 1: return k_chain<2, 1>;
+    case 2 * 4 + 2: return k_chain<2, 2>;
+    case 3 * 4 + 1: return k_chain<3, 1>;
+    case 3 * 4 + 2: return k_chain<3, 2>;
+    case 4 * 4 + 1: return k_chain<4, 1>;
+    case 4 * 4 + 2: return k_chain<4, 2>;
+    default: return nullptr;
+  }
+}
+
+bool chain_variant_exists(int mt, int nt_q, int nt_o, int nt_d) {
+  return nt_q == nt_o && nt_o == nt_d && chain_kernel(mt, nt_q) != nullptr;
+}
+
+hipError_t launch_chain(const ChainArgs& a, int grid, int block, int lds, hipStream_t stream) {
+  ChainKernel k = chain_kernel(a.mt, a.nt_q);
+  if (!k) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(block), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace sg

@@ -1,0 +1,44 @@
+// Host-side entry points of the kernel translation units, used by the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "stage_desc.h"
+
+namespace sg {
+
+constexpr int kMaxLayers = 64;
+constexpr int kChainStages = 4;  // Q, O, gate_up (paired, SiLU-gated), down
+
+struct ChainArgs {
+  StageDesc st[kChainStages];          // operands other than W/X/Y are filled per layer
+  const uint16_t* wq[kMaxLayers];
+  const uint16_t* wo[kMaxLayers];
+  const uint16_t* wgu[kMaxLayers];
+  const uint16_t* wdown[kMaxLayers];
+  const uint16_t* x0;                  // [M][d] bf16
+  uint16_t* act;                       // per-layer activations, see layout below
+  float* y_f32;                        // last layer's down projection, fp32
+  uint16_t* y_bf16;                    // its bf16 rounding (may be null)
+  unsigned* status;                    // workspace word 0
+  unsigned* lctr;                      // [kXcds][events] intra-XCD event counters
+  unsigned* gctr;                      // [events] global event counters
+  unsigned* done;                      // workgroups finished (reset by the last one)
+  unsigned long long* stamps;          // [grid][events][2] or null
+  int n_layers, M, d, q, dff;
+  size_t act_layer_elems;              // bf16 elements per layer of activations
+  size_t off_h1, off_h2, off_a, off_x; // element offsets inside one layer's block
+  int flat_sync;                       // every workgroup publishes globally
+  long long spin_ticks;                // watchdog budget (wall-clock ticks, 100 MHz)
+  int mt, nt_q, nt_o, nt_d;            // tile template parameters (MFMA path)
+};
+
+bool gemm_variant_exists(int path, int a, int b);
+hipError_t launch_gemm(const StageDesc& d, int path, int a, int b, int grid, int block, int lds,
+                       unsigned* status, hipStream_t stream);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+hipError_t launch_topology(int* out, int n, hipStream_t stream);
+
+bool chain_variant_exists(int mt, int nt_q, int nt_o, int nt_d);
+hipError_t launch_chain(const ChainArgs& a, int grid, int block, int lds, hipStream_t stream);
+
+}  // namespace sg

@@ -1,0 +1,51 @@
+// One GEMM "stage" as the device sees it: operands, the per-XCD column
+// partition and the split-K decomposition chosen by the planner.  Plain POD,
+// passed by value as a kernel argument (and as an array of them to the chain
+// kernel).
+#pragma once
+#include <stdint.h>
+
+namespace sg {
+
+constexpr int kXcds = 8;            // XCDs (chiplets) of an MI355X in SPX mode
+constexpr int kDot2KStep = 512;     // K values one dot2 wave step covers (64 lanes x 8)
+constexpr int kMfmaKStep = 64;      // K values one MFMA wave step covers (2 x 32)
+constexpr int kMaxWaves = 8;        // waves per workgroup (512 threads)
+
+enum OutMode : int {
+  OUT_F32 = 0,       // Y fp32
+  OUT_BF16 = 1,      // Y bf16 (RNE)
+  OUT_SILU_BF16 = 2, // paired gate/up tile: Y = bf16(silu(g) * u)
+  OUT_BF16_F32 = 3   // Y bf16 and Y2 fp32 (the chain's last down projection)
+};
+
+enum SyncMode : int { SYNC_AGENT = 0, SYNC_XCD = 1 };
+
+struct StageDesc {
+  const uint16_t* X;   // activations, row-major [M][ldx]
+  const uint16_t* W;   // weights, K-major [rows][K]
+  void* Y;             // output, row-major [M][ldy]
+  void* Y2;            // second output (OUT_BF16_F32), same layout, fp32
+  float* part;         // split-K partials of this stage
+  unsigned* ctr;       // split-K arrival counters of this stage (one per wave tile)
+  int M, K, N;         // N = output columns (gate columns when paired)
+  int ldx, ldy;
+  int Nx;              // columns owned by one XCD (XCD x: [x*Nx, min(N,(x+1)*Nx)))
+  int TN;              // columns per wave tile
+  int CB;              // columns per workgroup item = waves * TN
+  int NB;              // column blocks per XCD
+  int S;               // K splits
+  int KS;              // K values per split (multiple of 8)
+  int steps;           // wave k-steps per item
+  int items;           // items per XCD = NB * S (ordered split-major)
+  int win;             // LDS window width (elements) = steps * kstep
+  int xrow;            // LDS row stride (elements)
+  int pair_off;        // paired: weight row offset of the up half
+  int mode;            // OutMode
+  int sync;            // SyncMode of the split-K arrival
+  unsigned w_aux;      // cache-policy bits of the weight loads
+  unsigned x_bytes, w_bytes, y_bytes, y2_bytes;  // operand extents (buffer bounds)
+  unsigned part_bytes;                           // extent of the partial buffer
+};
+
+}  // namespace sg

@@ -1,0 +1,178 @@
+/*
+ * sgemm.h -- small-M decode GEMM and persistent per-layer projection chain on
+ * AMD Instinct MI355X (gfx950).  C ABI of libsgemm.so.
+ *
+ * The operation (Fleet, "Hierarchical Task-based Abstraction for Megakernels
+ * on Multi-Die GPUs", reading note: Summary, section 3f notation table and
+ * section 4; restated for MI355X by the news item "ROCm Low-Latency-GEMM-
+ * Kernel ... bis zu 1,79x auf Instinct MI355X", section "Was ist GEMM"):
+ *
+ *     Y[M,N] = X[M,K] . W[K,N]       bf16 inputs, fp32 accumulation,
+ *                                    M = 1..64 (the decode batch),
+ *                                    K and N in the thousands.
+ *
+ * Layouts (all dense, no padding):
+ *   X  row-major [M][K] bf16            (row m at X + m*K)
+ *   W  K-major   [N][K] bf16            (output column n is the contiguous run
+ *                                        W + n*K, the layout the per-chiplet
+ *                                        weight pointer base + k*(N/8)*K*2
+ *                                        presupposes; nn.Linear's layout)
+ *   Y  row-major [M][N] fp32 or bf16
+ *
+ * Ownership: the caller allocates and owns every device buffer (X, W, Y and the
+ * workspace).  A plan owns only host-side metadata.  No call allocates device
+ * memory, except sgemm_topology_probe, which does not either (it writes into a
+ * caller buffer).
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ * sgemm_run and layerchain_run enqueue work and return; they never
+ * synchronise.  Errors detected on the device (watchdog time-out, XCD mapping
+ * mismatch) are latched in the workspace status word and reported by
+ * sgemm_query_status.
+ *
+ * Errors: every call returns an sgemm_status; nothing throws across the ABI.
+ * Argument errors are detected before anything is enqueued.
+ */
+#ifndef SGEMM_H
+#define SGEMM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sgemm_plan_s* sgemm_plan;
+
+typedef enum {
+  SGEMM_OK = 0,
+  SGEMM_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad flag  */
+  SGEMM_ERR_UNSUPPORTED = -2, /* valid but outside what is built (e.g. M>64)  */
+  SGEMM_ERR_HIP = -3,         /* a HIP runtime call failed                    */
+  SGEMM_ERR_TIMEOUT = -4,     /* a device-side bounded wait expired           */
+  SGEMM_ERR_WORKSPACE = -5,   /* workspace too small / not initialised        */
+  SGEMM_ERR_TOPOLOGY = -6     /* a workgroup ran on another XCD than planned  */
+} sgemm_status;
+
+enum { SGEMM_KIND_GEMM = 0, SGEMM_KIND_LAYERCHAIN = 1 };
+enum { SGEMM_OUT_F32 = 0, SGEMM_OUT_BF16 = 1 };
+
+/* Plan flags (bitwise OR). */
+enum {
+  SGEMM_F_FORCE_DOT2 = 1u << 0,  /* use the VALU dot2 path whatever M is        */
+  SGEMM_F_FORCE_MFMA = 1u << 1,  /* use the MFMA path whatever M is             */
+  SGEMM_F_W_CACHED = 1u << 2,    /* weight loads without the nontemporal hint    */
+  SGEMM_F_SYNC_FLAT = 1u << 3,   /* chain: every workgroup publishes globally     */
+  SGEMM_F_SYNC_AGENT = 1u << 4,  /* split-K: device-scope release/acquire instead
+                                    of the XCD-local (same-L2) protocol          */
+  SGEMM_F_STAMPS = 1u << 5,      /* chain: record per-workgroup stage timestamps  */
+  SGEMM_F_WATCHDOG_TEST = 1u << 6, /* chain: spin budget of zero, to exercise the
+                                      time-out path from the host               */
+  SGEMM_F_W_SC1 = 1u << 7        /* weight loads with sc1|nt (streaming)         */
+};
+
+/*
+ * Problem description.
+ *   kind = SGEMM_KIND_GEMM:       M, K, N, out_dtype.
+ *   kind = SGEMM_KIND_LAYERCHAIN: M, n_layers, d_model, q_cols, d_ff.  Per layer
+ *       (Fleet reading note, sections 3f and 7b: gate and up concatenated and
+ *       SiLU-gated; one decoder layer's projections back to back):
+ *         h1 = bf16(x . Wq^T)  h2 = bf16(h1 . Wo^T)  [g|u] = h2 . Wgu^T
+ *         a = bf16(silu(g) * u)  x' = bf16(a . Wdown^T)
+ *       with Wq [q_cols][d_model], Wo [d_model][q_cols], Wgu [2 d_ff][d_model]
+ *       (g = rows 0..d_ff-1, u = rows d_ff..2 d_ff-1), Wdown [d_model][d_ff],
+ *       all K-major.
+ *   tn, splitk, waves: 0 lets the planner choose; otherwise they override the
+ *       columns per wave tile, the K split count and the waves per workgroup.
+ */
+typedef struct {
+  int kind;
+  int M, K, N;
+  int out_dtype;
+  int n_layers, d_model, q_cols, d_ff;
+  unsigned flags;
+  int tn, splitk, waves;
+} sgemm_problem;
+
+/*
+ * Build a plan for device `device` (a HIP ordinal).  Validates the problem,
+ * chooses the path (dot2 for M < 16, MFMA for M >= 16, unless forced), the
+ * per-XCD column partition, tile widths, split-K count and workspace layout.
+ * *workspace_bytes receives the size of the device workspace the runs need
+ * (>= 4 KiB).  Shape rules: 1 <= M <= 64; K >= 8, K % 8 == 0; N >= 1; every
+ * operand below 4 GiB.  Returns SGEMM_ERR_INVALID_ARG or
+ * SGEMM_ERR_UNSUPPORTED without creating a plan when they are violated.
+ */
+int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
+                      size_t* workspace_bytes);
+
+/* Release a plan (host memory only).  NULL is accepted. */
+int sgemm_plan_destroy(sgemm_plan plan);
+
+/*
+ * Zero a workspace of plan's size with a fill kernel on `stream`.  Must be
+ * called once after allocation (a zero-filled allocation is equivalent).
+ * Afterwards the runs keep it consistent themselves (split-K tile counters are
+ * reset by their last arriver; chain counters by the last workgroup to
+ * finish).  A workspace belongs to one plan and must not be used by two runs
+ * that can overlap in time.
+ */
+int sgemm_workspace_init(sgemm_plan plan, void* workspace, void* stream);
+
+/*
+ * Y = X . W (kind GEMM).  X [M][K] bf16, W [N][K] bf16, Y [M][N] (fp32 or bf16
+ * as planned); all device pointers, 16-byte aligned.  Enqueues one kernel on
+ * `stream` and returns.
+ */
+int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* workspace,
+              void* stream);
+
+/*
+ * The whole layer chain in one persistent launch (kind LAYERCHAIN).
+ * X0 [M][d_model] bf16 device pointer.  Wq, Wo, Wgu, Wdown are HOST arrays of
+ * n_layers DEVICE pointers each (layouts above).  Y_f32 [M][d_model] receives
+ * the last layer's down projection before rounding; Y_bf16 (may be NULL) its
+ * bf16 rounding.  Intermediate activations stay in the workspace (see
+ * sgemm_chain_buffer).  Enqueues one kernel and returns.
+ */
+int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq,
+                   const void* const* Wo, const void* const* Wgu, const void* const* Wdown,
+                   float* Y_f32, void* Y_bf16, void* workspace, void* stream);
+
+/*
+ * Where the chain keeps an intermediate activation in the workspace:
+ * which = 0 h1 [M][q_cols], 1 h2 [M][d_model], 2 a [M][d_ff], 3 x' [M][d_model]
+ * (all bf16, row-major) of layer `layer`.  Valid after the run has completed.
+ */
+int sgemm_chain_buffer(sgemm_plan plan, int layer, int which, size_t* offset, size_t* bytes);
+
+/*
+ * Synchronise `stream`, read and clear the workspace status word and return the
+ * first device-side error latched since the last query (SGEMM_OK if none).
+ */
+int sgemm_query_status(sgemm_plan plan, void* workspace, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* sgemm_status_string(int status);
+
+/*
+ * JSON description of the plan (path, tiles, split-K, waves, grid, workspace
+ * layout) written into buf (NUL-terminated, truncated to len).  Returns the
+ * length needed.
+ */
+int sgemm_plan_describe(sgemm_plan plan, char* buf, size_t len);
+
+/*
+ * Topology probe: launch n_wg workgroups of one wave; workgroup i writes the
+ * XCC id it ran on (the HW_REG_XCC_ID field) to xcc_out[i] (device int array
+ * of n_wg entries).  Enqueues on `stream`; used to confirm the round-robin
+ * workgroup-to-XCD dispatch the per-XCD partition relies on (Fleet reading
+ * note, section 3b: default dispatch spreads workgroups round-robin over the
+ * XCDs, and the runtime reads the hardware id to learn its XCD).
+ */
+int sgemm_topology_probe(int* xcc_out, int n_wg, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SGEMM_H */

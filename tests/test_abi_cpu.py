@@ -1,0 +1,146 @@
+"""CPU-side checks of the C ABI and the host logic: the library loads, exports
+every function the header declares, rejects bad arguments before enqueuing
+anything, and the planner's decompositions cover every output column and K
+value exactly once.  No GPU is needed (plan creation does not touch HIP)."""
+import json
+import math
+import os
+
+import pytest
+
+import chiplet_aware_persistent_amd as sg
+from chiplet_aware_persistent_amd import model
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sg.LIB_PATH), reason="libsgemm.so not built")
+
+
+def test_exports_every_header_function():
+    names = sg.header_functions()
+    assert len(names) >= 10
+    lib = sg.library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _create(**kw):
+    p = sg.Problem(kw.get("kind", sg.KIND_GEMM), kw.get("M", 1), kw.get("K", 64), kw.get("N", 64),
+                   kw.get("out", sg.OUT_F32), kw.get("L", 0), kw.get("d", 0), kw.get("q", 0), kw.get("dff", 0),
+                   kw.get("flags", 0), kw.get("tn", 0), kw.get("splitk", 0), kw.get("waves", 0))
+    rc, h, ws = sg.sgemm_plan_create(p)
+    if h:
+        sg.sgemm_plan_destroy(h)
+    return rc
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), sg.ERR_INVALID_ARG),
+    (dict(M=65), sg.ERR_UNSUPPORTED),
+    (dict(K=12), sg.ERR_INVALID_ARG),
+    (dict(K=0), sg.ERR_INVALID_ARG),
+    (dict(N=0), sg.ERR_INVALID_ARG),
+    (dict(out=7), sg.ERR_INVALID_ARG),
+    (dict(flags=sg.F_FORCE_DOT2 | sg.F_FORCE_MFMA), sg.ERR_INVALID_ARG),
+    (dict(waves=3), sg.ERR_INVALID_ARG),
+    (dict(splitk=65), sg.ERR_UNSUPPORTED),
+    (dict(kind=9), sg.ERR_INVALID_ARG),
+    (dict(K=1 << 20, N=1 << 12), sg.ERR_UNSUPPORTED),
+    (dict(kind=sg.KIND_LAYERCHAIN, M=4, L=0, d=64, q=64, dff=64), sg.ERR_INVALID_ARG),
+    (dict(kind=sg.KIND_LAYERCHAIN, M=4, L=2, d=60, q=64, dff=64), sg.ERR_INVALID_ARG),
+    (dict(kind=sg.KIND_LAYERCHAIN, M=4, L=65, d=64, q=64, dff=64), sg.ERR_UNSUPPORTED),
+    (dict(kind=sg.KIND_LAYERCHAIN, M=65, L=2, d=64, q=64, dff=64), sg.ERR_UNSUPPORTED),
+    (dict(M=1, K=8, N=1), sg.OK),
+    (dict(M=64, K=12288, N=4096), sg.OK),
+])
+def test_plan_create_validation(kw, code):
+    assert _create(**kw) == code
+
+
+def test_null_and_misaligned_arguments_rejected_before_launch():
+    lib = sg.library()
+    assert lib.sgemm_plan_create(None, 0, None, None) == sg.ERR_INVALID_ARG
+    g = sg.Gemm(4, 256, 128)
+    h = g.handle
+    assert sg.sgemm_run(h, 0, 16, 16, 16) == sg.ERR_INVALID_ARG
+    assert sg.sgemm_run(h, 16, 0, 16, 16) == sg.ERR_INVALID_ARG
+    assert sg.sgemm_run(h, 16, 16, 16, 0) == sg.ERR_INVALID_ARG
+    assert sg.sgemm_run(h, 18, 16, 16, 16) == sg.ERR_INVALID_ARG   # misaligned X
+    assert sg.sgemm_run(h, 16, 24, 16, 16) == sg.ERR_INVALID_ARG   # misaligned W
+    assert sg.sgemm_run(None, 16, 16, 16, 16) == sg.ERR_INVALID_ARG
+    assert sg.layerchain_run(h, 16, [16], [16], [16], [16], 16, 0, 16) == sg.ERR_INVALID_ARG  # kind
+    assert sg.sgemm_workspace_init(h, 0) == sg.ERR_INVALID_ARG
+    assert lib.sgemm_topology_probe(None, 4, None) == sg.ERR_INVALID_ARG
+    assert sg.status_string(sg.ERR_TIMEOUT) == "device wait timed out"
+
+
+SHAPES = [(1, 1024, 1024), (1, 4096, 6144), (1, 4096, 4096), (1, 4096, 24576), (1, 12288, 4096),
+          (8, 4096, 6144), (16, 4096, 4096), (32, 4096, 24576), (64, 12288, 4096), (1, 7168, 1536),
+          (2, 7168, 4096), (16, 7168, 18432), (3, 520, 1000), (17, 776, 530), (5, 8, 17), (64, 8, 1)]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+@pytest.mark.parametrize("splitk", [0, 3])
+def test_planner_covers_every_column_and_k_once(M, K, N, splitk):
+    try:
+        g = sg.Gemm(M, K, N, splitk=splitk)
+    except sg.SgemmError as e:
+        # a forced split count whose X window exceeds the LDS budget is refused
+        assert splitk and e.code == sg.ERR_UNSUPPORTED
+        return
+    st = g.describe()["stage"]
+    assert st["path"] == ("dot2" if M < 16 else "mfma")
+    Nx, CB, NB, S, KS = st["Nx"], st["CB"], st["NB"], st["S"], st["KS"]
+    assert CB == st["waves"] * st["TN"]
+    assert 8 * Nx >= N and 8 * (Nx - 16) < N          # per-XCD partition covers N, no spare XCD block
+    assert NB * CB >= Nx                               # column blocks cover the XCD's columns
+    assert S * KS >= K and (S - 1) * KS < K            # splits cover K, none empty
+    assert KS % 8 == 0 and st["items"] == NB * S
+    kstep = 512 if st["path"] == "dot2" else 64
+    assert st["steps"] * kstep >= KS
+    assert st["lds"] <= 64 * 1024
+    if splitk:
+        assert S == min(splitk, math.ceil(K / 8)) or S == math.ceil(K / math.ceil(K / splitk / 8) / 8)
+    # columns: every column owned by exactly one (xcd, block, wave, lane-column)
+    owned = set()
+    for x in range(8):
+        for b in range(NB):
+            for c in range(CB):
+                col = x * Nx + b * CB + c
+                if x * Nx + b * CB + c < min(N, (x + 1) * Nx) and b * CB + c < Nx:
+                    assert col not in owned
+                    owned.add(col)
+    assert owned == set(range(N))
+
+
+def test_chain_plan_and_buffers():
+    c = sg.LayerChain(64, 36, 4096, 4096, 12288)
+    d = c.describe()
+    assert d["kind"] == "layerchain" and len(d["stages"]) == 4
+    assert d["stages"][2]["paired"] == 1 and d["stages"][2]["N"] == 12288
+    spans = []
+    for l in (0, 17, 35):
+        for w in range(4):
+            rc, off, nb = sg.sgemm_chain_buffer(c.handle, l, w)
+            assert rc == 0 and off + nb <= c.workspace_bytes and off % 16 == 0
+            spans.append((off, off + nb))
+    spans.sort()
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    assert sg.sgemm_chain_buffer(c.handle, 36, 0)[0] == sg.ERR_INVALID_ARG
+    assert sg.sgemm_chain_buffer(c.handle, 0, 4)[0] == sg.ERR_INVALID_ARG
+
+
+def test_eq1_matches_the_pages_table():
+    g = json.load(open(os.path.join(GOLD, "eq1_l2_hit.json")))
+    for row in g["rows"]:
+        assert model.eq1_hit(row["B"], W=g["W"], T_M=g["T_M"]) == pytest.approx(row["predicted_hit"])
+    assert model.eq1_hit(10 ** 6, W=g["W"]) == pytest.approx(g["limit_hit_W31"], abs=1e-4)
+    ex = g["ai_eff_example"]
+    assert model.ai_eff(ex["B"], ex["hit"]) == pytest.approx(ex["ai_eff_approx"], rel=0.02)
+
+
+def test_roofline_floors():
+    # 2*K*N bytes at 8 TB/s: QKV 4096x6144 -> 6.29 us, down 12288x4096 -> 12.58 us
+    assert model.floor_us(4096, 6144) == pytest.approx(6.29, abs=0.01)
+    assert model.floor_us(12288, 4096) == pytest.approx(12.58, abs=0.01)
+    assert model.ridge_flop_per_byte() == pytest.approx(312.5)

@@ -1,0 +1,186 @@
+"""GPU parity of the persistent layer chain (layerchain_run) against the CPU
+oracle, plus structural race checks (stage timestamps, bitwise repeatability,
+flat vs two-level publication) and the watchdog path.
+
+Tolerance of a chained stage.  The first stage sees exact inputs and gets the
+stated bound 2e-3*sum|x w| + 1e-6 (+1 bf16 ulp of the reference output).  A
+later stage's GPU inputs differ from the oracle's by a known elementwise
+amount E (both are rounded results of the previous stage), which can move
+the output by at most sum_k |E_k| |w_k|; that term is added.  For the SiLU
+gate a = silu(g) u, with |silu'| <= 1.1 on the reals,
+|da| <= 1.1 |dg| (|u| + |du|) + (|silu(g)| + 1.1 |dg|) |du| (+ fp32 evaluation
+error 2^-20 |a| and one bf16 ulp of a).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import chiplet_aware_persistent_amd as sg
+import oracle
+import synth
+from helpers import device_tensor_bf16, host_bits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+special = pytest.importorskip("scipy.special")
+
+
+def f64(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def make_chain(M, L, d, q, dff, seed, dev):
+    layers = []
+    for l in range(L):
+        layers.append((synth.uniform_bf16(seed + 16 * l + 1, q, d, synth.weight_scale(d)),
+                       synth.uniform_bf16(seed + 16 * l + 2, d, q, synth.weight_scale(q)),
+                       synth.uniform_bf16(seed + 16 * l + 3, 2 * dff, d, synth.weight_scale(d)),
+                       synth.uniform_bf16(seed + 16 * l + 4, d, dff, synth.weight_scale(dff))))
+    x0 = synth.normal_bf16(seed, M, d)
+    dev_layers = [[device_tensor_bf16(w, dev) for w in ws] for ws in layers]
+    return x0, layers, device_tensor_bf16(x0, dev), dev_layers
+
+
+def run_chain(ch, X0, dl, ws=None, bf16=True):
+    Y = torch.empty((ch.M, ch.d), dtype=torch.float32, device=X0.device)
+    Yb = torch.empty((ch.M, ch.d), dtype=torch.bfloat16, device=X0.device) if bf16 else None
+    if ws is None:
+        ws = ch.new_workspace()
+    ch(X0, [w[0] for w in dl], [w[1] for w in dl], [w[2] for w in dl], [w[3] for w in dl], Y, ws, Y_bf16=Yb)
+    rc = ch.status(ws)
+    return rc, Y, Yb, ws
+
+
+def stage_bound(x_gpu, x_ref, w_bits):
+    """(y_ref, bound) for Y = X W^T, inputs differing by E = x_gpu - x_ref."""
+    y_ref, absdot = oracle.gemm(x_ref, w_bits)
+    e = np.abs(f64(x_gpu) - f64(x_ref))
+    prop = e @ np.abs(f64(w_bits)).T
+    return y_ref, oracle.REL_TOL * absdot + prop + oracle.ABS_TOL
+
+
+def check_chain(ch, ws, x0, layers, Y, Yb, M):
+    outs = oracle.chain(x0, layers)
+    x_in_gpu, x_in_ref = x0, x0
+    worst = 0.0
+    dff = ch.dff
+    for l, ((wq, wo, wgu, wdown), r) in enumerate(zip(layers, outs)):
+        got = [host_bits(ch.activation(ws, l, w)) for w in range(4)]
+        # Q and O
+        for (src_gpu, src_ref, w, name, idx) in ((x_in_gpu, x_in_ref, wq, "h1", 0), (got[0], r["h1"], wo, "h2", 1)):
+            _, b = stage_bound(src_gpu, src_ref, w)
+            ref = f64(r[name])
+            b = b + oracle.bf16_ulp(ref)
+            err = np.abs(f64(got[idx]) - ref)
+            assert np.all(err <= b), (l, name, float(np.max(err / b)))
+            worst = max(worst, float(np.max(err / b)))
+        # gate_up + SiLU
+        gu_ref, bgu = stage_bound(got[1], r["h2"], wgu)
+        g, u = gu_ref[:, :dff].astype(np.float32).astype(np.float64), gu_ref[:, dff:].astype(np.float32).astype(np.float64)
+        bg, bu = bgu[:, :dff], bgu[:, dff:]
+        a_ref = f64(r["a"])
+        ba = (1.1 * bg * (np.abs(u) + bu) + (np.abs(g * special.expit(g)) + 1.1 * bg) * bu
+              + 2.0 ** -20 * np.abs(a_ref) + oracle.bf16_ulp(a_ref))
+        err = np.abs(f64(got[2]) - a_ref)
+        assert np.all(err <= ba), (l, "a", float(np.max(err / ba)))
+        worst = max(worst, float(np.max(err / ba)))
+        # down
+        y_ref, b = stage_bound(got[2], r["a"], wdown)
+        xo = f64(r["x_out"])
+        err = np.abs(f64(got[3]) - xo)
+        assert np.all(err <= b + oracle.bf16_ulp(xo)), (l, "x_out")
+        if l == len(layers) - 1:
+            assert np.all(np.abs(Y.cpu().numpy().astype(np.float64) - y_ref) <= b)
+            assert np.array_equal(host_bits(Yb), got[3])
+        x_in_gpu, x_in_ref = got[3], r["x_out"]
+    return worst
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 33, 64])
+def test_chain_small_parity(cuda_device, M):
+    L, d, q, dff = 3, 256, 128, 384
+    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x1000 + M, cuda_device)
+    ch = sg.LayerChain(M, L, d, q, dff)
+    rc, Y, Yb, ws = run_chain(ch, X0, dl)
+    assert rc == sg.OK, sg.status_string(rc)
+    check_chain(ch, ws, x0, layers, Y, Yb, M)
+
+
+@pytest.mark.parametrize("M,L,d,q,dff", [(64, 2, 1024, 1024, 3072), (8, 4, 512, 256, 1536), (64, 1, 4096, 4096, 12288)])
+def test_chain_wider_parity(cuda_device, M, L, d, q, dff):
+    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x2000 + M + L, cuda_device)
+    ch = sg.LayerChain(M, L, d, q, dff)
+    rc, Y, Yb, ws = run_chain(ch, X0, dl)
+    assert rc == sg.OK, sg.status_string(rc)
+    check_chain(ch, ws, x0, layers, Y, Yb, M)
+
+
+def test_chain_one_hot_wiring(cuda_device):
+    """Identity Q/O, one-hot gate/up/down rows: x' = bf16(silu(x_p) x_q) selections."""
+    M, d, dff, L = 16, 64, 48, 2
+    rng = np.random.default_rng(3)
+    eye = synth.f32_to_bf16_bits(np.eye(d, dtype=np.float32))
+    layers = []
+    for l in range(L):
+        p, qq, sel = rng.integers(0, d, dff), rng.integers(0, d, dff), rng.integers(0, dff, d)
+        wgu = np.zeros((2 * dff, d), np.float32)
+        wgu[np.arange(dff), p] = 1.0
+        wgu[dff + np.arange(dff), qq] = 1.0
+        wd = np.zeros((d, dff), np.float32)
+        wd[np.arange(d), sel] = 1.0
+        layers.append((eye, eye, synth.f32_to_bf16_bits(wgu), synth.f32_to_bf16_bits(wd)))
+    x0 = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(synth.normal_bf16(5, M, d)) * np.float32(2.0))
+    dl = [[device_tensor_bf16(w, cuda_device) for w in ws] for ws in layers]
+    ch = sg.LayerChain(M, L, d, d, dff)
+    rc, Y, Yb, ws = run_chain(ch, device_tensor_bf16(x0, cuda_device), dl)
+    assert rc == sg.OK
+    outs = oracle.chain(x0, layers)
+    got0 = [host_bits(ch.activation(ws, 0, w)) for w in range(4)]
+    assert np.array_equal(got0[0], x0) and np.array_equal(got0[1], x0)
+    d_a = np.abs(got0[2].astype(np.int32) - outs[0]["a"].astype(np.int32))
+    assert d_a.max() <= 1 and np.mean(d_a == 0) > 0.95
+    assert np.array_equal(got0[3], got0[2][:, np.nonzero(layers[0][3])[1]])
+
+
+def test_chain_repeatable_and_sync_modes_agree(cuda_device):
+    M, L, d, q, dff = 64, 3, 512, 512, 1024
+    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x3000, cuda_device)
+    ch = sg.LayerChain(M, L, d, q, dff)
+    rc, Y1, _, ws = run_chain(ch, X0, dl)
+    rc2, Y2, _, _ = run_chain(ch, X0, dl, ws=ws)
+    assert rc == rc2 == sg.OK
+    assert torch.equal(Y1, Y2)
+    for flags in (sg.F_SYNC_FLAT, sg.F_SYNC_AGENT):
+        rc3, Y3, _, _ = run_chain(sg.LayerChain(M, L, d, q, dff, flags=flags), X0, dl)
+        assert rc3 == sg.OK
+        assert torch.equal(Y1, Y3)
+
+
+def test_chain_stamps_order_every_stage(cuda_device):
+    M, L, d, q, dff = 32, 4, 512, 256, 768
+    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x4000, cuda_device)
+    ch = sg.LayerChain(M, L, d, q, dff, flags=sg.F_STAMPS)
+    rc, Y, _, ws = run_chain(ch, X0, dl)
+    assert rc == sg.OK
+    info = ch.describe()
+    E = 4 * L
+    off = info["stamps_offset"]
+    st = ws[off:off + info["grid"] * E * 16].view(torch.int64).view(info["grid"], E, 2).cpu().numpy()
+    assert np.all(st[:, :, 1] >= st[:, :, 0])
+    for e in range(1, E):
+        assert st[:, e, 0].min() >= st[:, e - 1, 1].max(), e   # nobody starts e before all finished e-1
+
+
+def test_chain_watchdog_times_out_and_workspace_recovers(cuda_device):
+    M, L, d, q, dff = 16, 3, 256, 128, 384
+    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x5000, cuda_device)
+    bad = sg.LayerChain(M, L, d, q, dff, flags=sg.F_WATCHDOG_TEST)
+    good = sg.LayerChain(M, L, d, q, dff)
+    assert bad.workspace_bytes == good.workspace_bytes
+    rc, _, _, ws = run_chain(bad, X0, dl)
+    assert rc == sg.ERR_TIMEOUT
+    rc2, Y, Yb, _ = run_chain(good, X0, dl, ws=ws)
+    assert rc2 == sg.OK
+    check_chain(good, ws, x0, layers, Y, Yb, M)
