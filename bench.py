@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the small-M decode GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload proj|chain] [--sweep]
+
+Default workload ("proj"): the Qwen3-8B-shaped decode projections at M = 1
+(QKV 4096x6144, O 4096x4096, gate_up 4096x24576, down 12288x4096; 368 MiB of
+bf16 weights).  One step = one sgemm_run of each projection on one batch of
+synthetic input.  Weights rotate over enough copies (>= 1 GiB) that no launch
+finds its weights in the 256 MB Infinity Cache or the L2s: every step streams
+its weights from HBM.  ``value`` is weight bytes moved per second over the
+timed steps (GB/s); ``roofline`` reports the dominant kernel (gate_up) against
+the 8 TB/s HBM peak, its launch durations measured with HIP events on the
+launch stream; ``cpu_baseline`` is the CPU oracle on the same step.
+
+``--workload chain``: the 36-layer persistent chain at M = 64 (Q 4096x4096,
+O 4096x4096, gate_up 4096x24576 with SiLU gate, down 12288x4096 per layer;
+13.29 GB of weights) in one launch per step.
+
+Prints exactly one JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PROJ = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 24576), ("down", 12288, 4096)]
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chiplet_aware_persistent_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name: str):
+    """HBM traffic per launch from the committed rocprofv3 PMC summary, or None
+    when the kernels changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    if not os.path.exists(p):
+        return None
+    t = json.load(open(p))
+    if t.get("kernel_src_hash") != kernel_src_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline_proj(x_bits, w_host):
+    import oracle
+
+    t0 = time.perf_counter()
+    reps = 0
+    wbytes = 0
+    while True:
+        for (name, K, N), w in zip(PROJ, w_host):
+            oracle.gemm(x_bits[K], w, want_abs=False)
+            wbytes += 2 * K * N
+        reps += 1
+        if time.perf_counter() - t0 > 2.0 or reps >= 3:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d full step(s): all four projections, every output column, M=1, double accumulation"
+                      % reps}
+
+
+def bench_proj(args):
+    import numpy as np
+    import torch
+
+    import chiplet_aware_persistent_amd as sg
+    import synth
+
+    dev = torch.device("cuda:0")
+    M = 1
+    wbytes_step = sum(2 * K * N for _, K, N in PROJ)
+    copies = max(2, -(-(1 << 30) // wbytes_step))
+    log("proj: %d weight copies (%.1f MiB each set)" % (copies, wbytes_step / 2 ** 20))
+    W = []  # W[copy][proj]
+    for c in range(copies):
+        ws_ = []
+        for i, (name, K, N) in enumerate(PROJ):
+            seed = synth.seed_for(2, 0, 1 + i)
+            t = synth.uniform_bf16_torch(seed, N, K, synth.weight_scale(K), dev)
+            ws_.append(t)
+        W.append(ws_)
+    x_bits = {K: synth.normal_bf16(synth.seed_for(2, 0, synth.T_X, K % 16), M, K) for _, K, _ in PROJ}
+    X = {K: synth.to_torch_bf16(b, dev) for K, b in x_bits.items()}
+    plans = [sg.Gemm(M, K, N) for _, K, N in PROJ]
+    wss = [p.new_workspace() for p in plans]
+    Y = [torch.empty((M, N), dtype=torch.float32, device=dev) for _, _, N in PROJ]
+    stream = torch.cuda.current_stream()
+    h = int(stream.cuda_stream)
+    lib = sg.library()
+    ptrs = [[(plans[i].handle, X[K].data_ptr(), W[c][i].data_ptr(), Y[i].data_ptr(), wss[i].data_ptr())
+             for i, (_, K, _) in enumerate(PROJ)] for c in range(copies)]
+
+    def step(c, events=None):
+        for i, a in enumerate(ptrs[c]):
+            if events is not None:
+                events[i][0].record(stream)
+            rc = lib.sgemm_run(*a, h)
+            if rc:
+                raise sg.SgemmError(rc, "sgemm_run")
+            if events is not None:
+                events[i][1].record(stream)
+
+    for s in range(args.warmup):
+        step(s % copies)
+    torch.cuda.synchronize()
+    # timed region: K steps, wall clock
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(s % copies)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-kernel durations with HIP events (separate pass, same rotation)
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in PROJ]
+          for _ in range(args.steps)]
+    for s in range(args.steps):
+        step(s % copies, ev[s])
+    torch.cuda.synchronize()
+    per = {}
+    for i, (name, K, N) in enumerate(PROJ):
+        ts = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e3 for s in range(args.steps))  # us
+        med = ts[len(ts) // 2]
+        avg = sum(ts) / len(ts)
+        per[name] = {"K": K, "N": N, "us_median": round(med, 3), "us_avg": round(avg, 3),
+                     "us_p10": round(ts[len(ts) // 10], 3), "us_p90": round(ts[(9 * len(ts)) // 10], 3),
+                     "weight_GBps": round(2 * K * N / (med * 1e-6) / 1e9, 1),
+                     "plan": plans[i].describe()["stage"]}
+    for i, p in enumerate(plans):
+        rc = p.status(wss[i])
+        if rc:
+            raise sg.SgemmError(rc, "status")
+    ms_step = wall / args.steps * 1e3
+    value = wbytes_step / (wall / args.steps) / 1e9
+    dom = max(per, key=lambda k: per[k]["us_avg"])
+    K, N = per[dom]["K"], per[dom]["N"]
+    alg = 2 * K * N + 2 * M * K + 4 * M * N
+    achieved = alg / (per[dom]["us_avg"] * 1e-6) / 1e9
+    traffic = load_traffic("gemm_dot2_m1_gate_up")
+    out = {
+        "metric": "achieved HBM GB/s (weight bytes) and us per decode GEMM, M=1-64 bf16",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3_8b_decode_projections_m1", "M": M,
+                   "shapes_KxN": [[K_, N_] for _, K_, N_ in PROJ], "weight_bytes_per_step": wbytes_step,
+                   "cold_hbm_weight_copies": copies, "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "kernel": "sgemm dot2 %s %dx%d" % (dom, K, N),
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg, "avg_launch_us": per[dom]["us_avg"]},
+        "per_gemm": {k: {kk: v for kk, v in d.items() if kk != "plan"} for k, d in per.items()},
+        "plans": {k: {kk: d["plan"][kk] for kk in ("path", "waves", "TN", "S", "KS", "items")} for k, d in per.items()},
+    }
+    if not args.no_cpu:
+        w_host = [synth.from_torch_bf16(W[0][i]) for i in range(len(PROJ))]
+        out["cpu_baseline"] = cpu_baseline_proj(x_bits, w_host)
+    return out
+
+
+def bench_chain(args):
+    import torch
+
+    import chiplet_aware_persistent_amd as sg
+    import synth
+
+    dev = torch.device("cuda:0")
+    M, L, d, q, dff = 64, 36, 4096, 4096, 12288
+    wl = []
+    for l in range(L):
+        wl.append([synth.uniform_bf16_torch(synth.seed_for(5, l, 1), q, d, synth.weight_scale(d), dev),
+                   synth.uniform_bf16_torch(synth.seed_for(5, l, 2), d, q, synth.weight_scale(q), dev),
+                   synth.uniform_bf16_torch(synth.seed_for(5, l, 3), 2 * dff, d, synth.weight_scale(d), dev),
+                   synth.uniform_bf16_torch(synth.seed_for(5, l, 4), d, dff, synth.weight_scale(dff), dev)])
+    X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(5, 0, 0), M, d), dev)
+    ch = sg.LayerChain(M, L, d, q, dff)
+    ws = ch.new_workspace()
+    Y = torch.empty((M, d), dtype=torch.float32, device=dev)
+    wbytes = L * 2 * (q * d + d * q + 2 * dff * d + d * dff)
+    cols = [[w[i] for w in wl] for i in range(4)]
+    for _ in range(args.warmup):
+        ch(X0, *cols, Y, ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        ch(X0, *cols, Y, ws)
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rc = ch.status(ws)
+    if rc:
+        raise sg.SgemmError(rc, "chain status")
+    ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    avg = sum(ts) / len(ts)
+    value = wbytes / (wall / args.steps) / 1e9
+    achieved = wbytes / (avg * 1e-6) / 1e9
+    out = {
+        "metric": "achieved HBM GB/s (weight bytes) and us per decode GEMM, M=1-64 bf16",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "persistent_chain_36_layers_m64", "M": M, "layers": L, "d_model": d,
+                   "q_cols": q, "d_ff": dff, "weight_bytes_per_step": wbytes, "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "kernel": "k_chain", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic("chain_m64_36l"), "algorithmic_bytes_per_launch": wbytes,
+                     "avg_launch_us": round(avg, 2)},
+        "chain_us": {"median": round(ts[len(ts) // 2], 2), "min": round(ts[0], 2), "max": round(ts[-1], 2)},
+        "plan": [{k: st[k] for k in ("waves", "TN", "S", "KS", "items")} for st in ch.describe()["stages"]],
+    }
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["proj", "chain"], default="proj")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU shard of a "
+              "tensor-parallel layout is the same kernel at a narrower shape); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    out = bench_proj(args) if args.workload == "proj" else bench_chain(args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

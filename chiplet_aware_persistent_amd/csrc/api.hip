@@ -18,7 +18,7 @@ using namespace sg;
 namespace {
 
 constexpr size_t kCtl = 256;            // control block: status word, done counter
-constexpr int kLdsMax = 64 * 1024;      // LDS budget of one workgroup
+constexpr int kLdsMax = 128 * 1024;     // LDS budget of one workgroup (one per CU; 160 KB/CU)
 constexpr size_t kMaxOperand = (size_t)1 << 31;  // buffer extents are 31-bit here
 constexpr int kWgPerXcd = 32;           // one workgroup per CU, 32 CUs per XCD
 

@@ -185,6 +185,10 @@ bool chain_variant_exists(int mt, int nt_q, int nt_o, int nt_d) {
 hipError_t launch_chain(const ChainArgs& a, int grid, int block, int lds, hipStream_t stream) {
   ChainKernel k = chain_kernel(a.mt, a.nt_q);
   if (!k) return hipErrorInvalidValue;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k, dim3(grid), dim3(block), lds, stream, a);
   return hipGetLastError();
 }

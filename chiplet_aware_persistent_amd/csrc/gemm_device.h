@@ -96,12 +96,18 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + e) * u;
 }
 
-// acc + <w, x> over 8 bf16 pairs, four v_dot2_f32_bf16.
+// acc + <w, x> over 8 bf16 values, four v_dot2_f32_bf16.  The pairs are
+// built from a bf16x8 view: bit-casting the u4 elements one by one (w[i])
+// is lowered to four uses of dword 0 by this compiler.
 __device__ __forceinline__ float dot8(u4 w, u4 x, float acc) {
+  const bf16x8 a = __builtin_bit_cast(bf16x8, w);
+  const bf16x8 b = __builtin_bit_cast(bf16x8, x);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]),
-                                          __builtin_bit_cast(bf16x2, x[i]), acc, false);
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 p = {a[2 * i], a[2 * i + 1]};
+    const bf16x2 q = {b[2 * i], b[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, q, acc, false);
+  }
   return acc;
 }
 

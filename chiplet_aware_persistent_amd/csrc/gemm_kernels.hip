@@ -89,6 +89,10 @@ hipError_t launch_gemm(const StageDesc& d, int path, int a, int b, int grid, int
                        unsigned* status, hipStream_t stream) {
   GemmKernel k = path == 0 ? dot2_kernel(a, b) : mfma_kernel(a, b);
   if (!k) return hipErrorInvalidValue;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k, dim3(grid), dim3(block), lds, stream, d, status);
   return hipGetLastError();
 }
