@@ -8,7 +8,8 @@ Default workload ("proj"): the Qwen3-8B-shaped decode projections at M = 1
 bf16 weights).  One step = one sgemm_run of each projection on one batch of
 synthetic input.  Weights rotate over enough copies (>= 1 GiB) that no launch
 finds its weights in the 256 MB Infinity Cache or the L2s: every step streams
-its weights from HBM.  ``value`` is weight bytes moved per second over the
+its weights from HBM (the rotation spans >= 4 GiB: with only ~1 GiB some
+launches still hit the 256 MB Infinity Cache).  ``value`` is weight bytes moved per second over the
 timed steps (GB/s); ``roofline`` reports the dominant kernel (gate_up) against
 the 8 TB/s HBM peak, its launch durations measured with HIP events on the
 launch stream; ``cpu_baseline`` is the CPU oracle on the same step.
@@ -90,7 +91,7 @@ def bench_proj(args):
     dev = torch.device("cuda:0")
     M = 1
     wbytes_step = sum(2 * K * N for _, K, N in PROJ)
-    copies = max(2, -(-(1 << 30) // wbytes_step))
+    copies = max(2, -(-(4 << 30) // wbytes_step))
     log("proj: %d weight copies (%.1f MiB each set)" % (copies, wbytes_step / 2 ** 20))
     W = []  # W[copy][proj]
     for c in range(copies):
@@ -121,6 +122,14 @@ def bench_proj(args):
             if events is not None:
                 events[i][1].record(stream)
 
+    if args.copy_calibration:
+        # A plain device copy of known size, for scaling the FETCH_SIZE /
+        # WRITE_SIZE counters of a --pmc run (read 256 MiB, write 256 MiB).
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for s in range(args.warmup):
         step(s % copies)
     torch.cuda.synchronize()
@@ -130,20 +139,24 @@ def bench_proj(args):
         step(s % copies)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-kernel durations with HIP events (separate pass, same rotation)
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in PROJ]
-          for _ in range(args.steps)]
-    for s in range(args.steps):
-        step(s % copies, ev[s])
-    torch.cuda.synchronize()
+    # Per-kernel durations with HIP events on the launch stream: each
+    # projection launched back to back `steps` times (rotating weight copies)
+    # between two events; per-launch time = elapsed / steps.  Bracketing single
+    # launches would add the dispatch latency (~2-3 us) to every figure.
     per = {}
     for i, (name, K, N) in enumerate(PROJ):
-        ts = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e3 for s in range(args.steps))  # us
-        med = ts[len(ts) // 2]
-        avg = sum(ts) / len(ts)
-        per[name] = {"K": K, "N": N, "us_median": round(med, 3), "us_avg": round(avg, 3),
-                     "us_p10": round(ts[len(ts) // 10], 3), "us_p90": round(ts[(9 * len(ts)) // 10], 3),
-                     "weight_GBps": round(2 * K * N / (med * 1e-6) / 1e9, 1),
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a = ptrs[0][i]
+        e0.record(stream)
+        for s in range(args.steps):
+            rc = lib.sgemm_run(ptrs[s % copies][i][0], a[1], ptrs[s % copies][i][2], a[3], a[4], h)
+            if rc:
+                raise sg.SgemmError(rc, "sgemm_run")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg = e0.elapsed_time(e1) * 1e3 / args.steps  # us
+        per[name] = {"K": K, "N": N, "us_avg": round(avg, 3),
+                     "weight_GBps": round(2 * K * N / (avg * 1e-6) / 1e9, 1),
                      "plan": plans[i].describe()["stage"]}
     for i, p in enumerate(plans):
         rc = p.status(wss[i])
@@ -239,6 +252,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=["proj", "chain"], default="proj")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 256 MiB device copy first (counter calibration for --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU shard of a "

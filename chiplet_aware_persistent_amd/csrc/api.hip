@@ -18,7 +18,7 @@ using namespace sg;
 namespace {
 
 constexpr size_t kCtl = 256;            // control block: status word, done counter
-constexpr int kLdsMax = 128 * 1024;     // LDS budget of one workgroup (one per CU; 160 KB/CU)
+constexpr int kLdsMax = 160 * 1024;     // LDS budget of one workgroup (one per CU; 160 KB/CU)
 constexpr size_t kMaxOperand = (size_t)1 << 31;  // buffer extents are 31-bit here
 constexpr int kWgPerXcd = 32;           // one workgroup per CU, 32 CUs per XCD
 
@@ -30,7 +30,7 @@ struct Geo {
   int path = 0;        // 0 dot2, 1 MFMA
   int M = 0, K = 0, N = 0;
   int ta = 0, tb = 0;  // template parameters: dot2 (M, G); MFMA (MT, NT)
-  int waves = 8, TN = 0, CB = 0, Nx = 0, NB = 0, S = 1, KS = 0, steps = 0, items = 0;
+  int waves = 8, wpi = 8, ng = 1, TN = 0, CB = 0, Nx = 0, NB = 0, S = 1, KS = 0, steps = 0, items = 0;
   int win = 0, xrow = 0, lds = 0;
   int paired = 0, pair_off = 0;
   size_t ctr_count = 0, part_floats = 0;
@@ -47,29 +47,48 @@ int env_int(const char* name, int dflt) {
 bool shape_geo(Geo& g, int want_S) {
   const int kstep = g.path == 0 ? kDot2KStep : kMfmaKStep;
   g.TN = g.path == 0 ? g.tb : (g.paired ? 16 : 16 * g.tb);
-  g.CB = g.waves * g.TN;
+  g.ng = g.waves / g.wpi;
+  g.CB = g.wpi * g.TN;
   g.Nx = (int)round_up((size_t)ceil_div(g.N, kXcds), 16);
   g.NB = ceil_div(g.Nx, g.CB);
   g.KS = (int)round_up((size_t)ceil_div(g.K, want_S), 8);
   g.S = ceil_div(g.K, g.KS);
-  g.steps = ceil_div(g.KS, kstep);
-  g.win = g.steps * kstep;
+  const int ring = g.path == 0 ? ring_depth_dot2(g.tb) : ring_depth_mfma(g.paired ? 2 : g.tb);
+  g.steps = ceil_div(ceil_div(g.KS, kstep), ring) * ring;  // padded to the ring depth
+  g.items = g.NB * g.S;
+  // A workgroup stages X once for all splits its contiguous item range
+  // touches: the window is (span - 1) splits plus one item's padded steps.
+  int span = 1;
+  for (int w = 0; w < kWgPerXcd; ++w) {
+    const int i0 = (int)((long long)g.items * w / kWgPerXcd);
+    const int i1 = (int)((long long)g.items * (w + 1) / kWgPerXcd);
+    if (i0 < i1) span = std::max(span, (i1 - 1) / g.NB - i0 / g.NB + 1);
+  }
+  g.win = (span - 1) * g.KS + g.steps * kstep;
+  g.win = (int)round_up((size_t)g.win, 8);
   const int rows = g.path == 0 ? g.M : 16 * g.ta;
   g.xrow = g.path == 0 ? g.win : g.win + 8;
   g.lds = rows * g.xrow * 2;
-  g.items = g.NB * g.S;
   const int vals = g.path == 0 ? g.tb * g.M : g.tb * g.ta * 256;
-  g.ctr_count = (size_t)kXcds * g.NB * g.waves;
+  g.ctr_count = (size_t)kXcds * g.NB * g.wpi;
   g.part_floats = g.S > 1 ? g.ctr_count * (size_t)g.S * vals : 0;
   if (g.lds > kLdsMax) return false;
   if (!gemm_variant_exists(g.path, g.ta, g.tb) && !g.paired) return false;
   // Cost model (microseconds): streaming time of the busiest workgroup at the
-  // per-CU share of HBM bandwidth, plus per-item and split-K overheads.
-  const double bw_cu = 8.0e12 * 0.85 / 256.0;  // bytes/s per CU
-  const int rounds = ceil_div(g.items, kWgPerXcd);
+  // per-CU share of HBM bandwidth, a per-item cost, and for split-K the
+  // finalize round trips (arrival atomics, partial reads) at the end.  A
+  // workgroup keeps waves * 16 KB of weight loads in flight; fewer than 8
+  // waves leave the per-CU share unreached.  Wide dot2 tiles (G = 8) cost
+  // VALU time that shows from M = 4 on.
+  double bw_cu = 8.0e12 * 0.85 / 256.0 * (g.waves >= 8 ? 1.0 : 0.6);  // bytes/s per CU
+  if (g.path == 0 && g.tb == 8 && g.M >= 4) bw_cu *= 0.5;
+  const int per_stream = ceil_div(g.items, kWgPerXcd * g.ng);
   const double item_bytes = (double)g.CB * g.KS * 2.0 * (g.paired ? 2.0 : 1.0);
   const double part_bytes = g.S > 1 ? (double)g.CB * g.M * 4.0 * 2.0 : 0.0;
-  g.est_us = rounds * ((item_bytes + part_bytes) / bw_cu * 1e6 + 0.35) + (g.S > 1 ? 0.8 : 0.0);
+  const double wg_bytes = (double)g.ng * per_stream * (item_bytes + part_bytes);
+  const double pad = (double)g.steps * kstep / std::max(g.KS, 1);  // issue slots per useful K
+  g.est_us = wg_bytes / bw_cu * 1e6 + per_stream * 0.2 * pad + (g.S > 1 ? 2.5 : 0.0) +
+             (span > 1 ? 0.5 : 0.0);
   return true;
 }
 
@@ -79,9 +98,10 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
   for (int wi = 0; wi < 2; ++wi) {
     const int waves = waves_opts[wi];
     if (waves_o && waves != waves_o) continue;
+    for (int wpi = 1; wpi <= waves; wpi *= 2)
     for (int tb = 1; tb <= 8; ++tb) {
       Geo g;
-      g.path = path; g.M = M; g.K = K; g.N = N; g.waves = waves;
+      g.path = path; g.M = M; g.K = K; g.N = N; g.waves = waves; g.wpi = wpi;
       g.paired = paired;
       if (path == 0) {
         if (tb != 4 && tb != 8) continue;
@@ -184,6 +204,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     }
     layout_stage_ws(cur, pl->geo, pl->off_ctr, pl->off_part);
   } else if (p.kind == SGEMM_KIND_LAYERCHAIN) {
+    if (p.flags & (SGEMM_F_W_CACHED | SGEMM_F_W_SC1)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     if (p.M < 1 || p.n_layers < 1 || p.d_model < 8 || p.q_cols < 8 || p.d_ff < 8)
       { delete pl; return SGEMM_ERR_INVALID_ARG; }
     if (p.d_model % 8 || p.q_cols % 8 || p.d_ff % 8) { delete pl; return SGEMM_ERR_INVALID_ARG; }
@@ -260,7 +281,8 @@ static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
   StageDesc d;
   std::memset(&d, 0, sizeof d);
   d.M = g.M; d.K = g.K; d.N = g.N;
-  d.Nx = g.Nx; d.TN = g.TN; d.CB = g.CB; d.NB = g.NB; d.S = g.S; d.KS = g.KS;
+  d.Nx = g.Nx; d.TN = g.TN; d.wpi = g.wpi; d.ng = g.ng; d.CB = g.CB; d.NB = g.NB; d.S = g.S;
+  d.KS = g.KS;
   d.steps = g.steps; d.items = g.items; d.win = g.win; d.xrow = g.xrow;
   d.pair_off = g.pair_off;
   d.w_aux = w_aux;
@@ -405,10 +427,10 @@ const char* sgemm_status_string(int status) {
 static std::string geo_json(const Geo& g) {
   char b[512];
   std::snprintf(b, sizeof b,
-                "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,"
+                "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,\"wpi\":%d,"
                 "\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,\"steps\":%d,"
                 "\"items\":%d,\"lds\":%d,\"paired\":%d,\"est_us\":%.3f}",
-                g.path == 0 ? "dot2" : "mfma", g.M, g.K, g.N, g.ta, g.tb, g.waves, g.TN, g.CB, g.Nx,
+                g.path == 0 ? "dot2" : "mfma", g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.TN, g.CB, g.Nx,
                 g.NB, g.S, g.KS, g.steps, g.items, g.lds, g.paired, g.est_us);
   return b;
 }

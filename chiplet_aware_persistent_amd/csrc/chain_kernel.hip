@@ -31,15 +31,7 @@
 
 namespace sg {
 
-constexpr int kChainRing = 2;
-
 __device__ __forceinline__ unsigned long long now_ticks() { return wall_clock64(); }
-
-struct ChainState {
-  const ChainArgs* a;
-  int* alive;       // LDS flag shared by the workgroup
-  int xcd, nslots;
-};
 
 // Wait until event e is complete (all producers published).  Executed by the
 // whole workgroup; returns false when the wait timed out (here or elsewhere).
@@ -119,18 +111,11 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
         stamp(a, e, 0);
         return ok;
       };
-      // A workgroup without items in this stage still waits (its next stage
-      // needs this one) and still publishes.
-      const int n_my = d.items > slot ? 1 : 0;
-      if (n_my == 0) {
-        alive = hook();
+      // Every workgroup runs the hook (the wait), also one without items here.
+      if (s == 2) {
+        alive = mfma_stage<MT, 2, true, kAuxNt>(d, lds, xcd, slot, nslots, hook);
       } else {
-        if (s == 2) {
-          mfma_stage<MT, 2, kChainRing, true>(d, lds, xcd, slot, nslots, hook);
-        } else {
-          mfma_stage<MT, NT, kChainRing, false>(d, lds, xcd, slot, nslots, hook);
-        }
-        alive = sh_alive != 0 || e == 0;
+        alive = mfma_stage<MT, NT, false, kAuxNt>(d, lds, xcd, slot, nslots, hook);
       }
       if (!alive) break;
       stamp(a, e, 1);
@@ -153,7 +138,7 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
     for (int i = threadIdx.x; i < events; i += blockDim.x) a.gctr[i] = 0u;
     for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) a.lctr[i] = 0u;
     for (int s = 0; s < kChainStages; ++s) {
-      const int n = kXcds * a.st[s].NB * (a.st[s].CB / (s == 2 ? 16 : a.st[s].TN));
+      const int n = kXcds * a.st[s].NB * a.st[s].wpi;
       for (int i = threadIdx.x; i < n; i += blockDim.x) a.st[s].ctr[i] = 0u;
     }
     wait_vm0();

@@ -58,12 +58,6 @@ __device__ __forceinline__ u4 ld16(Rsrc r, unsigned off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
 }
 
-__device__ __forceinline__ u4 ld16_pol(Rsrc r, unsigned off, unsigned aux) {
-  if (aux == kAuxNt) return ld16<kAuxNt>(r, off);
-  if (aux == (kAuxNt | kAuxSc1)) return ld16<kAuxNt | kAuxSc1>(r, off);
-  return ld16<0>(r, off);
-}
-
 template <int AUX>
 __device__ __forceinline__ f4 ld_f4(Rsrc r, unsigned off) {
   return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
@@ -153,30 +147,56 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&v)[V], int lane) {
 
 constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
 
-// Split-K arrival of one wave tile.  The wave's partial stores are issued
-// before the call.  Returns true on the wave that completes the tile (its
-// arrival is the S-th); that wave then owns the reduction and has reset the
-// counter for the next use.
+// Split-K arrival.  A wave stores the partial of every (tile, split) it
+// computes without waiting; only after its last item does it make the
+// partials visible and bump the tile counters, so the weight stream is never
+// drained mid-way by a wait on its own stores (vmcnt counts loads and stores
+// in issue order).  The wave whose arrival is the S-th (counter old value
+// S-1) owns the tile: it resets the counter and adds the S partials in split
+// order, so the sum does not depend on which split arrived last.
 //   SYNC_XCD: all S contributors run on the same XCD, so their partials meet
 //     in one L2: wait until our stores are acknowledged (vmcnt), bump the
-//     counter; the reader bypasses its L1 (sc1 loads).
+//     counter; the owner reads with device-coherent (sc1) loads that skip its
+//     L1.
 //   SYNC_AGENT: device-scope release (L2 write-back) and acquire (L1/L2
 //     invalidate), valid whatever the placement.
-__device__ __forceinline__ bool wave_arrive(unsigned* ctr, int S, int sync, int lane) {
+__device__ __forceinline__ void splitk_release(int sync) {
   if (sync == SYNC_AGENT) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   } else {
     wait_vm0();
   }
+}
+
+__device__ __forceinline__ unsigned splitk_bump(unsigned* ctr, int lane) {
   unsigned old = 0;
   if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0);
+  return old;
+}
+
+__device__ __forceinline__ bool splitk_own(unsigned* ctr, unsigned old_lane0, int S, int sync, int lane) {
+  const unsigned old = __shfl(old_lane0, 0);
   const bool last = old == (unsigned)(S - 1);
   if (last) {
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (sync == SYNC_AGENT) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   return last;
+}
+
+// The waves of a workgroup form ng groups of wpi waves; each group is one
+// item stream.  Stream q of workgroup slot w runs the contiguous, balanced
+// range [i0, i1) of the XCD's items; the ranges of one workgroup's streams
+// are adjacent, so their union is contiguous too (one X window serves all).
+__device__ __forceinline__ void my_items(int items, int slot, int nslots, int ng, int q, int& i0,
+                                         int& i1) {
+  const long long nw = (long long)nslots * ng, w = (long long)slot * ng + q;
+  i0 = (int)((long long)items * w / nw);
+  i1 = (int)((long long)items * (w + 1) / nw);
+}
+
+__device__ __forceinline__ int first_item_of_wg(int items, int slot, int nslots) {
+  return (int)((long long)items * slot / nslots);
 }
 
 // Copy X[0:rows_p][k0:k0+win) into the LDS window (row stride d.xrow), zero
@@ -209,24 +229,32 @@ __device__ __forceinline__ void store_out(const StageDesc& d, Rsrc yr, Rsrc y2r,
   }
 }
 
-// ------------------------------------------------------------------ dot2
+// ------------------------------------------------------------------ stages
 struct NoHook {
   __device__ bool operator()() const { return true; }
 };
 
-// pre_x() runs after the first weight loads are in flight and before X is
-// staged; the chain waits there for the stage that produces X.  Returning
-// false abandons the stage.
-template <int M, int G, int P, typename Hook = NoHook>
-__device__ void dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
+// Per item: stage X for the item's split (only when it changes), stream the
+// item's padded steps through the P-deep ring (the issue cursor runs ahead
+// into the next items), reduce, then store Y (S == 1) or the partial.
+// pre_x() runs once the first P steps are in flight and before any X is read:
+// the chain waits there for the stage producing X.  It is called by every
+// workgroup, also one without items.  Returns false if pre_x() did.
+
+// ------------------------------------------------------------------ dot2
+// Lane l walks K eight values at a time (one contiguous kilobyte of a weight
+// row per 64-lane load); G columns per wave share the X registers.
+template <int M, int G, int AUX, typename Hook = NoHook>
+__device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                            Hook pre_x = Hook()) {
+  constexpr int P = ring_depth_dot2(G);
   constexpr int V = pow2_at_least(G * M);
   static_assert(V <= 64, "G*M must fit one wave");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int n_my = d.items > slot ? (d.items - slot + nslots - 1) / nslots : 0;
-  if (n_my <= 0) return;
-  const int total = n_my * d.steps;
+  int i0, i1;
+  my_items(d.items, slot, nslots, d.ng, wave / d.wpi, i0, i1);
+  const int wv = wave % d.wpi;  // wave's place within its item
   const int xc0 = xcd * d.Nx;
   const int xc1 = min(d.N, xc0 + d.Nx);
   const Rsrc wr = make_rsrc(d.W, d.w_bytes);
@@ -234,143 +262,173 @@ __device__ void dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   const Rsrc yr = make_rsrc(d.Y, d.y_bytes);
   const Rsrc y2r = make_rsrc(d.Y2, d.y2_bytes);
   const Rsrc pr = make_rsrc(d.part, d.part_bytes);
-  const unsigned aux = d.w_aux;
+  const int spad = d.steps;  // multiple of P
+  constexpr int GM = G * M;
+  constexpr int grp = 64 / V;
+  const int idx = lane / grp;
+  const bool owner = (lane % grp) == 0 && idx < GM;
+  const int oc = idx / M, om = idx - (idx / M) * M;
 
   u4 ring[P][G];
+  // Weight stream.  Slot p of the ring holds step t0+p of the current item;
+  // after consuming it the wave issues step t0+P+p, which falls in the next
+  // item for the last P steps.  Issue addresses are a per-item base plus a
+  // constant stride, and masked lanes (past K, past N, past the last item)
+  // point at the end of W, where the buffer range check returns zeros: no
+  // branch, so the compiler keeps exact counts of the loads in flight.
+  struct Src {
+    unsigned base;  // byte offset of (column colb, k = k0 + 8*lane)
+    int klim;       // steps * kstep with k < kend  -> valid while t*kstep + 8*lane < klim
+    int cols;       // columns of the wave tile that exist (col < xc1)
+  };
+  auto src_of = [&](int it) -> Src {
+    Src r;
+    if (it >= i1) { r.base = 0; r.klim = 0; r.cols = 0; return r; }
+    const int s_ = it / d.NB;
+    const int b_ = it - s_ * d.NB;
+    const int k0 = s_ * d.KS;
+    const int colb = xc0 + b_ * d.CB + wv * G;
+    r.base = ((unsigned)colb * (unsigned)d.K + (unsigned)k0) * 2u + (unsigned)lane * 16u;
+    r.klim = min(d.K, k0 + d.KS) - k0;
+    r.cols = min(G, xc1 - colb);
+    return r;
+  };
+  auto issue = [&](u4(&dst)[G], const Src& sr, int t) {
+    const bool kin = t * kDot2KStep + lane * 8 < sr.klim;
+#pragma unroll
+    for (int c = 0; c < G; ++c) {
+      const bool valid = kin && c < sr.cols;
+      const unsigned off = sr.base + (unsigned)c * (unsigned)d.K * 2u + (unsigned)t * (kDot2KStep * 2u);
+      dst[c] = ld16<AUX>(wr, valid ? off : d.w_bytes);
+    }
+  };
+
+  Src sc = src_of(i0), sn = src_of(i0 + 1);
+#pragma unroll
+  for (int p = 0; p < P; ++p) issue(ring[p], sc, p);
+  if (!pre_x()) return false;
+
+  // One X window per workgroup and stage: the K range of every split its
+  // items touch (the planner sizes d.win for the widest such range).
+  const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
+  stage_x(d, xs, M, s_first * d.KS, d.K, xr);
+  __syncthreads();
+
   float acc[G][M];
 #pragma unroll
   for (int c = 0; c < G; ++c)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[c][m] = 0.f;
-
-  int i_ord = 0, i_t = 0;  // issue cursor
-  auto issue = [&](u4(&dst)[G]) {
-    if (i_ord < n_my) {
-      const int item = slot + i_ord * nslots;
-      const int s = item / d.NB;
-      const int b = item - s * d.NB;
-      const int k0 = s * d.KS;
-      const int kend = min(d.K, k0 + d.KS);
-      const int k = k0 + i_t * kDot2KStep + lane * 8;
-      const int colb = xc0 + b * d.CB + wave * G;
+  int it = i0, t0 = 0;
+  int xoff = (i0 / d.NB - s_first) * d.KS;  // LDS column of the current item's k0
+  const int total = (i1 - i0) * spad;
+  for (int T = 0; T < total; T += P) {
+    const bool here = t0 + P < spad;
+    const Src& sr = here ? sc : sn;
+    const int tn = here ? t0 + P : t0 + P - spad;
+    const uint16_t* xb = xs + xoff + t0 * kDot2KStep + lane * 8;
 #pragma unroll
-      for (int c = 0; c < G; ++c) {
-        const int col = colb + c;
-        const bool valid = col < xc1 && k < kend;
-        const unsigned off = valid ? ((unsigned)col * (unsigned)d.K + (unsigned)k) * 2u : d.w_bytes;
-        dst[c] = ld16_pol(wr, off, aux);
-      }
+    for (int p = 0; p < P; ++p) {
+      u4 xv[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) xv[m] = *(const u4*)(xb + m * d.xrow + p * kDot2KStep);
+#pragma unroll
+      for (int c = 0; c < G; ++c)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[c][m] = dot8(ring[p][c], xv[m], acc[c][m]);
+      issue(ring[p], sr, tn + p);
+      // Pin the reload of slot p right behind its use: otherwise the
+      // scheduler sinks all reloads to the end of the unrolled group and the
+      // next group has to wait for every load (vmcnt(0)).
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (++i_t == d.steps) { i_t = 0; ++i_ord; }
-  };
+    t0 += P;
+    if (t0 == spad) {  // item complete
+      const int s = it / d.NB;
+      const int b = it - s * d.NB;
+      float v[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < G; ++c)
+#pragma unroll
+        for (int m = 0; m < M; ++m) v[c * M + m] = acc[c][m];
+      const float r = wave_reduce_scatter<V>(v, lane);
+      const int col = xc0 + b * d.CB + wv * G + oc;
+      if (d.S == 1) {
+        store_out(d, yr, y2r, owner && col < xc1 && om < d.M, om, col, r);
+      } else {
+        const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
+        st_f32<0>(pr, owner ? ((tile * d.S + s) * GM + idx) * 4u : d.part_bytes, r);
+      }
+#pragma unroll
+      for (int c = 0; c < G; ++c)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[c][m] = 0.f;
+      ++it;
+      t0 = 0;
+      sc = sn;
+      sn = src_of(it + 1);
+      xoff = (it / d.NB - s_first) * d.KS;
+    }
+  }
 
-  auto x_window = [&](int ord) {
-    const int item = slot + ord * nslots;
-    const int s = item / d.NB;
-    stage_x(d, xs, M, s * d.KS, min(d.K, s * d.KS + d.KS), xr);
-  };
-
-  auto epilogue = [&](int ord) {
-    float v[V];
+  if (d.S > 1 && i0 < i1) {
+    splitk_release(d.sync);
+    constexpr int B = 4;  // arrivals in flight at once
+    for (int c0 = i0; c0 < i1; c0 += B) {
+      unsigned old[B];
 #pragma unroll
-    for (int i = 0; i < V; ++i) v[i] = 0.f;
+      for (int j = 0; j < B; ++j) {
+        const int it = c0 + j;
+        const int b = it % d.NB;
+        old[j] = it < i1 ? splitk_bump(d.ctr + (xcd * d.NB + b) * d.wpi + wv, lane) : 0u;
+      }
 #pragma unroll
-    for (int c = 0; c < G; ++c)
-#pragma unroll
-      for (int m = 0; m < M; ++m) v[c * M + m] = acc[c][m];
-    float r = wave_reduce_scatter<V>(v, lane);
-    constexpr int grp = 64 / V;
-    const int idx = lane / grp;
-    const bool owner = (lane % grp) == 0 && idx < G * M;
-    const int c = idx / M, m = idx - (idx / M) * M;
-    const int item = slot + ord * nslots;
-    const int s = item / d.NB;
-    const int b = item - s * d.NB;
-    const int col = xc0 + b * d.CB + wave * G + c;
-    if (d.S > 1) {
-      const int tile = (xcd * d.NB + b) * (d.CB / G) + wave;
-      const unsigned base = (unsigned)tile * (unsigned)d.S;
-      st_f32<0>(pr, owner ? ((base + s) * (unsigned)(G * M) + idx) * 4u : d.part_bytes, r);
-      if (!wave_arrive(d.ctr + tile, d.S, d.sync, lane)) return;
-      float t = 0.f;
-      for (int q = 0; q < d.S; ++q) {
-        float pv;
-        if (q == s) {
-          pv = r;
-        } else {
-          const unsigned off = owner ? ((base + q) * (unsigned)(G * M) + idx) * 4u : d.part_bytes;
-          pv = d.sync == SYNC_XCD
+      for (int j = 0; j < B; ++j) {
+        const int it = c0 + j;
+        if (it >= i1) break;
+        const int b = it % d.NB;
+        const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
+        if (!splitk_own(d.ctr + tile, old[j], d.S, d.sync, lane)) continue;
+        float t = 0.f;
+        for (int q = 0; q < d.S; ++q) {
+          const unsigned off = owner ? ((tile * d.S + q) * GM + idx) * 4u : d.part_bytes;
+          t += d.sync == SYNC_XCD
                    ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, (int)off, 0, kAuxSc1))
                    : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, (int)off, 0, 0));
         }
-        t += pv;
-      }
-      r = t;
-    }
-    store_out(d, yr, y2r, owner && col < xc1 && m < d.M, m, col, r);
-  };
-
-#pragma unroll
-  for (int p = 0; p < P; ++p) issue(ring[p]);
-  if (!pre_x()) return;
-  x_window(0);
-  __syncthreads();
-
-  int c_ord = 0, c_t = 0;
-  int cur_s = slot / d.NB;
-  for (int T = 0; T < total; T += P) {
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (T + p < total) {
-        u4 xv[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) xv[m] = *(const u4*)(xs + m * d.xrow + c_t * kDot2KStep + lane * 8);
-#pragma unroll
-        for (int c = 0; c < G; ++c)
-#pragma unroll
-          for (int m = 0; m < M; ++m) acc[c][m] = dot8(ring[p][c], xv[m], acc[c][m]);
-        issue(ring[p]);
-        if (++c_t == d.steps) {
-          epilogue(c_ord);
-#pragma unroll
-          for (int c = 0; c < G; ++c)
-#pragma unroll
-            for (int m = 0; m < M; ++m) acc[c][m] = 0.f;
-          c_t = 0;
-          ++c_ord;
-          if (c_ord < n_my) {
-            const int s_new = (slot + c_ord * nslots) / d.NB;
-            if (s_new != cur_s) {
-              __syncthreads();
-              x_window(c_ord);
-              __syncthreads();
-              cur_s = s_new;
-            }
-          }
-        }
+        const int col = xc0 + b * d.CB + wv * G + oc;
+        store_out(d, yr, y2r, owner && col < xc1 && om < d.M, om, col, t);
       }
     }
   }
+  return true;
 }
 
 // ------------------------------------------------------------------ MFMA
 // NT n-tiles of 16 columns per wave (PAIRED: tile 0 = gate rows, tile 1 = the
-// matching up rows pair_off further), MT m-tiles of 16 rows.
-// Lane l: column l%16 of an n-tile, row l%16 of an m-tile, K group l/16.
-// Within a 64-wide k-step, lane group g reads k = 16g + 8h + (0..7) for
-// halves h = 0, 1, so each weight row's 128 bytes are one full cache line
-// spread over the two loads; A (from LDS) uses the same k slots, which is all
-// the dot product needs.
-template <int MT, int NT, int P, bool PAIRED, typename Hook = NoHook>
-__device__ void mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
+// matching up rows pair_off further), MT m-tiles of 16 rows; every weight
+// fragment feeds all MT m-tiles.
+// Loads are coalesced: for half h of a 64-wide k-step, lane l reads 16 bytes
+// of weight row l/4 at k = 32h + 8(l%4), so four consecutive lanes cover 64
+// contiguous bytes of one row.  The MFMA B operand wants lane l' to hold
+// column l'%16 at k-group l'/16, so each dword is moved with one ds_bpermute
+// from lane 4(l'%16) + l'/16.  The A operand (X, from LDS) uses the same k
+// slots: lane l' reads row l'%16 at k = 32h + 8(l'/16).
+template <int MT, int NT, bool PAIRED, int AUX, typename Hook = NoHook>
+__device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                            Hook pre_x = Hook()) {
+  constexpr int P = ring_depth_mfma(NT);
+  constexpr int TW = PAIRED ? 16 : 16 * NT;  // distinct output columns per wave
+  constexpr unsigned TILE = NT * MT * 256;   // floats of one wave tile
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  const int n_my = d.items > slot ? (d.items - slot + nslots - 1) / nslots : 0;
-  if (n_my <= 0) return;
-  const int total = n_my * d.steps;
+  int i0, i1;
+  my_items(d.items, slot, nslots, d.ng, wave / d.wpi, i0, i1);
+  const int wv = wave % d.wpi;  // wave's place within its item
   const int xc0 = xcd * d.Nx;
   const int xc1 = min(d.N, xc0 + d.Nx);
   const Rsrc wr = make_rsrc(d.W, d.w_bytes);
@@ -378,45 +436,51 @@ __device__ void mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   const Rsrc yr = make_rsrc(d.Y, d.y_bytes);
   const Rsrc y2r = make_rsrc(d.Y2, d.y2_bytes);
   const Rsrc pr = make_rsrc(d.part, d.part_bytes);
-  const unsigned aux = d.w_aux;
-  constexpr int TW = PAIRED ? 16 : 16 * NT;  // distinct output columns per wave
+  const int spad = d.steps;  // multiple of P
 
   u4 ring[P][NT][2];
-  f4 acc[NT][MT];
+  // Weight stream, organised as in the dot2 path (per-item base + constant
+  // stride, branch-free masking through the buffer range check).
+  struct Src {
+    unsigned base;  // byte offset of (weight row of column colb + lane/4, k = k0 + 8*(lane%4))
+    int klim;       // valid while t*64 + 32*h + 8*(lane%4) < klim
+    int col;        // the loaded row's column in n-tile 0 (n-tile j: col + 16 j unless paired)
+  };
+  const int lrow = lane >> 2;  // row within the n-tile this lane loads
+  const int lq = lane & 3;     // 16-byte chunk within the row's 64 bytes
+  auto src_of = [&](int it) -> Src {
+    Src r;
+    if (it >= i1) { r.base = 0; r.klim = 0; r.col = xc1; return r; }
+    const int s_ = it / d.NB;
+    const int b_ = it - s_ * d.NB;
+    const int k0 = s_ * d.KS;
+    const int col = xc0 + b_ * d.CB + wv * TW + lrow;
+    r.base = ((unsigned)col * (unsigned)d.K + (unsigned)k0 + 8u * (unsigned)lq) * 2u;
+    r.klim = min(d.K, k0 + d.KS) - k0;
+    r.col = col;
+    return r;
+  };
+  // byte distance between the weight rows of n-tile j and n-tile 0
+  const unsigned jstride = PAIRED ? (unsigned)d.pair_off * (unsigned)d.K * 2u : 16u * (unsigned)d.K * 2u;
+  auto issue = [&](u4(&dst)[NT][2], const Src& sr, int t) {
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
+    for (int j = 0; j < NT; ++j) {
+      const bool cj = (PAIRED ? sr.col : sr.col + 16 * j) < xc1;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) acc[j][i] = f4{0.f, 0.f, 0.f, 0.f};
-
-  int i_ord = 0, i_t = 0;
-  auto issue = [&](u4(&dst)[NT][2]) {
-    if (i_ord < n_my) {
-      const int item = slot + i_ord * nslots;
-      const int s = item / d.NB;
-      const int b = item - s * d.NB;
-      const int k0 = s * d.KS;
-      const int kend = min(d.K, k0 + d.KS);
-      const int colb = xc0 + b * d.CB + wave * TW;
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int col = PAIRED ? colb + r16 : colb + 16 * j + r16;
-        const unsigned row = PAIRED ? (unsigned)(col + j * d.pair_off) : (unsigned)col;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int k = k0 + i_t * kMfmaKStep + 16 * g4 + 8 * h;
-          const bool valid = col < xc1 && k < kend;
-          const unsigned off = valid ? (row * (unsigned)d.K + (unsigned)k) * 2u : d.w_bytes;
-          dst[j][h] = ld16_pol(wr, off, aux);
-        }
+      for (int h = 0; h < 2; ++h) {
+        const bool valid = cj && t * kMfmaKStep + 32 * h + 8 * lq < sr.klim;
+        const unsigned off = sr.base + (unsigned)j * jstride + (unsigned)t * (kMfmaKStep * 2u) + 64u * (unsigned)h;
+        dst[j][h] = ld16<AUX>(wr, valid ? off : d.w_bytes);
       }
     }
-    if (++i_t == d.steps) { i_t = 0; ++i_ord; }
   };
-
-  auto x_window = [&](int ord) {
-    const int item = slot + ord * nslots;
-    const int s = item / d.NB;
-    stage_x(d, xs, 16 * MT, s * d.KS, min(d.K, s * d.KS + d.KS), xr);
+  // lane l' takes the dwords of lane 4(l'%16) + l'/16 (byte address for bpermute)
+  const int perm_addr = (4 * r16 + g4) * 4;
+  auto to_b = [&](u4 v) -> bf16x8 {
+    u4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = (unsigned)__builtin_amdgcn_ds_bpermute(perm_addr, (int)v[q]);
+    return __builtin_bit_cast(bf16x8, o);
   };
 
   auto emit = [&](int colb, int j, int i, f4 v, f4 vu) {
@@ -425,120 +489,134 @@ __device__ void mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     for (int e = 0; e < 4; ++e) {
       const int m = 16 * i + 4 * g4 + e;
       const bool ok = m < d.M && col < xc1;
-      if (PAIRED) {
-        store_out(d, yr, y2r, ok, m, col, silu_mul(v[e], vu[e]));
-      } else {
-        store_out(d, yr, y2r, ok, m, col, v[e]);
-      }
+      store_out(d, yr, y2r, ok, m, col, PAIRED ? silu_mul(v[e], vu[e]) : v[e]);
     }
   };
 
-  auto epilogue = [&](int ord) {
-    const int item = slot + ord * nslots;
-    const int s = item / d.NB;
-    const int b = item - s * d.NB;
-    const int colb = xc0 + b * d.CB + wave * TW;
-    if (d.S > 1) {
-      constexpr unsigned TILE = NT * MT * 256;  // floats per wave tile
-      const int tile = (xcd * d.NB + b) * (d.CB / TW) + wave;
-      const unsigned base = (unsigned)tile * (unsigned)d.S;
+  Src sc = src_of(i0), sn = src_of(i0 + 1);
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+  for (int p = 0; p < P; ++p) issue(ring[p], sc, p);
+  if (!pre_x()) return false;
+
+  // One X window per workgroup and stage (see the dot2 path).
+  const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
+  stage_x(d, xs, 16 * MT, s_first * d.KS, d.K, xr);
+  __syncthreads();
+
+  f4 acc[NT][MT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[j][i] = f4{0.f, 0.f, 0.f, 0.f};
+  int it = i0, t0 = 0;
+  int xoff = (i0 / d.NB - s_first) * d.KS;
+  const int total = (i1 - i0) * spad;
+  for (int T = 0; T < total; T += P) {
+    const bool here = t0 + P < spad;
+    const Src& sr = here ? sc : sn;
+    const int tn = here ? t0 + P : t0 + P - spad;
+    const uint16_t* xb0 = xs + r16 * d.xrow + xoff + t0 * kMfmaKStep + 8 * g4;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint16_t* xb = xb0 + p * kMfmaKStep;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 xa[MT];
 #pragma unroll
         for (int i = 0; i < MT; ++i)
-          st_f4<0>(pr, (((base + s) * TILE) + (j * MT + i) * 256 + lane * 4) * 4u, acc[j][i]);
-      if (!wave_arrive(d.ctr + tile, d.S, d.sync, lane)) return;
-      f4 tot[NT][MT];
+          xa[i] = __builtin_bit_cast(bf16x8, *(const u4*)(xb + 16 * i * d.xrow + 32 * h));
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+        for (int j = 0; j < NT; ++j) {
+          const bf16x8 wb = to_b(ring[p][j][h]);
 #pragma unroll
-        for (int i = 0; i < MT; ++i) tot[j][i] = f4{0.f, 0.f, 0.f, 0.f};
-      for (int q = 0; q < d.S; ++q) {
+          for (int i = 0; i < MT; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], wb, acc[j][i], 0, 0, 0);
+        }
+      }
+      issue(ring[p], sr, tn + p);
+      __builtin_amdgcn_sched_barrier(0);  // as in the dot2 path
+    }
+    t0 += P;
+    if (t0 == spad) {  // item complete
+      const int s = it / d.NB;
+      const int b = it - s * d.NB;
+      const int colb = xc0 + b * d.CB + wv * TW;
+      if (d.S == 1) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          if (PAIRED) {
+            emit(colb, 0, i, acc[0][i], acc[1][i]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) emit(colb, j, i, acc[j][i], acc[j][i]);
+          }
+        }
+      } else {
+        const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
-          for (int i = 0; i < MT; ++i) {
-            f4 pv;
-            if (q == s) {
-              pv = acc[j][i];
-            } else {
-              const unsigned off = (((base + q) * TILE) + (j * MT + i) * 256 + lane * 4) * 4u;
-              pv = d.sync == SYNC_XCD ? ld_f4<kAuxSc1>(pr, off) : ld_f4<0>(pr, off);
-            }
-            tot[j][i] += pv;
-          }
-      }
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        if (PAIRED) {
-          emit(colb, 0, i, tot[0][i], tot[1][i]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < NT; ++j) emit(colb, j, i, tot[j][i], tot[j][i]);
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      if (PAIRED) {
-        emit(colb, 0, i, acc[0][i], acc[1][i]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) emit(colb, j, i, acc[j][i], acc[j][i]);
-      }
-    }
-  };
-
-#pragma unroll
-  for (int p = 0; p < P; ++p) issue(ring[p]);
-  if (!pre_x()) return;
-  x_window(0);
-  __syncthreads();
-
-  int c_ord = 0, c_t = 0;
-  int cur_s = slot / d.NB;
-  for (int T = 0; T < total; T += P) {
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (T + p < total) {
-        const uint16_t* xb = xs + r16 * d.xrow + c_t * kMfmaKStep + 16 * g4;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          bf16x8 xa[MT];
-#pragma unroll
           for (int i = 0; i < MT; ++i)
-            xa[i] = __builtin_bit_cast(bf16x8, *(const u4*)(xb + 16 * i * d.xrow + 8 * h));
+            st_f4<0>(pr, ((tile * d.S + s) * TILE + (j * MT + i) * 256 + lane * 4) * 4u, acc[j][i]);
+      }
 #pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            const bf16x8 wb = __builtin_bit_cast(bf16x8, ring[p][j][h]);
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int i = 0; i < MT; ++i)
-              acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], wb, acc[j][i], 0, 0, 0);
-          }
-        }
-        issue(ring[p]);
-        if (++c_t == d.steps) {
-          epilogue(c_ord);
+        for (int i = 0; i < MT; ++i) acc[j][i] = f4{0.f, 0.f, 0.f, 0.f};
+      ++it;
+      t0 = 0;
+      sc = sn;
+      sn = src_of(it + 1);
+      xoff = (it / d.NB - s_first) * d.KS;
+    }
+  }
+
+  if (d.S > 1 && i0 < i1) {
+    splitk_release(d.sync);
+    constexpr int B = 4;
+    for (int c0 = i0; c0 < i1; c0 += B) {
+      unsigned old[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        const int it = c0 + j;
+        const int b = it % d.NB;
+        old[j] = it < i1 ? splitk_bump(d.ctr + (xcd * d.NB + b) * d.wpi + wv, lane) : 0u;
+      }
+#pragma unroll
+      for (int jj = 0; jj < B; ++jj) {
+        const int it = c0 + jj;
+        if (it >= i1) break;
+        const int b = it % d.NB;
+        const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
+        if (!splitk_own(d.ctr + tile, old[jj], d.S, d.sync, lane)) continue;
+        f4 tot[NT][MT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int i = 0; i < MT; ++i) tot[j][i] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < d.S; ++q) {
 #pragma unroll
           for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int i = 0; i < MT; ++i) acc[j][i] = f4{0.f, 0.f, 0.f, 0.f};
-          c_t = 0;
-          ++c_ord;
-          if (c_ord < n_my) {
-            const int s_new = (slot + c_ord * nslots) / d.NB;
-            if (s_new != cur_s) {
-              __syncthreads();
-              x_window(c_ord);
-              __syncthreads();
-              cur_s = s_new;
+            for (int i = 0; i < MT; ++i) {
+              const unsigned off = ((tile * d.S + q) * TILE + (j * MT + i) * 256 + lane * 4) * 4u;
+              tot[j][i] += d.sync == SYNC_XCD ? ld_f4<kAuxSc1>(pr, off) : ld_f4<0>(pr, off);
             }
+        }
+        const int colb = xc0 + b * d.CB + wv * TW;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          if (PAIRED) {
+            emit(colb, 0, i, tot[0][i], tot[1][i]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) emit(colb, j, i, tot[j][i], tot[j][i]);
           }
         }
       }
     }
   }
+  return true;
 }
 
 }  // namespace sg

@@ -11,6 +11,12 @@ constexpr int kXcds = 8;            // XCDs (chiplets) of an MI355X in SPX mode
 constexpr int kDot2KStep = 512;     // K values one dot2 wave step covers (64 lanes x 8)
 constexpr int kMfmaKStep = 64;      // K values one MFMA wave step covers (2 x 32)
 constexpr int kMaxWaves = 8;        // waves per workgroup (512 threads)
+constexpr int kLoadsInFlight = 16;  // 16-byte weight loads per lane kept in flight
+
+// Ring depth (k-steps in flight) of each path; steps per item are padded to a
+// multiple of it.
+constexpr int ring_depth_dot2(int g) { return kLoadsInFlight / g > 2 ? kLoadsInFlight / g : 2; }
+constexpr int ring_depth_mfma(int nt) { return kLoadsInFlight / (2 * nt) > 2 ? kLoadsInFlight / (2 * nt) : 2; }
 
 enum OutMode : int {
   OUT_F32 = 0,       // Y fp32
@@ -32,12 +38,14 @@ struct StageDesc {
   int ldx, ldy;
   int Nx;              // columns owned by one XCD (XCD x: [x*Nx, min(N,(x+1)*Nx)))
   int TN;              // columns per wave tile
-  int CB;              // columns per workgroup item = waves * TN
+  int wpi;             // waves per item: a workgroup runs waves/wpi item streams
+  int CB;              // columns per item = wpi * TN
   int NB;              // column blocks per XCD
   int S;               // K splits
   int KS;              // K values per split (multiple of 8)
   int steps;           // wave k-steps per item
   int items;           // items per XCD = NB * S (ordered split-major)
+  int ng;              // item streams (wave groups) per workgroup = waves / wpi
   int win;             // LDS window width (elements) = steps * kstep
   int xrow;            // LDS row stride (elements)
   int pair_off;        // paired: weight row offset of the up half

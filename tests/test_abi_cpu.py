@@ -91,14 +91,14 @@ def test_planner_covers_every_column_and_k_once(M, K, N, splitk):
     st = g.describe()["stage"]
     assert st["path"] == ("dot2" if M < 16 else "mfma")
     Nx, CB, NB, S, KS = st["Nx"], st["CB"], st["NB"], st["S"], st["KS"]
-    assert CB == st["waves"] * st["TN"]
+    assert CB == st["wpi"] * st["TN"] and st["waves"] % st["wpi"] == 0
     assert 8 * Nx >= N and 8 * (Nx - 16) < N          # per-XCD partition covers N, no spare XCD block
     assert NB * CB >= Nx                               # column blocks cover the XCD's columns
     assert S * KS >= K and (S - 1) * KS < K            # splits cover K, none empty
     assert KS % 8 == 0 and st["items"] == NB * S
     kstep = 512 if st["path"] == "dot2" else 64
     assert st["steps"] * kstep >= KS
-    assert st["lds"] <= 128 * 1024
+    assert st["lds"] <= 160 * 1024
     if splitk:
         assert S == min(splitk, math.ceil(K / 8)) or S == math.ceil(K / math.ceil(K / splitk / 8) / 8)
     # columns: every column owned by exactly one (xcd, block, wave, lane-column)
