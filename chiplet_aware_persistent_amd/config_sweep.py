@@ -43,11 +43,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--launches", type=int, default=40)
     ap.add_argument("--json-overrides", default="{}")
+    ap.add_argument("--only", default="", help="semicolon-separated M,K,N shapes to run instead of all")
+    ap.add_argument("--warmup", type=int, default=6)
     a = ap.parse_args()
     extra = json.loads(a.json_overrides)
     dev = torch.device("cuda:0")
     cache = {}
-    for (M, K, N) in shapes():
+    todo = [tuple(int(v) for v in t.split(",")) for t in a.only.split(";") if t] or shapes()
+    for (M, K, N) in todo:
         wb = 2 * K * N
         copies = max(2, -(-(4 << 30) // wb))
         if (K, N) not in cache:
@@ -60,7 +63,7 @@ def main():
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
         g = sg.Gemm(M, K, N, **extra)
         ws = g.new_workspace()
-        for i in range(6):
+        for i in range(a.warmup):
             g(X, Ws[i % copies], Y, ws)
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

@@ -80,8 +80,15 @@ bool shape_geo(Geo& g, int want_S) {
   // workgroup keeps waves * 16 KB of weight loads in flight; fewer than 8
   // waves leave the per-CU share unreached.  Wide dot2 tiles (G = 8) cost
   // VALU time that shows from M = 4 on.
-  double bw_cu = 8.0e12 * 0.85 / 256.0 * (g.waves >= 8 ? 1.0 : 0.6);  // bytes/s per CU
-  if (g.path == 0 && g.tb == 8 && g.M >= 4) bw_cu *= 0.5;
+  // Per-CU rates (bytes of W per second): the HBM share, the LDS traffic the
+  // inner loop generates per weight byte (dot2: X reads M/G; MFMA: A reads
+  // MT/NT plus the B permute), and dot2's VALU time (4 M dot2 cycles per KB
+  // per SIMD quartet, on top of the loop overhead).
+  double bw_cu = 8.0e12 * 0.85 / 256.0 * (g.waves >= 8 ? 1.0 : 0.6);
+  const double lds_cu = 128.0 * 2.4e9 * 0.5;
+  const double lds_per_w = g.path == 0 ? (double)g.M / g.tb : (double)g.ta / g.tb + 1.0;
+  bw_cu = std::min(bw_cu, lds_cu / lds_per_w);
+  if (g.path == 0) bw_cu = std::min(bw_cu, 1024.0 / (4.0 * g.M + 4.0) * 2.4e9 * 0.7);
   const int per_stream = ceil_div(g.items, kWgPerXcd * g.ng);
   const double item_bytes = (double)g.CB * g.KS * 2.0 * (g.paired ? 2.0 : 1.0);
   const double part_bytes = g.S > 1 ? (double)g.CB * g.M * 4.0 * 2.0 : 0.0;
@@ -104,7 +111,7 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
       g.path = path; g.M = M; g.K = K; g.N = N; g.waves = waves; g.wpi = wpi;
       g.paired = paired;
       if (path == 0) {
-        if (tb != 4 && tb != 8) continue;
+        if (tb == 5 || tb == 6 || tb == 7) continue;
         if (tn_o && tb != tn_o) continue;
         g.ta = M; g.tb = tb;
       } else {
@@ -139,7 +146,7 @@ struct sgemm_plan_s {
   size_t ws_bytes = 0;
   size_t off_ctr = 0, off_part = 0;                 // GEMM (and chain stage 0..3 bases below)
   size_t c_ctr[kChainStages] = {0}, c_part[kChainStages] = {0};
-  size_t off_lctr = 0, off_gctr = 0, off_act = 0, off_stamps = 0;
+  size_t off_lctr = 0, off_gctr = 0, off_xflag = 0, off_act = 0, off_stamps = 0;
   size_t act_layer_elems = 0, a_h1 = 0, a_h2 = 0, a_a = 0, a_x = 0;
   long long spin_ticks = 0;
 };
@@ -243,6 +250,8 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     cur = round_up(cur + (size_t)kXcds * events * 4, 256);
     pl->off_gctr = cur;
     cur = round_up(cur + (size_t)events * 4, 256);
+    pl->off_xflag = cur;
+    cur = round_up(cur + (size_t)kXcds * events * 4, 256);
     const size_t M = p.M;
     pl->a_h1 = 0;
     pl->a_h2 = round_up(M * p.q_cols, 128);
@@ -365,6 +374,7 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   a.done = (unsigned*)(ws + 64);
   a.lctr = (unsigned*)(ws + plan->off_lctr);
   a.gctr = (unsigned*)(ws + plan->off_gctr);
+  a.xflag = (unsigned*)(ws + plan->off_xflag);
   a.stamps = (p.flags & SGEMM_F_STAMPS) ? (unsigned long long*)(ws + plan->off_stamps) : nullptr;
   a.n_layers = p.n_layers; a.M = p.M; a.d = p.d_model; a.q = p.q_cols; a.dff = p.d_ff;
   a.act_layer_elems = plan->act_layer_elems;

@@ -35,12 +35,30 @@ __device__ __forceinline__ unsigned long long now_ticks() { return wall_clock64(
 
 // Wait until event e is complete (all producers published).  Executed by the
 // whole workgroup; returns false when the wait timed out (here or elsewhere).
+// One leader per XCD (slot 0) polls the global counter with device-coherent
+// loads and, once it is complete, raises the XCD's flag; the other 31
+// workgroups of the XCD poll that flag, so only 8 pollers share the global
+// counter's address and the other 248 spread over 8 flags (the per-XCD
+// scheduler's polling role in the Fleet note, sections 2a and 3b, without a
+// dedicated workgroup).
 __device__ bool wait_event(const ChainArgs& a, int e, int* sh_alive) {
   if (threadIdx.x == 0) {
+    const int xcd = blockIdx.x & 7;
+    const int events = 4 * a.n_layers;
+    unsigned* flag = a.xflag + xcd * events + e;
     const unsigned target = a.flat_sync ? gridDim.x : (unsigned)kXcds;
+    const bool leader = (blockIdx.x >> 3) == 0 || a.flat_sync;
     int ok = 1;
     const unsigned long long t0 = now_ticks();
-    while (__hip_atomic_load(a.gctr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    for (;;) {
+      bool done;
+      if (leader) {
+        done = __hip_atomic_load(a.gctr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
+      } else {
+        // Device-scope read (it skips the CU's L1, which could hold a stale 0).
+        done = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+      }
+      if (done) break;
       if ((long long)(now_ticks() - t0) > a.spin_ticks ||
           (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout)) {
         __hip_atomic_fetch_or(a.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -50,6 +68,7 @@ __device__ bool wait_event(const ChainArgs& a, int e, int* sh_alive) {
       __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (leader && ok && !a.flat_sync) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *sh_alive = ok;
   }
   __syncthreads();
@@ -137,6 +156,7 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
     const int events = 4 * a.n_layers;
     for (int i = threadIdx.x; i < events; i += blockDim.x) a.gctr[i] = 0u;
     for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) a.lctr[i] = 0u;
+    for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) a.xflag[i] = 0u;
     for (int s = 0; s < kChainStages; ++s) {
       const int n = kXcds * a.st[s].NB * a.st[s].wpi;
       for (int i = threadIdx.x; i < n; i += blockDim.x) a.st[s].ctr[i] = 0u;

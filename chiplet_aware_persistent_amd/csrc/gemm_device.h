@@ -123,17 +123,18 @@ __device__ __forceinline__ void check_topology(unsigned* status) {
 
 // Reduce-scatter over the 64 lanes of a wave: v holds V (power of two <= 64)
 // per-lane partials; afterwards lane l holds the full sum of value l/(64/V).
-// Fixed exchange pattern, so the result is bitwise reproducible.
-template <int V>
-__device__ __forceinline__ float wave_reduce_scatter(float (&v)[V], int lane) {
+// Fixed exchange pattern, so the result is bitwise reproducible.  Stage ST
+// exchanges over lane distance 32 >> ST; every index is a compile-time
+// constant, so v stays in registers.
+template <int V, int ST>
+__device__ __forceinline__ void reduce_scatter_stage(float (&v)[V], int lane) {
+  if constexpr (ST < 6) {
+    constexpr int o = 32 >> ST;
+    constexpr int half = V >> (ST + 1);
+    if constexpr (half >= 1) {
+      const bool up = (lane & o) != 0;
 #pragma unroll
-  for (int st = 0; st < 6; ++st) {
-    const int o = 32 >> st;
-    const int half = V >> (st + 1);
-    const bool up = (lane & o) != 0;
-    if (half >= 1) {
-#pragma unroll
-      for (int i = 0; i < (half > 0 ? half : 1); ++i) {
+      for (int i = 0; i < half; ++i) {
         const float send = up ? v[i] : v[i + half];
         const float keep = up ? v[i + half] : v[i];
         v[i] = keep + __shfl_xor(send, o);
@@ -141,7 +142,13 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&v)[V], int lane) {
     } else {
       v[0] += __shfl_xor(v[0], o);
     }
+    reduce_scatter_stage<V, ST + 1>(v, lane);
   }
+}
+
+template <int V>
+__device__ __forceinline__ float wave_reduce_scatter(float (&v)[V], int lane) {
+  reduce_scatter_stage<V, 0>(v, lane);
   return v[0];
 }
 
@@ -199,22 +206,35 @@ __device__ __forceinline__ int first_item_of_wg(int items, int slot, int nslots)
   return (int)((long long)items * slot / nslots);
 }
 
-// Copy X[0:rows_p][k0:k0+win) into the LDS window (row stride d.xrow), zero
-// outside [0,M) x [k0,kend).
-__device__ __forceinline__ void stage_x(const StageDesc& d, uint16_t* xs, int rows_p, int k0,
-                                        int kend, Rsrc xr) {
+// X window: rows [0, rows_p) x columns [k0, k0 + win) of X go to LDS (row
+// stride d.xrow), zero outside [0,M) x [k0,kend).  Chunk q (16 bytes) is row
+// q / (win/8), column 8 * (q % (win/8)).
+__device__ __forceinline__ u4 x_chunk(const StageDesc& d, int q, int total, int k0, int kend, Rsrc xr) {
   const int cpr = d.win >> 3;
-  const int total = rows_p * cpr;
-#pragma unroll 4
-  for (int q = threadIdx.x; q < total; q += blockDim.x) {
-    const int row = q / cpr;
-    const int cc = q - row * cpr;
-    const int k = k0 + cc * 8;
-    const bool valid = row < d.M && k < kend;
-    const unsigned off = valid ? ((unsigned)row * (unsigned)d.ldx + (unsigned)k) * 2u : d.x_bytes;
-    *(u4*)(xs + row * d.xrow + cc * 8) = ld16<0>(xr, off);
-  }
+  const int row = q / cpr;
+  const int k = k0 + (q - row * cpr) * 8;
+  const bool valid = q < total && row < d.M && k < kend;
+  return ld16<0>(xr, valid ? ((unsigned)row * (unsigned)d.ldx + (unsigned)k) * 2u : d.x_bytes);
 }
+
+__device__ __forceinline__ void x_store(const StageDesc& d, uint16_t* xs, int q, u4 v) {
+  const int cpr = d.win >> 3;
+  const int row = q / cpr;
+  *(u4*)(xs + row * d.xrow + (q - row * cpr) * 8) = v;
+}
+
+// Copy chunks [q0, total) of the window with all threads.
+__device__ __forceinline__ void stage_x(const StageDesc& d, uint16_t* xs, int rows_p, int k0, int kend,
+                                        Rsrc xr, int q0 = 0) {
+  const int total = rows_p * (d.win >> 3);
+#pragma unroll 4
+  for (int q = q0 + threadIdx.x; q < total; q += blockDim.x) x_store(d, xs, q, x_chunk(d, q, total, k0, kend, xr));
+}
+
+// Without a wait before X (single GEMM), the first kEarlyX chunks per thread
+// are loaded before the weight ring so that waiting for them does not wait
+// for the weights (vmcnt counts in issue order).
+constexpr int kEarlyX = 4;
 
 // Store one output element according to the stage's mode.  Out-of-range
 // elements are dropped by the buffer range check (off = extent).
@@ -303,6 +323,15 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     }
   };
 
+  constexpr bool early = __is_same(Hook, NoHook);
+  const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
+  const int xtotal = (M) * (d.win >> 3);
+  u4 xe[kEarlyX];
+  if constexpr (early) {
+#pragma unroll
+    for (int i = 0; i < kEarlyX; ++i)
+      xe[i] = x_chunk(d, (int)threadIdx.x + i * (int)blockDim.x, xtotal, s_first * d.KS, d.K, xr);
+  }
   Src sc = src_of(i0), sn = src_of(i0 + 1);
 #pragma unroll
   for (int p = 0; p < P; ++p) issue(ring[p], sc, p);
@@ -310,8 +339,16 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
 
   // One X window per workgroup and stage: the K range of every split its
   // items touch (the planner sizes d.win for the widest such range).
-  const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
-  stage_x(d, xs, M, s_first * d.KS, d.K, xr);
+  if constexpr (early) {
+#pragma unroll
+    for (int i = 0; i < kEarlyX; ++i) {
+      const int q = (int)threadIdx.x + i * (int)blockDim.x;
+      if (q < xtotal) x_store(d, xs, q, xe[i]);
+    }
+    stage_x(d, xs, M, s_first * d.KS, d.K, xr, kEarlyX * (int)blockDim.x);
+  } else {
+    stage_x(d, xs, M, s_first * d.KS, d.K, xr);
+  }
   __syncthreads();
 
   float acc[G][M];
@@ -410,12 +447,16 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
 // NT n-tiles of 16 columns per wave (PAIRED: tile 0 = gate rows, tile 1 = the
 // matching up rows pair_off further), MT m-tiles of 16 rows; every weight
 // fragment feeds all MT m-tiles.
-// Loads are coalesced: for half h of a 64-wide k-step, lane l reads 16 bytes
-// of weight row l/4 at k = 32h + 8(l%4), so four consecutive lanes cover 64
-// contiguous bytes of one row.  The MFMA B operand wants lane l' to hold
-// column l'%16 at k-group l'/16, so each dword is moved with one ds_bpermute
-// from lane 4(l'%16) + l'/16.  The A operand (X, from LDS) uses the same k
-// slots: lane l' reads row l'%16 at k = 32h + 8(l'/16).
+// Loads read whole 128-byte lines: for a 64-wide k-step of a 16-row n-tile,
+// load 0 gives lane l the 16-byte chunk l%8 of row l/8 and load 1 gives it
+// chunk (l%8)^4 of row 8 + l/8 (so eight lanes cover one line either way).
+// One v_cndmask per dword then gathers the chunks of MFMA half 0 (k 0..31:
+// chunks 0-3 of all 16 rows) into one register and those of half 1 into
+// another, and one ds_bpermute per dword moves them to the B-operand layout
+// (lane l' holds column l'%16 at k-group l'/16).  Issuing each line in one
+// instruction halves the L2 requests against two 64-byte halves per line.
+// The A operand (X, from LDS) uses the same k slots: lane l' reads row l'%16
+// at k = 32h + 8(l'/16).
 template <int MT, int NT, bool PAIRED, int AUX, typename Hook = NoHook>
 __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                            Hook pre_x = Hook()) {
@@ -442,22 +483,28 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   // Weight stream, organised as in the dot2 path (per-item base + constant
   // stride, branch-free masking through the buffer range check).
   struct Src {
-    unsigned base;  // byte offset of (weight row of column colb + lane/4, k = k0 + 8*(lane%4))
-    int klim;       // valid while t*64 + 32*h + 8*(lane%4) < klim
-    int col;        // the loaded row's column in n-tile 0 (n-tile j: col + 16 j unless paired)
+    unsigned base;  // byte offset of (weight row of column col0, k = k0)
+    int klim;       // chunk c of step t is valid while t*64 + 8c < klim
+    int col0;       // first column of n-tile 0 (n-tile j: col0 + 16 j unless paired)
   };
-  const int lrow = lane >> 2;  // row within the n-tile this lane loads
-  const int lq = lane & 3;     // 16-byte chunk within the row's 64 bytes
+  const int lr8 = lane >> 3;  // row within the 8-row half of the n-tile
+  int lch[2];                 // 16-byte chunk this lane loads, per load
+  unsigned loff[2];           // its byte offset from the n-tile's (row 0, k0)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    lch[h] = (lane & 7) ^ (4 * h);
+    loff[h] = ((unsigned)(8 * h + lr8) * (unsigned)d.K + 8u * (unsigned)lch[h]) * 2u;
+  }
   auto src_of = [&](int it) -> Src {
     Src r;
-    if (it >= i1) { r.base = 0; r.klim = 0; r.col = xc1; return r; }
+    if (it >= i1) { r.base = 0; r.klim = 0; r.col0 = xc1; return r; }
     const int s_ = it / d.NB;
     const int b_ = it - s_ * d.NB;
     const int k0 = s_ * d.KS;
-    const int col = xc0 + b_ * d.CB + wv * TW + lrow;
-    r.base = ((unsigned)col * (unsigned)d.K + (unsigned)k0 + 8u * (unsigned)lq) * 2u;
+    const int col0 = xc0 + b_ * d.CB + wv * TW;
+    r.base = ((unsigned)col0 * (unsigned)d.K + (unsigned)k0) * 2u;
     r.klim = min(d.K, k0 + d.KS) - k0;
-    r.col = col;
+    r.col0 = col0;
     return r;
   };
   // byte distance between the weight rows of n-tile j and n-tile 0
@@ -465,21 +512,29 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   auto issue = [&](u4(&dst)[NT][2], const Src& sr, int t) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const bool cj = (PAIRED ? sr.col : sr.col + 16 * j) < xc1;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const bool valid = cj && t * kMfmaKStep + 32 * h + 8 * lq < sr.klim;
-        const unsigned off = sr.base + (unsigned)j * jstride + (unsigned)t * (kMfmaKStep * 2u) + 64u * (unsigned)h;
+        const int col = sr.col0 + (PAIRED ? 0 : 16 * j) + 8 * h + lr8;
+        const bool valid = col < xc1 && t * kMfmaKStep + 8 * lch[h] < sr.klim;
+        const unsigned off = sr.base + loff[h] + (unsigned)j * jstride + (unsigned)t * (kMfmaKStep * 2u);
         dst[j][h] = ld16<AUX>(wr, valid ? off : d.w_bytes);
       }
     }
   };
-  // lane l' takes the dwords of lane 4(l'%16) + l'/16 (byte address for bpermute)
-  const int perm_addr = (4 * r16 + g4) * 4;
-  auto to_b = [&](u4 v) -> bf16x8 {
+  // Gather: half 0 takes load 0 on lanes with l%8 < 4 and load 1 elsewhere,
+  // half 1 the opposite.  Then lane l' = (c = l'%16, g = l'/16) takes the
+  // dwords of lane 8(c%8) + 4(c/8 ^ hh) + g (byte address for bpermute).
+  const bool lo = (lane & 7) < 4;
+  int perm_addr[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) perm_addr[hh] = (8 * (r16 & 7) + 4 * ((r16 >> 3) ^ hh) + g4) * 4;
+  auto to_b = [&](const u4(&v)[2], int hh) -> bf16x8 {
     u4 o;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = (unsigned)__builtin_amdgcn_ds_bpermute(perm_addr, (int)v[q]);
+    for (int q = 0; q < 4; ++q) {
+      const unsigned m = (lo == (hh == 0)) ? v[0][q] : v[1][q];
+      o[q] = (unsigned)__builtin_amdgcn_ds_bpermute(perm_addr[hh], (int)m);
+    }
     return __builtin_bit_cast(bf16x8, o);
   };
 
@@ -493,14 +548,32 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     }
   };
 
+  constexpr bool early = __is_same(Hook, NoHook);
+  const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
+  const int xtotal = (16 * MT) * (d.win >> 3);
+  u4 xe[kEarlyX];
+  if constexpr (early) {
+#pragma unroll
+    for (int i = 0; i < kEarlyX; ++i)
+      xe[i] = x_chunk(d, (int)threadIdx.x + i * (int)blockDim.x, xtotal, s_first * d.KS, d.K, xr);
+  }
   Src sc = src_of(i0), sn = src_of(i0 + 1);
 #pragma unroll
   for (int p = 0; p < P; ++p) issue(ring[p], sc, p);
   if (!pre_x()) return false;
 
-  // One X window per workgroup and stage (see the dot2 path).
-  const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
-  stage_x(d, xs, 16 * MT, s_first * d.KS, d.K, xr);
+  // One X window per workgroup and stage: the K range of every split its
+  // items touch (the planner sizes d.win for the widest such range).
+  if constexpr (early) {
+#pragma unroll
+    for (int i = 0; i < kEarlyX; ++i) {
+      const int q = (int)threadIdx.x + i * (int)blockDim.x;
+      if (q < xtotal) x_store(d, xs, q, xe[i]);
+    }
+    stage_x(d, xs, 16 * MT, s_first * d.KS, d.K, xr, kEarlyX * (int)blockDim.x);
+  } else {
+    stage_x(d, xs, 16 * MT, s_first * d.KS, d.K, xr);
+  }
   __syncthreads();
 
   f4 acc[NT][MT];
@@ -527,7 +600,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
           xa[i] = __builtin_bit_cast(bf16x8, *(const u4*)(xb + 16 * i * d.xrow + 32 * h));
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          const bf16x8 wb = to_b(ring[p][j][h]);
+          const bf16x8 wb = to_b(ring[p][j], h);
 #pragma unroll
           for (int i = 0; i < MT; ++i)
             acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], wb, acc[j][i], 0, 0, 0);

@@ -24,11 +24,14 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(StageDesc d, unsigned* status
   mfma_stage<MT, NT, false, AUX>(d, lds, blockIdx.x & 7, blockIdx.x >> 3, gridDim.x >> 3);
 }
 
-// dot2: M = 1..15, G in {4, 8} with G*M <= 64.  MFMA: MT = 1..4, NT = 1, 2.
+// dot2: M = 1..15, G in {1, 2, 3, 4, 8} with G*M <= 64.  MFMA: MT = 1..4, NT = 1, 2.
 template <int AUX>
 GemmKernel gemm_kernel_for(int path, int a, int b) {
 #define SG_D2(m)                                                    \
   case m:                                                           \
+    if (b == 1) return k_gemm_dot2<m, 1, AUX>;                      \
+    if (b == 2) return k_gemm_dot2<m, 2, AUX>;                      \
+    if (b == 3) return k_gemm_dot2<m, 3, AUX>;                      \
     if (b == 4) return k_gemm_dot2<m, 4, AUX>;                      \
     if (b == 8 && m * 8 <= 64) return k_gemm_dot2<m, (m * 8 <= 64 ? 8 : 4), AUX>; \
     return nullptr;

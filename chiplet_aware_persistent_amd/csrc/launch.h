@@ -22,6 +22,7 @@ struct ChainArgs {
   unsigned* status;                    // workspace word 0
   unsigned* lctr;                      // [kXcds][events] intra-XCD event counters
   unsigned* gctr;                      // [events] global event counters
+  unsigned* xflag;                     // [kXcds][events] per-XCD 'event seen' flags
   unsigned* done;                      // workgroups finished (reset by the last one)
   unsigned long long* stamps;          // [grid][events][2] or null
   int n_layers, M, d, q, dff;
