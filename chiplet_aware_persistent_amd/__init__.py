@@ -44,7 +44,8 @@ class Problem(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("M", ctypes.c_int), ("K", ctypes.c_int), ("N", ctypes.c_int),
                 ("out_dtype", ctypes.c_int), ("n_layers", ctypes.c_int), ("d_model", ctypes.c_int),
                 ("q_cols", ctypes.c_int), ("d_ff", ctypes.c_int), ("flags", ctypes.c_uint),
-                ("tn", ctypes.c_int), ("splitk", ctypes.c_int), ("waves", ctypes.c_int)]
+                ("tn", ctypes.c_int), ("splitk", ctypes.c_int), ("waves", ctypes.c_int),
+                ("kslices", ctypes.c_int)]
 
 
 _lib = None
@@ -192,8 +193,8 @@ class Gemm(_PlanBase):
     """Y[M,N] = X[M,K] . W^T with W stored [N][K] (K-major), bf16 in, fp32 (or bf16) out."""
 
     def __init__(self, M: int, K: int, N: int, out_dtype: int = OUT_F32, flags: int = 0, tn: int = 0,
-                 splitk: int = 0, waves: int = 0, device: int = 0):
-        p = Problem(KIND_GEMM, M, K, N, out_dtype, 0, 0, 0, 0, flags, tn, splitk, waves)
+                 splitk: int = 0, waves: int = 0, kslices: int = 0, device: int = 0):
+        p = Problem(KIND_GEMM, M, K, N, out_dtype, 0, 0, 0, 0, flags, tn, splitk, waves, kslices)
         super().__init__(p, device)
         self.M, self.K, self.N, self.out_dtype = M, K, N, out_dtype
 
@@ -215,8 +216,9 @@ class LayerChain(_PlanBase):
     """The per-layer projection chain (Q, O, gate_up + SiLU gate, down) in one launch."""
 
     def __init__(self, M: int, n_layers: int, d_model: int, q_cols: int, d_ff: int, flags: int = 0,
-                 tn: int = 0, splitk: int = 0, waves: int = 0, device: int = 0):
-        p = Problem(KIND_LAYERCHAIN, M, 0, 0, 0, n_layers, d_model, q_cols, d_ff, flags, tn, splitk, waves)
+                 tn: int = 0, splitk: int = 0, waves: int = 0, kslices: int = 0, device: int = 0):
+        p = Problem(KIND_LAYERCHAIN, M, 0, 0, 0, n_layers, d_model, q_cols, d_ff, flags, tn, splitk, waves,
+                    kslices)
         super().__init__(p, device)
         self.M, self.n_layers, self.d, self.q, self.dff = M, n_layers, d_model, q_cols, d_ff
 

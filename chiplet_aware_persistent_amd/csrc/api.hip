@@ -31,7 +31,8 @@ struct Geo {
   int M = 0, K = 0, N = 0;
   int ta = 0, tb = 0;  // template parameters: dot2 (M, G); MFMA (MT, NT)
   int waves = 8, wpi = 8, ng = 1, TN = 0, CB = 0, Nx = 0, NB = 0, S = 1, KS = 0, steps = 0, items = 0;
-  int win = 0, xrow = 0, lds = 0;
+  int ksl = 1, kss = 0;
+  int win = 0, xrow = 0, lds = 0, red_off = 0, stash_off = 0, stash_cap = 0;
   int paired = 0, pair_off = 0;
   size_t ctr_count = 0, part_floats = 0;
   double est_us = 0.0;
@@ -42,44 +43,59 @@ int env_int(const char* name, int dflt) {
   return v && *v ? std::atoi(v) : dflt;
 }
 
-// Fill the derived fields of g for (path, template params, waves, S); returns
-// false when the candidate does not fit (LDS, registers, instantiations).
+// Fill the derived fields of g for (path, template params, waves, wpi, ksl,
+// S); returns false when the candidate does not fit (LDS, instantiations).
 bool shape_geo(Geo& g, int want_S) {
   const int kstep = g.path == 0 ? kDot2KStep : kMfmaKStep;
+  if (g.wpi % g.ksl) return false;
   g.TN = g.path == 0 ? g.tb : (g.paired ? 16 : 16 * g.tb);
   g.ng = g.waves / g.wpi;
-  g.CB = g.wpi * g.TN;
+  if (g.ksl > 1 && g.ng != 1) return false;  // K slices reduce with workgroup barriers
+  g.CB = g.wpi / g.ksl * g.TN;
   g.Nx = (int)round_up((size_t)ceil_div(g.N, kXcds), 16);
   g.NB = ceil_div(g.Nx, g.CB);
   g.KS = (int)round_up((size_t)ceil_div(g.K, want_S), 8);
   g.S = ceil_div(g.K, g.KS);
+  g.kss = g.ksl > 1 ? (int)round_up((size_t)ceil_div(g.KS, g.ksl), kstep) : g.KS;
+  if (g.ksl > 1 && (g.ksl - 1) * g.kss >= g.KS) return false;  // an empty slice
   const int ring = g.path == 0 ? ring_depth_dot2(g.tb) : ring_depth_mfma(g.paired ? 2 : g.tb);
-  g.steps = ceil_div(ceil_div(g.KS, kstep), ring) * ring;  // padded to the ring depth
+  g.steps = ceil_div(ceil_div(g.kss, kstep), ring) * ring;  // padded to the ring depth
   g.items = g.NB * g.S;
   // A workgroup stages X once for all splits its contiguous item range
-  // touches: the window is (span - 1) splits plus one item's padded steps.
+  // touches: the window is (span - 1) splits plus the last slice's padded steps.
   int span = 1;
   for (int w = 0; w < kWgPerXcd; ++w) {
     const int i0 = (int)((long long)g.items * w / kWgPerXcd);
     const int i1 = (int)((long long)g.items * (w + 1) / kWgPerXcd);
     if (i0 < i1) span = std::max(span, (i1 - 1) / g.NB - i0 / g.NB + 1);
   }
-  g.win = (span - 1) * g.KS + g.steps * kstep;
+  g.win = (span - 1) * g.KS + (g.ksl - 1) * g.kss + g.steps * kstep;
   g.win = (int)round_up((size_t)g.win, 8);
   const int rows = g.path == 0 ? g.M : 16 * g.ta;
   g.xrow = g.path == 0 ? g.win : g.win + 8;
-  g.lds = rows * g.xrow * 2;
+  // LDS: X window, K-slice reduction buffer, output stash.
+  const int tile_bytes = g.path == 0 ? 64 * 4 : g.tb * g.ta * 1024;  // one wave's item result
+  g.red_off = (int)round_up((size_t)rows * g.xrow * 2, 1024);  // X is staged in 1 KB chunks
+  const int red_bytes = g.ksl > 1 ? (g.wpi / g.ksl) * (g.ksl - 1) * tile_bytes : 0;
+  g.stash_off = g.red_off + red_bytes;
+  const int owners = g.ksl > 1 ? g.wpi / g.ksl : g.waves;
+  const int per_stream = ceil_div(g.items, kWgPerXcd * g.ng);
+  g.stash_cap = std::max(0, std::min(per_stream, (kLdsMax - g.stash_off) / (owners * tile_bytes)));
+  g.lds = g.stash_off + owners * g.stash_cap * tile_bytes;
   const int vals = g.path == 0 ? g.tb * g.M : g.tb * g.ta * 256;
   g.ctr_count = (size_t)kXcds * g.NB * g.wpi;
   g.part_floats = g.S > 1 ? g.ctr_count * (size_t)g.S * vals : 0;
-  if (g.lds > kLdsMax) return false;
+  if (g.stash_off > kLdsMax) return false;
+  // MFMA with S == 1 emits Y only from the stash (no epilogue inside the
+  // weight loop), so every item of a stream must fit it.
+  if (g.path == 1 && g.S == 1 && g.stash_cap < per_stream) return false;
   if (!gemm_variant_exists(g.path, g.ta, g.tb) && !g.paired) return false;
   // Cost model (microseconds): streaming time of the busiest workgroup at the
-  // per-CU share of HBM bandwidth, a per-item cost, and for split-K the
-  // finalize round trips (arrival atomics, partial reads) at the end.  A
-  // workgroup keeps waves * 16 KB of weight loads in flight; fewer than 8
-  // waves leave the per-CU share unreached.  Wide dot2 tiles (G = 8) cost
-  // VALU time that shows from M = 4 on.
+  // per-CU share of HBM bandwidth, its X staging from L2, per-item costs
+  // (a store at item end, K-slice barriers), and for split-K the finalize
+  // round trips (arrival atomics, partial reads) at the end.  A workgroup
+  // keeps waves * 16 KB of weight loads in flight; fewer than 8 waves leave
+  // the per-CU share unreached.
   // Per-CU rates (bytes of W per second): the HBM share, the LDS traffic the
   // inner loop generates per weight byte (dot2: X reads M/G; MFMA: A reads
   // MT/NT plus the B permute), and dot2's VALU time (4 M dot2 cycles per KB
@@ -89,26 +105,30 @@ bool shape_geo(Geo& g, int want_S) {
   const double lds_per_w = g.path == 0 ? (double)g.M / g.tb : (double)g.ta / g.tb + 1.0;
   bw_cu = std::min(bw_cu, lds_cu / lds_per_w);
   if (g.path == 0) bw_cu = std::min(bw_cu, 1024.0 / (4.0 * g.M + 4.0) * 2.4e9 * 0.7);
-  const int per_stream = ceil_div(g.items, kWgPerXcd * g.ng);
   const double item_bytes = (double)g.CB * g.KS * 2.0 * (g.paired ? 2.0 : 1.0);
   const double part_bytes = g.S > 1 ? (double)g.CB * g.M * 4.0 * 2.0 : 0.0;
   const double wg_bytes = (double)g.ng * per_stream * (item_bytes + part_bytes);
-  const double pad = (double)g.steps * kstep / std::max(g.KS, 1);  // issue slots per useful K
-  g.est_us = wg_bytes / bw_cu * 1e6 + per_stream * 0.2 * pad + (g.S > 1 ? 2.5 : 0.0) +
+  const double pad = (double)g.steps * kstep * g.ksl / std::max(g.KS, 1);  // issue slots per useful K
+  const double x_us = (double)rows * g.win * 2.0 / 200.0e9 * 1e6;
+  const double item_us = (per_stream > g.stash_cap ? 0.2 : 0.05) + (g.ksl > 1 ? 0.1 : 0.0);
+  g.est_us = wg_bytes / bw_cu * 1e6 + per_stream * item_us * pad + x_us + (g.S > 1 ? 2.5 : 0.0) +
              (span > 1 ? 0.5 : 0.0);
   return true;
 }
 
-bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, int s_o, int waves_o) {
+bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, int s_o, int waves_o,
+              int ksl_o) {
   bool found = false;
   const int waves_opts[2] = {8, 4};
   for (int wi = 0; wi < 2; ++wi) {
     const int waves = waves_opts[wi];
     if (waves_o && waves != waves_o) continue;
     for (int wpi = 1; wpi <= waves; wpi *= 2)
+    for (int ksl = 1; ksl <= (path == 1 ? wpi : 1); ksl *= 2)
     for (int tb = 1; tb <= 8; ++tb) {
+      if (ksl_o && ksl != ksl_o) continue;
       Geo g;
-      g.path = path; g.M = M; g.K = K; g.N = N; g.waves = waves; g.wpi = wpi;
+      g.path = path; g.M = M; g.K = K; g.N = N; g.waves = waves; g.wpi = wpi; g.ksl = ksl;
       g.paired = paired;
       if (path == 0) {
         if (tb == 5 || tb == 6 || tb == 7) continue;
@@ -185,8 +205,10 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
   *out = nullptr;
   const sgemm_problem& p = *problem;
   if ((p.flags & SGEMM_F_FORCE_DOT2) && (p.flags & SGEMM_F_FORCE_MFMA)) return SGEMM_ERR_INVALID_ARG;
-  if (p.tn < 0 || p.splitk < 0 || p.waves < 0) return SGEMM_ERR_INVALID_ARG;
+  if (p.tn < 0 || p.splitk < 0 || p.waves < 0 || p.kslices < 0) return SGEMM_ERR_INVALID_ARG;
   if (p.waves && p.waves != 4 && p.waves != 8) return SGEMM_ERR_INVALID_ARG;
+  if (p.kslices && p.kslices != 1 && p.kslices != 2 && p.kslices != 4 && p.kslices != 8)
+    return SGEMM_ERR_INVALID_ARG;
   if (p.splitk > 64) return SGEMM_ERR_UNSUPPORTED;
   if (device < 0) return SGEMM_ERR_INVALID_ARG;
 
@@ -199,13 +221,15 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
   const int tn_o = p.tn ? p.tn : env_int("SGEMM_TN", 0);
   const int s_o = p.splitk ? p.splitk : env_int("SGEMM_SPLITK", 0);
   const int w_o = p.waves ? p.waves : env_int("SGEMM_WAVES", 0);
+  const int k_o = p.kslices ? p.kslices : env_int("SGEMM_KSLICES", 0);
 
   size_t cur = kCtl;
   if (p.kind == SGEMM_KIND_GEMM) {
     int rc = validate_gemm(p);
     if (rc != SGEMM_OK) { delete pl; return rc; }
     const int path = choose_path(p);
-    if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o)) {
+    if (path == 0 && k_o > 1) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o)) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
     }
@@ -231,7 +255,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
         bool ok = chain_variant_exists((p.M + 15) / 16, nt, nt, nt);
         for (int s = 0; s < kChainStages && ok; ++s) {
           const int paired = s == 2;
-          ok = plan_geo(c[s], p.M, Ks[s], Ns[s], 1, paired, paired ? 0 : 16 * nt, s_o, waves);
+          ok = plan_geo(c[s], p.M, Ks[s], Ns[s], 1, paired, paired ? 0 : 16 * nt, s_o, waves, k_o);
           if (ok && paired) c[s].pair_off = p.d_ff;
           tot += ok ? c[s].est_us : 0.0;
         }
@@ -291,8 +315,9 @@ static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
   std::memset(&d, 0, sizeof d);
   d.M = g.M; d.K = g.K; d.N = g.N;
   d.Nx = g.Nx; d.TN = g.TN; d.wpi = g.wpi; d.ng = g.ng; d.CB = g.CB; d.NB = g.NB; d.S = g.S;
-  d.KS = g.KS;
+  d.KS = g.KS; d.ksl = g.ksl; d.kss = g.kss;
   d.steps = g.steps; d.items = g.items; d.win = g.win; d.xrow = g.xrow;
+  d.red_off = g.red_off; d.stash_off = g.stash_off; d.stash_cap = g.stash_cap;
   d.pair_off = g.pair_off;
   d.w_aux = w_aux;
   d.sync = sync;
@@ -438,10 +463,11 @@ static std::string geo_json(const Geo& g) {
   char b[512];
   std::snprintf(b, sizeof b,
                 "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,\"wpi\":%d,"
-                "\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,\"steps\":%d,"
-                "\"items\":%d,\"lds\":%d,\"paired\":%d,\"est_us\":%.3f}",
-                g.path == 0 ? "dot2" : "mfma", g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.TN, g.CB, g.Nx,
-                g.NB, g.S, g.KS, g.steps, g.items, g.lds, g.paired, g.est_us);
+                "\"ksl\":%d,\"kss\":%d,\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,"
+                "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
+                "\"est_us\":%.3f}",
+                g.path == 0 ? "dot2" : "mfma", g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
+                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.est_us);
   return b;
 }
 

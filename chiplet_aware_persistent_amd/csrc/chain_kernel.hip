@@ -176,14 +176,15 @@ static ChainKernel chain_kernel(int mt, int nt) {
     case 2 * 4 + 1: return k_chain<2, 1>;
     case 2 * 4 + 2: return k_chain<2, 2>;
     case 3 * 4 + 1: return k_chain<3, 1>;
-    case 3 * 4 + 2: return k_chain<3, 2>;
     case 4 * 4 + 1: return k_chain<4, 1>;
-    case 4 * 4 + 2: return k_chain<4, 2>;
     default: return nullptr;
   }
 }
 
 bool chain_variant_exists(int mt, int nt_q, int nt_o, int nt_d) {
+  // MT >= 3 with two n-tiles in the unpaired stages does not fit the register
+  // file next to the paired gate_up stage (it spills), so it is not offered.
+  if (mt >= 3 && nt_q == 2) return false;
   return nt_q == nt_o && nt_o == nt_d && chain_kernel(mt, nt_q) != nullptr;
 }
 

@@ -14,6 +14,14 @@
 //     (from LDS) and W as the B operand (straight from the load registers);
 //     every weight fragment feeds all ceil(M/16) m-tiles before it is dropped,
 //     which is the M-major reuse of a weight column done in registers.
+// MFMA items can also be cut along K inside the workgroup: ksl waves share a
+// column group, each streams one K slice, and the slices are added up in slice
+// order through LDS at the end of the item (the intra-CTA K-slice of the
+// MI355X low-latency GEMM news item, technique 2), which gives every wave a
+// share of a small GEMM without going through global memory.
+// Item results wait in an LDS stash and are stored after the weight stream:
+// vmcnt counts loads and stores in issue order, so a store issued mid-stream
+// would make the next wait for a weight load also wait for the store.
 // With S > 1 the K splits of a wave tile land in an fp32 workspace and the
 // wave that arrives last (arrival counter, old value S-1) adds them up in
 // split order and writes Y, so the result does not depend on arrival order.
@@ -207,34 +215,36 @@ __device__ __forceinline__ int first_item_of_wg(int items, int slot, int nslots)
 }
 
 // X window: rows [0, rows_p) x columns [k0, k0 + win) of X go to LDS (row
-// stride d.xrow), zero outside [0,M) x [k0,kend).  Chunk q (16 bytes) is row
-// q / (win/8), column 8 * (q % (win/8)).
-__device__ __forceinline__ u4 x_chunk(const StageDesc& d, int q, int total, int k0, int kend, Rsrc xr) {
-  const int cpr = d.win >> 3;
-  const int row = q / cpr;
-  const int k = k0 + (q - row * cpr) * 8;
-  const bool valid = q < total && row < d.M && k < kend;
-  return ld16<0>(xr, valid ? ((unsigned)row * (unsigned)d.ldx + (unsigned)k) * 2u : d.x_bytes);
+// stride d.xrow elements), zero outside [0,M) x [k0,kend) and in the row
+// padding.  The window is filled with gfx950's buffer-to-LDS loads: one wave
+// instruction fills one kilobyte of LDS (lane l the 16 bytes at 16 l), and
+// each lane fetches the X values that belong at its LDS position, so no
+// registers or LDS writes are involved and the loads can be issued ahead of
+// the weight ring.  d.red_off (the end of the window region) is a multiple of
+// 1 KB, so every chunk stays inside the window region.
+__device__ __forceinline__ void stage_x_lds(const StageDesc& d, uint16_t* xs, int rows_p, int k0, int kend,
+                                            Rsrc xr) {
+  const int lane = threadIdx.x & 63;
+  const int nw = (int)(blockDim.x >> 6);
+  const int chunks = d.red_off >> 10;
+  for (int c = (int)(threadIdx.x >> 6); c < chunks; c += nw) {
+    const int e = (c * 1024 + lane * 16) >> 1;  // element of the window buffer
+    const int row = e / d.xrow;
+    const int col = e - row * d.xrow;
+    const int k = k0 + col;
+    const bool valid = row < rows_p && row < d.M && col < d.win && k < kend;
+    const unsigned off = valid ? ((unsigned)row * (unsigned)d.ldx + (unsigned)k) * 2u : d.x_bytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)((char*)xs + c * 1024),
+                                             16, off, 0, 0, 0);
+  }
 }
 
-__device__ __forceinline__ void x_store(const StageDesc& d, uint16_t* xs, int q, u4 v) {
-  const int cpr = d.win >> 3;
-  const int row = q / cpr;
-  *(u4*)(xs + row * d.xrow + (q - row * cpr) * 8) = v;
+// s_waitcnt vmcnt(n) (n < 64), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-
-// Copy chunks [q0, total) of the window with all threads.
-__device__ __forceinline__ void stage_x(const StageDesc& d, uint16_t* xs, int rows_p, int k0, int kend,
-                                        Rsrc xr, int q0 = 0) {
-  const int total = rows_p * (d.win >> 3);
-#pragma unroll 4
-  for (int q = q0 + threadIdx.x; q < total; q += blockDim.x) x_store(d, xs, q, x_chunk(d, q, total, k0, kend, xr));
-}
-
-// Without a wait before X (single GEMM), the first kEarlyX chunks per thread
-// are loaded before the weight ring so that waiting for them does not wait
-// for the weights (vmcnt counts in issue order).
-constexpr int kEarlyX = 4;
 
 // Store one output element according to the stage's mode.  Out-of-range
 // elements are dropped by the buffer range check (off = extent).
@@ -288,6 +298,19 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   const int idx = lane / grp;
   const bool owner = (lane % grp) == 0 && idx < GM;
   const int oc = idx / M, om = idx - (idx / M) * M;
+  float* stash = (float*)((char*)xs + d.stash_off);  // [wave][stash_cap][64]
+  // Result of item `it` (lane value r): Y when S == 1, else the partial.
+  auto out_item = [&](int it, float r) {
+    const int s = it / d.NB;
+    const int b = it - s * d.NB;
+    const int col = xc0 + b * d.CB + wv * G + oc;
+    if (d.S == 1) {
+      store_out(d, yr, y2r, owner && col < xc1 && om < d.M, om, col, r);
+    } else {
+      const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
+      st_f32<0>(pr, owner ? ((tile * d.S + s) * GM + idx) * 4u : d.part_bytes, r);
+    }
+  };
 
   u4 ring[P][G];
   // Weight stream.  Slot p of the ring holds step t0+p of the current item;
@@ -323,32 +346,26 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     }
   };
 
+  // One X window per workgroup and stage: the K range of every split its
+  // items touch (the planner sizes d.win for the widest such range).  In a
+  // single launch the window loads go out before the weight ring, so waiting
+  // until only the ring's loads are outstanding covers them; in the chain X
+  // exists only after the wait, so its loads follow the ring.
   constexpr bool early = __is_same(Hook, NoHook);
   const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
-  const int xtotal = (M) * (d.win >> 3);
-  u4 xe[kEarlyX];
-  if constexpr (early) {
-#pragma unroll
-    for (int i = 0; i < kEarlyX; ++i)
-      xe[i] = x_chunk(d, (int)threadIdx.x + i * (int)blockDim.x, xtotal, s_first * d.KS, d.K, xr);
-  }
+  if constexpr (early) stage_x_lds(d, xs, M, s_first * d.KS, d.K, xr);
   Src sc = src_of(i0), sn = src_of(i0 + 1);
 #pragma unroll
   for (int p = 0; p < P; ++p) issue(ring[p], sc, p);
   if (!pre_x()) return false;
-
-  // One X window per workgroup and stage: the K range of every split its
-  // items touch (the planner sizes d.win for the widest such range).
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (early) {
-#pragma unroll
-    for (int i = 0; i < kEarlyX; ++i) {
-      const int q = (int)threadIdx.x + i * (int)blockDim.x;
-      if (q < xtotal) x_store(d, xs, q, xe[i]);
-    }
-    stage_x(d, xs, M, s_first * d.KS, d.K, xr, kEarlyX * (int)blockDim.x);
+    wait_vm<P * G>();
   } else {
-    stage_x(d, xs, M, s_first * d.KS, d.K, xr);
+    stage_x_lds(d, xs, M, s_first * d.KS, d.K, xr);
+    wait_vm0();
   }
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
   float acc[G][M];
@@ -381,8 +398,6 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     }
     t0 += P;
     if (t0 == spad) {  // item complete
-      const int s = it / d.NB;
-      const int b = it - s * d.NB;
       float v[V];
 #pragma unroll
       for (int i = 0; i < V; ++i) v[i] = 0.f;
@@ -391,12 +406,11 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
 #pragma unroll
         for (int m = 0; m < M; ++m) v[c * M + m] = acc[c][m];
       const float r = wave_reduce_scatter<V>(v, lane);
-      const int col = xc0 + b * d.CB + wv * G + oc;
-      if (d.S == 1) {
-        store_out(d, yr, y2r, owner && col < xc1 && om < d.M, om, col, r);
+      const int li = it - i0;
+      if (li < d.stash_cap) {
+        stash[(wave * d.stash_cap + li) * 64 + lane] = r;
       } else {
-        const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
-        st_f32<0>(pr, owner ? ((tile * d.S + s) * GM + idx) * 4u : d.part_bytes, r);
+        out_item(it, r);
       }
 #pragma unroll
       for (int c = 0; c < G; ++c)
@@ -408,6 +422,12 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
       sn = src_of(it + 1);
       xoff = (it / d.NB - s_first) * d.KS;
     }
+  }
+
+  // Stored items: results of the stream, written after its last load.
+  {
+    const int n = min(i1 - i0, d.stash_cap);
+    for (int li = 0; li < n; ++li) out_item(i0 + li, stash[(wave * d.stash_cap + li) * 64 + lane]);
   }
 
   if (d.S > 1 && i0 < i1) {
@@ -470,6 +490,10 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   int i0, i1;
   my_items(d.items, slot, nslots, d.ng, wave / d.wpi, i0, i1);
   const int wv = wave % d.wpi;  // wave's place within its item
+  const int CG = d.wpi / d.ksl; // column groups per item
+  const int cg = wv % CG;       // this wave's column group
+  const int kq = wv / CG;       // this wave's K slice
+  const bool owner = kq == 0;   // ends up with the item's tile (then wv == cg)
   const int xc0 = xcd * d.Nx;
   const int xc1 = min(d.N, xc0 + d.Nx);
   const Rsrc wr = make_rsrc(d.W, d.w_bytes);
@@ -478,6 +502,11 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   const Rsrc y2r = make_rsrc(d.Y2, d.y2_bytes);
   const Rsrc pr = make_rsrc(d.part, d.part_bytes);
   const int spad = d.steps;  // multiple of P
+  // LDS after the X window: K-slice reduction [CG][ksl-1][NT*MT][64] and the
+  // output stash [owner][stash_cap][NT*MT][64], f4 per lane.
+  f4* red = (f4*)((char*)xs + d.red_off);
+  f4* stash = (f4*)((char*)xs + d.stash_off);
+  const int own = d.ksl > 1 ? cg : wave;
 
   u4 ring[P][NT][2];
   // Weight stream, organised as in the dot2 path (per-item base + constant
@@ -500,10 +529,10 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     if (it >= i1) { r.base = 0; r.klim = 0; r.col0 = xc1; return r; }
     const int s_ = it / d.NB;
     const int b_ = it - s_ * d.NB;
-    const int k0 = s_ * d.KS;
-    const int col0 = xc0 + b_ * d.CB + wv * TW;
+    const int k0 = s_ * d.KS + kq * d.kss;
+    const int col0 = xc0 + b_ * d.CB + cg * TW;
     r.base = ((unsigned)col0 * (unsigned)d.K + (unsigned)k0) * 2u;
-    r.klim = min(d.K, k0 + d.KS) - k0;
+    r.klim = min(min(d.K, (s_ + 1) * d.KS) - k0, d.kss);  // <= 0: slice past the split
     r.col0 = col0;
     return r;
   };
@@ -547,33 +576,52 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
       store_out(d, yr, y2r, ok, m, col, PAIRED ? silu_mul(v[e], vu[e]) : v[e]);
     }
   };
+  // The finished tile of item `it` (owner wave): Y when S == 1, else the
+  // split's partial.
+  auto out_tile = [&](int it, const f4(&v)[NT][MT]) {
+    const int s = it / d.NB;
+    const int b = it - s * d.NB;
+    if (d.S == 1) {
+      const int colb = xc0 + b * d.CB + wv * TW;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        if (PAIRED) {
+          emit(colb, 0, i, v[0][i], v[1][i]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NT; ++j) emit(colb, j, i, v[j][i], v[j][i]);
+        }
+      }
+    } else {
+      const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          st_f4<0>(pr, ((tile * d.S + s) * TILE + (j * MT + i) * 256 + lane * 4) * 4u, v[j][i]);
+    }
+  };
 
+  // One X window per workgroup and stage: the K range of every split its
+  // items touch (the planner sizes d.win for the widest such range).  In a
+  // single launch the window loads go out before the weight ring, so waiting
+  // until only the ring's loads are outstanding covers them; in the chain X
+  // exists only after the wait, so its loads follow the ring.
   constexpr bool early = __is_same(Hook, NoHook);
   const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
-  const int xtotal = (16 * MT) * (d.win >> 3);
-  u4 xe[kEarlyX];
-  if constexpr (early) {
-#pragma unroll
-    for (int i = 0; i < kEarlyX; ++i)
-      xe[i] = x_chunk(d, (int)threadIdx.x + i * (int)blockDim.x, xtotal, s_first * d.KS, d.K, xr);
-  }
+  if constexpr (early) stage_x_lds(d, xs, 16 * MT, s_first * d.KS, d.K, xr);
   Src sc = src_of(i0), sn = src_of(i0 + 1);
 #pragma unroll
   for (int p = 0; p < P; ++p) issue(ring[p], sc, p);
   if (!pre_x()) return false;
-
-  // One X window per workgroup and stage: the K range of every split its
-  // items touch (the planner sizes d.win for the widest such range).
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (early) {
-#pragma unroll
-    for (int i = 0; i < kEarlyX; ++i) {
-      const int q = (int)threadIdx.x + i * (int)blockDim.x;
-      if (q < xtotal) x_store(d, xs, q, xe[i]);
-    }
-    stage_x(d, xs, 16 * MT, s_first * d.KS, d.K, xr, kEarlyX * (int)blockDim.x);
+    wait_vm<P * NT * 2>();
   } else {
-    stage_x(d, xs, 16 * MT, s_first * d.KS, d.K, xr);
+    stage_x_lds(d, xs, 16 * MT, s_first * d.KS, d.K, xr);
+    wait_vm0();
   }
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
   f4 acc[NT][MT];
@@ -582,7 +630,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[j][i] = f4{0.f, 0.f, 0.f, 0.f};
   int it = i0, t0 = 0;
-  int xoff = (i0 / d.NB - s_first) * d.KS;
+  int xoff = (i0 / d.NB - s_first) * d.KS + kq * d.kss;
   const int total = (i1 - i0) * spad;
   for (int T = 0; T < total; T += P) {
     const bool here = t0 + P < spad;
@@ -611,26 +659,48 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     }
     t0 += P;
     if (t0 == spad) {  // item complete
-      const int s = it / d.NB;
-      const int b = it - s * d.NB;
-      const int colb = xc0 + b * d.CB + wv * TW;
-      if (d.S == 1) {
+      if (d.ksl > 1) {
+        // Slices 1..ksl-1 hand their sums to the slice-0 wave, which adds
+        // them in slice order.  All waves of the workgroup share one item
+        // stream here, so they reach these barriers together.
+        if (!owner) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          if (PAIRED) {
-            emit(colb, 0, i, acc[0][i], acc[1][i]);
-          } else {
+          for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) emit(colb, j, i, acc[j][i], acc[j][i]);
+            for (int i = 0; i < MT; ++i)
+              red[((cg * (d.ksl - 1) + kq - 1) * (NT * MT) + j * MT + i) * 64 + lane] = acc[j][i];
+        }
+        __syncthreads();
+        if (owner) {
+          for (int q = 1; q < d.ksl; ++q) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+              for (int i = 0; i < MT; ++i)
+                acc[j][i] += red[((cg * (d.ksl - 1) + q - 1) * (NT * MT) + j * MT + i) * 64 + lane];
           }
         }
-      } else {
-        const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
+        __syncthreads();
+      }
+      if (owner) {
+        const int li = it - i0;
+        if (li < d.stash_cap) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+          for (int j = 0; j < NT; ++j)
 #pragma unroll
-          for (int i = 0; i < MT; ++i)
-            st_f4<0>(pr, ((tile * d.S + s) * TILE + (j * MT + i) * 256 + lane * 4) * 4u, acc[j][i]);
+            for (int i = 0; i < MT; ++i) stash[((own * d.stash_cap + li) * (NT * MT) + j * MT + i) * 64 + lane] = acc[j][i];
+        } else {
+          // Stash full (the planner allows this only with S > 1): the
+          // split's partial goes out now.  Only this plain store sits in the
+          // loop, which keeps the epilogue's registers out of it.
+          const int s = it / d.NB;
+          const unsigned tile = (unsigned)((xcd * d.NB + (it - s * d.NB)) * d.wpi + wv);
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+              st_f4<0>(pr, ((tile * d.S + s) * TILE + (j * MT + i) * 256 + lane * 4) * 4u, acc[j][i]);
+        }
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j)
@@ -640,11 +710,24 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
       t0 = 0;
       sc = sn;
       sn = src_of(it + 1);
-      xoff = (it / d.NB - s_first) * d.KS;
+      xoff = (it / d.NB - s_first) * d.KS + kq * d.kss;
     }
   }
 
-  if (d.S > 1 && i0 < i1) {
+  // Stored items: results of the stream, written after its last load.
+  if (owner) {
+    const int n = min(i1 - i0, d.stash_cap);
+    for (int li = 0; li < n; ++li) {
+      f4 v[NT][MT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) v[j][i] = stash[((own * d.stash_cap + li) * (NT * MT) + j * MT + i) * 64 + lane];
+      out_tile(i0 + li, v);
+    }
+  }
+
+  if (d.S > 1 && i0 < i1 && owner) {
     splitk_release(d.sync);
     constexpr int B = 4;
     for (int c0 = i0; c0 < i1; c0 += B) {

@@ -39,15 +39,21 @@ struct StageDesc {
   int Nx;              // columns owned by one XCD (XCD x: [x*Nx, min(N,(x+1)*Nx)))
   int TN;              // columns per wave tile
   int wpi;             // waves per item: a workgroup runs waves/wpi item streams
-  int CB;              // columns per item = wpi * TN
+  int ksl;             // K slices per item (MFMA): wpi = (wpi/ksl) column groups x ksl
+  int kss;             // K values per slice (multiple of the k-step when ksl > 1)
+  int CB;              // columns per item = (wpi / ksl) * TN
   int NB;              // column blocks per XCD
   int S;               // K splits
   int KS;              // K values per split (multiple of 8)
-  int steps;           // wave k-steps per item
+  int steps;           // wave k-steps per item (per K slice), padded to the ring depth
   int items;           // items per XCD = NB * S (ordered split-major)
   int ng;              // item streams (wave groups) per workgroup = waves / wpi
-  int win;             // LDS window width (elements) = steps * kstep
+  int win;             // LDS window width (elements)
   int xrow;            // LDS row stride (elements)
+  int red_off;         // LDS byte offset of the K-slice reduction buffer
+  int stash_off;       // LDS byte offset of the output stash
+  int stash_cap;       // items per owning wave whose results wait in LDS until the
+                       // weight stream ends (the rest are stored at item end)
   int pair_off;        // paired: weight row offset of the up half
   int mode;            // OutMode
   int sync;            // SyncMode of the split-K arrival

@@ -82,8 +82,10 @@ enum {
  *       with Wq [q_cols][d_model], Wo [d_model][q_cols], Wgu [2 d_ff][d_model]
  *       (g = rows 0..d_ff-1, u = rows d_ff..2 d_ff-1), Wdown [d_model][d_ff],
  *       all K-major.
- *   tn, splitk, waves: 0 lets the planner choose; otherwise they override the
- *       columns per wave tile, the K split count and the waves per workgroup.
+ *   tn, splitk, waves, kslices: 0 lets the planner choose; otherwise they
+ *       override the columns per wave tile, the K split count across
+ *       workgroups, the waves per workgroup and (MFMA path) the K slices per
+ *       item inside a workgroup (1, 2, 4 or 8; slices are reduced through LDS).
  */
 typedef struct {
   int kind;
@@ -91,7 +93,7 @@ typedef struct {
   int out_dtype;
   int n_layers, d_model, q_cols, d_ff;
   unsigned flags;
-  int tn, splitk, waves;
+  int tn, splitk, waves, kslices;
 } sgemm_problem;
 
 /*

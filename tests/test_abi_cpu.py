@@ -27,7 +27,8 @@ def test_exports_every_header_function():
 def _create(**kw):
     p = sg.Problem(kw.get("kind", sg.KIND_GEMM), kw.get("M", 1), kw.get("K", 64), kw.get("N", 64),
                    kw.get("out", sg.OUT_F32), kw.get("L", 0), kw.get("d", 0), kw.get("q", 0), kw.get("dff", 0),
-                   kw.get("flags", 0), kw.get("tn", 0), kw.get("splitk", 0), kw.get("waves", 0))
+                   kw.get("flags", 0), kw.get("tn", 0), kw.get("splitk", 0), kw.get("waves", 0),
+                   kw.get("ksl", 0))
     rc, h, ws = sg.sgemm_plan_create(p)
     if h:
         sg.sgemm_plan_destroy(h)
@@ -44,6 +45,10 @@ def _create(**kw):
     (dict(flags=sg.F_FORCE_DOT2 | sg.F_FORCE_MFMA), sg.ERR_INVALID_ARG),
     (dict(waves=3), sg.ERR_INVALID_ARG),
     (dict(splitk=65), sg.ERR_UNSUPPORTED),
+    (dict(ksl=3), sg.ERR_INVALID_ARG),
+    (dict(ksl=-1), sg.ERR_INVALID_ARG),
+    (dict(M=4, ksl=2), sg.ERR_UNSUPPORTED),               # K slices are an MFMA-path option
+    (dict(M=16, K=4096, N=4096, ksl=8), sg.OK),
     (dict(kind=9), sg.ERR_INVALID_ARG),
     (dict(K=1 << 20, N=1 << 12), sg.ERR_UNSUPPORTED),
     (dict(kind=sg.KIND_LAYERCHAIN, M=4, L=0, d=64, q=64, dff=64), sg.ERR_INVALID_ARG),
@@ -91,14 +96,28 @@ def test_planner_covers_every_column_and_k_once(M, K, N, splitk):
     st = g.describe()["stage"]
     assert st["path"] == ("dot2" if M < 16 else "mfma")
     Nx, CB, NB, S, KS = st["Nx"], st["CB"], st["NB"], st["S"], st["KS"]
-    assert CB == st["wpi"] * st["TN"] and st["waves"] % st["wpi"] == 0
+    ksl, kss = st["ksl"], st["kss"]
+    assert st["wpi"] % ksl == 0 and CB == st["wpi"] // ksl * st["TN"] and st["waves"] % st["wpi"] == 0
+    assert ksl == 1 or (st["path"] == "mfma" and st["wpi"] == st["waves"])  # one item stream per workgroup
     assert 8 * Nx >= N and 8 * (Nx - 16) < N          # per-XCD partition covers N, no spare XCD block
     assert NB * CB >= Nx                               # column blocks cover the XCD's columns
     assert S * KS >= K and (S - 1) * KS < K            # splits cover K, none empty
+    assert ksl * kss >= KS and (ksl - 1) * kss < KS    # slices cover a split, none empty
     assert KS % 8 == 0 and st["items"] == NB * S
     kstep = 512 if st["path"] == "dot2" else 64
-    assert st["steps"] * kstep >= KS
+    assert ksl == 1 or kss % kstep == 0
+    assert st["steps"] * kstep >= kss
     assert st["lds"] <= 160 * 1024
+    # every k of a split is streamed by exactly one slice, and the LDS window
+    # holds what the last slice reads including its padded steps
+    for s in range(S):
+        seen = []
+        for q in range(ksl):
+            k0 = s * KS + q * kss
+            klim = min(min(K, (s + 1) * KS) - k0, kss)
+            seen += list(range(k0, k0 + max(klim, 0)))
+        assert seen == list(range(s * KS, min(K, (s + 1) * KS)))
+    assert st["win"] >= (ksl - 1) * kss + st["steps"] * kstep
     if splitk:
         assert S == min(splitk, math.ceil(K / 8)) or S == math.ceil(K / math.ceil(K / splitk / 8) / 8)
     # columns: every column owned by exactly one (xcd, block, wave, lane-column)

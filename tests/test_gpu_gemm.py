@@ -91,6 +91,22 @@ def test_parity_tilings(cuda_device, waves, tn):
         check(run(g, X, W).cpu().numpy(), x, w)
 
 
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 1040), (33, 2056, 777), (64, 1000, 530), (20, 12288, 300),
+                                   (48, 520, 64)])
+@pytest.mark.parametrize("ksl", [2, 4, 8])
+@pytest.mark.parametrize("splitk", [0, 3])
+def test_parity_kslices(cuda_device, M, K, N, ksl, splitk):
+    x, w, X, W = gemm_inputs(M, K, N, 9700 + M, 9800 + K, cuda_device)
+    try:
+        g = sg.Gemm(M, K, N, kslices=ksl, splitk=splitk)
+    except sg.SgemmError as e:
+        assert e.code == sg.ERR_UNSUPPORTED
+        pytest.skip("no plan with these K slices fits (empty slice or LDS)")
+    st = g.describe()["stage"]
+    assert st["ksl"] == ksl and st["wpi"] == st["waves"]
+    check(run(g, X, W).cpu().numpy(), x, w)
+
+
 @pytest.mark.parametrize("M", [2, 20])
 def test_bf16_output(cuda_device, M):
     K, N = 2056, 900
