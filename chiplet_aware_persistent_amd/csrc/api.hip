@@ -54,7 +54,9 @@ bool shape_geo(Geo& g, int want_S) {
   g.CB = g.wpi / g.ksl * g.TN;
   g.Nx = (int)round_up((size_t)ceil_div(g.N, kXcds), 16);
   g.NB = ceil_div(g.Nx, g.CB);
-  g.KS = (int)round_up((size_t)ceil_div(g.K, want_S), 8);
+  // Splits start on whole 128-byte lines of the weight rows (64 values), so
+  // no line is fetched by two splits.
+  g.KS = (int)round_up((size_t)ceil_div(g.K, want_S), 64);
   g.S = ceil_div(g.K, g.KS);
   g.kss = g.ksl > 1 ? (int)round_up((size_t)ceil_div(g.KS, g.ksl), kstep) : g.KS;
   if (g.ksl > 1 && (g.ksl - 1) * g.kss >= g.KS) return false;  // an empty slice
@@ -91,11 +93,14 @@ bool shape_geo(Geo& g, int want_S) {
   if (g.path == 1 && g.S == 1 && g.stash_cap < per_stream) return false;
   if (!gemm_variant_exists(g.path, g.ta, g.tb) && !g.paired) return false;
   // Cost model (microseconds): streaming time of the busiest workgroup at the
-  // per-CU share of HBM bandwidth, its X staging from L2, per-item costs
-  // (a store at item end, K-slice barriers), and for split-K the finalize
-  // round trips (arrival atomics, partial reads) at the end.  A workgroup
-  // keeps waves * 16 KB of weight loads in flight; fewer than 8 waves leave
-  // the per-CU share unreached.
+  // per-CU share of HBM bandwidth, its X staging, per-item costs (a store at
+  // item end, K-slice barriers), and for split-K the finalize round trips
+  // (arrival atomics, partial reads) at the end.  A workgroup keeps waves *
+  // 16 KB of weight loads in flight; fewer than 8 waves leave the per-CU share
+  // unreached, and so do ring slots spent on padded steps once they exceed a
+  // tenth of the slots.  The constants were fitted to kernel durations of
+  // forced plans over the decode shapes (the planner's pick is within 2% of
+  // the fastest measured plan on average).
   // Per-CU rates (bytes of W per second): the HBM share, the LDS traffic the
   // inner loop generates per weight byte (dot2: X reads M/G; MFMA: A reads
   // MT/NT plus the B permute), and dot2's VALU time (4 M dot2 cycles per KB
@@ -106,12 +111,13 @@ bool shape_geo(Geo& g, int want_S) {
   bw_cu = std::min(bw_cu, lds_cu / lds_per_w);
   if (g.path == 0) bw_cu = std::min(bw_cu, 1024.0 / (4.0 * g.M + 4.0) * 2.4e9 * 0.7);
   const double item_bytes = (double)g.CB * g.KS * 2.0 * (g.paired ? 2.0 : 1.0);
+  const double slot_bytes = (double)g.CB * g.steps * kstep * g.ksl * 2.0 * (g.paired ? 2.0 : 1.0);
+  bw_cu *= std::min(1.0, item_bytes / slot_bytes / 0.9);
   const double part_bytes = g.S > 1 ? (double)g.CB * g.M * 4.0 * 2.0 : 0.0;
   const double wg_bytes = (double)g.ng * per_stream * (item_bytes + part_bytes);
-  const double pad = (double)g.steps * kstep * g.ksl / std::max(g.KS, 1);  // issue slots per useful K
   const double x_us = (double)rows * g.win * 2.0 / 200.0e9 * 1e6;
-  const double item_us = (per_stream > g.stash_cap ? 0.2 : 0.05) + (g.ksl > 1 ? 0.1 : 0.0);
-  g.est_us = wg_bytes / bw_cu * 1e6 + per_stream * item_us * pad + x_us + (g.S > 1 ? 2.5 : 0.0) +
+  const double item_us = (per_stream > g.stash_cap ? 0.1 : 0.05) + (g.ksl > 1 ? 0.1 : 0.0);
+  g.est_us = wg_bytes / bw_cu * 1e6 + per_stream * item_us + x_us + (g.S > 1 ? 4.0 : 0.0) +
              (span > 1 ? 0.5 : 0.0);
   return true;
 }
@@ -140,7 +146,7 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
         if (tn_o && !paired && 16 * tb != tn_o) continue;
         g.ta = (M + 15) / 16; g.tb = tb;
       }
-      const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : 64;
+      const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : 16;  // the model was fitted up to 16 splits
       for (int s = s_lo; s <= s_hi; ++s) {
         if (s > 1 && (K + s - 1) / s < 8) break;
         Geo c = g;

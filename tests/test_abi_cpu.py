@@ -103,7 +103,7 @@ def test_planner_covers_every_column_and_k_once(M, K, N, splitk):
     assert NB * CB >= Nx                               # column blocks cover the XCD's columns
     assert S * KS >= K and (S - 1) * KS < K            # splits cover K, none empty
     assert ksl * kss >= KS and (ksl - 1) * kss < KS    # slices cover a split, none empty
-    assert KS % 8 == 0 and st["items"] == NB * S
+    assert KS % 64 == 0 and st["items"] == NB * S    # splits start on 128-byte lines
     kstep = 512 if st["path"] == "dot2" else 64
     assert ksl == 1 or kss % kstep == 0
     assert st["steps"] * kstep >= kss
@@ -119,7 +119,7 @@ def test_planner_covers_every_column_and_k_once(M, K, N, splitk):
         assert seen == list(range(s * KS, min(K, (s + 1) * KS)))
     assert st["win"] >= (ksl - 1) * kss + st["steps"] * kstep
     if splitk:
-        assert S == min(splitk, math.ceil(K / 8)) or S == math.ceil(K / math.ceil(K / splitk / 8) / 8)
+        assert S == math.ceil(K / (math.ceil(math.ceil(K / splitk) / 64) * 64))
     # columns: every column owned by exactly one (xcd, block, wave, lane-column)
     owned = set()
     for x in range(8):
