@@ -72,13 +72,13 @@ def cpu_baseline_proj(x_bits, w_host):
             oracle.gemm(x_bits[K], w, want_abs=False)
             wbytes += 2 * K * N
         reps += 1
-        if time.perf_counter() - t0 > 2.0 or reps >= 3:
+        if time.perf_counter() - t0 > 10.0 or reps >= 2000:
             break
     dt = time.perf_counter() - t0
     return {"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "%d full step(s): all four projections, every output column, M=1, double accumulation"
-                      % reps}
+            "sample": "%d full steps (%.1f s): all four projections, every output column, M=1, double "
+                      "accumulation" % (reps, dt)}
 
 
 def bench_proj(args):
@@ -182,7 +182,8 @@ def bench_proj(args):
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg, "avg_launch_us": per[dom]["us_avg"]},
         "per_gemm": {k: {kk: v for kk, v in d.items() if kk != "plan"} for k, d in per.items()},
-        "plans": {k: {kk: d["plan"][kk] for kk in ("path", "waves", "TN", "S", "KS", "items")} for k, d in per.items()},
+        "plans": {k: {kk: d["plan"][kk] for kk in ("path", "waves", "TN", "ksl", "S", "KS", "items")}
+                  for k, d in per.items()},
     }
     if not args.no_cpu:
         w_host = [synth.from_torch_bf16(W[0][i]) for i in range(len(PROJ))]
@@ -210,6 +211,12 @@ def bench_chain(args):
     Y = torch.empty((M, d), dtype=torch.float32, device=dev)
     wbytes = L * 2 * (q * d + d * q + 2 * dff * d + d * dff)
     cols = [[w[i] for w in wl] for i in range(4)]
+    if args.copy_calibration:
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         ch(X0, *cols, Y, ws)
     torch.cuda.synchronize()
@@ -240,7 +247,8 @@ def bench_chain(args):
                      "traffic": load_traffic("chain_m64_36l"), "algorithmic_bytes_per_launch": wbytes,
                      "avg_launch_us": round(avg, 2)},
         "chain_us": {"median": round(ts[len(ts) // 2], 2), "min": round(ts[0], 2), "max": round(ts[-1], 2)},
-        "plan": [{k: st[k] for k in ("waves", "TN", "S", "KS", "items")} for st in ch.describe()["stages"]],
+        "plan": [{k: st[k] for k in ("path", "waves", "TN", "ksl", "S", "KS", "items")}
+                 for st in ch.describe()["stages"]],
     }
     return out
 

@@ -78,7 +78,7 @@ def main():
         st = g.describe()["stage"]
         print(json.dumps({"M": M, "K": K, "N": N, "us": round(med, 2), "min": round(ts[0], 2),
                           "GBps": round(wb / med / 1e3, 1), "rc": g.status(ws),
-                          "plan": [st[k] for k in ("path", "tb", "waves", "wpi", "S", "KS", "items")]}),
+                          "plan": {k: st[k] for k in ("path", "tb", "waves", "wpi", "ksl", "S", "KS", "items")}}),
               flush=True)
 
 

@@ -3,11 +3,16 @@
     python -m chiplet_aware_persistent_amd.profile_tools trace <kernel_trace.csv> [--roles a,b,c] [--skip N]
     python -m chiplet_aware_persistent_amd.profile_tools traffic <fetch_counter_collection.csv> \
         <write_counter_collection.csv> [--roles a,b,c] [--skip N]
+    python -m chiplet_aware_persistent_amd.profile_tools sweep <config_sweep stdout> <kernel_trace.csv>
+    python -m chiplet_aware_persistent_amd.profile_tools tcc <config_sweep stdout> <counter_collection.csv>
 
 ``trace``: per-role kernel durations.  The decode projections launch the same
-kernel template for several shapes, so durations are split by launch order
-(role i = every len(roles)-th sgemm/chain dispatch); ``--skip`` drops warm-up
-steps.
+kernel template for several shapes, so durations are split by launch order:
+with ``--bench STEPS,WARMUP`` the dispatch order of ``bench.py --steps STEPS
+--warmup WARMUP`` (warm-up and timed steps launch the roles in turn, then each
+role runs STEPS times back to back for its solo timing) and only the timed
+steps are summarised; without it role i is every len(roles)-th dispatch and
+``--skip`` drops warm-up steps.
 
 ``traffic``: HBM bytes per launch from the FETCH_SIZE and WRITE_SIZE counters
 (KiB per dispatch), each scaled by what the same counter reads for the largest
@@ -28,14 +33,25 @@ def _ours(name: str) -> bool:
     return "sg::k_gemm" in name or "sg::k_chain" in name
 
 
-def kernel_durations(trace_csv: str, roles, skip: int = 0):
+def role_sequence(n: int, roles, skip: int = 0, bench=None):
+    """Role of each of n dispatches (None: not summarised)."""
+    if bench is None:
+        return [roles[i % len(roles)] if i // len(roles) >= skip else None for i in range(n)]
+    steps, warmup = bench
+    seq = [roles[i % len(roles)] if i // len(roles) >= warmup else None
+           for i in range((warmup + steps) * len(roles))]
+    seq += [None] * (steps * len(roles))  # solo back-to-back timing blocks
+    assert len(seq) == n, (len(seq), n)
+    return seq
+
+
+def kernel_durations(trace_csv: str, roles, skip: int = 0, bench=None):
     rows = [r for r in csv.DictReader(open(trace_csv)) if _ours(r["Kernel_Name"])]
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))  # the CSV is not in launch order
     per = collections.OrderedDict((r, []) for r in roles)
     names = {}
-    for i, r in enumerate(rows):
-        role = roles[i % len(roles)]
-        if i // len(roles) < skip:
+    for r, role in zip(rows, role_sequence(len(rows), roles, skip, bench)):
+        if role is None:
             continue
         per[role].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         names[role] = r["Kernel_Name"].split("(")[0]
@@ -57,7 +73,7 @@ def _per_dispatch(counter_csv: str):
     return [disp[k] for k in sorted(disp)]
 
 
-def traffic(fetch_csv: str, write_csv: str, roles, skip: int = 0):
+def traffic(fetch_csv: str, write_csv: str, roles, skip: int = 0, bench=None):
     f, w = _per_dispatch(fetch_csv), _per_dispatch(write_csv)
     copies_f = [d for d in f if "copyBuffer" in d["name"]]
     copies_w = [d for d in w if "copyBuffer" in d["name"]]
@@ -67,16 +83,62 @@ def traffic(fetch_csv: str, write_csv: str, roles, skip: int = 0):
     w_scale = 1.0
     ours_f = [d["value"] for d in f if _ours(d["name"])]
     ours_w = [d["value"] for d in w if _ours(d["name"])]
+    seq_f = role_sequence(len(ours_f), roles, skip, bench)
+    seq_w = role_sequence(len(ours_w), roles, skip, bench)
     out = {"calibration": {"copy_KiB": true_kib, "fetch_scale": round(f_scale, 5), "write_scale": w_scale}}
-    for j, role in enumerate(roles):
-        fs = [v for i, v in enumerate(ours_f) if i % len(roles) == j and i // len(roles) >= skip]
-        ws = [v for i, v in enumerate(ours_w) if i % len(roles) == j and i // len(roles) >= skip]
+    for role in roles:
+        fs = [v for v, r in zip(ours_f, seq_f) if r == role]
+        ws = [v for v, r in zip(ours_w, seq_w) if r == role]
         if not fs:
             continue
         fb = statistics.mean(fs) * f_scale * 1024
         wb = statistics.mean(ws) * w_scale * 1024
         out[role] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
                      "launches": len(fs)}
+    return out
+
+
+def _sweep_groups(sweep_log: str, rows):
+    """Split dispatches of a config_sweep run into its shapes (warm-up
+    launches first, then the timed ones, one JSON line per shape)."""
+    shapes = [json.loads(l) for l in open(sweep_log) if l.startswith("{")]
+    per = len(rows) // max(len(shapes), 1)
+    assert per * len(shapes) == len(rows), (len(rows), len(shapes))
+    return shapes, per
+
+
+def sweep_durations(sweep_log: str, trace_csv: str, warmup: int = 6):
+    rows = [r for r in csv.DictReader(open(trace_csv)) if _ours(r["Kernel_Name"])]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    shapes, per = _sweep_groups(sweep_log, rows)
+    out = []
+    for i, sh in enumerate(shapes):
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[i * per + warmup:(i + 1) * per]]
+        us = statistics.mean(d)
+        wb = 2 * sh["K"] * sh["N"]
+        out.append({"M": sh["M"], "K": sh["K"], "N": sh["N"], "kernel": rows[i * per]["Kernel_Name"].split("(")[0],
+                    "launches": len(d), "avg_us": round(us, 3), "median_us": round(statistics.median(d), 3),
+                    "weight_GBps": round(wb / us / 1e3, 1), "frac_8TBps": round(wb / us / 8e6, 4),
+                    "plan": sh["plan"]})
+    return out
+
+
+def sweep_tcc(sweep_log: str, counter_csv: str, warmup: int = 1):
+    disp = collections.OrderedDict()
+    for r in csv.DictReader(open(counter_csv)):
+        if not _ours(r["Kernel_Name"]):
+            continue
+        d = disp.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    rows = [disp[k] for k in sorted(disp)]
+    shapes, per = _sweep_groups(sweep_log, rows)
+    out = []
+    for i, sh in enumerate(shapes):
+        g = rows[i * per + warmup:(i + 1) * per]
+        hit = sum(x.get("TCC_HIT_sum", 0.0) for x in g)
+        miss = sum(x.get("TCC_MISS_sum", 0.0) for x in g)
+        out.append({"M": sh["M"], "K": sh["K"], "N": sh["N"], "tcc_hit": round(hit / max(hit + miss, 1.0), 4),
+                    "plan": sh["plan"]})
     return out
 
 
@@ -87,17 +149,32 @@ def main():
     t.add_argument("csv")
     t.add_argument("--roles", default="qkv,o,gate_up,down")
     t.add_argument("--skip", type=int, default=0)
+    t.add_argument("--bench", default="", help="STEPS,WARMUP of the bench.py run that was traced")
     c = sub.add_parser("traffic")
     c.add_argument("fetch")
     c.add_argument("write")
     c.add_argument("--roles", default="qkv,o,gate_up,down")
     c.add_argument("--skip", type=int, default=0)
+    c.add_argument("--bench", default="", help="STEPS,WARMUP of the bench.py run that was counted")
+    w = sub.add_parser("sweep")
+    w.add_argument("log")
+    w.add_argument("csv")
+    w.add_argument("--warmup", type=int, default=6)
+    h = sub.add_parser("tcc")
+    h.add_argument("log")
+    h.add_argument("csv")
+    h.add_argument("--warmup", type=int, default=1)
     a = ap.parse_args()
-    roles = a.roles.split(",")
-    if a.cmd == "trace":
-        print(json.dumps(kernel_durations(a.csv, roles, a.skip), indent=1))
+    if a.cmd == "sweep":
+        print(json.dumps(sweep_durations(a.log, a.csv, a.warmup), indent=1))
+    elif a.cmd == "tcc":
+        print(json.dumps(sweep_tcc(a.log, a.csv, a.warmup), indent=1))
+    elif a.cmd == "trace":
+        bench = tuple(int(v) for v in a.bench.split(",")) if a.bench else None
+        print(json.dumps(kernel_durations(a.csv, a.roles.split(","), a.skip, bench), indent=1))
     else:
-        print(json.dumps(traffic(a.fetch, a.write, roles, a.skip), indent=1))
+        bench = tuple(int(v) for v in a.bench.split(",")) if a.bench else None
+        print(json.dumps(traffic(a.fetch, a.write, a.roles.split(","), a.skip, bench), indent=1))
 
 
 if __name__ == "__main__":
