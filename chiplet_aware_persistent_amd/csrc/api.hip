@@ -45,7 +45,7 @@ int env_int(const char* name, int dflt) {
 
 // Fill the derived fields of g for (path, template params, waves, wpi, ksl,
 // S); returns false when the candidate does not fit (LDS, instantiations).
-bool shape_geo(Geo& g, int want_S) {
+bool shape_geo(Geo& g, int want_S, double alpha) {
   const int kstep = g.path == 0 ? kDot2KStep : kMfmaKStep;
   if (g.wpi % g.ksl) return false;
   g.TN = g.path == 0 ? g.tb : (g.paired ? 16 : 16 * g.tb);
@@ -97,10 +97,10 @@ bool shape_geo(Geo& g, int want_S) {
   // item end, K-slice barriers), and for split-K the finalize round trips
   // (arrival atomics, partial reads) at the end.  A workgroup keeps waves *
   // 16 KB of weight loads in flight; fewer than 8 waves leave the per-CU share
-  // unreached, and so do ring slots spent on padded steps once they exceed a
-  // tenth of the slots.  The constants were fitted to kernel durations of
-  // forced plans over the decode shapes (the planner's pick is within 2% of
-  // the fastest measured plan on average).
+  // unreached, and so do ring slots spent on padded steps.  The constants
+  // were fitted to kernel durations of forced plans over the decode shapes
+  // (the planner's pick is within 1.5% of the fastest measured plan on
+  // average).
   // Per-CU rates (bytes of W per second): the HBM share, the LDS traffic the
   // inner loop generates per weight byte (dot2: X reads M/G; MFMA: A reads
   // MT/NT plus the B permute), and dot2's VALU time (4 M dot2 cycles per KB
@@ -112,18 +112,27 @@ bool shape_geo(Geo& g, int want_S) {
   if (g.path == 0) bw_cu = std::min(bw_cu, 1024.0 / (4.0 * g.M + 4.0) * 2.4e9 * 0.7);
   const double item_bytes = (double)g.CB * g.KS * 2.0 * (g.paired ? 2.0 : 1.0);
   const double slot_bytes = (double)g.CB * g.steps * kstep * g.ksl * 2.0 * (g.paired ? 2.0 : 1.0);
-  bw_cu *= std::min(1.0, item_bytes / slot_bytes / 0.9);
-  const double part_bytes = g.S > 1 ? (double)g.CB * g.M * 4.0 * 2.0 : 0.0;
-  const double wg_bytes = (double)g.ng * per_stream * (item_bytes + part_bytes);
+  bw_cu *= item_bytes / slot_bytes;
+  const double part_bytes = g.S > 1 ? (double)g.CB * g.M * 4.0 * 2.0 * (g.paired ? 2.0 : 1.0) : 0.0;
+  // The busiest workgroup's bytes, or its busiest stream's at alpha times
+  // the stream's fair share of the CU if that is longer.  Alpha is 1 for a
+  // single launch; inside the chain the neighbouring stages keep HBM busy and
+  // unevenly loaded waves cost less (alpha 4; measured on the 36-layer chain).
+  const double wg_items = ceil_div(g.items, kWgPerXcd);
+  const double wg_bytes = std::max(wg_items * (item_bytes + part_bytes),
+                                   (double)g.ng * per_stream * (item_bytes + part_bytes) / alpha);
   const double x_us = (double)rows * g.win * 2.0 / 200.0e9 * 1e6;
-  const double item_us = (per_stream > g.stash_cap ? 0.1 : 0.05) + (g.ksl > 1 ? 0.1 : 0.0);
-  g.est_us = wg_bytes / bw_cu * 1e6 + per_stream * item_us + x_us + (g.S > 1 ? 4.0 : 0.0) +
+  const double item_us = per_stream > g.stash_cap ? 0.1 : 0.05;
+  // split-K finalize: arrival round trips plus the owner's partial reads
+  // (S tiles of tile_bytes; a dot2 owner lane reads S floats).
+  const double fin_kb = g.S * (g.path == 0 ? 0.25 : tile_bytes / 1024.0);
+  g.est_us = wg_bytes / bw_cu * 1e6 + per_stream * item_us + x_us + (g.S > 1 ? 6.0 + 0.05 * fin_kb : 0.0) +
              (span > 1 ? 0.5 : 0.0);
   return true;
 }
 
 bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, int s_o, int waves_o,
-              int ksl_o) {
+              int ksl_o, double alpha) {
   bool found = false;
   const int waves_opts[2] = {8, 4};
   for (int wi = 0; wi < 2; ++wi) {
@@ -150,7 +159,7 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
       for (int s = s_lo; s <= s_hi; ++s) {
         if (s > 1 && (K + s - 1) / s < 8) break;
         Geo c = g;
-        if (!shape_geo(c, s)) continue;
+        if (!shape_geo(c, s, alpha)) continue;
         if (c.S != s && !s_o) continue;  // rounding collapsed it to another count
         if (!found || c.est_us < best.est_us - 1e-9) { best = c; found = true; }
       }
@@ -235,7 +244,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     if (rc != SGEMM_OK) { delete pl; return rc; }
     const int path = choose_path(p);
     if (path == 0 && k_o > 1) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
-    if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o)) {
+    if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, 1.0)) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
     }
@@ -251,6 +260,17 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     // One block size and one n-tile width for the unpaired stages per launch.
     const int Ks[4] = {p.d_model, p.q_cols, p.d_model, p.d_ff};
     const int Ns[4] = {p.q_cols, p.d_model, p.d_ff, p.d_model};
+    // Per-stage overrides for experiments: SGEMM_CHAIN_S / SGEMM_CHAIN_KSL =
+    // four comma-separated values (Q, O, gate_up, down), 0 = planner's choice.
+    int s_st[4] = {s_o, s_o, s_o, s_o}, k_st[4] = {k_o, k_o, k_o, k_o};
+    for (int which = 0; which < 2; ++which) {
+      const char* e = std::getenv(which == 0 ? "SGEMM_CHAIN_S" : "SGEMM_CHAIN_KSL");
+      if (!e || !*e) continue;
+      int v[4] = {0, 0, 0, 0};
+      if (std::sscanf(e, "%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]) != 4) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+      for (int i = 0; i < 4; ++i)
+        if (v[i]) (which == 0 ? s_st : k_st)[i] = v[i];
+    }
     double best = -1.0;
     for (int waves = 8; waves >= 4; waves -= 4) {
       if (w_o && waves != w_o) continue;
@@ -261,7 +281,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
         bool ok = chain_variant_exists((p.M + 15) / 16, nt, nt, nt);
         for (int s = 0; s < kChainStages && ok; ++s) {
           const int paired = s == 2;
-          ok = plan_geo(c[s], p.M, Ks[s], Ns[s], 1, paired, paired ? 0 : 16 * nt, s_o, waves, k_o);
+          ok = plan_geo(c[s], p.M, Ks[s], Ns[s], 1, paired, paired ? 0 : 16 * nt, s_st[s], waves, k_st[s], 4.0);
           if (ok && paired) c[s].pair_off = p.d_ff;
           tot += ok ? c[s].est_us : 0.0;
         }

@@ -199,6 +199,55 @@ __device__ __forceinline__ bool splitk_own(unsigned* ctr, unsigned old_lane0, in
   return last;
 }
 
+// Split-K finalize: add the S partials of a tile in split order.  The partial
+// loads go out QB splits at a time (S is a run-time value, so a plain loop
+// would wait for every split's loads before issuing the next split's).
+// Past-S slots read the buffer's extent (zeros) and are not added, so the sum
+// is the same sequence of additions as one load per split.
+template <int AUX, int QB>
+__device__ __forceinline__ float sum_partials(Rsrc pr, unsigned base, unsigned stride, int S, bool valid,
+                                              unsigned oob) {
+  float t = 0.f;
+  for (int q0 = 0; q0 < S; q0 += QB) {
+    float p[QB];
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq) {
+      const unsigned off = valid && q0 + qq < S ? (base + (unsigned)(q0 + qq) * stride) * 4u : oob;
+      p[qq] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, (int)off, 0, AUX));
+    }
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq)
+      if (q0 + qq < S) t += p[qq];
+  }
+  return t;
+}
+
+template <int AUX, int NT, int MT>
+__device__ __forceinline__ void sum_partials_f4(Rsrc pr, unsigned base, unsigned stride, int S, int lane,
+                                                f4 (&tot)[NT][MT], unsigned oob) {
+  constexpr int QB = 16 / (NT * MT) > 1 ? 16 / (NT * MT) : 1;  // <= 16 fragments in flight
+  for (int q0 = 0; q0 < S; q0 += QB) {
+    f4 p[QB][NT][MT];
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const unsigned e = base + (unsigned)(q0 + qq) * stride + (unsigned)((j * MT + i) * 256 + lane * 4);
+          p[qq][j][i] = ld_f4<AUX>(pr, q0 + qq < S ? e * 4u : oob);
+        }
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq)
+      if (q0 + qq < S) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int i = 0; i < MT; ++i) tot[j][i] += p[qq][j][i];
+      }
+  }
+}
+
 // The waves of a workgroup form ng groups of wpi waves; each group is one
 // item stream.  Stream q of workgroup slot w runs the contiguous, balanced
 // range [i0, i1) of the XCD's items; the ranges of one workgroup's streams
@@ -448,13 +497,9 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
         const int b = it % d.NB;
         const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
         if (!splitk_own(d.ctr + tile, old[j], d.S, d.sync, lane)) continue;
-        float t = 0.f;
-        for (int q = 0; q < d.S; ++q) {
-          const unsigned off = owner ? ((tile * d.S + q) * GM + idx) * 4u : d.part_bytes;
-          t += d.sync == SYNC_XCD
-                   ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, (int)off, 0, kAuxSc1))
-                   : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, (int)off, 0, 0));
-        }
+        const unsigned base = tile * d.S * GM + idx;
+        const float t = d.sync == SYNC_XCD ? sum_partials<kAuxSc1, 8>(pr, base, GM, d.S, owner, d.part_bytes)
+                                           : sum_partials<0, 8>(pr, base, GM, d.S, owner, d.part_bytes);
         const int col = xc0 + b * d.CB + wv * G + oc;
         store_out(d, yr, y2r, owner && col < xc1 && om < d.M, om, col, t);
       }
@@ -750,14 +795,10 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
         for (int j = 0; j < NT; ++j)
 #pragma unroll
           for (int i = 0; i < MT; ++i) tot[j][i] = f4{0.f, 0.f, 0.f, 0.f};
-        for (int q = 0; q < d.S; ++q) {
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int i = 0; i < MT; ++i) {
-              const unsigned off = ((tile * d.S + q) * TILE + (j * MT + i) * 256 + lane * 4) * 4u;
-              tot[j][i] += d.sync == SYNC_XCD ? ld_f4<kAuxSc1>(pr, off) : ld_f4<0>(pr, off);
-            }
+        if (d.sync == SYNC_XCD) {
+          sum_partials_f4<kAuxSc1, NT, MT>(pr, tile * d.S * TILE, TILE, d.S, lane, tot, d.part_bytes);
+        } else {
+          sum_partials_f4<0, NT, MT>(pr, tile * d.S * TILE, TILE, d.S, lane, tot, d.part_bytes);
         }
         const int colb = xc0 + b * d.CB + wv * TW;
 #pragma unroll
