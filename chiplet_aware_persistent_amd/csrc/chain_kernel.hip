@@ -137,6 +137,7 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
         alive = mfma_stage<MT, NT, false, kAuxNt>(d, lds, xcd, slot, nslots, hook);
       }
       if (!alive) break;
+      if (a.stamps) __syncthreads();  // the stamp marks the end of the workgroup's last wave
       stamp(a, e, 1);
       signal_event(a, e, xcd, nslots);
       __syncthreads();  // LDS window reuse by the next stage
