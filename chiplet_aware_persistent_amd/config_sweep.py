@@ -6,7 +6,8 @@ Shapes: the four Qwen3-8B projection shapes at M in {1, 8, 16, 32, 64}, the
 K = 7168 shapes at M in {1, 2, 4, 8, 16} x N in {1536, 4096, 18432}, and the
 1024 x 1024 case at M = 1.  For each shape: 6 warm-up launches, then
 ``--launches`` launches timed one by one with HIP events, rotating over
-weight copies spanning >= 4 GiB so every launch reads its weights from HBM.
+weight copies spanning >= 4 GiB so every launch reads its weights from HBM
+(``--warm``: one buffer, so later launches find their weights in the caches).
 One JSON line per shape.  Run under ``rocprofv3 --kernel-trace`` for kernel
 durations without the dispatch latency the events include.
 """
@@ -45,6 +46,8 @@ def main():
     ap.add_argument("--json-overrides", default="{}")
     ap.add_argument("--only", default="", help="semicolon-separated M,K,N shapes to run instead of all")
     ap.add_argument("--warmup", type=int, default=6)
+    ap.add_argument("--warm", action="store_true",
+                    help="reuse one weight buffer (warm caches) instead of rotating over >= 4 GiB of copies")
     a = ap.parse_args()
     extra = json.loads(a.json_overrides)
     dev = torch.device("cuda:0")
@@ -52,7 +55,7 @@ def main():
     todo = [tuple(int(v) for v in t.split(",")) for t in a.only.split(";") if t] or shapes()
     for (M, K, N) in todo:
         wb = 2 * K * N
-        copies = max(2, -(-(4 << 30) // wb))
+        copies = 1 if a.warm else max(2, -(-(4 << 30) // wb))
         if (K, N) not in cache:
             cache.clear()
             torch.cuda.empty_cache()
@@ -75,8 +78,10 @@ def main():
         torch.cuda.synchronize()
         ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
         med = ts[len(ts) // 2]
+        p10, p90 = ts[len(ts) // 10], ts[min(len(ts) - 1, (9 * len(ts)) // 10)]
         st = g.describe()["stage"]
         print(json.dumps({"M": M, "K": K, "N": N, "us": round(med, 2), "min": round(ts[0], 2),
+                          "p10": round(p10, 2), "p90": round(p90, 2), "warm": a.warm, "flags": extra.get("flags", 0),
                           "GBps": round(wb / med / 1e3, 1), "rc": g.status(ws),
                           "plan": {k: st[k] for k in ("path", "tb", "waves", "wpi", "ksl", "S", "KS", "items")}}),
               flush=True)

@@ -116,8 +116,10 @@ def sweep_durations(sweep_log: str, trace_csv: str, warmup: int = 6):
         d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[i * per + warmup:(i + 1) * per]]
         us = statistics.mean(d)
         wb = 2 * sh["K"] * sh["N"]
+        ds = sorted(d)
         out.append({"M": sh["M"], "K": sh["K"], "N": sh["N"], "kernel": rows[i * per]["Kernel_Name"].split("(")[0],
                     "launches": len(d), "avg_us": round(us, 3), "median_us": round(statistics.median(d), 3),
+                    "p10_us": round(ds[len(ds) // 10], 3), "p90_us": round(ds[min(len(ds) - 1, 9 * len(ds) // 10)], 3),
                     "weight_GBps": round(wb / us / 1e3, 1), "frac_8TBps": round(wb / us / 8e6, 4),
                     "plan": sh["plan"]})
     return out
@@ -137,8 +139,14 @@ def sweep_tcc(sweep_log: str, counter_csv: str, warmup: int = 1):
         g = rows[i * per + warmup:(i + 1) * per]
         hit = sum(x.get("TCC_HIT_sum", 0.0) for x in g)
         miss = sum(x.get("TCC_MISS_sum", 0.0) for x in g)
-        out.append({"M": sh["M"], "K": sh["K"], "N": sh["N"], "tcc_hit": round(hit / max(hit + miss, 1.0), 4),
-                    "plan": sh["plan"]})
+        r = {"M": sh["M"], "K": sh["K"], "N": sh["N"], "plan": sh["plan"]}
+        if hit + miss > 0:
+            r["tcc_hit"] = round(hit / (hit + miss), 4)
+        if g and "SQ_VALU_MFMA_BUSY_CYCLES" in g[0]:
+            # matrix-core busy cycles summed over the 1024 SIMDs, per launch; divided by
+            # (kernel time x 2.4 GHz x 1024) this is the MFMA utilisation
+            r["mfma_busy_cycles"] = round(sum(x["SQ_VALU_MFMA_BUSY_CYCLES"] for x in g) / len(g))
+        out.append(r)
     return out
 
 
