@@ -14,7 +14,8 @@ timed steps (GB/s); ``roofline`` reports the dominant kernel (gate_up) against
 the 8 TB/s HBM peak, its launch durations measured with HIP events on the
 launch stream; ``cpu_baseline`` is the CPU oracle on the same step.
 
-``--workload chain``: the 36-layer persistent chain at M = 64 (Q 4096x4096,
+``--workload chain``: the 36-layer persistent chain at M = 64 (``--chain-m``
+selects another row count; Q 4096x4096,
 O 4096x4096, gate_up 4096x24576 with SiLU gate, down 12288x4096 per layer;
 13.29 GB of weights) in one launch per step.
 
@@ -198,7 +199,7 @@ def bench_chain(args):
     import synth
 
     dev = torch.device("cuda:0")
-    M, L, d, q, dff = 64, 36, 4096, 4096, 12288
+    M, L, d, q, dff = args.chain_m, 36, 4096, 4096, 12288
     wl = []
     for l in range(L):
         wl.append([synth.uniform_bf16_torch(synth.seed_for(5, l, 1), q, d, synth.weight_scale(d), dev),
@@ -240,11 +241,11 @@ def bench_chain(args):
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "persistent_chain_36_layers_m64", "M": M, "layers": L, "d_model": d,
+        "config": {"workload": f"persistent_chain_36_layers_m{M}", "M": M, "layers": L, "d_model": d,
                    "q_cols": q, "d_ff": dff, "weight_bytes_per_step": wbytes, "parallelism": "single_gpu"},
         "roofline": {"bound": "hbm", "kernel": "k_chain", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": load_traffic("chain_m64_36l"), "algorithmic_bytes_per_launch": wbytes,
+                     "traffic": load_traffic(f"chain_m{M}_36l"), "algorithmic_bytes_per_launch": wbytes,
                      "avg_launch_us": round(avg, 2)},
         "chain_us": {"median": round(ts[len(ts) // 2], 2), "min": round(ts[0], 2), "max": round(ts[-1], 2)},
         "plan": [{k: st[k] for k in ("path", "waves", "TN", "ksl", "S", "KS", "items")}
@@ -259,6 +260,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=["proj", "chain"], default="proj")
+    ap.add_argument("--chain-m", type=int, default=64, help="rows of the chain workload (1-64)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (counter calibration for --pmc runs)")

@@ -34,6 +34,7 @@ struct Geo {
   int ksl = 1, kss = 0;
   int win = 0, xrow = 0, lds = 0, red_off = 0, stash_off = 0, stash_cap = 0;
   int paired = 0, pair_off = 0;
+  int ring = 0;  // ring depth (k-steps in flight per wave)
   size_t ctr_count = 0, part_floats = 0;
   double est_us = 0.0;
 };
@@ -43,9 +44,21 @@ int env_int(const char* name, int dflt) {
   return v && *v ? std::atoi(v) : dflt;
 }
 
+// Cost-model constants of one launch context (a single GEMM launch, or a
+// stage inside the persistent chain, where X comes from other XCDs' fresh
+// writes and the neighbouring stages overlap the tails).
+struct Cost {
+  double alpha;      // how far one item stream may exceed its 1/ng share of the CU
+  double x_bw;       // X staging rate per CU, bytes/s
+  double split_us;   // split-K arrival and finalize round trip
+  double fin_us_kb;  // per kilobyte of partials an owner reads
+};
+constexpr Cost kCostGemm{1.0, 200.0e9, 6.0, 0.05};
+constexpr Cost kCostChain{1.5, 200.0e9, 6.0, 0.05};
+
 // Fill the derived fields of g for (path, template params, waves, wpi, ksl,
 // S); returns false when the candidate does not fit (LDS, instantiations).
-bool shape_geo(Geo& g, int want_S, double alpha) {
+bool shape_geo(Geo& g, int want_S, const Cost& cost) {
   const int kstep = g.path == 0 ? kDot2KStep : kMfmaKStep;
   if (g.wpi % g.ksl) return false;
   g.TN = g.path == 0 ? g.tb : (g.paired ? 16 : 16 * g.tb);
@@ -62,6 +75,7 @@ bool shape_geo(Geo& g, int want_S, double alpha) {
   if (g.ksl > 1 && (g.ksl - 1) * g.kss >= g.KS) return false;  // an empty slice
   const int ring = g.path == 0 ? ring_depth_dot2(g.tb) : ring_depth_mfma(g.paired ? 2 : g.tb);
   g.steps = ceil_div(ceil_div(g.kss, kstep), ring) * ring;  // padded to the ring depth
+  g.ring = ring;
   g.items = g.NB * g.S;
   // A workgroup stages X once for all splits its contiguous item range
   // touches: the window is (span - 1) splits plus the last slice's padded steps.
@@ -73,7 +87,8 @@ bool shape_geo(Geo& g, int want_S, double alpha) {
   }
   g.win = (span - 1) * g.KS + (g.ksl - 1) * g.kss + g.steps * kstep;
   g.win = (int)round_up((size_t)g.win, 8);
-  const int rows = g.path == 0 ? g.M : 16 * g.ta;
+  // MFMA: the rows of X plus one zero row when the M-tiles overhang M.
+  const int rows = g.path == 0 ? g.M : std::min(16 * g.ta, g.M + 1);
   g.xrow = g.path == 0 ? g.win : g.win + 8;
   // LDS: X window, K-slice reduction buffer, output stash.
   const int tile_bytes = g.path == 0 ? 64 * 4 : g.tb * g.ta * 1024;  // one wave's item result
@@ -120,19 +135,20 @@ bool shape_geo(Geo& g, int want_S, double alpha) {
   // unevenly loaded waves cost less (alpha 4; measured on the 36-layer chain).
   const double wg_items = ceil_div(g.items, kWgPerXcd);
   const double wg_bytes = std::max(wg_items * (item_bytes + part_bytes),
-                                   (double)g.ng * per_stream * (item_bytes + part_bytes) / alpha);
-  const double x_us = (double)rows * g.win * 2.0 / 200.0e9 * 1e6;
+                                   (double)g.ng * per_stream * (item_bytes + part_bytes) / cost.alpha);
+  const double x_us = (double)rows * g.win * 2.0 / cost.x_bw * 1e6;
   const double item_us = per_stream > g.stash_cap ? 0.1 : 0.05;
   // split-K finalize: arrival round trips plus the owner's partial reads
   // (S tiles of tile_bytes; a dot2 owner lane reads S floats).
   const double fin_kb = g.S * (g.path == 0 ? 0.25 : tile_bytes / 1024.0);
-  g.est_us = wg_bytes / bw_cu * 1e6 + per_stream * item_us + x_us + (g.S > 1 ? 6.0 + 0.05 * fin_kb : 0.0) +
+  g.est_us = wg_bytes / bw_cu * 1e6 + per_stream * item_us + x_us +
+             (g.S > 1 ? cost.split_us + cost.fin_us_kb * fin_kb : 0.0) +
              (span > 1 ? 0.5 : 0.0);
   return true;
 }
 
 bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, int s_o, int waves_o,
-              int ksl_o, double alpha) {
+              int ksl_o, const Cost& cost, int wpi_o = 0) {
   bool found = false;
   const int waves_opts[2] = {8, 4};
   for (int wi = 0; wi < 2; ++wi) {
@@ -142,6 +158,7 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
     for (int ksl = 1; ksl <= (path == 1 ? wpi : 1); ksl *= 2)
     for (int tb = 1; tb <= 8; ++tb) {
       if (ksl_o && ksl != ksl_o) continue;
+      if (wpi_o && wpi != wpi_o) continue;
       Geo g;
       g.path = path; g.M = M; g.K = K; g.N = N; g.waves = waves; g.wpi = wpi; g.ksl = ksl;
       g.paired = paired;
@@ -159,7 +176,7 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
       for (int s = s_lo; s <= s_hi; ++s) {
         if (s > 1 && (K + s - 1) / s < 8) break;
         Geo c = g;
-        if (!shape_geo(c, s, alpha)) continue;
+        if (!shape_geo(c, s, cost)) continue;
         if (c.S != s && !s_o) continue;  // rounding collapsed it to another count
         if (!found || c.est_us < best.est_us - 1e-9) { best = c; found = true; }
       }
@@ -244,7 +261,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     if (rc != SGEMM_OK) { delete pl; return rc; }
     const int path = choose_path(p);
     if (path == 0 && k_o > 1) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
-    if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, 1.0)) {
+    if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, kCostGemm)) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
     }
@@ -260,16 +277,28 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     // One block size and one n-tile width for the unpaired stages per launch.
     const int Ks[4] = {p.d_model, p.q_cols, p.d_model, p.d_ff};
     const int Ns[4] = {p.q_cols, p.d_model, p.d_ff, p.d_model};
-    // Per-stage overrides for experiments: SGEMM_CHAIN_S / SGEMM_CHAIN_KSL =
+    // Per-stage overrides for experiments: SGEMM_CHAIN_S / _KSL / _WPI =
     // four comma-separated values (Q, O, gate_up, down), 0 = planner's choice.
-    int s_st[4] = {s_o, s_o, s_o, s_o}, k_st[4] = {k_o, k_o, k_o, k_o};
-    for (int which = 0; which < 2; ++which) {
-      const char* e = std::getenv(which == 0 ? "SGEMM_CHAIN_S" : "SGEMM_CHAIN_KSL");
+    int s_st[4] = {s_o, s_o, s_o, s_o}, k_st[4] = {k_o, k_o, k_o, k_o}, w_st[4] = {0, 0, 0, 0};
+    for (int which = 0; which < 3; ++which) {
+      const char* e = std::getenv(which == 0 ? "SGEMM_CHAIN_S" : which == 1 ? "SGEMM_CHAIN_KSL" : "SGEMM_CHAIN_WPI");
       if (!e || !*e) continue;
       int v[4] = {0, 0, 0, 0};
       if (std::sscanf(e, "%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]) != 4) { delete pl; return SGEMM_ERR_INVALID_ARG; }
       for (int i = 0; i < 4; ++i)
-        if (v[i]) (which == 0 ? s_st : k_st)[i] = v[i];
+        if (v[i]) (which == 0 ? s_st : which == 1 ? k_st : w_st)[i] = v[i];
+    }
+    // SGEMM_CHAIN_COST = "alpha,x_gbps,split_us,fin_us_kb" replaces the chain's
+    // cost constants (for calibration runs).
+    Cost cost = kCostChain;
+    if (const char* ce = std::getenv("SGEMM_CHAIN_COST"); ce && *ce) {
+      double x_gbps = 0.0;
+      if (std::sscanf(ce, "%lf,%lf,%lf,%lf", &cost.alpha, &x_gbps, &cost.split_us, &cost.fin_us_kb) != 4 ||
+          !(cost.alpha >= 1.0 && cost.alpha <= 8.0) || !(x_gbps > 0.0) || cost.split_us < 0.0 || cost.fin_us_kb < 0.0) {
+        delete pl;
+        return SGEMM_ERR_INVALID_ARG;
+      }
+      cost.x_bw = x_gbps * 1e9;
     }
     double best = -1.0;
     for (int waves = 8; waves >= 4; waves -= 4) {
@@ -281,7 +310,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
         bool ok = chain_variant_exists((p.M + 15) / 16, nt, nt, nt);
         for (int s = 0; s < kChainStages && ok; ++s) {
           const int paired = s == 2;
-          ok = plan_geo(c[s], p.M, Ks[s], Ns[s], 1, paired, paired ? 0 : 16 * nt, s_st[s], waves, k_st[s], 4.0);
+          ok = plan_geo(c[s], p.M, Ks[s], Ns[s], 1, paired, paired ? 0 : 16 * nt, s_st[s], waves, k_st[s], cost, w_st[s]);
           if (ok && paired) c[s].pair_off = p.d_ff;
           tot += ok ? c[s].est_us : 0.0;
         }
@@ -491,9 +520,9 @@ static std::string geo_json(const Geo& g) {
                 "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,\"wpi\":%d,"
                 "\"ksl\":%d,\"kss\":%d,\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,"
                 "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
-                "\"est_us\":%.3f}",
+                "\"ring\":%d,\"est_us\":%.3f}",
                 g.path == 0 ? "dot2" : "mfma", g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
-                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.est_us);
+                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.est_us);
   return b;
 }
 

@@ -520,8 +520,9 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
 // another, and one ds_bpermute per dword moves them to the B-operand layout
 // (lane l' holds column l'%16 at k-group l'/16).  Issuing each line in one
 // instruction halves the L2 requests against two 64-byte halves per line.
-// The A operand (X, from LDS) uses the same k slots: lane l' reads row l'%16
-// at k = 32h + 8(l'/16).
+// The A operand (X, from LDS) uses the same k slots: for m-tile i lane l'
+// reads row 16i + l'%16 (the zero row M where that passes M) at
+// k = 32h + 8(l'/16).
 template <int MT, int NT, bool PAIRED, int AUX, typename Hook = NoHook>
 __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                            Hook pre_x = Hook()) {
@@ -654,7 +655,13 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   // exists only after the wait, so its loads follow the ring.
   constexpr bool early = __is_same(Hook, NoHook);
   const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
-  if constexpr (early) stage_x_lds(d, xs, 16 * MT, s_first * d.KS, d.K, xr);
+  // The window holds rows [0, M) and, when the M-tiles overhang M, one zero
+  // row (row M) that the overhanging lanes of the A operand read instead.
+  const int xrows = min(16 * MT, d.M + 1);
+  int xro[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) xro[i] = min(16 * i + r16, d.M) * d.xrow;
+  if constexpr (early) stage_x_lds(d, xs, xrows, s_first * d.KS, d.K, xr);
   Src sc = src_of(i0), sn = src_of(i0 + 1);
 #pragma unroll
   for (int p = 0; p < P; ++p) issue(ring[p], sc, p);
@@ -663,7 +670,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   if constexpr (early) {
     wait_vm<P * NT * 2>();
   } else {
-    stage_x_lds(d, xs, 16 * MT, s_first * d.KS, d.K, xr);
+    stage_x_lds(d, xs, xrows, s_first * d.KS, d.K, xr);
     wait_vm0();
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -681,7 +688,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     const bool here = t0 + P < spad;
     const Src& sr = here ? sc : sn;
     const int tn = here ? t0 + P : t0 + P - spad;
-    const uint16_t* xb0 = xs + r16 * d.xrow + xoff + t0 * kMfmaKStep + 8 * g4;
+    const uint16_t* xb0 = xs + xoff + t0 * kMfmaKStep + 8 * g4;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint16_t* xb = xb0 + p * kMfmaKStep;
@@ -690,7 +697,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
         bf16x8 xa[MT];
 #pragma unroll
         for (int i = 0; i < MT; ++i)
-          xa[i] = __builtin_bit_cast(bf16x8, *(const u4*)(xb + 16 * i * d.xrow + 32 * h));
+          xa[i] = __builtin_bit_cast(bf16x8, *(const u4*)(xb + xro[i] + 32 * h));
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
           const bf16x8 wb = to_b(ring[p][j], h);
