@@ -32,6 +32,7 @@ F_SYNC_AGENT = 1 << 4
 F_STAMPS = 1 << 5
 F_WATCHDOG_TEST = 1 << 6
 F_W_SC1 = 1 << 7
+F_POLL_LEADER = 1 << 8
 
 
 class SgemmError(RuntimeError):

@@ -460,6 +460,7 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   a.act_layer_elems = plan->act_layer_elems;
   a.off_h1 = plan->a_h1; a.off_h2 = plan->a_h2; a.off_a = plan->a_a; a.off_x = plan->a_x;
   a.flat_sync = (p.flags & SGEMM_F_SYNC_FLAT) ? 1 : 0;
+  a.poll_leader = (p.flags & SGEMM_F_POLL_LEADER) ? 1 : 0;
   a.spin_ticks = plan->spin_ticks;
   a.mt = plan->cg[0].ta;
   a.nt_q = plan->cg[0].tb; a.nt_o = plan->cg[1].tb; a.nt_d = plan->cg[3].tb;

@@ -35,19 +35,20 @@ __device__ __forceinline__ unsigned long long now_ticks() { return wall_clock64(
 
 // Wait until event e is complete (all producers published).  Executed by the
 // whole workgroup; returns false when the wait timed out (here or elsewhere).
-// One leader per XCD (slot 0) polls the global counter with device-coherent
-// loads and, once it is complete, raises the XCD's flag; the other 31
-// workgroups of the XCD poll that flag, so only 8 pollers share the global
-// counter's address and the other 248 spread over 8 flags (the per-XCD
-// scheduler's polling role in the Fleet note, sections 2a and 3b, without a
-// dedicated workgroup).
+// Thread 0 of every workgroup polls the global counter with device-coherent
+// loads.  With poll_leader, one leader per XCD (slot 0) polls it instead and,
+// once it is complete, raises the XCD's flag, which the other 31 workgroups
+// of the XCD poll (the per-XCD scheduler's polling role in the Fleet note,
+// sections 2a and 3b, without a dedicated workgroup): fewer pollers share the
+// counter's address, but the extra hop costs about a microsecond per stage
+// on MI355X, more than the contention of 256 pollers does.
 __device__ bool wait_event(const ChainArgs& a, int e, int* sh_alive) {
   if (threadIdx.x == 0) {
     const int xcd = blockIdx.x & 7;
     const int events = 4 * a.n_layers;
     unsigned* flag = a.xflag + xcd * events + e;
     const unsigned target = a.flat_sync ? gridDim.x : (unsigned)kXcds;
-    const bool leader = (blockIdx.x >> 3) == 0 || a.flat_sync;
+    const bool leader = (blockIdx.x >> 3) == 0 || a.flat_sync || !a.poll_leader;
     int ok = 1;
     const unsigned long long t0 = now_ticks();
     for (;;) {
@@ -68,7 +69,8 @@ __device__ bool wait_event(const ChainArgs& a, int e, int* sh_alive) {
       __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (leader && ok && !a.flat_sync) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (leader && ok && !a.flat_sync && a.poll_leader)
+      __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *sh_alive = ok;
   }
   __syncthreads();

@@ -29,6 +29,7 @@ struct ChainArgs {
   size_t act_layer_elems;              // bf16 elements per layer of activations
   size_t off_h1, off_h2, off_a, off_x; // element offsets inside one layer's block
   int flat_sync;                       // every workgroup publishes globally
+  int poll_leader;                     // one workgroup per XCD polls and raises the XCD's flag
   long long spin_ticks;                // watchdog budget (wall-clock ticks, 100 MHz)
   int mt, nt_q, nt_o, nt_d;            // tile template parameters (MFMA path)
 };

@@ -68,7 +68,11 @@ enum {
   SGEMM_F_STAMPS = 1u << 5,      /* chain: record per-workgroup stage timestamps  */
   SGEMM_F_WATCHDOG_TEST = 1u << 6, /* chain: spin budget of zero, to exercise the
                                       time-out path from the host               */
-  SGEMM_F_W_SC1 = 1u << 7        /* weight loads with sc1|nt (streaming)         */
+  SGEMM_F_W_SC1 = 1u << 7,       /* weight loads with sc1|nt (streaming)         */
+  SGEMM_F_POLL_LEADER = 1u << 8  /* chain: one workgroup per XCD polls the global
+                                    counter and raises a per-XCD flag that the
+                                    XCD's other workgroups poll (default: every
+                                    workgroup polls the global counter)         */
 };
 
 /*

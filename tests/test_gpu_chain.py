@@ -152,16 +152,17 @@ def test_chain_repeatable_and_sync_modes_agree(cuda_device):
     rc2, Y2, _, _ = run_chain(ch, X0, dl, ws=ws)
     assert rc == rc2 == sg.OK
     assert torch.equal(Y1, Y2)
-    for flags in (sg.F_SYNC_FLAT, sg.F_SYNC_AGENT):
+    for flags in (sg.F_SYNC_FLAT, sg.F_SYNC_AGENT, sg.F_POLL_LEADER):
         rc3, Y3, _, _ = run_chain(sg.LayerChain(M, L, d, q, dff, flags=flags), X0, dl)
         assert rc3 == sg.OK
         assert torch.equal(Y1, Y3)
 
 
-def test_chain_stamps_order_every_stage(cuda_device):
+@pytest.mark.parametrize("flags", [0, sg.F_POLL_LEADER, sg.F_SYNC_FLAT])
+def test_chain_stamps_order_every_stage(cuda_device, flags):
     M, L, d, q, dff = 32, 4, 512, 256, 768
     x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x4000, cuda_device)
-    ch = sg.LayerChain(M, L, d, q, dff, flags=sg.F_STAMPS)
+    ch = sg.LayerChain(M, L, d, q, dff, flags=sg.F_STAMPS | flags)
     rc, Y, _, ws = run_chain(ch, X0, dl)
     assert rc == sg.OK
     info = ch.describe()
