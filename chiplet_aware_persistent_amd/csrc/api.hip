@@ -52,9 +52,14 @@ struct Cost {
   double x_bw;       // X staging rate per CU, bytes/s
   double split_us;   // split-K arrival and finalize round trip
   double fin_us_kb;  // per kilobyte of partials an owner reads
+  double ksl_us;     // per item with K slices (two workgroup barriers, LDS exchange)
 };
-constexpr Cost kCostGemm{1.0, 200.0e9, 6.0, 0.05};
-constexpr Cost kCostChain{1.5, 200.0e9, 6.0, 0.05};
+constexpr Cost kCostGemm{1.0, 200.0e9, 6.0, 0.05, 0.0};
+// Chain constants fitted to whole-chain times of per-stage forced plans at
+// M = 1..64 (36 layers, d = q = 4096, d_ff = 12288): X comes from other XCDs'
+// fresh writes (slower than a warm window), while a split's finalize overlaps
+// the neighbouring stages' streams.
+constexpr Cost kCostChain{1.25, 75.0e9, 0.5, 0.05, 0.25};
 
 // Fill the derived fields of g for (path, template params, waves, wpi, ksl,
 // S); returns false when the candidate does not fit (LDS, instantiations).
@@ -132,12 +137,12 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
   // The busiest workgroup's bytes, or its busiest stream's at alpha times
   // the stream's fair share of the CU if that is longer.  Alpha is 1 for a
   // single launch; inside the chain the neighbouring stages keep HBM busy and
-  // unevenly loaded waves cost less (alpha 4; measured on the 36-layer chain).
+  // unevenly loaded waves cost less.
   const double wg_items = ceil_div(g.items, kWgPerXcd);
   const double wg_bytes = std::max(wg_items * (item_bytes + part_bytes),
                                    (double)g.ng * per_stream * (item_bytes + part_bytes) / cost.alpha);
   const double x_us = (double)rows * g.win * 2.0 / cost.x_bw * 1e6;
-  const double item_us = per_stream > g.stash_cap ? 0.1 : 0.05;
+  const double item_us = (per_stream > g.stash_cap ? 0.1 : 0.05) + (g.ksl > 1 ? cost.ksl_us : 0.0);
   // split-K finalize: arrival round trips plus the owner's partial reads
   // (S tiles of tile_bytes; a dot2 owner lane reads S floats).
   const double fin_kb = g.S * (g.path == 0 ? 0.25 : tile_bytes / 1024.0);
@@ -288,13 +293,15 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
       for (int i = 0; i < 4; ++i)
         if (v[i]) (which == 0 ? s_st : which == 1 ? k_st : w_st)[i] = v[i];
     }
-    // SGEMM_CHAIN_COST = "alpha,x_gbps,split_us,fin_us_kb" replaces the chain's
+    // SGEMM_CHAIN_COST = "alpha,x_gbps,split_us,fin_us_kb,ksl_us" replaces the chain's
     // cost constants (for calibration runs).
     Cost cost = kCostChain;
     if (const char* ce = std::getenv("SGEMM_CHAIN_COST"); ce && *ce) {
       double x_gbps = 0.0;
-      if (std::sscanf(ce, "%lf,%lf,%lf,%lf", &cost.alpha, &x_gbps, &cost.split_us, &cost.fin_us_kb) != 4 ||
-          !(cost.alpha >= 1.0 && cost.alpha <= 8.0) || !(x_gbps > 0.0) || cost.split_us < 0.0 || cost.fin_us_kb < 0.0) {
+      if (std::sscanf(ce, "%lf,%lf,%lf,%lf,%lf", &cost.alpha, &x_gbps, &cost.split_us, &cost.fin_us_kb,
+                      &cost.ksl_us) != 5 ||
+          !(cost.alpha >= 1.0 && cost.alpha <= 8.0) || !(x_gbps > 0.0) || cost.split_us < 0.0 ||
+          cost.fin_us_kb < 0.0 || cost.ksl_us < 0.0) {
         delete pl;
         return SGEMM_ERR_INVALID_ARG;
       }
