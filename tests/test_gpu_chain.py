@@ -187,8 +187,8 @@ def test_chain_watchdog_times_out_and_workspace_recovers(cuda_device):
     check_chain(good, ws, x0, layers, Y, Yb, M)
 
 
-def test_config5_full_chain_every_stage_sampled(cuda_device):
-    """Configuration 5 as benchmarked: 36 layers, M = 64, d = q = 4096, d_ff = 12288,
+def test_chain_36_layers_m64_full_size_every_stage_sampled(cuda_device):
+    """The benchmarked 36-layer chain: M = 64, d = q = 4096, d_ff = 12288,
     distinct seeded weights per layer (drawn on the GPU, 13.3 GB), one launch in
     the bench's plan.  Every one of the 144 stages is checked against the oracle
     on sampled output columns, each with the GPU's own input to that stage (the
