@@ -4,13 +4,15 @@
 
 Every translation unit under csrc/ is compiled to an object in parallel and
 linked into chiplet_aware_persistent_amd/libsgemm.so.  Packed-fp32 instruction
-selection is disabled for all device code.
+selection is disabled for all device code.  The build fails if any kernel
+uses scratch memory (SGEMM_ALLOW_SCRATCH=1 lets experiments through).
 """
 from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,13 +36,28 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
+def _compile(src: str):
+    """Compile one translation unit; returns (object path, {kernel: scratch bytes per lane})."""
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr[-6000:]))
-    return obj
+    return obj, scratch_usage(r.stderr)
+
+
+def scratch_usage(remarks: str) -> dict:
+    """Per-kernel private (scratch) bytes per lane from the compiler's resource-usage remarks."""
+    out, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name:
+            out[name] = int(m.group(1))
+    return out
 
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
@@ -48,7 +65,14 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     srcs = sources()
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 8)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        res = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in res]
+    # A kernel that spills (register pressure past 256 VGPRs, a dynamically
+    # indexed array, a copy of the kernel arguments) runs several times slower
+    # on this path; refuse to link one.
+    spills = {k: v for _, u in res for k, v in u.items() if v > 0}
+    if spills and not os.environ.get("SGEMM_ALLOW_SCRATCH"):
+        raise RuntimeError("kernels use scratch memory (bytes per lane): %s" % spills)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

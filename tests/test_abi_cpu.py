@@ -163,3 +163,15 @@ def test_roofline_floors():
     assert model.floor_us(4096, 6144) == pytest.approx(6.29, abs=0.01)
     assert model.floor_us(12288, 4096) == pytest.approx(12.58, abs=0.01)
     assert model.ridge_flop_per_byte() == pytest.approx(312.5)
+
+
+def test_build_reads_scratch_usage_from_compiler_remarks():
+    from chiplet_aware_persistent_amd import build
+    remarks = "\n".join([
+        "x.hip:14:1: remark: Function Name: _ZN2sg4k_aEv [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:14:1: remark:     VGPRs: 105 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:14:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:21:1: remark: Function Name: _ZN2sg4k_bEv [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:21:1: remark:     ScratchSize [bytes/lane]: 3136 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert build.scratch_usage(remarks) == {"_ZN2sg4k_aEv": 0, "_ZN2sg4k_bEv": 3136}
