@@ -74,9 +74,10 @@ def library() -> ctypes.CDLL:
         lib.sgemm_status_string.restype = ctypes.c_char_p
         lib.sgemm_plan_describe.argtypes = [vp, ctypes.c_char_p, sz]
         lib.sgemm_topology_probe.argtypes = [vp, ctypes.c_int, vp]
+        lib.sgemm_read_probe.argtypes = [vp, sz, ctypes.c_int, vp, ctypes.c_int, vp]
         for f in ("sgemm_plan_create", "sgemm_plan_destroy", "sgemm_workspace_init", "sgemm_run",
                   "layerchain_run", "sgemm_chain_buffer", "sgemm_query_status", "sgemm_plan_describe",
-                  "sgemm_topology_probe"):
+                  "sgemm_topology_probe", "sgemm_read_probe"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -147,6 +148,10 @@ def sgemm_plan_describe(plan) -> dict:
 
 def sgemm_topology_probe(xcc_out: int, n_wg: int, stream: int = 0) -> int:
     return library().sgemm_topology_probe(xcc_out, n_wg, stream)
+
+
+def sgemm_read_probe(src: int, nbytes: int, pattern: int, sink: int, grid: int = 256, stream: int = 0) -> int:
+    return library().sgemm_read_probe(src, nbytes, pattern, sink, grid, stream)
 
 
 # ------------------------------------------------------------ conveniences
@@ -250,6 +255,20 @@ class LayerChain(_PlanBase):
         _check(rc, "sgemm_chain_buffer")
         cols = nb // (2 * self.M)
         return workspace[off:off + nb].view(torch.bfloat16).view(self.M, cols)
+
+
+def read_probe(buf, pattern: int = 0, sink=None, grid: int = 256, nbytes: int | None = None):
+    """Enqueue one streaming read of ``buf`` (a CUDA tensor) on the current stream;
+    xors its 32-bit words into ``sink`` (an int32 CUDA tensor of one element,
+    created zeroed when None) and returns ``sink``."""
+    import torch
+
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check(sgemm_read_probe(buf.data_ptr(), n, pattern, sink.data_ptr(), grid, _stream_handle(None)),
+           "sgemm_read_probe")
+    return sink
 
 
 def topology(n_wg: int = 256, device: int = 0):

@@ -564,4 +564,12 @@ int sgemm_topology_probe(int* xcc_out, int n_wg, void* stream) {
   return launch_topology(xcc_out, n_wg, (hipStream_t)stream) == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
 }
 
+int sgemm_read_probe(const void* src, size_t bytes, int pattern, unsigned* sink, int grid, void* stream) {
+  if (!src || !sink || !aligned16(src) || ((uintptr_t)sink & 3u)) return SGEMM_ERR_INVALID_ARG;
+  if (bytes < 16 || bytes % 16 || bytes >= kMaxOperand) return SGEMM_ERR_INVALID_ARG;
+  if ((pattern != 0 && pattern != 1) || grid < 8 || grid > 4096 || grid % 8) return SGEMM_ERR_INVALID_ARG;
+  return launch_stream_read(src, bytes, pattern, sink, grid, (hipStream_t)stream) == hipSuccess ? SGEMM_OK
+                                                                                               : SGEMM_ERR_HIP;
+}
+
 }  // extern "C"

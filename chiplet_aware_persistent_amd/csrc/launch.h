@@ -39,6 +39,8 @@ hipError_t launch_gemm(const StageDesc& d, int path, int a, int b, int grid, int
                        unsigned* status, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_topology(int* out, int n, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, size_t bytes, int pattern, unsigned* sink, int grid,
+                              hipStream_t stream);
 
 bool chain_variant_exists(int mt, int nt_q, int nt_o, int nt_d);
 hipError_t launch_chain(const ChainArgs& a, int grid, int block, int lds, hipStream_t stream);

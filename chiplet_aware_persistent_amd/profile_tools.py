@@ -5,6 +5,7 @@
         <write_counter_collection.csv> [--roles a,b,c] [--skip N]
     python -m chiplet_aware_persistent_amd.profile_tools sweep <config_sweep stdout> <kernel_trace.csv>
     python -m chiplet_aware_persistent_amd.profile_tools tcc <config_sweep stdout> <counter_collection.csv>
+    python -m chiplet_aware_persistent_amd.profile_tools read <read_probe stdout> <kernel_trace.csv>
 
 ``trace``: per-role kernel durations.  The decode projections launch the same
 kernel template for several shapes, so durations are split by launch order:
@@ -150,6 +151,23 @@ def sweep_tcc(sweep_log: str, counter_csv: str, warmup: int = 1):
     return out
 
 
+def read_durations(probe_log: str, trace_csv: str, warmup: int = 3):
+    """Kernel durations of the read probe (k_stream_read) per (bytes, pattern)
+    line of the read_probe driver's output, warm-up launches dropped."""
+    rows = [r for r in csv.DictReader(open(trace_csv)) if "k_stream_read" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    ents = [json.loads(l) for l in open(probe_log) if l.startswith("{")]
+    out, pos = [], 0
+    for e in ents:
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[pos + warmup:pos + e["launches"]]]
+        pos += e["launches"]
+        us = statistics.mean(d)
+        out.append({"bytes": e["bytes"], "pattern": e["pattern"], "launches": len(d), "avg_us": round(us, 3),
+                    "median_us": round(statistics.median(d), 3), "GBps": round(e["bytes"] / us / 1e3, 1),
+                    "frac_8TBps": round(e["bytes"] / us / 8e6, 4)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -172,8 +190,14 @@ def main():
     h.add_argument("log")
     h.add_argument("csv")
     h.add_argument("--warmup", type=int, default=1)
+    q = sub.add_parser("read")
+    q.add_argument("log")
+    q.add_argument("csv")
+    q.add_argument("--warmup", type=int, default=3)
     a = ap.parse_args()
-    if a.cmd == "sweep":
+    if a.cmd == "read":
+        print(json.dumps(read_durations(a.log, a.csv, a.warmup), indent=1))
+    elif a.cmd == "sweep":
         print(json.dumps(sweep_durations(a.log, a.csv, a.warmup), indent=1))
     elif a.cmd == "tcc":
         print(json.dumps(sweep_tcc(a.log, a.csv, a.warmup), indent=1))

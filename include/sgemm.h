@@ -21,8 +21,7 @@
  *
  * Ownership: the caller allocates and owns every device buffer (X, W, Y and the
  * workspace).  A plan owns only host-side metadata.  No call allocates device
- * memory, except sgemm_topology_probe, which does not either (it writes into a
- * caller buffer).
+ * memory; sgemm_topology_probe and sgemm_read_probe write into caller buffers.
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).
  * sgemm_run and layerchain_run enqueue work and return; they never
@@ -177,6 +176,22 @@ int sgemm_plan_describe(sgemm_plan plan, char* buf, size_t len);
  * XCDs, and the runtime reads the hardware id to learn its XCD).
  */
 int sgemm_topology_probe(int* xcc_out, int n_wg, void* stream);
+
+/*
+ * Read probe: the attainable-bandwidth reference for the weight stream (the
+ * decode GEMM moves its 2*K*N weight bytes from HBM once, Fleet reading note,
+ * section 2b roofline; this kernel only reads).  Launches `grid` workgroups
+ * of 512 threads (grid a multiple of 8, 8..4096) that read `bytes` bytes at
+ * `src` (device, 16-byte aligned, bytes a multiple of 16 and below 2 GiB) with
+ * 16-byte nontemporal loads and xor all its 32-bit words into *sink (device,
+ * 4-byte aligned; the caller zeroes it first if it checks the value).
+ *   pattern 0: grid-stride order;
+ *   pattern 1: the decode GEMM's order (XCD x reads the x-th eighth, each
+ *              wave a contiguous share of it).
+ * Enqueues on `stream`; returns SGEMM_ERR_INVALID_ARG for a bad argument
+ * before enqueuing anything.
+ */
+int sgemm_read_probe(const void* src, size_t bytes, int pattern, unsigned* sink, int grid, void* stream);
 
 #ifdef __cplusplus
 }

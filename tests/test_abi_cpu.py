@@ -175,3 +175,16 @@ def test_build_reads_scratch_usage_from_compiler_remarks():
         "x.hip:21:1: remark:     ScratchSize [bytes/lane]: 3136 [-Rpass-analysis=kernel-resource-usage]",
     ])
     assert build.scratch_usage(remarks) == {"_ZN2sg4k_aEv": 0, "_ZN2sg4k_bEv": 3136}
+
+
+def test_read_probe_rejects_bad_arguments_before_launch():
+    lib = sg.library()
+    assert lib.sgemm_read_probe(None, 1024, 0, 16, 256, None) == sg.ERR_INVALID_ARG
+    assert lib.sgemm_read_probe(16, 1024, 0, None, 256, None) == sg.ERR_INVALID_ARG
+    assert lib.sgemm_read_probe(24, 1024, 0, 16, 256, None) == sg.ERR_INVALID_ARG    # misaligned source
+    assert lib.sgemm_read_probe(16, 1024, 0, 18, 256, None) == sg.ERR_INVALID_ARG    # misaligned sink
+    assert lib.sgemm_read_probe(16, 1000, 0, 16, 256, None) == sg.ERR_INVALID_ARG    # not whole 16-byte chunks
+    assert lib.sgemm_read_probe(16, 1 << 31, 0, 16, 256, None) == sg.ERR_INVALID_ARG  # past the buffer extent
+    assert lib.sgemm_read_probe(16, 1024, 2, 16, 256, None) == sg.ERR_INVALID_ARG    # pattern
+    assert lib.sgemm_read_probe(16, 1024, 0, 16, 12, None) == sg.ERR_INVALID_ARG     # grid not a multiple of 8
+    assert lib.sgemm_read_probe(16, 1024, 0, 16, 8192, None) == sg.ERR_INVALID_ARG

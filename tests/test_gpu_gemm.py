@@ -212,3 +212,17 @@ def _full_size(dev, M, K, N, config):
     w_rows = synth.uniform_bf16_rows(seed_w, K, synth.weight_scale(K), cols)
     check(Y[:, cols], x, w_rows)
     assert np.all(np.isfinite(Y))
+
+
+@pytest.mark.parametrize("n16", [1, 63, 64, 777, 12345, 1 << 20, (50 << 20) // 16 + 5])
+@pytest.mark.parametrize("pattern,grid", [(0, 256), (1, 256), (1, 8), (0, 1024)])
+def test_read_probe_reads_every_byte_once(cuda_device, n16, pattern, grid):
+    """The attainable-bandwidth probe xors every 32-bit word it reads into the
+    sink: equal to the host xor of the buffer only if each word was read
+    exactly once (a missed or repeated chunk changes it for random data)."""
+    rng = np.random.default_rng(n16 * 7 + pattern)
+    host = rng.integers(0, 2 ** 32, size=4 * n16, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(cuda_device)
+    sink = sg.read_probe(buf, pattern, grid=grid)
+    torch.cuda.synchronize()
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host))
