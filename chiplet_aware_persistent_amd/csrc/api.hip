@@ -34,7 +34,8 @@ struct Geo {
   int ksl = 1, kss = 0;
   int win = 0, xrow = 0, lds = 0, red_off = 0, stash_off = 0, stash_cap = 0;
   int paired = 0, pair_off = 0;
-  int ring = 0;  // ring depth (k-steps in flight per wave)
+  int ring = 0;    // ring depth (k-steps in flight per wave)
+  int mtiles = 1;  // m-tile items (ablation): items per (split, column block), m-tile fastest
   size_t ctr_count = 0, part_floats = 0;
   double est_us = 0.0;
 };
@@ -81,19 +82,20 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
   const int ring = g.path == 0 ? ring_depth_dot2(g.tb) : ring_depth_mfma(g.paired ? 2 : g.tb);
   g.steps = ceil_div(ceil_div(g.kss, kstep), ring) * ring;  // padded to the ring depth
   g.ring = ring;
-  g.items = g.NB * g.S;
+  g.items = g.NB * g.S * g.mtiles;
   // A workgroup stages X once for all splits its contiguous item range
   // touches: the window is (span - 1) splits plus the last slice's padded steps.
+  const int per_split = g.NB * g.mtiles;
   int span = 1;
   for (int w = 0; w < kWgPerXcd; ++w) {
     const int i0 = (int)((long long)g.items * w / kWgPerXcd);
     const int i1 = (int)((long long)g.items * (w + 1) / kWgPerXcd);
-    if (i0 < i1) span = std::max(span, (i1 - 1) / g.NB - i0 / g.NB + 1);
+    if (i0 < i1) span = std::max(span, (i1 - 1) / per_split - i0 / per_split + 1);
   }
   g.win = (span - 1) * g.KS + (g.ksl - 1) * g.kss + g.steps * kstep;
   g.win = (int)round_up((size_t)g.win, 8);
   // MFMA: the rows of X plus one zero row when the M-tiles overhang M.
-  const int rows = g.path == 0 ? g.M : std::min(16 * g.ta, g.M + 1);
+  const int rows = g.path == 0 ? g.M : std::min(16 * g.ta * g.mtiles, g.M + 1);
   g.xrow = g.path == 0 ? g.win : g.win + 8;
   // LDS: X window, K-slice reduction buffer, output stash.
   const int tile_bytes = g.path == 0 ? 64 * 4 : g.tb * g.ta * 1024;  // one wave's item result
@@ -105,7 +107,7 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
   g.stash_cap = std::max(0, std::min(per_stream, (kLdsMax - g.stash_off) / (owners * tile_bytes)));
   g.lds = g.stash_off + owners * g.stash_cap * tile_bytes;
   const int vals = g.path == 0 ? g.tb * g.M : g.tb * g.ta * 256;
-  g.ctr_count = (size_t)kXcds * g.NB * g.wpi;
+  g.ctr_count = (size_t)kXcds * g.NB * g.wpi * g.mtiles;
   g.part_floats = g.S > 1 ? g.ctr_count * (size_t)g.S * vals : 0;
   if (g.stash_off > kLdsMax) return false;
   // MFMA with S == 1 emits Y only from the stash (no epilogue inside the
@@ -153,7 +155,7 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
 }
 
 bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, int s_o, int waves_o,
-              int ksl_o, const Cost& cost, int wpi_o = 0) {
+              int ksl_o, const Cost& cost, int wpi_o = 0, bool mtile_items = false) {
   bool found = false;
   const int waves_opts[2] = {8, 4};
   for (int wi = 0; wi < 2; ++wi) {
@@ -176,6 +178,11 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
         if (paired && tb != 2) continue;
         if (tn_o && !paired && 16 * tb != tn_o) continue;
         g.ta = (M + 15) / 16; g.tb = tb;
+        if (mtile_items) {  // one 16-row m-tile per item, one wave per item
+          if (wpi != 1 || ksl != 1) continue;
+          g.mtiles = g.ta;
+          g.ta = 1;
+        }
       }
       const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : 16;  // the model was fitted up to 16 splits
       for (int s = s_lo; s <= s_hi; ++s) {
@@ -264,15 +271,17 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
   if (p.kind == SGEMM_KIND_GEMM) {
     int rc = validate_gemm(p);
     if (rc != SGEMM_OK) { delete pl; return rc; }
-    const int path = choose_path(p);
-    if (path == 0 && k_o > 1) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
-    if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, kCostGemm)) {
+    const bool mti = (p.flags & SGEMM_F_MTILE_ITEMS) != 0;
+    if (mti && (p.flags & SGEMM_F_FORCE_DOT2)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+    const int path = mti ? 1 : choose_path(p);
+    if ((path == 0 || mti) && k_o > 1) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, kCostGemm, 0, mti)) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
     }
     layout_stage_ws(cur, pl->geo, pl->off_ctr, pl->off_part);
   } else if (p.kind == SGEMM_KIND_LAYERCHAIN) {
-    if (p.flags & (SGEMM_F_W_CACHED | SGEMM_F_W_SC1)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    if (p.flags & (SGEMM_F_W_CACHED | SGEMM_F_W_SC1 | SGEMM_F_MTILE_ITEMS)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     if (p.M < 1 || p.n_layers < 1 || p.d_model < 8 || p.q_cols < 8 || p.d_ff < 8)
       { delete pl; return SGEMM_ERR_INVALID_ARG; }
     if (p.d_model % 8 || p.q_cols % 8 || p.d_ff % 8) { delete pl; return SGEMM_ERR_INVALID_ARG; }
@@ -381,6 +390,8 @@ static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
   d.steps = g.steps; d.items = g.items; d.win = g.win; d.xrow = g.xrow;
   d.red_off = g.red_off; d.stash_off = g.stash_off; d.stash_cap = g.stash_cap;
   d.pair_off = g.pair_off;
+  d.mtiles = g.mtiles;
+  d.interleave = g.mtiles > 1 ? 1 : 0;
   d.w_aux = w_aux;
   d.sync = sync;
   return d;
@@ -528,9 +539,9 @@ static std::string geo_json(const Geo& g) {
                 "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,\"wpi\":%d,"
                 "\"ksl\":%d,\"kss\":%d,\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,"
                 "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
-                "\"ring\":%d,\"est_us\":%.3f}",
+                "\"ring\":%d,\"mtiles\":%d,\"est_us\":%.3f}",
                 g.path == 0 ? "dot2" : "mfma", g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
-                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.est_us);
+                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles, g.est_us);
   return b;
 }
 

@@ -533,8 +533,23 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  int i0, i1;
-  my_items(d.items, slot, nslots, d.ng, wave / d.wpi, i0, i1);
+  // Items: (split, column block, m-tile), m-tile fastest (d.mtiles is 1
+  // unless each item covers one 16-row m-tile).  A stream runs the items
+  // i0, i0 + istep, ... below i1: a contiguous range, or with d.interleave
+  // every ng-th item of the workgroup's range.
+  int i0, i1, istep = 1;
+  if (d.interleave) {
+    i0 = first_item_of_wg(d.items, slot, nslots) + wave / d.wpi;
+    i1 = first_item_of_wg(d.items, slot + 1, nslots);
+    istep = d.ng;
+  } else {
+    my_items(d.items, slot, nslots, d.ng, wave / d.wpi, i0, i1);
+  }
+  const int nit = i0 < i1 ? (i1 - i0 + istep - 1) / istep : 0;  // items of this stream
+  const int per_split = d.NB * d.mtiles;
+  auto split_of = [&](int it) { return it / per_split; };
+  auto block_of = [&](int it) { return (it - split_of(it) * per_split) / d.mtiles; };
+  auto mtile_of = [&](int it) { return it % d.mtiles; };
   const int wv = wave % d.wpi;  // wave's place within its item
   const int CG = d.wpi / d.ksl; // column groups per item
   const int cg = wv % CG;       // this wave's column group
@@ -573,8 +588,8 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   auto src_of = [&](int it) -> Src {
     Src r;
     if (it >= i1) { r.base = 0; r.klim = 0; r.col0 = xc1; return r; }
-    const int s_ = it / d.NB;
-    const int b_ = it - s_ * d.NB;
+    const int s_ = split_of(it);
+    const int b_ = block_of(it);
     const int k0 = s_ * d.KS + kq * d.kss;
     const int col0 = xc0 + b_ * d.CB + cg * TW;
     r.base = ((unsigned)col0 * (unsigned)d.K + (unsigned)k0) * 2u;
@@ -617,29 +632,33 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     const int col = colb + (PAIRED ? 0 : 16 * j) + r16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int m = 16 * i + 4 * g4 + e;
+      const int m = 16 * i + 4 * g4 + e;  // i: the m-tile (counted from 0 over all rows)
       const bool ok = m < d.M && col < xc1;
       store_out(d, yr, y2r, ok, m, col, PAIRED ? silu_mul(v[e], vu[e]) : v[e]);
     }
   };
   // The finished tile of item `it` (owner wave): Y when S == 1, else the
   // split's partial.
+  auto tile_of = [&](int it) {  // split-K tile (counter and partial block) of item it
+    return (unsigned)(((xcd * d.NB + block_of(it)) * d.wpi + wv) * d.mtiles + mtile_of(it));
+  };
   auto out_tile = [&](int it, const f4(&v)[NT][MT]) {
-    const int s = it / d.NB;
-    const int b = it - s * d.NB;
+    const int s = split_of(it);
+    const int b = block_of(it);
     if (d.S == 1) {
       const int colb = xc0 + b * d.CB + wv * TW;
+      const int mt = mtile_of(it);
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         if (PAIRED) {
-          emit(colb, 0, i, v[0][i], v[1][i]);
+          emit(colb, 0, mt + i, v[0][i], v[1][i]);
         } else {
 #pragma unroll
-          for (int j = 0; j < NT; ++j) emit(colb, j, i, v[j][i], v[j][i]);
+          for (int j = 0; j < NT; ++j) emit(colb, j, mt + i, v[j][i], v[j][i]);
         }
       }
     } else {
-      const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
+      const unsigned tile = tile_of(it);
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -654,15 +673,19 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   // until only the ring's loads are outstanding covers them; in the chain X
   // exists only after the wait, so its loads follow the ring.
   constexpr bool early = __is_same(Hook, NoHook);
-  const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
+  const int s_first = split_of(first_item_of_wg(d.items, slot, nslots));
   // The window holds rows [0, M) and, when the M-tiles overhang M, one zero
   // row (row M) that the overhanging lanes of the A operand read instead.
-  const int xrows = min(16 * MT, d.M + 1);
+  const int xrows = min(16 * MT * d.mtiles, d.M + 1);
   int xro[MT];
+  auto set_rows = [&](int it) {  // A-operand row offsets of item it's m-tiles
+    const int m0 = 16 * (it < i1 ? mtile_of(it) : 0);
 #pragma unroll
-  for (int i = 0; i < MT; ++i) xro[i] = min(16 * i + r16, d.M) * d.xrow;
+    for (int i = 0; i < MT; ++i) xro[i] = min(m0 + 16 * i + r16, d.M) * d.xrow;
+  };
+  set_rows(i0);
   if constexpr (early) stage_x_lds(d, xs, xrows, s_first * d.KS, d.K, xr);
-  Src sc = src_of(i0), sn = src_of(i0 + 1);
+  Src sc = src_of(i0), sn = src_of(i0 + istep);
 #pragma unroll
   for (int p = 0; p < P; ++p) issue(ring[p], sc, p);
   if (!pre_x()) return false;
@@ -681,9 +704,9 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[j][i] = f4{0.f, 0.f, 0.f, 0.f};
-  int it = i0, t0 = 0;
-  int xoff = (i0 / d.NB - s_first) * d.KS + kq * d.kss;
-  const int total = (i1 - i0) * spad;
+  int it = i0, li = 0, t0 = 0;
+  int xoff = (split_of(i0) - s_first) * d.KS + kq * d.kss;
+  const int total = nit * spad;
   for (int T = 0; T < total; T += P) {
     const bool here = t0 + P < spad;
     const Src& sr = here ? sc : sn;
@@ -735,7 +758,6 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
         __syncthreads();
       }
       if (owner) {
-        const int li = it - i0;
         if (li < d.stash_cap) {
 #pragma unroll
           for (int j = 0; j < NT; ++j)
@@ -745,8 +767,8 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
           // Stash full (the planner allows this only with S > 1): the
           // split's partial goes out now.  Only this plain store sits in the
           // loop, which keeps the epilogue's registers out of it.
-          const int s = it / d.NB;
-          const unsigned tile = (unsigned)((xcd * d.NB + (it - s * d.NB)) * d.wpi + wv);
+          const int s = split_of(it);
+          const unsigned tile = tile_of(it);
 #pragma unroll
           for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -758,44 +780,45 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
       for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int i = 0; i < MT; ++i) acc[j][i] = f4{0.f, 0.f, 0.f, 0.f};
-      ++it;
+      it += istep;
+      ++li;
       t0 = 0;
       sc = sn;
-      sn = src_of(it + 1);
-      xoff = (it / d.NB - s_first) * d.KS + kq * d.kss;
+      sn = src_of(it + istep);
+      xoff = (split_of(it) - s_first) * d.KS + kq * d.kss;
+      if (d.mtiles > 1) set_rows(it);
     }
   }
 
   // Stored items: results of the stream, written after its last load.
   if (owner) {
-    const int n = min(i1 - i0, d.stash_cap);
+    const int n = min(nit, d.stash_cap);
     for (int li = 0; li < n; ++li) {
       f4 v[NT][MT];
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int i = 0; i < MT; ++i) v[j][i] = stash[((own * d.stash_cap + li) * (NT * MT) + j * MT + i) * 64 + lane];
-      out_tile(i0 + li, v);
+      out_tile(i0 + li * istep, v);
     }
   }
 
   if (d.S > 1 && i0 < i1 && owner) {
     splitk_release(d.sync);
     constexpr int B = 4;
-    for (int c0 = i0; c0 < i1; c0 += B) {
+    for (int c0 = 0; c0 < nit; c0 += B) {
       unsigned old[B];
 #pragma unroll
       for (int j = 0; j < B; ++j) {
-        const int it = c0 + j;
-        const int b = it % d.NB;
-        old[j] = it < i1 ? splitk_bump(d.ctr + (xcd * d.NB + b) * d.wpi + wv, lane) : 0u;
+        const int it = i0 + (c0 + j) * istep;
+        old[j] = c0 + j < nit ? splitk_bump(d.ctr + tile_of(it), lane) : 0u;
       }
 #pragma unroll
       for (int jj = 0; jj < B; ++jj) {
-        const int it = c0 + jj;
-        if (it >= i1) break;
-        const int b = it % d.NB;
-        const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
+        const int it = i0 + (c0 + jj) * istep;
+        if (c0 + jj >= nit) break;
+        const int b = block_of(it);
+        const unsigned tile = tile_of(it);
         if (!splitk_own(d.ctr + tile, old[jj], d.S, d.sync, lane)) continue;
         f4 tot[NT][MT];
 #pragma unroll
@@ -808,13 +831,14 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
           sum_partials_f4<0, NT, MT>(pr, tile * d.S * TILE, TILE, d.S, lane, tot, d.part_bytes);
         }
         const int colb = xc0 + b * d.CB + wv * TW;
+        const int mt = mtile_of(it);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
           if (PAIRED) {
-            emit(colb, 0, i, tot[0][i], tot[1][i]);
+            emit(colb, 0, mt + i, tot[0][i], tot[1][i]);
           } else {
 #pragma unroll
-            for (int j = 0; j < NT; ++j) emit(colb, j, i, tot[j][i], tot[j][i]);
+            for (int j = 0; j < NT; ++j) emit(colb, j, mt + i, tot[j][i], tot[j][i]);
           }
         }
       }

@@ -55,6 +55,8 @@ struct StageDesc {
   int stash_cap;       // items per owning wave whose results wait in LDS until the
                        // weight stream ends (the rest are stored at item end)
   int pair_off;        // paired: weight row offset of the up half
+  int mtiles;          // MFMA: items per (split, column block), one 16-row m-tile each (1: all rows)
+  int interleave;      // streams of a workgroup take every ng-th item of its range
   int mode;            // OutMode
   int sync;            // SyncMode of the split-K arrival
   unsigned w_aux;      // cache-policy bits of the weight loads

@@ -68,10 +68,17 @@ enum {
   SGEMM_F_WATCHDOG_TEST = 1u << 6, /* chain: spin budget of zero, to exercise the
                                       time-out path from the host               */
   SGEMM_F_W_SC1 = 1u << 7,       /* weight loads with sc1|nt (streaming)         */
-  SGEMM_F_POLL_LEADER = 1u << 8  /* chain: one workgroup per XCD polls the global
+  SGEMM_F_POLL_LEADER = 1u << 8, /* chain: one workgroup per XCD polls the global
                                     counter and raises a per-XCD flag that the
                                     XCD's other workgroups poll (default: every
                                     workgroup polls the global counter)         */
+  SGEMM_F_MTILE_ITEMS = 1u << 9  /* GEMM, ablation: one 16-row m-tile per item,
+                                    m-tile fastest, consecutive items on
+                                    neighbouring waves, so the m-tiles of a
+                                    column block share its weights through the
+                                    caches (Fleet reading note, section 3f,
+                                    M-major window) instead of in registers;
+                                    MFMA path, no K slices                      */
 };
 
 /*

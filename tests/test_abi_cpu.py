@@ -56,6 +56,10 @@ def _create(**kw):
     (dict(kind=sg.KIND_LAYERCHAIN, M=4, L=65, d=64, q=64, dff=64), sg.ERR_UNSUPPORTED),
     (dict(kind=sg.KIND_LAYERCHAIN, M=65, L=2, d=64, q=64, dff=64), sg.ERR_UNSUPPORTED),
     (dict(M=1, K=8, N=1), sg.OK),
+    (dict(M=32, flags=sg.F_MTILE_ITEMS | sg.F_FORCE_DOT2), sg.ERR_INVALID_ARG),
+    (dict(M=32, K=1024, N=1024, flags=sg.F_MTILE_ITEMS, ksl=2), sg.ERR_UNSUPPORTED),
+    (dict(M=32, K=1024, N=1024, flags=sg.F_MTILE_ITEMS), sg.OK),
+    (dict(kind=sg.KIND_LAYERCHAIN, M=32, L=2, d=64, q=64, dff=64, flags=sg.F_MTILE_ITEMS), sg.ERR_UNSUPPORTED),
     (dict(M=64, K=12288, N=4096), sg.OK),
 ])
 def test_plan_create_validation(kw, code):
@@ -86,15 +90,21 @@ SHAPES = [(1, 1024, 1024), (1, 4096, 6144), (1, 4096, 4096), (1, 4096, 24576), (
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
 @pytest.mark.parametrize("splitk", [0, 3])
-def test_planner_covers_every_column_and_k_once(M, K, N, splitk):
+@pytest.mark.parametrize("flags", [0, sg.F_MTILE_ITEMS])
+def test_planner_covers_every_column_and_k_once(M, K, N, splitk, flags):
+    if flags and M < 16:
+        return
     try:
-        g = sg.Gemm(M, K, N, splitk=splitk)
+        g = sg.Gemm(M, K, N, splitk=splitk, flags=flags)
     except sg.SgemmError as e:
         # a forced split count whose X window exceeds the LDS budget is refused
         assert splitk and e.code == sg.ERR_UNSUPPORTED
         return
     st = g.describe()["stage"]
     assert st["path"] == ("dot2" if M < 16 else "mfma")
+    mt = st["mtiles"]
+    assert mt == (math.ceil(M / 16) if flags else 1) and (mt == 1 or st["ta"] == 1)
+    assert 16 * st["ta"] * mt >= M                     # m-tiles cover every row
     Nx, CB, NB, S, KS = st["Nx"], st["CB"], st["NB"], st["S"], st["KS"]
     ksl, kss = st["ksl"], st["kss"]
     assert st["wpi"] % ksl == 0 and CB == st["wpi"] // ksl * st["TN"] and st["waves"] % st["wpi"] == 0
@@ -103,7 +113,7 @@ def test_planner_covers_every_column_and_k_once(M, K, N, splitk):
     assert NB * CB >= Nx                               # column blocks cover the XCD's columns
     assert S * KS >= K and (S - 1) * KS < K            # splits cover K, none empty
     assert ksl * kss >= KS and (ksl - 1) * kss < KS    # slices cover a split, none empty
-    assert KS % 64 == 0 and st["items"] == NB * S    # splits start on 128-byte lines
+    assert KS % 64 == 0 and st["items"] == NB * S * mt  # splits start on 128-byte lines
     kstep = 512 if st["path"] == "dot2" else 64
     assert ksl == 1 or kss % kstep == 0
     assert st["steps"] * kstep >= kss

@@ -226,3 +226,21 @@ def test_read_probe_reads_every_byte_once(cuda_device, n16, pattern, grid):
     sink = sg.read_probe(buf, pattern, grid=grid)
     torch.cuda.synchronize()
     assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host))
+
+
+@pytest.mark.parametrize("M,K,N", [(17, 776, 530), (33, 2056, 900), (64, 4096, 1536), (48, 520, 64),
+                                   (64, 12288, 4096)])
+@pytest.mark.parametrize("splitk", [0, 3])
+def test_parity_mtile_items(cuda_device, M, K, N, splitk):
+    """The m-tile-item ablation (one 16-row m-tile per item, neighbouring waves
+    share a column block's weights through the caches) computes the same
+    GEMM."""
+    x, w, X, W = gemm_inputs(M, K, N, 9900 + M, 9950 + K, cuda_device)
+    try:
+        g = sg.Gemm(M, K, N, flags=sg.F_MTILE_ITEMS, splitk=splitk)
+    except sg.SgemmError as e:
+        assert splitk and e.code == sg.ERR_UNSUPPORTED
+        pytest.skip("no plan with this split count fits the LDS")
+    st = g.describe()["stage"]
+    assert st["mtiles"] == -(-M // 16) and st["ta"] == 1
+    check(run(g, X, W).cpu().numpy(), x, w)
