@@ -421,7 +421,7 @@ int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* work
   d.y_bytes = (unsigned)((size_t)p.M * p.N * (p.out_dtype == SGEMM_OUT_F32 ? 4 : 2));
   d.y2_bytes = 0;
   if (hipSetDevice(plan->device) != hipSuccess) return SGEMM_ERR_HIP;
-  hipError_t e = launch_gemm(d, g.path, g.ta, g.tb, plan->grid, g.waves * 64, g.lds, (unsigned*)ws,
+  hipError_t e = launch_gemm(d, g.mtiles > 1 ? 2 : g.path, g.ta, g.tb, plan->grid, g.waves * 64, g.lds, (unsigned*)ws,
                              (hipStream_t)stream);
   return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
 }

@@ -523,7 +523,7 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
 // The A operand (X, from LDS) uses the same k slots: for m-tile i lane l'
 // reads row 16i + l'%16 (the zero row M where that passes M) at
 // k = 32h + 8(l'/16).
-template <int MT, int NT, bool PAIRED, int AUX, typename Hook = NoHook>
+template <int MT, int NT, bool PAIRED, int AUX, typename Hook = NoHook, bool MTI = false>
 __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                            Hook pre_x = Hook()) {
   constexpr int P = ring_depth_mfma(NT);
@@ -533,12 +533,14 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  // Items: (split, column block, m-tile), m-tile fastest (d.mtiles is 1
-  // unless each item covers one 16-row m-tile).  A stream runs the items
-  // i0, i0 + istep, ... below i1: a contiguous range, or with d.interleave
-  // every ng-th item of the workgroup's range.
+  // Items: (split, column block, m-tile), m-tile fastest.  MTI (the m-tile-
+  // item variant): d.mtiles items per (split, column block), one 16-row
+  // m-tile each; otherwise one item covers every row.  A stream runs the
+  // items i0, i0 + istep, ... below i1: a contiguous range, or with
+  // d.interleave every ng-th item of the workgroup's range.
+  const int mtl = MTI ? d.mtiles : 1;
   int i0, i1, istep = 1;
-  if (d.interleave) {
+  if (MTI && d.interleave) {
     i0 = first_item_of_wg(d.items, slot, nslots) + wave / d.wpi;
     i1 = first_item_of_wg(d.items, slot + 1, nslots);
     istep = d.ng;
@@ -546,10 +548,10 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     my_items(d.items, slot, nslots, d.ng, wave / d.wpi, i0, i1);
   }
   const int nit = i0 < i1 ? (i1 - i0 + istep - 1) / istep : 0;  // items of this stream
-  const int per_split = d.NB * d.mtiles;
+  const int per_split = d.NB * mtl;
   auto split_of = [&](int it) { return it / per_split; };
-  auto block_of = [&](int it) { return (it - split_of(it) * per_split) / d.mtiles; };
-  auto mtile_of = [&](int it) { return it % d.mtiles; };
+  auto block_of = [&](int it) { return (it - split_of(it) * per_split) / mtl; };
+  auto mtile_of = [&](int it) { return it % mtl; };
   const int wv = wave % d.wpi;  // wave's place within its item
   const int CG = d.wpi / d.ksl; // column groups per item
   const int cg = wv % CG;       // this wave's column group
@@ -640,7 +642,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   // The finished tile of item `it` (owner wave): Y when S == 1, else the
   // split's partial.
   auto tile_of = [&](int it) {  // split-K tile (counter and partial block) of item it
-    return (unsigned)(((xcd * d.NB + block_of(it)) * d.wpi + wv) * d.mtiles + mtile_of(it));
+    return (unsigned)(((xcd * d.NB + block_of(it)) * d.wpi + wv) * mtl + mtile_of(it));
   };
   auto out_tile = [&](int it, const f4(&v)[NT][MT]) {
     const int s = split_of(it);
@@ -676,7 +678,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   const int s_first = split_of(first_item_of_wg(d.items, slot, nslots));
   // The window holds rows [0, M) and, when the M-tiles overhang M, one zero
   // row (row M) that the overhanging lanes of the A operand read instead.
-  const int xrows = min(16 * MT * d.mtiles, d.M + 1);
+  const int xrows = min(16 * MT * mtl, d.M + 1);
   int xro[MT];
   auto set_rows = [&](int it) {  // A-operand row offsets of item it's m-tiles
     const int m0 = 16 * (it < i1 ? mtile_of(it) : 0);
@@ -786,7 +788,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
       sc = sn;
       sn = src_of(it + istep);
       xoff = (split_of(it) - s_first) * d.KS + kq * d.kss;
-      if (d.mtiles > 1) set_rows(it);
+      if constexpr (MTI) set_rows(it);
     }
   }
 

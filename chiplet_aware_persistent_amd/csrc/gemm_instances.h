@@ -17,14 +17,15 @@ __global__ __launch_bounds__(512) void k_gemm_dot2(StageDesc d, unsigned* status
   dot2_stage<M, G, AUX>(d, lds, blockIdx.x & 7, blockIdx.x >> 3, gridDim.x >> 3);
 }
 
-template <int MT, int NT, int AUX>
+template <int MT, int NT, int AUX, bool MTI = false>
 __global__ __launch_bounds__(512) void k_gemm_mfma(StageDesc d, unsigned* status) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   check_topology(status);
-  mfma_stage<MT, NT, false, AUX>(d, lds, blockIdx.x & 7, blockIdx.x >> 3, gridDim.x >> 3);
+  mfma_stage<MT, NT, false, AUX, NoHook, MTI>(d, lds, blockIdx.x & 7, blockIdx.x >> 3, gridDim.x >> 3);
 }
 
 // dot2: M = 1..15, G in {1, 2, 3, 4, 8} with G*M <= 64.  MFMA: MT = 1..4, NT = 1, 2.
+// Path 2: the MFMA m-tile-item variant (MT = 1, NT = 1, 2).
 template <int AUX>
 GemmKernel gemm_kernel_for(int path, int a, int b) {
 #define SG_D2(m)                                                    \
@@ -40,6 +41,12 @@ GemmKernel gemm_kernel_for(int path, int a, int b) {
     if (b == 1) return k_gemm_mfma<mt, 1, AUX>;     \
     if (b == 2) return k_gemm_mfma<mt, 2, AUX>;     \
     return nullptr;
+  if (path == 2) {
+    if (a != 1) return nullptr;
+    if (b == 1) return k_gemm_mfma<1, 1, AUX, true>;
+    if (b == 2) return k_gemm_mfma<1, 2, AUX, true>;
+    return nullptr;
+  }
   if (path == 0) {
     switch (a) {
       SG_D2(1) SG_D2(2) SG_D2(3) SG_D2(4) SG_D2(5) SG_D2(6) SG_D2(7) SG_D2(8)
