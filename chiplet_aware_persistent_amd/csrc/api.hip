@@ -40,9 +40,19 @@ struct Geo {
   double est_us = 0.0;
 };
 
-int env_int(const char* name, int dflt) {
+// Integer from the environment: dflt when unset or empty; false when the
+// value is not a whole decimal integer.
+bool env_int(const char* name, int dflt, int* out) {
   const char* v = std::getenv(name);
-  return v && *v ? std::atoi(v) : dflt;
+  if (!v || !*v) {
+    *out = dflt;
+    return true;
+  }
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  if (*end != '\0' || x < -(1L << 30) || x > (1L << 30)) return false;
+  *out = (int)x;
+  return true;
 }
 
 // Cost-model constants of one launch context (a single GEMM launch, or a
@@ -249,12 +259,22 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
   *out = nullptr;
   const sgemm_problem& p = *problem;
   if ((p.flags & SGEMM_F_FORCE_DOT2) && (p.flags & SGEMM_F_FORCE_MFMA)) return SGEMM_ERR_INVALID_ARG;
-  if (p.tn < 0 || p.splitk < 0 || p.waves < 0 || p.kslices < 0) return SGEMM_ERR_INVALID_ARG;
-  if (p.waves && p.waves != 4 && p.waves != 8) return SGEMM_ERR_INVALID_ARG;
-  if (p.kslices && p.kslices != 1 && p.kslices != 2 && p.kslices != 4 && p.kslices != 8)
-    return SGEMM_ERR_INVALID_ARG;
-  if (p.splitk > 64) return SGEMM_ERR_UNSUPPORTED;
   if (device < 0) return SGEMM_ERR_INVALID_ARG;
+  // Overrides: the problem's fields, else the environment (0: planner's choice).
+  int tn_o = p.tn, s_o = p.splitk, w_o = p.waves, k_o = p.kslices;
+  if ((!tn_o && !env_int("SGEMM_TN", 0, &tn_o)) || (!s_o && !env_int("SGEMM_SPLITK", 0, &s_o)) ||
+      (!w_o && !env_int("SGEMM_WAVES", 0, &w_o)) || (!k_o && !env_int("SGEMM_KSLICES", 0, &k_o)))
+    return SGEMM_ERR_INVALID_ARG;
+  if (tn_o < 0 || s_o < 0 || w_o < 0 || k_o < 0) return SGEMM_ERR_INVALID_ARG;
+  if (w_o && w_o != 4 && w_o != 8) return SGEMM_ERR_INVALID_ARG;
+  if (k_o && k_o != 1 && k_o != 2 && k_o != 4 && k_o != 8) return SGEMM_ERR_INVALID_ARG;
+  if (s_o > 64) return SGEMM_ERR_UNSUPPORTED;
+  double watchdog_s = 5.0;  // seconds a chain stage may wait for its producer
+  if (const char* ws = std::getenv("SGEMM_WATCHDOG_S"); ws && *ws) {
+    char* end = nullptr;
+    watchdog_s = std::strtod(ws, &end);
+    if (*end != '\0' || !(watchdog_s > 0.0 && watchdog_s <= 3600.0)) return SGEMM_ERR_INVALID_ARG;
+  }
 
   sgemm_plan_s* pl = new (std::nothrow) sgemm_plan_s();
   if (!pl) return SGEMM_ERR_INVALID_ARG;
@@ -262,10 +282,6 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
   pl->device = device;
   pl->w_aux = (p.flags & SGEMM_F_W_CACHED) ? 0u : ((p.flags & SGEMM_F_W_SC1) ? 18u : 2u);
   pl->sync = (p.flags & SGEMM_F_SYNC_AGENT) ? SYNC_AGENT : SYNC_XCD;
-  const int tn_o = p.tn ? p.tn : env_int("SGEMM_TN", 0);
-  const int s_o = p.splitk ? p.splitk : env_int("SGEMM_SPLITK", 0);
-  const int w_o = p.waves ? p.waves : env_int("SGEMM_WAVES", 0);
-  const int k_o = p.kslices ? p.kslices : env_int("SGEMM_KSLICES", 0);
 
   size_t cur = kCtl;
   if (p.kind == SGEMM_KIND_GEMM) {
@@ -357,8 +373,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     cur = round_up(cur + pl->act_layer_elems * 2 * p.n_layers, 256);
     pl->off_stamps = cur;
     if (p.flags & SGEMM_F_STAMPS) cur = round_up(cur + (size_t)pl->grid * events * 2 * 8, 256);
-    const double secs = std::atof(std::getenv("SGEMM_WATCHDOG_S") ? std::getenv("SGEMM_WATCHDOG_S") : "5");
-    pl->spin_ticks = (p.flags & SGEMM_F_WATCHDOG_TEST) ? 0 : (long long)(secs * 1.0e8);
+    pl->spin_ticks = (p.flags & SGEMM_F_WATCHDOG_TEST) ? 0 : (long long)(watchdog_s * 1.0e8);
   } else {
     delete pl;
     return SGEMM_ERR_INVALID_ARG;

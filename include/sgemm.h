@@ -112,8 +112,20 @@ typedef struct {
  * per-XCD column partition, tile widths, split-K count and workspace layout.
  * *workspace_bytes receives the size of the device workspace the runs need
  * (>= 4 KiB).  Shape rules: 1 <= M <= 64; K >= 8, K % 8 == 0; N >= 1; every
- * operand below 4 GiB.  Returns SGEMM_ERR_INVALID_ARG or
+ * operand below 2 GiB.  Returns SGEMM_ERR_INVALID_ARG or
  * SGEMM_ERR_UNSUPPORTED without creating a plan when they are violated.
+ *
+ * Environment, read here (for experiments and calibration):
+ *   SGEMM_TN, SGEMM_SPLITK, SGEMM_WAVES, SGEMM_KSLICES: used for the problem
+ *       fields tn, splitk, waves, kslices when those are 0;
+ *   SGEMM_CHAIN_S, SGEMM_CHAIN_KSL, SGEMM_CHAIN_WPI: "q,o,gate_up,down", the
+ *       split count, K slices and waves per item of each chain stage
+ *       (0 = the planner's choice);
+ *   SGEMM_CHAIN_COST: "alpha,x_gbps,split_us,fin_us_kb,ksl_us", the chain
+ *       planner's cost constants;
+ *   SGEMM_WATCHDOG_S: seconds a chain stage may wait for its producer before
+ *       the run stops with SGEMM_ERR_TIMEOUT (default 5, at most 3600).
+ * A malformed value makes the call return SGEMM_ERR_INVALID_ARG.
  */
 int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
                       size_t* workspace_bytes);

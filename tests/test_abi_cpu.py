@@ -198,3 +198,23 @@ def test_read_probe_rejects_bad_arguments_before_launch():
     assert lib.sgemm_read_probe(16, 1024, 2, 16, 256, None) == sg.ERR_INVALID_ARG    # pattern
     assert lib.sgemm_read_probe(16, 1024, 0, 16, 12, None) == sg.ERR_INVALID_ARG     # grid not a multiple of 8
     assert lib.sgemm_read_probe(16, 1024, 0, 16, 8192, None) == sg.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name,value,kind", [
+    ("SGEMM_SPLITK", "two", sg.KIND_GEMM), ("SGEMM_WAVES", "6", sg.KIND_GEMM), ("SGEMM_KSLICES", "3", sg.KIND_GEMM),
+    ("SGEMM_TN", "-1", sg.KIND_GEMM), ("SGEMM_WATCHDOG_S", "abc", sg.KIND_LAYERCHAIN),
+    ("SGEMM_WATCHDOG_S", "0", sg.KIND_LAYERCHAIN), ("SGEMM_CHAIN_COST", "1.5,75", sg.KIND_LAYERCHAIN),
+    ("SGEMM_CHAIN_COST", "0.5,75,0.5,0.05,0.25", sg.KIND_LAYERCHAIN), ("SGEMM_CHAIN_S", "1,2", sg.KIND_LAYERCHAIN)])
+def test_malformed_environment_overrides_are_rejected(monkeypatch, name, value, kind):
+    monkeypatch.setenv(name, value)
+    if kind == sg.KIND_GEMM:
+        assert _create(M=16, K=1024, N=1024) == sg.ERR_INVALID_ARG
+    else:
+        assert _create(kind=kind, M=4, L=2, d=256, q=128, dff=384) == sg.ERR_INVALID_ARG
+
+
+def test_environment_overrides_apply(monkeypatch):
+    monkeypatch.setenv("SGEMM_SPLITK", "4")
+    monkeypatch.setenv("SGEMM_WATCHDOG_S", "2.5")
+    assert sg.Gemm(16, 4096, 1024).describe()["stage"]["S"] == 4
+    assert _create(kind=sg.KIND_LAYERCHAIN, M=4, L=2, d=256, q=128, dff=384) == sg.OK
