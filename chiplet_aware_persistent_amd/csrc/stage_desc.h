@@ -15,7 +15,7 @@ constexpr int kLoadsInFlight = 16;  // 16-byte weight loads per lane kept in fli
 
 // Ring depth (k-steps in flight) of each path; steps per item are padded to a
 // multiple of it.
-constexpr int ring_depth_dot2(int g) { return g <= 2 ? 8 : (g <= 4 ? 4 : 2); }
+constexpr int ring_depth_dot2(int g) { return g <= 1 ? 8 : (g <= 4 ? 4 : 2); }
 constexpr int ring_depth_mfma(int nt) { return kLoadsInFlight / (2 * nt) > 2 ? kLoadsInFlight / (2 * nt) : 2; }
 
 enum OutMode : int {
