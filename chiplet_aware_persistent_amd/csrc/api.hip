@@ -64,13 +64,14 @@ struct Cost {
   double split_us;   // split-K arrival and finalize round trip
   double fin_us_kb;  // per kilobyte of partials an owner reads
   double ksl_us;     // per item with K slices (two workgroup barriers, LDS exchange)
+  bool chain;        // a chain stage (up to two m-tiles it keeps the deeper MFMA ring)
 };
-constexpr Cost kCostGemm{1.0, 200.0e9, 6.0, 0.05, 0.0};
+constexpr Cost kCostGemm{1.0, 200.0e9, 6.0, 0.05, 0.0, false};
 // Chain constants fitted to whole-chain times of per-stage forced plans at
 // M = 1..64 (36 layers, d = q = 4096, d_ff = 12288): X comes from other XCDs'
 // fresh writes (slower than a warm window), while a split's finalize overlaps
 // the neighbouring stages' streams.
-constexpr Cost kCostChain{1.25, 75.0e9, 0.5, 0.05, 0.25};
+constexpr Cost kCostChain{1.25, 75.0e9, 0.5, 0.05, 0.25, true};
 
 // Fill the derived fields of g for (path, template params, waves, wpi, ksl,
 // S); returns false when the candidate does not fit (LDS, instantiations).
@@ -89,8 +90,10 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
   g.S = ceil_div(g.K, g.KS);
   g.kss = g.ksl > 1 ? (int)round_up((size_t)ceil_div(g.KS, g.ksl), kstep) : g.KS;
   if (g.ksl > 1 && (g.ksl - 1) * g.kss >= g.KS) return false;  // an empty slice
-  const int ring = g.path == 0 ? ring_depth_dot2(g.tb) : ring_depth_mfma(g.paired ? 2 : g.tb);
-  g.steps = ceil_div(ceil_div(g.kss, kstep), ring) * ring;  // padded to the ring depth
+  const int ring = g.path == 0 ? ring_depth_dot2(g.tb)
+                                : ring_depth_mfma(g.paired ? 2 : g.tb, cost.chain && g.ta <= 2);
+  const int pad = g.path == 0 ? ring : step_pad_mfma(g.paired ? 2 : g.tb);
+  g.steps = ceil_div(ceil_div(g.kss, kstep), pad) * pad;  // a multiple of the ring depth
   g.ring = ring;
   g.items = g.NB * g.S * g.mtiles;
   // A workgroup stages X once for all splits its contiguous item range

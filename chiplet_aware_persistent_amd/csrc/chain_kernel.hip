@@ -133,10 +133,12 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
         return ok;
       };
       // Every workgroup runs the hook (the wait), also one without items here.
+      // Up to two m-tiles (M <= 32) keep the deeper ring: across the stage
+      // barriers it measured faster there, the shallow one at M = 64.
       if (s == 2) {
-        alive = mfma_stage<MT, 2, true, kAuxNt>(d, lds, xcd, slot, nslots, hook);
+        alive = mfma_stage<MT, 2, true, kAuxNt, (MT <= 2)>(d, lds, xcd, slot, nslots, hook);
       } else {
-        alive = mfma_stage<MT, NT, false, kAuxNt>(d, lds, xcd, slot, nslots, hook);
+        alive = mfma_stage<MT, NT, false, kAuxNt, (MT <= 2)>(d, lds, xcd, slot, nslots, hook);
       }
       if (!alive) break;
       if (a.stamps) __syncthreads();  // the stamp marks the end of the workgroup's last wave

@@ -523,10 +523,10 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
 // The A operand (X, from LDS) uses the same k slots: for m-tile i lane l'
 // reads row 16i + l'%16 (the zero row M where that passes M) at
 // k = 32h + 8(l'/16).
-template <int MT, int NT, bool PAIRED, int AUX, typename Hook = NoHook, bool MTI = false>
+template <int MT, int NT, bool PAIRED, int AUX, bool DEEP = false, typename Hook = NoHook, bool MTI = false>
 __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                            Hook pre_x = Hook()) {
-  constexpr int P = ring_depth_mfma(NT);
+  constexpr int P = ring_depth_mfma(NT, DEEP);
   constexpr int TW = PAIRED ? 16 : 16 * NT;  // distinct output columns per wave
   constexpr unsigned TILE = NT * MT * 256;   // floats of one wave tile
   const int lane = threadIdx.x & 63;

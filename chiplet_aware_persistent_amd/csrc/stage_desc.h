@@ -16,7 +16,13 @@ constexpr int kLoadsInFlight = 16;  // 16-byte weight loads per lane kept in fli
 // Ring depth (k-steps in flight) of each path; steps per item are padded to a
 // multiple of it.
 constexpr int ring_depth_dot2(int g) { return g <= 1 ? 8 : (g <= 4 ? 4 : 2); }
-constexpr int ring_depth_mfma(int nt) { return kLoadsInFlight / (2 * nt) > 2 ? kLoadsInFlight / (2 * nt) : 2; }
+// MFMA: 2 NT loads per lane and step.  One n-tile keeps 4 steps (8 loads) in
+// flight, or 8 steps (16 loads) when `deep`; two n-tiles keep 4 steps.
+constexpr int ring_depth_mfma(int nt, bool deep = false) {
+  return nt == 1 ? (deep ? 8 : 4) : kLoadsInFlight / (2 * nt);
+}
+// MFMA steps per item are padded to this multiple of every ring depth above.
+constexpr int step_pad_mfma(int nt) { return kLoadsInFlight / (2 * nt) > 2 ? kLoadsInFlight / (2 * nt) : 2; }
 
 enum OutMode : int {
   OUT_F32 = 0,       // Y fp32
