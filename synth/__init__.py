@@ -41,9 +41,11 @@ MASK64 = (1 << 64) - 1
 T_X, T_WQ, T_WO, T_WGU, T_WDOWN = 0, 1, 2, 3, 4
 
 
-def seed_for(config: int, layer: int = 0, tensor: int = 0, variant: int = 0) -> int:
-    """Seed scheme: one 64-bit seed per (config, layer, tensor, variant)."""
-    return (0x5EED0000 + (config << 16) + (layer << 8) + (tensor << 4) + variant) & MASK64
+def seed_for(workload: int, layer: int = 0, tensor: int = 0, variant: int = 0) -> int:
+    """Seed scheme: one 64-bit seed per (workload, layer, tensor, variant).
+    Workloads: 1 the 1x1024x1024 GEMM, 2 the decode projections at M = 1,
+    3 the same shapes at M = 8..64, 4 the K = 7168 GEMMs, 5 the 36-layer chain."""
+    return (0x5EED0000 + (workload << 16) + (layer << 8) + (tensor << 4) + variant) & MASK64
 
 
 # ---------------------------------------------------------------- reference

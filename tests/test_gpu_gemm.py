@@ -135,12 +135,12 @@ def _int_inputs(M, K, N, dev):
     return xb, wb, device_tensor_bf16(xb, dev), device_tensor_bf16(wb, dev)
 
 
-CONFIG_SHAPES = [(1, 4096, 6144), (1, 4096, 4096), (1, 4096, 24576), (1, 12288, 4096),
+DECODE_SHAPES = [(1, 4096, 6144), (1, 4096, 4096), (1, 4096, 24576), (1, 12288, 4096),
                  (8, 12288, 4096), (16, 4096, 6144), (32, 4096, 24576), (64, 12288, 4096),
                  (1, 7168, 1536), (2, 7168, 18432), (4, 7168, 4096), (16, 7168, 1536)]
 
 
-@pytest.mark.parametrize("M,K,N", CONFIG_SHAPES)
+@pytest.mark.parametrize("M,K,N", DECODE_SHAPES)
 def test_integer_inputs_bitwise_at_full_size(cuda_device, M, K, N):
     xb, wb, X, W = _int_inputs(M, K, N, cuda_device)
     Y = run(sg.Gemm(M, K, N), X, W).cpu().numpy()
@@ -185,27 +185,27 @@ def test_power_of_two_scaling_and_determinism(cuda_device, M):
     assert torch.equal(Y3, Y1 * 4.0)
 
 
-# ------------------------------------------------------------- full-size configs
+# ----------------------------------------------------------- full-size workloads
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 6144), (1, 4096, 4096), (1, 4096, 24576), (1, 12288, 4096)])
-def test_config2_decode_projections_m1(cuda_device, M, K, N):
-    _full_size(cuda_device, M, K, N, config=2)
+def test_decode_projections_m1_full_size(cuda_device, M, K, N):
+    _full_size(cuda_device, M, K, N, workload=2)
 
 
 @pytest.mark.parametrize("M", [8, 16, 32, 64])
 @pytest.mark.parametrize("K,N", [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)])
-def test_config3_decode_projections(cuda_device, M, K, N):
-    _full_size(cuda_device, M, K, N, config=3)
+def test_decode_projections_m8_to_64_full_size(cuda_device, M, K, N):
+    _full_size(cuda_device, M, K, N, workload=3)
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("N", [1536, 4096, 18432])
-def test_config4_k7168(cuda_device, M, N):
-    _full_size(cuda_device, M, 7168, N, config=4)
+def test_k7168_decode_gemms_full_size(cuda_device, M, N):
+    _full_size(cuda_device, M, 7168, N, workload=4)
 
 
-def _full_size(dev, M, K, N, config):
-    seed_x = synth.seed_for(config, 0, synth.T_X, M)
-    seed_w = synth.seed_for(config, 0, synth.T_WQ, K % 251 + N % 241)
+def _full_size(dev, M, K, N, workload):
+    seed_x = synth.seed_for(workload, 0, synth.T_X, M)
+    seed_w = synth.seed_for(workload, 0, synth.T_WQ, K % 251 + N % 241)
     x, _, X, W = gemm_inputs(M, K, N, seed_x, seed_w, dev, w_on_device=True)
     Y = run(sg.Gemm(M, K, N), X, W).cpu().numpy()
     cols = sampled_columns(N, 64, seed=M + N)
