@@ -79,6 +79,10 @@ enum {
                                     caches (Fleet reading note, section 3f,
                                     M-major window) instead of in registers;
                                     MFMA path, no K slices                      */
+  SGEMM_F_COOPERATIVE = 1u << 10 /* chain: cooperative launch, which the runtime
+                                    refuses (SGEMM_ERR_HIP) unless the whole
+                                    grid can be resident at once (about 1%
+                                    slower at M = 1)                            */
 };
 
 /*
@@ -158,6 +162,15 @@ int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* work
  * the last layer's down projection before rounding; Y_bf16 (may be NULL) its
  * bf16 rounding.  Intermediate activations stay in the workspace (see
  * sgemm_chain_buffer).  Enqueues one kernel and returns.
+ *
+ * Residency: the launch is a persistent grid of one workgroup per CU (256),
+ * whose stages wait for each other, so it needs every one of its workgroups
+ * resident at once.  Work running concurrently on the GPU (another stream)
+ * delays it until CUs free up; two chain launches overlapping in time can
+ * each hold CUs the other waits for, and then both end after the watchdog
+ * budget (SGEMM_WATCHDOG_S) with SGEMM_ERR_TIMEOUT latched in the workspace.
+ * Run chains on one stream, or serialise them; SGEMM_F_COOPERATIVE makes the
+ * runtime check at launch that the grid fits the device.
  */
 int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq,
                    const void* const* Wo, const void* const* Wgu, const void* const* Wdown,
