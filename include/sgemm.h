@@ -72,7 +72,7 @@ enum {
                                     counter and raises a per-XCD flag that the
                                     XCD's other workgroups poll (default: every
                                     workgroup polls the global counter)         */
-  SGEMM_F_MTILE_ITEMS = 1u << 9  /* GEMM, ablation: one 16-row m-tile per item,
+  SGEMM_F_MTILE_ITEMS = 1u << 9, /* GEMM, ablation: one 16-row m-tile per item,
                                     m-tile fastest, consecutive items on
                                     neighbouring waves, so the m-tiles of a
                                     column block share its weights through the

@@ -218,3 +218,19 @@ def test_environment_overrides_apply(monkeypatch):
     monkeypatch.setenv("SGEMM_WATCHDOG_S", "2.5")
     assert sg.Gemm(16, 4096, 1024).describe()["stage"]["S"] == 4
     assert _create(kind=sg.KIND_LAYERCHAIN, M=4, L=2, d=256, q=128, dff=384) == sg.OK
+
+
+@pytest.mark.parametrize("lang,compiler", [("c", "gcc"), ("c++", "g++")])
+def test_header_is_plain_c_and_cpp(tmp_path, lang, compiler):
+    """include/sgemm.h compiles on its own as C and as C++ (no HIP types)."""
+    import shutil
+    import subprocess
+
+    if not shutil.which(compiler):
+        pytest.skip(compiler + " not found")
+    src = tmp_path / ("t." + ("c" if lang == "c" else "cpp"))
+    src.write_text('#include "sgemm.h"\nint main(void) { return SGEMM_F_COOPERATIVE != 0 ? 0 : 1; }\n')
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    r = subprocess.run([compiler, "-std=c11" if lang == "c" else "-std=c++17", "-Wall", "-Werror", "-fsyntax-only",
+                        "-I", inc, str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
