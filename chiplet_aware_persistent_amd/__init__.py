@@ -34,7 +34,6 @@ F_WATCHDOG_TEST = 1 << 6
 F_W_SC1 = 1 << 7
 F_POLL_LEADER = 1 << 8
 F_MTILE_ITEMS = 1 << 9
-F_COOPERATIVE = 1 << 10
 
 
 class SgemmError(RuntimeError):

@@ -503,8 +503,7 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   int lds = 0;
   for (int s = 0; s < kChainStages; ++s) lds = std::max(lds, plan->cg[s].lds);
   if (hipSetDevice(plan->device) != hipSuccess) return SGEMM_ERR_HIP;
-  hipError_t e = launch_chain(a, plan->grid, plan->cg[0].waves * 64, lds, (p.flags & SGEMM_F_COOPERATIVE) != 0,
-                              (hipStream_t)stream);
+  hipError_t e = launch_chain(a, plan->grid, plan->cg[0].waves * 64, lds, (hipStream_t)stream);
   if (e == hipSuccess && Y_bf16) {
     const size_t off = plan->off_act + ((size_t)(p.n_layers - 1) * plan->act_layer_elems + plan->a_x) * 2;
     e = hipMemcpyAsync(Y_bf16, ws + off, (size_t)p.M * p.d_model * 2, hipMemcpyDeviceToDevice,

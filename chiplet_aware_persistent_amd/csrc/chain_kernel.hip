@@ -193,17 +193,12 @@ bool chain_variant_exists(int mt, int nt_q, int nt_o, int nt_d) {
   return nt_q == nt_o && nt_o == nt_d && chain_kernel(mt, nt_q) != nullptr;
 }
 
-hipError_t launch_chain(const ChainArgs& a, int grid, int block, int lds, bool cooperative, hipStream_t stream) {
+hipError_t launch_chain(const ChainArgs& a, int grid, int block, int lds, hipStream_t stream) {
   ChainKernel k = chain_kernel(a.mt, a.nt_q);
   if (!k) return hipErrorInvalidValue;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-  }
-  if (cooperative) {  // the runtime refuses the launch unless every workgroup can be resident at once
-    ChainArgs arg = a;
-    void* args[] = {(void*)&arg};
-    return hipLaunchCooperativeKernel((const void*)k, dim3(grid), dim3(block), args, (unsigned)lds, stream);
   }
   hipLaunchKernelGGL(k, dim3(grid), dim3(block), lds, stream, a);
   return hipGetLastError();

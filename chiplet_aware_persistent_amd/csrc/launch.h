@@ -43,6 +43,6 @@ hipError_t launch_stream_read(const void* src, size_t bytes, int pattern, unsign
                               hipStream_t stream);
 
 bool chain_variant_exists(int mt, int nt_q, int nt_o, int nt_d);
-hipError_t launch_chain(const ChainArgs& a, int grid, int block, int lds, bool cooperative, hipStream_t stream);
+hipError_t launch_chain(const ChainArgs& a, int grid, int block, int lds, hipStream_t stream);
 
 }  // namespace sg

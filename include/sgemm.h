@@ -72,17 +72,13 @@ enum {
                                     counter and raises a per-XCD flag that the
                                     XCD's other workgroups poll (default: every
                                     workgroup polls the global counter)         */
-  SGEMM_F_MTILE_ITEMS = 1u << 9, /* GEMM, ablation: one 16-row m-tile per item,
+  SGEMM_F_MTILE_ITEMS = 1u << 9  /* GEMM, ablation: one 16-row m-tile per item,
                                     m-tile fastest, consecutive items on
                                     neighbouring waves, so the m-tiles of a
                                     column block share its weights through the
                                     caches (Fleet reading note, section 3f,
                                     M-major window) instead of in registers;
                                     MFMA path, no K slices                      */
-  SGEMM_F_COOPERATIVE = 1u << 10 /* chain: cooperative launch, which the runtime
-                                    refuses (SGEMM_ERR_HIP) unless the whole
-                                    grid can be resident at once (about 1%
-                                    slower at M = 1)                            */
 };
 
 /*
@@ -169,8 +165,7 @@ int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* work
  * delays it until CUs free up; two chain launches overlapping in time can
  * each hold CUs the other waits for, and then both end after the watchdog
  * budget (SGEMM_WATCHDOG_S) with SGEMM_ERR_TIMEOUT latched in the workspace.
- * Run chains on one stream, or serialise them; SGEMM_F_COOPERATIVE makes the
- * runtime check at launch that the grid fits the device.
+ * Run chains on one stream, or serialise them.
  */
 int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq,
                    const void* const* Wo, const void* const* Wgu, const void* const* Wdown,

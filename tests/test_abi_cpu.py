@@ -229,7 +229,7 @@ def test_header_is_plain_c_and_cpp(tmp_path, lang, compiler):
     if not shutil.which(compiler):
         pytest.skip(compiler + " not found")
     src = tmp_path / ("t." + ("c" if lang == "c" else "cpp"))
-    src.write_text('#include "sgemm.h"\nint main(void) { return SGEMM_F_COOPERATIVE != 0 ? 0 : 1; }\n')
+    src.write_text('#include "sgemm.h"\nint main(void) { return SGEMM_F_MTILE_ITEMS != 0 ? 0 : 1; }\n')
     inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
     r = subprocess.run([compiler, "-std=c11" if lang == "c" else "-std=c++17", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", inc, str(src)], capture_output=True, text=True)

@@ -152,7 +152,7 @@ def test_chain_repeatable_and_sync_modes_agree(cuda_device):
     rc2, Y2, _, _ = run_chain(ch, X0, dl, ws=ws)
     assert rc == rc2 == sg.OK
     assert torch.equal(Y1, Y2)
-    for flags in (sg.F_SYNC_FLAT, sg.F_SYNC_AGENT, sg.F_POLL_LEADER, sg.F_COOPERATIVE):
+    for flags in (sg.F_SYNC_FLAT, sg.F_SYNC_AGENT, sg.F_POLL_LEADER):
         rc3, Y3, _, _ = run_chain(sg.LayerChain(M, L, d, q, dff, flags=flags), X0, dl)
         assert rc3 == sg.OK
         assert torch.equal(Y1, Y3)
