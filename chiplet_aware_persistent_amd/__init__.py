@@ -34,6 +34,7 @@ F_WATCHDOG_TEST = 1 << 6
 F_W_SC1 = 1 << 7
 F_POLL_LEADER = 1 << 8
 F_MTILE_ITEMS = 1 << 9
+F_LAUNCH_PER_STAGE = 1 << 10
 
 
 class SgemmError(RuntimeError):

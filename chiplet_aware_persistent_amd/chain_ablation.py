@@ -1,0 +1,96 @@
+"""Launch granularity of the 36-layer chain: one persistent launch against one
+launch per projection stage (the kernel boundary as the barrier), each
+enqueued eagerly and as a replayed HIP graph.
+
+    python -m chiplet_aware_persistent_amd.chain_ablation [--m 1 16 64] [--launches 10]
+
+Weights: the benchmarked chain's (distinct seeded U(-1/sqrt(K), 1/sqrt(K))
+bf16 per layer, d = q = 4096, d_ff = 12288).  Per mode: 2 warm-up calls,
+then ``--launches`` timed calls with HIP events around each on the current
+stream.  One JSON line per (M, mode) with the median and the 10th and 90th
+percentiles in microseconds, and whether the output equals the one-launch
+output bitwise.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+D_MODEL, Q_COLS, D_FF, LAYERS = 4096, 4096, 12288, 36
+
+
+def main():
+    import torch
+
+    import chiplet_aware_persistent_amd as sg
+    import synth
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--m", type=int, nargs="+", default=[1, 16, 64])
+    ap.add_argument("--launches", type=int, default=10)
+    a = ap.parse_args()
+    dev = torch.device("cuda:0")
+    d, q, dff = D_MODEL, Q_COLS, D_FF
+    wl = []
+    for l in range(LAYERS):
+        wl.append([synth.uniform_bf16_torch(synth.seed_for(5, l, synth.T_WQ), q, d, synth.weight_scale(d), dev),
+                   synth.uniform_bf16_torch(synth.seed_for(5, l, synth.T_WO), d, q, synth.weight_scale(q), dev),
+                   synth.uniform_bf16_torch(synth.seed_for(5, l, synth.T_WGU), 2 * dff, d, synth.weight_scale(d), dev),
+                   synth.uniform_bf16_torch(synth.seed_for(5, l, synth.T_WDOWN), d, dff, synth.weight_scale(dff), dev)])
+    cols = [[w[i] for w in wl] for i in range(4)]
+    modes = (("one_launch", 0, False), ("launch_per_stage", sg.F_LAUNCH_PER_STAGE, False),
+             ("one_launch_graph", 0, True), ("launch_per_stage_graph", sg.F_LAUNCH_PER_STAGE, True))
+    for M in a.m:
+        X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(5, 0, synth.T_X), M, d), dev)
+        ref = None
+        for name, flags, graph in modes:
+            ch = sg.LayerChain(M, LAYERS, d, q, dff, flags=flags)
+            ws = ch.new_workspace()
+            Y = torch.empty((M, d), dtype=torch.float32, device=dev)
+
+            def call():
+                ch(X0, *cols, Y, ws)
+
+            fn = call
+            if graph:
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    call()
+                torch.cuda.current_stream().wait_stream(side)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    call()
+                fn = g.replay
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(a.launches):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            rc = ch.status(ws)
+            if rc != sg.OK:
+                raise RuntimeError("chain status %s (M=%d, %s)" % (sg.status_string(rc), M, name))
+            if ref is None:
+                ref = Y.clone()
+            ts.sort()
+            n = len(ts)
+            print(json.dumps({"M": M, "mode": name, "launches": a.launches, "median_us": round(ts[n // 2], 1),
+                              "p10_us": round(ts[n // 10], 1), "p90_us": round(ts[(9 * n) // 10], 1),
+                              "bitwise_equal_to_one_launch": bool(torch.equal(ref, Y))}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

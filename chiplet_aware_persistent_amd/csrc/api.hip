@@ -17,7 +17,7 @@ using namespace sg;
 
 namespace {
 
-constexpr size_t kCtl = 256;            // control block: status word, done counter
+constexpr size_t kCtl = 256;            // control block: status word, done counter, slot claims
 constexpr int kLdsMax = 160 * 1024;     // LDS budget of one workgroup (one per CU; 160 KB/CU)
 constexpr size_t kMaxOperand = (size_t)1 << 31;  // buffer extents are 31-bit here
 constexpr int kWgPerXcd = 32;           // one workgroup per CU, 32 CUs per XCD
@@ -488,6 +488,7 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   a.y_bf16 = (uint16_t*)Y_bf16;
   a.status = (unsigned*)ws;
   a.done = (unsigned*)(ws + 64);
+  a.claim = (unsigned*)(ws + 128);
   a.lctr = (unsigned*)(ws + plan->off_lctr);
   a.gctr = (unsigned*)(ws + plan->off_gctr);
   a.xflag = (unsigned*)(ws + plan->off_xflag);
@@ -503,7 +504,15 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   int lds = 0;
   for (int s = 0; s < kChainStages; ++s) lds = std::max(lds, plan->cg[s].lds);
   if (hipSetDevice(plan->device) != hipSuccess) return SGEMM_ERR_HIP;
-  hipError_t e = launch_chain(a, plan->grid, plan->cg[0].waves * 64, lds, (hipStream_t)stream);
+  // One launch runs every event; the per-stage ablation launches once per event.
+  const int events = 4 * p.n_layers;
+  const int per_launch = (p.flags & SGEMM_F_LAUNCH_PER_STAGE) ? 1 : events;
+  hipError_t e = hipSuccess;
+  for (int e0 = 0; e0 < events && e == hipSuccess; e0 += per_launch) {
+    a.e_begin = e0;
+    a.e_end = e0 + per_launch;
+    e = launch_chain(a, plan->grid, plan->cg[0].waves * 64, lds, (hipStream_t)stream);
+  }
   if (e == hipSuccess && Y_bf16) {
     const size_t off = plan->off_act + ((size_t)(p.n_layers - 1) * plan->act_layer_elems + plan->a_x) * 2;
     e = hipMemcpyAsync(Y_bf16, ws + off, (size_t)p.M * p.d_model * 2, hipMemcpyDeviceToDevice,
@@ -546,7 +555,7 @@ const char* sgemm_status_string(int status) {
     case SGEMM_ERR_HIP: return "HIP runtime error";
     case SGEMM_ERR_TIMEOUT: return "device wait timed out";
     case SGEMM_ERR_WORKSPACE: return "workspace error";
-    case SGEMM_ERR_TOPOLOGY: return "workgroup ran on an unexpected XCD";
+    case SGEMM_ERR_TOPOLOGY: return "workgroups did not map onto the XCDs as a rotated round-robin";
     default: return "unknown status";
   }
 }

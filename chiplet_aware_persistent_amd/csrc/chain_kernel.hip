@@ -42,13 +42,12 @@ __device__ __forceinline__ unsigned long long now_ticks() { return wall_clock64(
 // sections 2a and 3b, without a dedicated workgroup): fewer pollers share the
 // counter's address, but the extra hop costs about a microsecond per stage
 // on MI355X, more than the contention of 256 pollers does.
-__device__ bool wait_event(const ChainArgs& a, int e, int* sh_alive) {
+__device__ bool wait_event(const ChainArgs& a, int e, int xcd, int slot, int* sh_alive) {
   if (threadIdx.x == 0) {
-    const int xcd = blockIdx.x & 7;
     const int events = 4 * a.n_layers;
     unsigned* flag = a.xflag + xcd * events + e;
     const unsigned target = a.flat_sync ? gridDim.x : (unsigned)kXcds;
-    const bool leader = (blockIdx.x >> 3) == 0 || a.flat_sync || !a.poll_leader;
+    const bool leader = slot == 0 || a.flat_sync || !a.poll_leader;
     int ok = 1;
     const unsigned long long t0 = now_ticks();
     for (;;) {
@@ -109,16 +108,28 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ int sh_alive;
   __shared__ int sh_last;
-  const int xcd = blockIdx.x & 7;
+  const int xcd = xcd_of_wg(a.status);
   const int slot = blockIdx.x >> 3;
   const int nslots = gridDim.x >> 3;
-  check_topology(a.status);
+  // Each workgroup claims its (XCD, slot) pair.  A pair claimed twice (or a
+  // slot past 31) means the dispatch was not a rotated round-robin, and the
+  // XCD-local counters would be wrong: recorded as a topology error.
+  if (threadIdx.x == 0) {
+    const unsigned bit = slot < 32 ? 1u << slot : 0u;
+    const unsigned old = __hip_atomic_fetch_or(a.claim + xcd, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (bit == 0u || (old & bit))
+      __hip_atomic_fetch_or(a.status, kStatusTopology, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   bool alive = true;
-  for (int l = 0; l < a.n_layers && alive; ++l) {
+  // Events e = 4 l + s of this launch, in order (all of them unless the
+  // per-stage ablation splits the chain into launches).  The stage loop has a
+  // compile-time s, so each stage's descriptor is selected statically.
+  for (int l = a.e_begin >> 2; 4 * l < a.e_end && alive; ++l) {
     uint16_t* act = a.act + (size_t)l * a.act_layer_elems;
     const uint16_t* xin = l == 0 ? a.x0 : a.act + (size_t)(l - 1) * a.act_layer_elems + a.off_x;
     for (int s = 0; s < kChainStages && alive; ++s) {
       const int e = 4 * l + s;
+      if (e < a.e_begin || e >= a.e_end) continue;  // another launch runs it
       StageDesc d = a.st[s];
       if (s == 0) { d.X = xin; d.W = a.wq[l]; d.Y = act + a.off_h1; }
       if (s == 1) { d.X = act + a.off_h1; d.W = a.wo[l]; d.Y = act + a.off_h2; }
@@ -128,7 +139,8 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
         if (l == a.n_layers - 1) { d.mode = OUT_BF16_F32; d.Y2 = a.y_f32; }
       }
       auto hook = [&]() -> bool {
-        const bool ok = e == 0 ? true : wait_event(a, e - 1, &sh_alive);
+        // The launch's first event has its X complete (the previous launch, or the input).
+        const bool ok = e == a.e_begin ? true : wait_event(a, e - 1, xcd, slot, &sh_alive);
         stamp(a, e, 0);
         return ok;
       };
@@ -143,7 +155,7 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
       if (!alive) break;
       if (a.stamps) __syncthreads();  // the stamp marks the end of the workgroup's last wave
       stamp(a, e, 1);
-      signal_event(a, e, xcd, nslots);
+      if (e + 1 < a.e_end) signal_event(a, e, xcd, nslots);  // the launch's last event has no waiter
       __syncthreads();  // LDS window reuse by the next stage
     }
   }
@@ -162,6 +174,7 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
     for (int i = threadIdx.x; i < events; i += blockDim.x) a.gctr[i] = 0u;
     for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) a.lctr[i] = 0u;
     for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) a.xflag[i] = 0u;
+    if (threadIdx.x < kXcds) a.claim[threadIdx.x] = 0u;
     for (int s = 0; s < kChainStages; ++s) {
       const int n = kXcds * a.st[s].NB * a.st[s].wpi;
       for (int i = threadIdx.x; i < n; i += blockDim.x) a.st[s].ctr[i] = 0u;

@@ -122,11 +122,18 @@ __device__ __forceinline__ unsigned xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xF;  // HW_REG_XCC_ID[3:0]
 }
 
-// Record (once per workgroup) that this workgroup did not run on the XCD its
-// index assigns it to under round-robin dispatch.
-__device__ __forceinline__ void check_topology(unsigned* status) {
-  if (threadIdx.x == 0 && xcc_id() != (blockIdx.x & 7u))
+// The XCD this workgroup runs on, read from the hardware.  The dispatcher
+// hands the workgroups of a launch to the 8 XCDs round-robin, but from a
+// starting XCD that changes between launches (graph launches move it), so
+// workgroup i runs on XCD (i + r) mod 8 for one r per launch.  Work is indexed
+// by (this XCD, i / 8): for a grid of 8 * slots workgroups that covers every
+// (XCD, slot) pair once, whatever r is.  An id outside 0..7 (another
+// partition mode) is recorded as a topology error.
+__device__ __forceinline__ int xcd_of_wg(unsigned* status) {
+  const unsigned x = xcc_id();
+  if (x >= (unsigned)kXcds && threadIdx.x == 0)
     __hip_atomic_fetch_or(status, kStatusTopology, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (int)(x & 7u);
 }
 
 // Reduce-scatter over the 64 lanes of a wave: v holds V (power of two <= 64)

@@ -13,15 +13,13 @@ typedef void (*GemmKernel)(StageDesc, unsigned*);
 template <int M, int G, int AUX>
 __global__ __launch_bounds__(512) void k_gemm_dot2(StageDesc d, unsigned* status) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  check_topology(status);
-  dot2_stage<M, G, AUX>(d, lds, blockIdx.x & 7, blockIdx.x >> 3, gridDim.x >> 3);
+  dot2_stage<M, G, AUX>(d, lds, xcd_of_wg(status), blockIdx.x >> 3, gridDim.x >> 3);
 }
 
 template <int MT, int NT, int AUX, bool MTI = false>
 __global__ __launch_bounds__(512) void k_gemm_mfma(StageDesc d, unsigned* status) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  check_topology(status);
-  mfma_stage<MT, NT, false, AUX, false, NoHook, MTI>(d, lds, blockIdx.x & 7, blockIdx.x >> 3, gridDim.x >> 3);
+  mfma_stage<MT, NT, false, AUX, false, NoHook, MTI>(d, lds, xcd_of_wg(status), blockIdx.x >> 3, gridDim.x >> 3);
 }
 
 // dot2: M = 1..15, G in {1, 2, 3, 4, 8} with G*M <= 64.  MFMA: MT = 1..4, NT = 1, 2.

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(512) void k_stream_read(const void* src, unsigned n
     for (; i < n16; i += nth) acc ^= fold(ld16<kAuxNt>(r, i * 16u));
   } else {
     const unsigned wpb = blockDim.x >> 6;
-    const unsigned xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+    const unsigned xcd = xcc_id() & 7u, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
     const unsigned units = n16 >> 6;  // whole kilobytes
     const unsigned u0 = (unsigned)((unsigned long long)units * xcd / 8);
     const unsigned u1 = (unsigned)((unsigned long long)units * (xcd + 1) / 8);

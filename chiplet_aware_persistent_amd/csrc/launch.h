@@ -24,6 +24,7 @@ struct ChainArgs {
   unsigned* gctr;                      // [events] global event counters
   unsigned* xflag;                     // [kXcds][events] per-XCD 'event seen' flags
   unsigned* done;                      // workgroups finished (reset by the last one)
+  unsigned* claim;                     // [kXcds] slots claimed per XCD (reset by the last one)
   unsigned long long* stamps;          // [grid][events][2] or null
   int n_layers, M, d, q, dff;
   size_t act_layer_elems;              // bf16 elements per layer of activations
@@ -32,6 +33,7 @@ struct ChainArgs {
   int poll_leader;                     // one workgroup per XCD polls and raises the XCD's flag
   long long spin_ticks;                // watchdog budget (wall-clock ticks, 100 MHz)
   int mt, nt_q, nt_o, nt_d;            // tile template parameters (MFMA path)
+  int e_begin, e_end;                  // events this launch runs: [e_begin, e_end)
 };
 
 bool gemm_variant_exists(int path, int a, int b);

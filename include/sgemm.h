@@ -50,7 +50,8 @@ typedef enum {
   SGEMM_ERR_HIP = -3,         /* a HIP runtime call failed                    */
   SGEMM_ERR_TIMEOUT = -4,     /* a device-side bounded wait expired           */
   SGEMM_ERR_WORKSPACE = -5,   /* workspace too small / not initialised        */
-  SGEMM_ERR_TOPOLOGY = -6     /* a workgroup ran on another XCD than planned  */
+  SGEMM_ERR_TOPOLOGY = -6     /* workgroups did not map onto the XCDs as a
+                                 round-robin from some starting XCD          */
 } sgemm_status;
 
 enum { SGEMM_KIND_GEMM = 0, SGEMM_KIND_LAYERCHAIN = 1 };
@@ -72,13 +73,18 @@ enum {
                                     counter and raises a per-XCD flag that the
                                     XCD's other workgroups poll (default: every
                                     workgroup polls the global counter)         */
-  SGEMM_F_MTILE_ITEMS = 1u << 9  /* GEMM, ablation: one 16-row m-tile per item,
+  SGEMM_F_MTILE_ITEMS = 1u << 9, /* GEMM, ablation: one 16-row m-tile per item,
                                     m-tile fastest, consecutive items on
                                     neighbouring waves, so the m-tiles of a
                                     column block share its weights through the
                                     caches (Fleet reading note, section 3f,
                                     M-major window) instead of in registers;
                                     MFMA path, no K slices                      */
+  SGEMM_F_LAUNCH_PER_STAGE = 1u << 10 /* chain, ablation: one launch of the same
+                                    kernel per projection stage, so the kernel
+                                    boundary is the barrier between stages and
+                                    no weights are prefetched across it; the
+                                    results are bitwise those of one launch     */
 };
 
 /*
@@ -200,7 +206,9 @@ int sgemm_plan_describe(sgemm_plan plan, char* buf, size_t len);
  * of n_wg entries).  Enqueues on `stream`; used to confirm the round-robin
  * workgroup-to-XCD dispatch the per-XCD partition relies on (Fleet reading
  * note, section 3b: default dispatch spreads workgroups round-robin over the
- * XCDs, and the runtime reads the hardware id to learn its XCD).
+ * XCDs, and the runtime reads the hardware id to learn its XCD).  The
+ * starting XCD varies between launches (graph launches move it), so the
+ * kernels take their XCD from the hardware id and their slot from i / 8.
  */
 int sgemm_topology_probe(int* xcc_out, int n_wg, void* stream);
 

@@ -152,13 +152,46 @@ def test_chain_repeatable_and_sync_modes_agree(cuda_device):
     rc2, Y2, _, _ = run_chain(ch, X0, dl, ws=ws)
     assert rc == rc2 == sg.OK
     assert torch.equal(Y1, Y2)
-    for flags in (sg.F_SYNC_FLAT, sg.F_SYNC_AGENT, sg.F_POLL_LEADER):
+    for flags in (sg.F_SYNC_FLAT, sg.F_SYNC_AGENT, sg.F_POLL_LEADER, sg.F_LAUNCH_PER_STAGE):
         rc3, Y3, _, _ = run_chain(sg.LayerChain(M, L, d, q, dff, flags=flags), X0, dl)
         assert rc3 == sg.OK
         assert torch.equal(Y1, Y3)
 
 
-@pytest.mark.parametrize("flags", [0, sg.F_POLL_LEADER, sg.F_SYNC_FLAT])
+@pytest.mark.parametrize("flags", [0, sg.F_LAUNCH_PER_STAGE])
+def test_chain_graph_replays_match_eager(cuda_device, flags):
+    """A HIP graph of one chain call (one launch, or one launch per stage)
+    replays to the eager result bitwise, with eager chain runs and host
+    synchronisation between the replays."""
+    M, L, d, q, dff = 16, 3, 512, 512, 1024
+    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x3800, cuda_device)
+    ch = sg.LayerChain(M, L, d, q, dff, flags=flags)
+    rc, Ye, Ybe, ws = run_chain(ch, X0, dl)
+    assert rc == sg.OK
+    cols = [[w[i] for w in dl] for i in range(4)]
+    Y, Yb = torch.empty_like(Ye), torch.empty_like(Ybe)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ch(X0, *cols, Y, ws, Y_bf16=Yb)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ch(X0, *cols, Y, ws, Y_bf16=Yb)
+    for r in range(4):
+        Y.zero_()
+        Yb.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert ch.status(ws) == sg.OK, r
+        assert torch.equal(Y, Ye) and torch.equal(Yb, Ybe), r
+        rc2, Y2, _, _ = run_chain(ch, X0, dl, ws=ws)
+        assert rc2 == sg.OK and torch.equal(Y2, Ye), r
+
+
+@pytest.mark.parametrize("flags", [0, sg.F_POLL_LEADER, sg.F_SYNC_FLAT, sg.F_LAUNCH_PER_STAGE])
 def test_chain_stamps_order_every_stage(cuda_device, flags):
     M, L, d, q, dff = 32, 4, 512, 256, 768
     x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x4000, cuda_device)

@@ -31,10 +31,37 @@ def run(g: sg.Gemm, X, W, ws=None):
     return Y
 
 
+def _rotation(ids):
+    """r when workgroup i ran on XCD (i + r) mod 8 for every i, else None."""
+    r = {(x - i) % 8 for i, x in enumerate(ids)}
+    return r.pop() if len(r) == 1 and all(0 <= x < 8 for x in ids) else None
+
+
 def test_topology_is_round_robin(cuda_device):
+    """Workgroups go to the 8 XCDs round-robin from some starting XCD, in eager
+    launches on two streams and in graph replays (which move the starting
+    XCD): the kernels index work by (hardware XCD, i / 8), which needs exactly
+    this."""
     ids = sg.topology(256)
     assert sorted(set(ids)) == list(range(8))
-    assert ids == [i % 8 for i in range(256)], ids[:32]
+    assert _rotation(ids) is not None, ids[:32]
+    out = torch.full((256,), -1, dtype=torch.int32, device=cuda_device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        assert sg.sgemm_topology_probe(out.data_ptr(), 256, sg._stream_handle(None)) == sg.OK
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert _rotation(out.cpu().tolist()) is not None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sg.sgemm_topology_probe(out.data_ptr(), 256, sg._stream_handle(None))
+    for _ in range(3):
+        out.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert _rotation(out.cpu().tolist()) is not None
+    assert _rotation(sg.topology(256)) is not None
 
 
 def test_generator_on_device_matches_host(cuda_device):
@@ -126,6 +153,37 @@ def test_sync_and_cache_variants_bitwise_equal(cuda_device, flags, M):
     other = run(sg.Gemm(M, K, N, splitk=S, flags=flags), X, W)
     assert torch.equal(base, other)
     check(base.cpu().numpy(), x, w)
+
+
+@pytest.mark.parametrize("M,S", [(1, 1), (8, 4), (32, 8)])
+def test_graph_replays_match_eager(cuda_device, M, S):
+    """A HIP graph of sgemm_run (split-K counters included) replays to the
+    eager result bitwise, with eager runs and host synchronisation between
+    the replays."""
+    K, N = 4096, 1536
+    x, w, X, W = gemm_inputs(M, K, N, 9700 + M, 9800, cuda_device)
+    g = sg.Gemm(M, K, N, splitk=S)
+    ws = g.new_workspace()
+    Ye = run(g, X, W, ws)
+    Y = torch.empty_like(Ye)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g(X, W, Y, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g(X, W, Y, ws)
+    for r in range(4):
+        Y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert g.status(ws) == sg.OK, r
+        assert torch.equal(Y, Ye), r
+        assert torch.equal(run(g, X, W, ws), Ye), r
+    check(Ye.cpu().numpy(), x, w)
 
 
 # ------------------------------------------------------------- exactness pins
