@@ -1,8 +1,13 @@
-"""Launch granularity of the 36-layer chain: one persistent launch against one
-launch per projection stage (the kernel boundary as the barrier), each
-enqueued eagerly and as a replayed HIP graph.
+"""Ablations of the 36-layer chain's synchronisation, same weights and inputs:
 
-    python -m chiplet_aware_persistent_amd.chain_ablation [--m 1 16 64] [--launches 10]
+- launch granularity: one persistent launch against one launch per
+  projection stage (the kernel boundary as the barrier), each enqueued
+  eagerly and as a replayed HIP graph;
+- completion counters: one leader per XCD polling (SGEMM_F_POLL_LEADER),
+  flat counters (SGEMM_F_SYNC_FLAT), device-scope split-K arrivals
+  (SGEMM_F_SYNC_AGENT).
+
+    python -m chiplet_aware_persistent_amd.chain_ablation [--m 1 16 64] [--launches 10] [--modes ...]
 
 Weights: the benchmarked chain's (distinct seeded U(-1/sqrt(K), 1/sqrt(K))
 bf16 per layer, d = q = 4096, d_ff = 12288).  Per mode: 2 warm-up calls,
@@ -34,6 +39,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--m", type=int, nargs="+", default=[1, 16, 64])
     ap.add_argument("--launches", type=int, default=10)
+    ap.add_argument("--modes", nargs="+", default=None, help="subset of the mode names (default: all)")
     a = ap.parse_args()
     dev = torch.device("cuda:0")
     d, q, dff = D_MODEL, Q_COLS, D_FF
@@ -44,8 +50,16 @@ def main():
                    synth.uniform_bf16_torch(synth.seed_for(5, l, synth.T_WGU), 2 * dff, d, synth.weight_scale(d), dev),
                    synth.uniform_bf16_torch(synth.seed_for(5, l, synth.T_WDOWN), d, dff, synth.weight_scale(dff), dev)])
     cols = [[w[i] for w in wl] for i in range(4)]
-    modes = (("one_launch", 0, False), ("launch_per_stage", sg.F_LAUNCH_PER_STAGE, False),
-             ("one_launch_graph", 0, True), ("launch_per_stage_graph", sg.F_LAUNCH_PER_STAGE, True))
+    modes = [("one_launch", 0, False), ("launch_per_stage", sg.F_LAUNCH_PER_STAGE, False),
+             ("one_launch_graph", 0, True), ("launch_per_stage_graph", sg.F_LAUNCH_PER_STAGE, True),
+             ("poll_leader", sg.F_POLL_LEADER, False), ("sync_flat", sg.F_SYNC_FLAT, False),
+             ("sync_agent", sg.F_SYNC_AGENT, False)]
+    if a.modes:
+        unknown = set(a.modes) - {m[0] for m in modes}
+        if unknown:
+            raise SystemExit("unknown modes: %s" % sorted(unknown))
+        # the first mode is the reference the others are compared with bitwise
+        modes = [m for m in modes if m[0] == "one_launch" or m[0] in a.modes]
     for M in a.m:
         X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(5, 0, synth.T_X), M, d), dev)
         ref = None
