@@ -78,7 +78,9 @@ constexpr Cost kCostChain{1.25, 75.0e9, 0.5, 0.05, 0.25, true};
 bool shape_geo(Geo& g, int want_S, const Cost& cost) {
   const int kstep = g.path == 0 ? kDot2KStep : kMfmaKStep;
   if (g.wpi % g.ksl) return false;
-  g.TN = g.path == 0 ? g.tb : (g.paired ? 16 : 16 * g.tb);
+  // Output columns per wave: dot2 G (paired: G/2 gate/up pairs), MFMA 16 per n-tile.
+  if (g.path == 0 && g.paired && g.tb % 2) return false;
+  g.TN = g.path == 0 ? (g.paired ? g.tb / 2 : g.tb) : (g.paired ? 16 : 16 * g.tb);
   g.ng = g.waves / g.wpi;
   if (g.ksl > 1 && g.ng != 1) return false;  // K slices reduce with workgroup barriers
   g.CB = g.wpi / g.ksl * g.TN;
@@ -335,17 +337,31 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
       }
       cost.x_bw = x_gbps * 1e9;
     }
+    // dot2 stages (G weight rows per wave, the gate_up stage holding G/2
+    // gate/up pairs) at M <= 2, MFMA stages above: in the 36-layer chain the
+    // dot2 stages measured 4% faster at M = 1, even at M = 2 and 2-45% slower
+    // from M = 3 to 15.  SGEMM_F_FORCE_DOT2 (M < 16) and SGEMM_F_FORCE_MFMA
+    // choose the path.
+    if ((p.flags & SGEMM_F_FORCE_DOT2) && p.M >= 16) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    const int path = (p.flags & SGEMM_F_FORCE_DOT2) ? 0 : (p.flags & SGEMM_F_FORCE_MFMA) ? 1 : (p.M <= 2 ? 0 : 1);
     double best = -1.0;
     for (int waves = 8; waves >= 4; waves -= 4) {
       if (w_o && waves != w_o) continue;
-      for (int nt = 1; nt <= 2; ++nt) {
-        if (tn_o && tn_o != 16 * nt) continue;
+      for (int nt = 1; nt <= (path == 0 ? 4 : 2); ++nt) {
+        // dot2: G = 2 or 4 rows per wave in every stage; MFMA: NT = 1 or 2.
+        const int tb = nt;
+        if (path == 0 && tb != 2 && tb != 4) continue;
+        if (tn_o && tn_o != (path == 0 ? tb : 16 * tb)) continue;
+        const int a = path == 0 ? p.M : (p.M + 15) / 16;
         Geo c[kChainStages];
         double tot = 0.0;
-        bool ok = chain_variant_exists((p.M + 15) / 16, nt, nt, nt);
+        bool ok = chain_variant_exists(path, a, tb);
         for (int s = 0; s < kChainStages && ok; ++s) {
           const int paired = s == 2;
-          ok = plan_geo(c[s], p.M, Ks[s], Ns[s], 1, paired, paired ? 0 : 16 * nt, s_st[s], waves, k_st[s], cost, w_st[s]);
+          const int tn = path == 0 ? tb : (paired ? 0 : 16 * tb);
+          if (path == 0 && k_st[s] > 1) { ok = false; break; }  // no K slices on the dot2 path
+          ok = plan_geo(c[s], p.M, Ks[s], Ns[s], path, paired, tn, s_st[s], waves, path == 0 ? 1 : k_st[s], cost,
+                        w_st[s]);
           if (ok && paired) c[s].pair_off = p.d_ff;
           tot += ok ? c[s].est_us : 0.0;
         }
@@ -499,6 +515,7 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   a.flat_sync = (p.flags & SGEMM_F_SYNC_FLAT) ? 1 : 0;
   a.poll_leader = (p.flags & SGEMM_F_POLL_LEADER) ? 1 : 0;
   a.spin_ticks = plan->spin_ticks;
+  a.path = plan->cg[0].path;
   a.mt = plan->cg[0].ta;
   a.nt_q = plan->cg[0].tb; a.nt_o = plan->cg[1].tb; a.nt_d = plan->cg[3].tb;
   int lds = 0;
@@ -543,7 +560,7 @@ int sgemm_query_status(sgemm_plan plan, void* workspace, void* stream) {
     if (hipMemcpy(workspace, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return SGEMM_ERR_HIP;
   }
   if (st & 1u) return SGEMM_ERR_TIMEOUT;
-  if ((st & 2u) && plan->sync == SYNC_XCD) return SGEMM_ERR_TOPOLOGY;
+  if (st & 2u) return SGEMM_ERR_TOPOLOGY;  // work indexed by XCD would be duplicated or missing
   return SGEMM_OK;
 }
 

@@ -329,13 +329,18 @@ struct NoHook {
 
 // ------------------------------------------------------------------ dot2
 // Lane l walks K eight values at a time (one contiguous kilobyte of a weight
-// row per 64-lane load); G columns per wave share the X registers.
-template <int M, int G, int AUX, typename Hook = NoHook>
+// row per 64-lane load); G weight rows per wave share the X registers.
+// PAIRED (the chain's gate_up stage): the wave's G rows are G/2 gate rows and
+// the G/2 up rows pair_off further on; the wave owns G/2 output columns and
+// writes silu(gate) * up.
+template <int M, int G, int AUX, bool PAIRED = false, typename Hook = NoHook>
 __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                            Hook pre_x = Hook()) {
   constexpr int P = ring_depth_dot2(G);
   constexpr int V = pow2_at_least(G * M);
   static_assert(V <= 64, "G*M must fit one wave");
+  static_assert(!PAIRED || G % 2 == 0, "a paired wave holds whole (gate, up) pairs");
+  constexpr int GO = PAIRED ? G / 2 : G;  // output columns per wave
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   int i0, i1;
@@ -355,13 +360,23 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   const bool owner = (lane % grp) == 0 && idx < GM;
   const int oc = idx / M, om = idx - (idx / M) * M;
   float* stash = (float*)((char*)xs + d.stash_off);  // [wave][stash_cap][64]
+  // The finished value of output column oc, row om (lane value r, all lanes
+  // call): paired, the up sum of the same column is GO*M values further on.
+  auto store_col = [&](int colb, float r) {
+    const int col = colb + oc;
+    if constexpr (PAIRED) {
+      const float u = __shfl(r, lane + GO * M * grp);
+      store_out(d, yr, y2r, owner && oc < GO && col < xc1 && om < d.M, om, col, silu_mul(r, u));
+    } else {
+      store_out(d, yr, y2r, owner && col < xc1 && om < d.M, om, col, r);
+    }
+  };
   // Result of item `it` (lane value r): Y when S == 1, else the partial.
   auto out_item = [&](int it, float r) {
     const int s = it / d.NB;
     const int b = it - s * d.NB;
-    const int col = xc0 + b * d.CB + wv * G + oc;
     if (d.S == 1) {
-      store_out(d, yr, y2r, owner && col < xc1 && om < d.M, om, col, r);
+      store_col(xc0 + b * d.CB + wv * GO, r);
     } else {
       const unsigned tile = (unsigned)((xcd * d.NB + b) * d.wpi + wv);
       st_f32<0>(pr, owner ? ((tile * d.S + s) * GM + idx) * 4u : d.part_bytes, r);
@@ -376,9 +391,9 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   // point at the end of W, where the buffer range check returns zeros: no
   // branch, so the compiler keeps exact counts of the loads in flight.
   struct Src {
-    unsigned base;  // byte offset of (column colb, k = k0 + 8*lane)
+    unsigned base;  // byte offset of (weight row of output column colb, k = k0 + 8*lane)
     int klim;       // steps * kstep with k < kend  -> valid while t*kstep + 8*lane < klim
-    int cols;       // columns of the wave tile that exist (col < xc1)
+    int cols;       // output columns of the wave tile that exist (col < xc1)
   };
   auto src_of = [&](int it) -> Src {
     Src r;
@@ -386,18 +401,23 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     const int s_ = it / d.NB;
     const int b_ = it - s_ * d.NB;
     const int k0 = s_ * d.KS;
-    const int colb = xc0 + b_ * d.CB + wv * G;
+    const int colb = xc0 + b_ * d.CB + wv * GO;
     r.base = ((unsigned)colb * (unsigned)d.K + (unsigned)k0) * 2u + (unsigned)lane * 16u;
     r.klim = min(d.K, k0 + d.KS) - k0;
-    r.cols = min(G, xc1 - colb);
+    r.cols = min(GO, xc1 - colb);
     return r;
+  };
+  // Weight row of the wave's row c relative to row colb (paired: up rows
+  // pair_off further on).
+  auto row_of = [&](int c) -> unsigned {
+    return PAIRED && c >= GO ? (unsigned)(d.pair_off + c - GO) : (unsigned)c;
   };
   auto issue = [&](u4(&dst)[G], const Src& sr, int t) {
     const bool kin = t * kDot2KStep + lane * 8 < sr.klim;
 #pragma unroll
     for (int c = 0; c < G; ++c) {
-      const bool valid = kin && c < sr.cols;
-      const unsigned off = sr.base + (unsigned)c * (unsigned)d.K * 2u + (unsigned)t * (kDot2KStep * 2u);
+      const bool valid = kin && (PAIRED ? c % GO : c) < sr.cols;
+      const unsigned off = sr.base + row_of(c) * (unsigned)d.K * 2u + (unsigned)t * (kDot2KStep * 2u);
       dst[c] = ld16<AUX>(wr, valid ? off : d.w_bytes);
     }
   };
@@ -507,8 +527,7 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
         const unsigned base = tile * d.S * GM + idx;
         const float t = d.sync == SYNC_XCD ? sum_partials<kAuxSc1, 8>(pr, base, GM, d.S, owner, d.part_bytes)
                                            : sum_partials<0, 8>(pr, base, GM, d.S, owner, d.part_bytes);
-        const int col = xc0 + b * d.CB + wv * G + oc;
-        store_out(d, yr, y2r, owner && col < xc1 && om < d.M, om, col, t);
+        store_col(xc0 + b * d.CB + wv * GO, t);
       }
     }
   }

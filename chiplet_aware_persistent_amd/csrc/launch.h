@@ -32,7 +32,8 @@ struct ChainArgs {
   int flat_sync;                       // every workgroup publishes globally
   int poll_leader;                     // one workgroup per XCD polls and raises the XCD's flag
   long long spin_ticks;                // watchdog budget (wall-clock ticks, 100 MHz)
-  int mt, nt_q, nt_o, nt_d;            // tile template parameters (MFMA path)
+  int path;                            // 1: MFMA stages, 0: dot2 stages (M < 16)
+  int mt, nt_q, nt_o, nt_d;            // template parameters: MFMA (MT, NT); dot2 (M in mt, G in nt_*)
   int e_begin, e_end;                  // events this launch runs: [e_begin, e_end)
 };
 
@@ -44,7 +45,7 @@ hipError_t launch_topology(int* out, int n, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, int pattern, unsigned* sink, int grid,
                               hipStream_t stream);
 
-bool chain_variant_exists(int mt, int nt_q, int nt_o, int nt_d);
+bool chain_variant_exists(int path, int a, int b);  // MFMA (MT, NT) or dot2 (M, G)
 hipError_t launch_chain(const ChainArgs& a, int grid, int block, int lds, hipStream_t stream);
 
 }  // namespace sg

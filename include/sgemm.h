@@ -59,7 +59,8 @@ enum { SGEMM_OUT_F32 = 0, SGEMM_OUT_BF16 = 1 };
 
 /* Plan flags (bitwise OR). */
 enum {
-  SGEMM_F_FORCE_DOT2 = 1u << 0,  /* use the VALU dot2 path whatever M is        */
+  SGEMM_F_FORCE_DOT2 = 1u << 0,  /* use the VALU dot2 path whatever M is (M < 16
+                                    only in the chain)                          */
   SGEMM_F_FORCE_MFMA = 1u << 1,  /* use the MFMA path whatever M is             */
   SGEMM_F_W_CACHED = 1u << 2,    /* weight loads without the nontemporal hint    */
   SGEMM_F_SYNC_FLAT = 1u << 3,   /* chain: every workgroup publishes globally     */

@@ -159,6 +159,25 @@ def test_chain_plan_and_buffers():
     assert sg.sgemm_chain_buffer(c.handle, 0, 4)[0] == sg.ERR_INVALID_ARG
 
 
+def test_chain_path_choice():
+    """dot2 stages at M <= 2 (G weight rows per wave, gate_up holding G/2
+    gate/up pairs), MFMA stages above; SGEMM_F_FORCE_DOT2 (M < 16) and
+    SGEMM_F_FORCE_MFMA choose the path, and FORCE_DOT2 is refused at M >= 16."""
+    def paths(M, flags=0):
+        return [s["path"] for s in sg.LayerChain(M, 4, 4096, 4096, 12288, flags=flags).describe()["stages"]]
+    for M, flags in ((1, 0), (2, 0), (3, sg.F_FORCE_DOT2), (8, sg.F_FORCE_DOT2), (15, sg.F_FORCE_DOT2)):
+        st = sg.LayerChain(M, 4, 4096, 4096, 12288, flags=flags).describe()["stages"]
+        assert [s["path"] for s in st] == ["dot2"] * 4, M
+        g = st[0]["tb"]
+        assert g in (2, 4) and all(s["tb"] == g for s in st) and g * M <= 64
+        assert st[2]["paired"] == 1 and st[2]["TN"] == g // 2 and st[0]["TN"] == g
+    for M in (3, 8, 15, 16, 17, 64):
+        assert paths(M) == ["mfma"] * 4, M
+    assert paths(1, sg.F_FORCE_MFMA) == ["mfma"] * 4
+    with pytest.raises(sg.SgemmError):
+        sg.LayerChain(16, 4, 4096, 4096, 12288, flags=sg.F_FORCE_DOT2)
+
+
 def test_eq1_matches_the_pages_table():
     g = json.load(open(os.path.join(GOLD, "eq1_l2_hit.json")))
     for row in g["rows"]:

@@ -98,17 +98,22 @@ def check_chain(ch, ws, x0, layers, Y, Yb, M):
     return worst
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 33, 64])
-def test_chain_small_parity(cuda_device, M):
+@pytest.mark.parametrize("M,flags", [(1, 0), (2, 0), (5, 0), (16, 0), (33, 0), (64, 0), (1, sg.F_FORCE_MFMA),
+                                     (5, sg.F_FORCE_DOT2), (9, sg.F_FORCE_DOT2), (15, sg.F_FORCE_DOT2)])
+def test_chain_small_parity(cuda_device, M, flags):
+    """dot2 stages at M <= 2 and when forced below 16, MFMA otherwise."""
     L, d, q, dff = 3, 256, 128, 384
     x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x1000 + M, cuda_device)
-    ch = sg.LayerChain(M, L, d, q, dff)
+    ch = sg.LayerChain(M, L, d, q, dff, flags=flags)
+    dot2 = flags == sg.F_FORCE_DOT2 or (M <= 2 and flags == 0)
+    assert {s["path"] for s in ch.describe()["stages"]} == {"dot2" if dot2 else "mfma"}
     rc, Y, Yb, ws = run_chain(ch, X0, dl)
     assert rc == sg.OK, sg.status_string(rc)
     check_chain(ch, ws, x0, layers, Y, Yb, M)
 
 
-@pytest.mark.parametrize("M,L,d,q,dff", [(64, 2, 1024, 1024, 3072), (8, 4, 512, 256, 1536), (64, 1, 4096, 4096, 12288)])
+@pytest.mark.parametrize("M,L,d,q,dff", [(64, 2, 1024, 1024, 3072), (8, 4, 512, 256, 1536), (64, 1, 4096, 4096, 12288),
+                                         (2, 2, 256, 128, 200), (1, 1, 4096, 4096, 12288)])
 def test_chain_wider_parity(cuda_device, M, L, d, q, dff):
     x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x2000 + M + L, cuda_device)
     ch = sg.LayerChain(M, L, d, q, dff)
@@ -117,9 +122,11 @@ def test_chain_wider_parity(cuda_device, M, L, d, q, dff):
     check_chain(ch, ws, x0, layers, Y, Yb, M)
 
 
-def test_chain_one_hot_wiring(cuda_device):
-    """Identity Q/O, one-hot gate/up/down rows: x' = bf16(silu(x_p) x_q) selections."""
-    M, d, dff, L = 16, 64, 48, 2
+@pytest.mark.parametrize("M,flags", [(16, 0), (3, 0), (3, sg.F_FORCE_DOT2), (1, 0)])
+def test_chain_one_hot_wiring(cuda_device, M, flags):
+    """Identity Q/O, one-hot gate/up/down rows: x' = bf16(silu(x_p) x_q) selections
+    (MFMA and dot2 stages)."""
+    d, dff, L = 64, 48, 2
     rng = np.random.default_rng(3)
     eye = synth.f32_to_bf16_bits(np.eye(d, dtype=np.float32))
     layers = []
@@ -133,7 +140,7 @@ def test_chain_one_hot_wiring(cuda_device):
         layers.append((eye, eye, synth.f32_to_bf16_bits(wgu), synth.f32_to_bf16_bits(wd)))
     x0 = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(synth.normal_bf16(5, M, d)) * np.float32(2.0))
     dl = [[device_tensor_bf16(w, cuda_device) for w in ws] for ws in layers]
-    ch = sg.LayerChain(M, L, d, d, dff)
+    ch = sg.LayerChain(M, L, d, d, dff, flags=flags)
     rc, Y, Yb, ws = run_chain(ch, device_tensor_bf16(x0, cuda_device), dl)
     assert rc == sg.OK
     outs = oracle.chain(x0, layers)
@@ -220,8 +227,10 @@ def test_chain_watchdog_times_out_and_workspace_recovers(cuda_device):
     check_chain(good, ws, x0, layers, Y, Yb, M)
 
 
-def test_chain_36_layers_m64_full_size_every_stage_sampled(cuda_device):
-    """The benchmarked 36-layer chain: M = 64, d = q = 4096, d_ff = 12288,
+@pytest.mark.parametrize("M", [64, 1])
+def test_chain_36_layers_full_size_every_stage_sampled(cuda_device, M):
+    """The benchmarked 36-layer chain: M = 64 (MFMA stages) and M = 1 (dot2
+    stages), d = q = 4096, d_ff = 12288,
     distinct seeded weights per layer (drawn on the GPU, 13.3 GB), one launch in
     the bench's plan.  Every one of the 144 stages is checked against the oracle
     on sampled output columns, each with the GPU's own input to that stage (the
@@ -230,7 +239,7 @@ def test_chain_36_layers_m64_full_size_every_stage_sampled(cuda_device):
     The configured distributions make the activations collapse towards zero
     within a few layers (bf16 keeps them representable for a while); the later
     stages are still checked, against near-zero references."""
-    M, L, d, q, dff = 64, 36, 4096, 4096, 12288
+    L, d, q, dff = 36, 4096, 4096, 12288
     seeds = [[synth.seed_for(5, l, t) for t in (synth.T_WQ, synth.T_WO, synth.T_WGU, synth.T_WDOWN)]
              for l in range(L)]
     shapes = [(q, d), (d, q), (2 * dff, d), (d, dff)]
@@ -321,7 +330,7 @@ def check_chain_own_inputs(ch, ws, x0, layers, Y, Yb):
     return rms
 
 
-@pytest.mark.parametrize("M", [16, 64])
+@pytest.mark.parametrize("M", [16, 64, 1])
 def test_chain_gain_normalised_36_layers(cuda_device, M):
     """36 layers (d = q = 512, d_ff = 1536) whose activations stay of order one.
     Each layer maps its input to roughly the square of it (the SiLU-gated
