@@ -5,7 +5,9 @@
   eagerly and as a replayed HIP graph;
 - completion counters: one leader per XCD polling (SGEMM_F_POLL_LEADER),
   flat counters (SGEMM_F_SYNC_FLAT), device-scope split-K arrivals
-  (SGEMM_F_SYNC_AGENT).
+  (SGEMM_F_SYNC_AGENT);
+- stage path: dot2 stages (SGEMM_F_FORCE_DOT2, M < 16) and MFMA stages
+  (SGEMM_F_FORCE_MFMA) whatever the planner's choice is.
 
     python -m chiplet_aware_persistent_amd.chain_ablation [--m 1 16 64] [--launches 10] [--modes ...]
 
@@ -53,7 +55,8 @@ def main():
     modes = [("one_launch", 0, False), ("launch_per_stage", sg.F_LAUNCH_PER_STAGE, False),
              ("one_launch_graph", 0, True), ("launch_per_stage_graph", sg.F_LAUNCH_PER_STAGE, True),
              ("poll_leader", sg.F_POLL_LEADER, False), ("sync_flat", sg.F_SYNC_FLAT, False),
-             ("sync_agent", sg.F_SYNC_AGENT, False)]
+             ("sync_agent", sg.F_SYNC_AGENT, False), ("path_dot2", sg.F_FORCE_DOT2, False),
+             ("path_mfma", sg.F_FORCE_MFMA, False)]
     if a.modes:
         unknown = set(a.modes) - {m[0] for m in modes}
         if unknown:
@@ -64,6 +67,8 @@ def main():
         X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(5, 0, synth.T_X), M, d), dev)
         ref = None
         for name, flags, graph in modes:
+            if name == "path_dot2" and M >= 16:
+                continue  # no dot2 chain from M = 16 on
             ch = sg.LayerChain(M, LAYERS, d, q, dff, flags=flags)
             ws = ch.new_workspace()
             Y = torch.empty((M, d), dtype=torch.float32, device=dev)
@@ -101,7 +106,8 @@ def main():
                 ref = Y.clone()
             ts.sort()
             n = len(ts)
-            print(json.dumps({"M": M, "mode": name, "launches": a.launches, "median_us": round(ts[n // 2], 1),
+            print(json.dumps({"M": M, "mode": name, "path": ch.describe()["stages"][0]["path"],
+                              "launches": a.launches, "median_us": round(ts[n // 2], 1),
                               "p10_us": round(ts[n // 10], 1), "p90_us": round(ts[(9 * n) // 10], 1),
                               "bitwise_equal_to_one_launch": bool(torch.equal(ref, Y))}), flush=True)
 
