@@ -253,3 +253,30 @@ def test_header_is_plain_c_and_cpp(tmp_path, lang, compiler):
     r = subprocess.run([compiler, "-std=c11" if lang == "c" else "-std=c++17", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", inc, str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_python_constants_match_the_header(tmp_path):
+    """Every SGEMM_* enumerator of include/sgemm.h has the same value in the
+    binding (flags, status codes, kinds, output types)."""
+    import re
+    import shutil
+    import subprocess
+
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not found")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    header = open(os.path.join(inc, "sgemm.h")).read()
+    names = sorted(set(re.findall(r"\b(SGEMM_(?:F|ERR|KIND|OUT)_[A-Z0-9_]+|SGEMM_OK)\s*=", header)))
+    assert len(names) > 15
+    src = tmp_path / "c.c"
+    src.write_text('#include <stdio.h>\n#include "sgemm.h"\nint main(void) {\n' +
+                   "".join('  printf("%s %%lld\\n", (long long)%s);\n' % (n, n) for n in names) + "  return 0;\n}\n")
+    exe = tmp_path / "c"
+    r = subprocess.run(["gcc", "-std=c11", "-I", inc, str(src), "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    for line in out.splitlines():
+        name, value = line.split()
+        py = name[len("SGEMM_"):]
+        assert hasattr(sg, py), name
+        assert getattr(sg, py) == int(value), (name, getattr(sg, py), value)
