@@ -35,6 +35,7 @@ F_W_SC1 = 1 << 7
 F_POLL_LEADER = 1 << 8
 F_MTILE_ITEMS = 1 << 9
 F_LAUNCH_PER_STAGE = 1 << 10
+F_SCHEDULER = 1 << 11
 
 
 class SgemmError(RuntimeError):

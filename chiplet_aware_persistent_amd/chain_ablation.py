@@ -7,7 +7,10 @@
   flat counters (SGEMM_F_SYNC_FLAT), device-scope split-K arrivals
   (SGEMM_F_SYNC_AGENT);
 - stage path: dot2 stages (SGEMM_F_FORCE_DOT2, M < 16) and MFMA stages
-  (SGEMM_F_FORCE_MFMA) whatever the planner's choice is.
+  (SGEMM_F_FORCE_MFMA) whatever the planner's choice is;
+- runtime: the per-XCD scheduler workgroup releasing each task to 31
+  workers through their ready-task words (SGEMM_F_SCHEDULER) against the
+  static schedule in which all 32 workgroups poll the global counter.
 
     python -m chiplet_aware_persistent_amd.chain_ablation [--m 1 16 64] [--launches 10] [--modes ...]
 
@@ -56,7 +59,7 @@ def main():
              ("one_launch_graph", 0, True), ("launch_per_stage_graph", sg.F_LAUNCH_PER_STAGE, True),
              ("poll_leader", sg.F_POLL_LEADER, False), ("sync_flat", sg.F_SYNC_FLAT, False),
              ("sync_agent", sg.F_SYNC_AGENT, False), ("path_dot2", sg.F_FORCE_DOT2, False),
-             ("path_mfma", sg.F_FORCE_MFMA, False)]
+             ("path_mfma", sg.F_FORCE_MFMA, False), ("scheduler", sg.F_SCHEDULER, False)]
     if a.modes:
         unknown = set(a.modes) - {m[0] for m in modes}
         if unknown:

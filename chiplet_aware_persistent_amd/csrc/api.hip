@@ -36,6 +36,7 @@ struct Geo {
   int paired = 0, pair_off = 0;
   int ring = 0;    // ring depth (k-steps in flight per wave)
   int mtiles = 1;  // m-tile items (ablation): items per (split, column block), m-tile fastest
+  int slots = 32;  // workgroups per XCD that share the items (31 with a scheduler workgroup)
   size_t ctr_count = 0, part_floats = 0;
   double est_us = 0.0;
 };
@@ -102,9 +103,9 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
   // touches: the window is (span - 1) splits plus the last slice's padded steps.
   const int per_split = g.NB * g.mtiles;
   int span = 1;
-  for (int w = 0; w < kWgPerXcd; ++w) {
-    const int i0 = (int)((long long)g.items * w / kWgPerXcd);
-    const int i1 = (int)((long long)g.items * (w + 1) / kWgPerXcd);
+  for (int w = 0; w < g.slots; ++w) {
+    const int i0 = (int)((long long)g.items * w / g.slots);
+    const int i1 = (int)((long long)g.items * (w + 1) / g.slots);
     if (i0 < i1) span = std::max(span, (i1 - 1) / per_split - i0 / per_split + 1);
   }
   g.win = (span - 1) * g.KS + (g.ksl - 1) * g.kss + g.steps * kstep;
@@ -118,7 +119,7 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
   const int red_bytes = g.ksl > 1 ? (g.wpi / g.ksl) * (g.ksl - 1) * tile_bytes : 0;
   g.stash_off = g.red_off + red_bytes;
   const int owners = g.ksl > 1 ? g.wpi / g.ksl : g.waves;
-  const int per_stream = ceil_div(g.items, kWgPerXcd * g.ng);
+  const int per_stream = ceil_div(g.items, g.slots * g.ng);
   g.stash_cap = std::max(0, std::min(per_stream, (kLdsMax - g.stash_off) / (owners * tile_bytes)));
   g.lds = g.stash_off + owners * g.stash_cap * tile_bytes;
   const int vals = g.path == 0 ? g.tb * g.M : g.tb * g.ta * 256;
@@ -155,7 +156,7 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
   // the stream's fair share of the CU if that is longer.  Alpha is 1 for a
   // single launch; inside the chain the neighbouring stages keep HBM busy and
   // unevenly loaded waves cost less.
-  const double wg_items = ceil_div(g.items, kWgPerXcd);
+  const double wg_items = ceil_div(g.items, g.slots);
   const double wg_bytes = std::max(wg_items * (item_bytes + part_bytes),
                                    (double)g.ng * per_stream * (item_bytes + part_bytes) / cost.alpha);
   const double x_us = (double)rows * g.win * 2.0 / cost.x_bw * 1e6;
@@ -170,7 +171,7 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
 }
 
 bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, int s_o, int waves_o,
-              int ksl_o, const Cost& cost, int wpi_o = 0, bool mtile_items = false) {
+              int ksl_o, const Cost& cost, int wpi_o = 0, bool mtile_items = false, int slots = kWgPerXcd) {
   bool found = false;
   const int waves_opts[2] = {8, 4};
   for (int wi = 0; wi < 2; ++wi) {
@@ -184,6 +185,7 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
       Geo g;
       g.path = path; g.M = M; g.K = K; g.N = N; g.waves = waves; g.wpi = wpi; g.ksl = ksl;
       g.paired = paired;
+      g.slots = slots;
       if (path == 0) {
         if (tb == 5 || tb == 6 || tb == 7) continue;
         if (tn_o && tb != tn_o) continue;
@@ -199,7 +201,10 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
           g.ta = 1;
         }
       }
-      const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : 16;  // the model was fitted up to 16 splits
+      // The model was fitted up to 16 splits.  With 31 worker slots a
+      // workgroup's items straddle two splits, which doubles its X window;
+      // up to 32 splits keep it inside the LDS at M = 64 and K = 12288.
+      const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : (slots < kWgPerXcd ? 32 : 16);
       for (int s = s_lo; s <= s_hi; ++s) {
         if (s > 1 && (K + s - 1) / s < 8) break;
         Geo c = g;
@@ -225,7 +230,7 @@ struct sgemm_plan_s {
   size_t ws_bytes = 0;
   size_t off_ctr = 0, off_part = 0;                 // GEMM (and chain stage 0..3 bases below)
   size_t c_ctr[kChainStages] = {0}, c_part[kChainStages] = {0};
-  size_t off_lctr = 0, off_gctr = 0, off_xflag = 0, off_act = 0, off_stamps = 0;
+  size_t off_lctr = 0, off_gctr = 0, off_xflag = 0, off_ready = 0, off_act = 0, off_stamps = 0;
   size_t act_layer_elems = 0, a_h1 = 0, a_h2 = 0, a_a = 0, a_x = 0;
   long long spin_ticks = 0;
 };
@@ -290,6 +295,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
 
   size_t cur = kCtl;
   if (p.kind == SGEMM_KIND_GEMM) {
+    if (p.flags & SGEMM_F_SCHEDULER) { delete pl; return SGEMM_ERR_UNSUPPORTED; }  // a chain runtime
     int rc = validate_gemm(p);
     if (rc != SGEMM_OK) { delete pl; return rc; }
     const bool mti = (p.flags & SGEMM_F_MTILE_ITEMS) != 0;
@@ -303,6 +309,9 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     layout_stage_ws(cur, pl->geo, pl->off_ctr, pl->off_part);
   } else if (p.kind == SGEMM_KIND_LAYERCHAIN) {
     if (p.flags & (SGEMM_F_W_CACHED | SGEMM_F_W_SC1 | SGEMM_F_MTILE_ITEMS)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    const bool sched = (p.flags & SGEMM_F_SCHEDULER) != 0;
+    if (sched && (p.flags & (SGEMM_F_SYNC_FLAT | SGEMM_F_POLL_LEADER))) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    const int slots = sched ? kWgPerXcd - 1 : kWgPerXcd;  // the scheduler workgroup takes no items
     if (p.M < 1 || p.n_layers < 1 || p.d_model < 8 || p.q_cols < 8 || p.d_ff < 8)
       { delete pl; return SGEMM_ERR_INVALID_ARG; }
     if (p.d_model % 8 || p.q_cols % 8 || p.d_ff % 8) { delete pl; return SGEMM_ERR_INVALID_ARG; }
@@ -361,7 +370,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
           const int tn = path == 0 ? tb : (paired ? 0 : 16 * tb);
           if (path == 0 && k_st[s] > 1) { ok = false; break; }  // no K slices on the dot2 path
           ok = plan_geo(c[s], p.M, Ks[s], Ns[s], path, paired, tn, s_st[s], waves, path == 0 ? 1 : k_st[s], cost,
-                        w_st[s]);
+                        w_st[s], false, slots);
           if (ok && paired) c[s].pair_off = p.d_ff;
           tot += ok ? c[s].est_us : 0.0;
         }
@@ -382,6 +391,8 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     cur = round_up(cur + (size_t)events * 4, 256);
     pl->off_xflag = cur;
     cur = round_up(cur + (size_t)kXcds * events * 4, 256);
+    pl->off_ready = cur;
+    cur = round_up(cur + (size_t)kXcds * kWgPerXcd * 4, 256);
     const size_t M = p.M;
     pl->a_h1 = 0;
     pl->a_h2 = round_up(M * p.q_cols, 128);
@@ -508,12 +519,14 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   a.lctr = (unsigned*)(ws + plan->off_lctr);
   a.gctr = (unsigned*)(ws + plan->off_gctr);
   a.xflag = (unsigned*)(ws + plan->off_xflag);
+  a.ready = (unsigned*)(ws + plan->off_ready);
   a.stamps = (p.flags & SGEMM_F_STAMPS) ? (unsigned long long*)(ws + plan->off_stamps) : nullptr;
   a.n_layers = p.n_layers; a.M = p.M; a.d = p.d_model; a.q = p.q_cols; a.dff = p.d_ff;
   a.act_layer_elems = plan->act_layer_elems;
   a.off_h1 = plan->a_h1; a.off_h2 = plan->a_h2; a.off_a = plan->a_a; a.off_x = plan->a_x;
   a.flat_sync = (p.flags & SGEMM_F_SYNC_FLAT) ? 1 : 0;
   a.poll_leader = (p.flags & SGEMM_F_POLL_LEADER) ? 1 : 0;
+  a.sched = (p.flags & SGEMM_F_SCHEDULER) ? 1 : 0;
   a.spin_ticks = plan->spin_ticks;
   a.path = plan->cg[0].path;
   a.mt = plan->cg[0].ta;
@@ -583,9 +596,9 @@ static std::string geo_json(const Geo& g) {
                 "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,\"wpi\":%d,"
                 "\"ksl\":%d,\"kss\":%d,\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,"
                 "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
-                "\"ring\":%d,\"mtiles\":%d,\"est_us\":%.3f}",
+                "\"ring\":%d,\"mtiles\":%d,\"slots\":%d,\"est_us\":%.3f}",
                 g.path == 0 ? "dot2" : "mfma", g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
-                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles, g.est_us);
+                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles, g.slots, g.est_us);
   return b;
 }
 

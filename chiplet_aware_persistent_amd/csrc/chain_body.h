@@ -22,6 +22,14 @@
 // Consumers wait for G[e] == 8.  With SGEMM_F_SYNC_FLAT every workgroup does
 // the release and bumps G[e] (target = grid), flowchart (a).
 //
+// With SGEMM_F_SCHEDULER (the per-XCD scheduler runtime of the Fleet reading
+// note, sections 3b and 5 and the runtime layout figure of section 4) slot 0
+// of each XCD runs no stage: it waits for each event's global counter and
+// then releases the next task to the XCD's 31 workers by writing its id into
+// their ready-task words (the per-worker last-ready-task id of section 11a,
+// finding 4).  A worker polls only its own word; the stages' items are split
+// over the 31 workers, and an XCD's last worker is the 31st to arrive.
+//
 // Before waiting, a workgroup already has the first weight steps of the next
 // stage in flight (weights do not depend on the activations).  Every wait is
 // bounded by a wall-clock budget; on expiry the time-out bit is latched in
@@ -57,7 +65,11 @@ static __device__ bool wait_event(const ChainArgs& a, int e, int xcd, int slot, 
     const unsigned long long t0 = now_ticks();
     for (;;) {
       bool done;
-      if (leader) {
+      if (a.sched) {
+        // Released by the XCD's scheduler once event e is complete.
+        done = __hip_atomic_load(a.ready + xcd * 32 + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+               (unsigned)(e + 1);
+      } else if (leader) {
         done = __hip_atomic_load(a.gctr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
       } else {
         // Device-scope read (it skips the CU's L1, which could hold a stale 0).
@@ -72,8 +84,11 @@ static __device__ bool wait_event(const ChainArgs& a, int e, int xcd, int slot, 
       }
       __builtin_amdgcn_s_sleep(1);
     }
+    // Acquire: with the producers' release (or, in scheduler mode, the
+    // scheduler's acquire-release) it orders the stage's X reads after the
+    // producers' writes.
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (leader && ok && !a.flat_sync && a.poll_leader)
+    if (leader && ok && !a.flat_sync && a.poll_leader && !a.sched)
       __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *sh_alive = ok;
   }
@@ -99,6 +114,37 @@ static __device__ void signal_event(const ChainArgs& a, int e, int xcd, int nslo
       }
     }
   }
+}
+
+// Scheduler mode, slot 0 of XCD xcd (wave 0 only): for every event of the
+// launch that has a successor, wait until all XCDs completed it, then write
+// the successor's id into the ready-task words of the XCD's workers (one
+// 128-byte line, lanes 1..nslots-1 at once).  The acquire-release fence
+// between the two makes the producers' writes visible to a worker that
+// acquires after reading its word.  Returns false if a wait timed out.
+static __device__ bool run_scheduler(const ChainArgs& a, int xcd, int nslots) {
+  const int lane = threadIdx.x & 63;
+  for (int e = a.e_begin; e + 1 < a.e_end; ++e) {
+    int ok = 1;
+    if (lane == 0) {
+      const unsigned long long t0 = now_ticks();
+      for (;;) {
+        if (__hip_atomic_load(a.gctr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)kXcds) break;
+        if ((long long)(now_ticks() - t0) > a.spin_ticks ||
+            (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout)) {
+          __hip_atomic_fetch_or(a.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    if (!__shfl(ok, 0)) return false;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+    if (lane >= 1 && lane < nslots)
+      __hip_atomic_store(a.ready + xcd * 32 + lane, (unsigned)(e + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return true;
 }
 
 static __device__ void stamp(const ChainArgs& a, int e, int which) {
@@ -128,7 +174,14 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
     if (bit == 0u || (old & bit))
       __hip_atomic_fetch_or(a.status, kStatusTopology, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  bool alive = true;
+  // The scheduler (scheduler mode, slot 0) runs no stage; its other waves
+  // go straight to the final barrier.
+  const bool scheduler = a.sched && slot == 0;
+  if (scheduler && threadIdx.x < 64) run_scheduler(a, xcd, nslots);
+  // Workers: the stages' items are split over wn workgroups, wslot is ours.
+  const int wslot = a.sched ? slot - 1 : slot;
+  const int wn = a.sched ? nslots - 1 : nslots;
+  bool alive = !scheduler;
   // Events e = 4 l + s of this launch, in order (all of them unless the
   // per-stage ablation splits the chain into launches).  The stage loop has a
   // compile-time s, so each stage's descriptor is selected statically.
@@ -157,21 +210,21 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
         // Up to two m-tiles (M <= 32) keep the deeper ring: across the stage
         // barriers it measured faster there, the shallow one at M = 64.
         if (s == 2) {
-          alive = mfma_stage<A, 2, true, kAuxNt, (A <= 2)>(d, lds, xcd, slot, nslots, hook);
+          alive = mfma_stage<A, 2, true, kAuxNt, (A <= 2)>(d, lds, xcd, wslot, wn, hook);
         } else {
-          alive = mfma_stage<A, B, false, kAuxNt, (A <= 2)>(d, lds, xcd, slot, nslots, hook);
+          alive = mfma_stage<A, B, false, kAuxNt, (A <= 2)>(d, lds, xcd, wslot, wn, hook);
         }
       } else {
         if (s == 2) {
-          alive = dot2_stage<A, B, kAuxNt, true>(d, lds, xcd, slot, nslots, hook);
+          alive = dot2_stage<A, B, kAuxNt, true>(d, lds, xcd, wslot, wn, hook);
         } else {
-          alive = dot2_stage<A, B, kAuxNt, false>(d, lds, xcd, slot, nslots, hook);
+          alive = dot2_stage<A, B, kAuxNt, false>(d, lds, xcd, wslot, wn, hook);
         }
       }
       if (!alive) break;
       if (a.stamps) __syncthreads();  // the stamp marks the end of the workgroup's last wave
       stamp(a, e, 1);
-      if (e + 1 < a.e_end) signal_event(a, e, xcd, nslots);  // the launch's last event has no waiter
+      if (e + 1 < a.e_end) signal_event(a, e, xcd, wn);  // the launch's last event has no waiter
       __syncthreads();  // LDS window reuse by the next stage
     }
   }
@@ -191,6 +244,7 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
     for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) a.lctr[i] = 0u;
     for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) a.xflag[i] = 0u;
     if (threadIdx.x < kXcds) a.claim[threadIdx.x] = 0u;
+    if (threadIdx.x < kXcds * 32) a.ready[threadIdx.x] = 0u;
     for (int s = 0; s < kChainStages; ++s) {
       const int n = kXcds * a.st[s].NB * a.st[s].wpi;
       for (int i = threadIdx.x; i < n; i += blockDim.x) a.st[s].ctr[i] = 0u;

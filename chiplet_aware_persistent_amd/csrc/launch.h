@@ -25,12 +25,14 @@ struct ChainArgs {
   unsigned* xflag;                     // [kXcds][events] per-XCD 'event seen' flags
   unsigned* done;                      // workgroups finished (reset by the last one)
   unsigned* claim;                     // [kXcds] slots claimed per XCD (reset by the last one)
+  unsigned* ready;                     // [kXcds][32] scheduler mode: last task id released to each slot
   unsigned long long* stamps;          // [grid][events][2] or null
   int n_layers, M, d, q, dff;
   size_t act_layer_elems;              // bf16 elements per layer of activations
   size_t off_h1, off_h2, off_a, off_x; // element offsets inside one layer's block
   int flat_sync;                       // every workgroup publishes globally
   int poll_leader;                     // one workgroup per XCD polls and raises the XCD's flag
+  int sched;                           // slot 0 of each XCD schedules, slots 1..31 work
   long long spin_ticks;                // watchdog budget (wall-clock ticks, 100 MHz)
   int path;                            // 1: MFMA stages, 0: dot2 stages (M < 16)
   int mt, nt_q, nt_o, nt_d;            // template parameters: MFMA (MT, NT); dot2 (M in mt, G in nt_*)

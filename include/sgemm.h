@@ -81,11 +81,25 @@ enum {
                                     caches (Fleet reading note, section 3f,
                                     M-major window) instead of in registers;
                                     MFMA path, no K slices                      */
-  SGEMM_F_LAUNCH_PER_STAGE = 1u << 10 /* chain, ablation: one launch of the same
+  SGEMM_F_LAUNCH_PER_STAGE = 1u << 10, /* chain, ablation: one launch of the same
                                     kernel per projection stage, so the kernel
                                     boundary is the barrier between stages and
                                     no weights are prefetched across it; the
                                     results are bitwise those of one launch     */
+  SGEMM_F_SCHEDULER = 1u << 11   /* chain, ablation: the per-XCD scheduler
+                                    runtime (Fleet reading note, sections 3b
+                                    and 5, the runtime layout figure of
+                                    section 4, the per-worker ready-task id
+                                    of section 11a, finding 4): slot 0
+                                    of each XCD does no GEMM work; it polls
+                                    the global counter of each event and then
+                                    writes the next task id into the
+                                    ready-task word of each of the XCD's 31
+                                    workers, which poll only their own word.
+                                    The other 31 slots share the stages'
+                                    items.  Not combined with
+                                    SGEMM_F_SYNC_FLAT or SGEMM_F_POLL_LEADER
+                                    (SGEMM_ERR_UNSUPPORTED)                     */
 };
 
 /*

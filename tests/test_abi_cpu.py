@@ -178,6 +178,24 @@ def test_chain_path_choice():
         sg.LayerChain(16, 4, 4096, 4096, 12288, flags=sg.F_FORCE_DOT2)
 
 
+def test_chain_scheduler_plan():
+    """With SGEMM_F_SCHEDULER the stages are planned over 31 worker slots per
+    XCD (slot 0 schedules); the grid stays 8 x 32.  The mode is a chain runtime:
+    refused for a single GEMM and with the flat or poll-leader counters."""
+    for M in (1, 16, 64):
+        base = sg.LayerChain(M, 4, 4096, 4096, 12288).describe()
+        sch = sg.LayerChain(M, 4, 4096, 4096, 12288, flags=sg.F_SCHEDULER).describe()
+        assert sch["grid"] == base["grid"] == 256
+        assert [s["slots"] for s in base["stages"]] == [32] * 4
+        assert [s["slots"] for s in sch["stages"]] == [31] * 4
+        assert [s["path"] for s in sch["stages"]] == [s["path"] for s in base["stages"]]
+    for flags in (sg.F_SCHEDULER | sg.F_SYNC_FLAT, sg.F_SCHEDULER | sg.F_POLL_LEADER):
+        with pytest.raises(sg.SgemmError):
+            sg.LayerChain(16, 4, 4096, 4096, 12288, flags=flags)
+    with pytest.raises(sg.SgemmError):
+        sg.Gemm(16, 4096, 4096, flags=sg.F_SCHEDULER)
+
+
 def test_eq1_matches_the_pages_table():
     g = json.load(open(os.path.join(GOLD, "eq1_l2_hit.json")))
     for row in g["rows"]:

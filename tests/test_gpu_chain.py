@@ -99,13 +99,16 @@ def check_chain(ch, ws, x0, layers, Y, Yb, M):
 
 
 @pytest.mark.parametrize("M,flags", [(1, 0), (2, 0), (5, 0), (16, 0), (33, 0), (64, 0), (1, sg.F_FORCE_MFMA),
-                                     (5, sg.F_FORCE_DOT2), (9, sg.F_FORCE_DOT2), (15, sg.F_FORCE_DOT2)])
+                                     (5, sg.F_FORCE_DOT2), (9, sg.F_FORCE_DOT2), (15, sg.F_FORCE_DOT2),
+                                     (1, sg.F_SCHEDULER), (5, sg.F_SCHEDULER), (16, sg.F_SCHEDULER),
+                                     (64, sg.F_SCHEDULER)])
 def test_chain_small_parity(cuda_device, M, flags):
-    """dot2 stages at M <= 2 and when forced below 16, MFMA otherwise."""
+    """dot2 stages at M <= 2 and when forced below 16, MFMA otherwise; also
+    under the per-XCD scheduler runtime (31 workers per XCD)."""
     L, d, q, dff = 3, 256, 128, 384
     x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x1000 + M, cuda_device)
     ch = sg.LayerChain(M, L, d, q, dff, flags=flags)
-    dot2 = flags == sg.F_FORCE_DOT2 or (M <= 2 and flags == 0)
+    dot2 = flags == sg.F_FORCE_DOT2 or (M <= 2 and flags in (0, sg.F_SCHEDULER))
     assert {s["path"] for s in ch.describe()["stages"]} == {"dot2" if dot2 else "mfma"}
     rc, Y, Yb, ws = run_chain(ch, X0, dl)
     assert rc == sg.OK, sg.status_string(rc)
@@ -117,6 +120,19 @@ def test_chain_small_parity(cuda_device, M, flags):
 def test_chain_wider_parity(cuda_device, M, L, d, q, dff):
     x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x2000 + M + L, cuda_device)
     ch = sg.LayerChain(M, L, d, q, dff)
+    rc, Y, Yb, ws = run_chain(ch, X0, dl)
+    assert rc == sg.OK, sg.status_string(rc)
+    check_chain(ch, ws, x0, layers, Y, Yb, M)
+
+
+@pytest.mark.parametrize("M,L,d,q,dff", [(64, 1, 4096, 4096, 12288), (1, 1, 4096, 4096, 12288),
+                                         (8, 4, 512, 256, 1536), (2, 2, 256, 128, 200)])
+def test_chain_scheduler_parity(cuda_device, M, L, d, q, dff):
+    """The per-XCD scheduler runtime at the configured layer width and on
+    ragged shapes: slot 0 of each XCD releases each task to its 31 workers."""
+    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x2800 + M + L, cuda_device)
+    ch = sg.LayerChain(M, L, d, q, dff, flags=sg.F_SCHEDULER)
+    assert all(s["slots"] == 31 for s in ch.describe()["stages"])
     rc, Y, Yb, ws = run_chain(ch, X0, dl)
     assert rc == sg.OK, sg.status_string(rc)
     check_chain(ch, ws, x0, layers, Y, Yb, M)
@@ -165,7 +181,7 @@ def test_chain_repeatable_and_sync_modes_agree(cuda_device):
         assert torch.equal(Y1, Y3)
 
 
-@pytest.mark.parametrize("flags", [0, sg.F_LAUNCH_PER_STAGE])
+@pytest.mark.parametrize("flags", [0, sg.F_LAUNCH_PER_STAGE, sg.F_SCHEDULER])
 def test_chain_graph_replays_match_eager(cuda_device, flags):
     """A HIP graph of one chain call (one launch, or one launch per stage)
     replays to the eager result bitwise, with eager chain runs and host
@@ -198,7 +214,7 @@ def test_chain_graph_replays_match_eager(cuda_device, flags):
         assert rc2 == sg.OK and torch.equal(Y2, Ye), r
 
 
-@pytest.mark.parametrize("flags", [0, sg.F_POLL_LEADER, sg.F_SYNC_FLAT, sg.F_LAUNCH_PER_STAGE])
+@pytest.mark.parametrize("flags", [0, sg.F_POLL_LEADER, sg.F_SYNC_FLAT, sg.F_LAUNCH_PER_STAGE, sg.F_SCHEDULER])
 def test_chain_stamps_order_every_stage(cuda_device, flags):
     M, L, d, q, dff = 32, 4, 512, 256, 768
     x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x4000, cuda_device)
@@ -209,16 +225,19 @@ def test_chain_stamps_order_every_stage(cuda_device, flags):
     E = 4 * L
     off = info["stamps_offset"]
     st = ws[off:off + info["grid"] * E * 16].view(torch.int64).view(info["grid"], E, 2).cpu().numpy()
+    if flags == sg.F_SCHEDULER:
+        st = st[8:]  # workgroups 0..7 are the schedulers (slot 0 of each XCD) and run no stage
     assert np.all(st[:, :, 1] >= st[:, :, 0])
     for e in range(1, E):
         assert st[:, e, 0].min() >= st[:, e - 1, 1].max(), e   # nobody starts e before all finished e-1
 
 
-def test_chain_watchdog_times_out_and_workspace_recovers(cuda_device):
+@pytest.mark.parametrize("mode", [0, sg.F_SCHEDULER])
+def test_chain_watchdog_times_out_and_workspace_recovers(cuda_device, mode):
     M, L, d, q, dff = 16, 3, 256, 128, 384
     x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x5000, cuda_device)
-    bad = sg.LayerChain(M, L, d, q, dff, flags=sg.F_WATCHDOG_TEST)
-    good = sg.LayerChain(M, L, d, q, dff)
+    bad = sg.LayerChain(M, L, d, q, dff, flags=sg.F_WATCHDOG_TEST | mode)
+    good = sg.LayerChain(M, L, d, q, dff, flags=mode)
     assert bad.workspace_bytes == good.workspace_bytes
     rc, _, _, ws = run_chain(bad, X0, dl)
     assert rc == sg.ERR_TIMEOUT
