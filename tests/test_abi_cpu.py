@@ -298,3 +298,22 @@ def test_python_constants_match_the_header(tmp_path):
         py = name[len("SGEMM_"):]
         assert hasattr(sg, py), name
         assert getattr(sg, py) == int(value), (name, getattr(sg, py), value)
+
+
+def test_chain_stamps_breakdown_on_a_made_up_timeline():
+    """Two workgroups and five events (Q, O, gate_up and down of one layer,
+    then Q of the next); every figure is worked out by hand below."""
+    import numpy as np
+    from chiplet_aware_persistent_amd.chain_stamps import stage_breakdown
+    st = np.zeros((2, 5, 2))
+    t = 0.0
+    for e in range(5):
+        st[0, e] = (t + 1.0, t + 5.0)   # workgroup 0 starts 1 us after the barrier, works 4 us
+        st[1, e] = (t + 2.0, t + 8.0)   # workgroup 1 starts 2 us after, works 6 us
+        t += 8.0
+    b = stage_breakdown(st)
+    assert set(b) == {"Q", "O", "gate_up", "down"}
+    # release: first start (t+1) minus the previous last end (t)
+    # skew 1; med_start 0.5; work_med 5; tail: 8 - median(5, 8) = 1.5; span: 8 - 1 = 7
+    for v in b.values():
+        assert v == [1.0, 1.0, 0.5, 5.0, 1.5, 7.0]
