@@ -229,23 +229,37 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
     }
   }
   // Finish: the last workgroup resets all counters for the next launch.
+  // Every counter is touched only by device-scope atomics, and vmcnt(0) has
+  // seen each of this workgroup's complete before it counts itself done, so
+  // no release (an L2 write-back per workgroup) precedes the done count: no
+  // other workgroup reads this one's data after this point, and the end of
+  // the kernel writes it back.
   wait_vm0();
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const unsigned old = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh_last = old == gridDim.x - 1;
     if (sh_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   if (sh_last) {
+    // Only this launch's events [e_begin, e_end) and their stages touched
+    // counters; every other event's counters are still zero.
     const int events = 4 * a.n_layers;
-    for (int i = threadIdx.x; i < events; i += blockDim.x) a.gctr[i] = 0u;
-    for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) a.lctr[i] = 0u;
-    for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) a.xflag[i] = 0u;
+    const int ne = a.e_end - a.e_begin;
+    for (int i = threadIdx.x; i < ne; i += blockDim.x) a.gctr[a.e_begin + i] = 0u;
+    for (int i = threadIdx.x; i < kXcds * ne; i += blockDim.x) {
+      const int x = i / ne;
+      const int e = a.e_begin + (i - x * ne);
+      a.lctr[x * events + e] = 0u;
+      a.xflag[x * events + e] = 0u;
+    }
     if (threadIdx.x < kXcds) a.claim[threadIdx.x] = 0u;
     if (threadIdx.x < kXcds * 32) a.ready[threadIdx.x] = 0u;
     for (int s = 0; s < kChainStages; ++s) {
+      bool used = ne >= kChainStages;
+      for (int e = a.e_begin; e < a.e_end && !used; ++e) used = (e & 3) == s;
+      if (!used) continue;
       const int n = kXcds * a.st[s].NB * a.st[s].wpi;
       for (int i = threadIdx.x; i < n; i += blockDim.x) a.st[s].ctr[i] = 0u;
     }
