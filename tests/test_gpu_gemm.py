@@ -85,6 +85,19 @@ def test_parity_small(cuda_device, M, K, N):
     check(Y, x, w)
 
 
+# One GPU's share of the Qwen3-8B decode projections under 8-way tensor parallelism:
+# QKV and gate_up split by output columns (N / 8), O and down by K (K / 8).
+TP8_SHARDS = [(4096, 768), (512, 4096), (4096, 3072), (1536, 4096)]
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+@pytest.mark.parametrize("K,N", TP8_SHARDS)
+def test_parity_tp8_shard_shapes(cuda_device, M, K, N):
+    x, w, X, W = gemm_inputs(M, K, N, 5000 + M, 6000 + K + N, cuda_device)
+    g = sg.Gemm(M, K, N)
+    check(run(g, X, W).cpu().numpy(), x, w)
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 1024, 1024), (4, 2056, 999), (8, 4096, 512), (12, 776, 530),
                                    (16, 1024, 2048), (33, 2048, 1536), (64, 1000, 1000)])
 @pytest.mark.parametrize("splitk", [2, 5, 11])
