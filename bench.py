@@ -287,7 +287,7 @@ def main():
                     help="run one 256 MiB device copy first (counter calibration for --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU shard of a "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the per-GPU shard of a "
               "tensor-parallel layout is the same kernel at a narrower shape); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
