@@ -84,6 +84,28 @@ def cpu_baseline_proj(x_bits, w_host):
                       "accumulation" % (reps, dt)}
 
 
+def cpu_baseline_chain(M, x_bits, layer_w):
+    """The oracle's chain layer (Q, O, gate_up with SiLU gate, down) on the
+    host cores, repeated on layer 0's weights for about 10 s."""
+    import oracle
+
+    t0 = time.perf_counter()
+    reps = 0
+    wbytes = 0
+    layer_bytes = sum(2 * w.size for w in layer_w)
+    while True:
+        oracle.layer(x_bits, *layer_w)
+        wbytes += layer_bytes
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 2000:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d chain layers (%.1f s) on layer 0's weights and input: Q, O, gate_up with SiLU "
+                      "gate, down, every output column, M=%d, double accumulation" % (reps, dt, M)}
+
+
 def bench_proj(args):
     import numpy as np
     import torch
@@ -272,6 +294,9 @@ def bench_chain(args):
         "plan": [{k: st[k] for k in ("path", "waves", "TN", "ksl", "S", "KS", "items")}
                  for st in ch.describe()["stages"]],
     }
+    if not args.no_cpu:
+        layer_w = [synth.from_torch_bf16(wl[0][i]) for i in range(4)]
+        out["cpu_baseline"] = cpu_baseline_chain(M, synth.from_torch_bf16(X0), layer_w)
     return out
 
 
