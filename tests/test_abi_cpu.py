@@ -317,3 +317,16 @@ def test_chain_stamps_breakdown_on_a_made_up_timeline():
     # skew 1; med_start 0.5; work_med 5; tail: 8 - median(5, 8) = 1.5; span: 8 - 1 = 7
     for v in b.values():
         assert v == [1.0, 1.0, 0.5, 5.0, 1.5, 7.0]
+
+
+def test_bench_cpu_baselines_report_the_contract_fields():
+    """Both workloads' CPU baselines time the oracle as it stands and say what
+    they timed (tiny shapes here; the bench uses the full ones)."""
+    import bench
+    import synth
+    x = synth.normal_bf16(1, 2, 256)
+    ws = [synth.uniform_bf16(2, 128, 256, 0.05), synth.uniform_bf16(3, 256, 128, 0.05),
+          synth.uniform_bf16(4, 2 * 384, 256, 0.05), synth.uniform_bf16(5, 256, 384, 0.05)]
+    r = bench.cpu_baseline_chain(2, x, ws)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0 and r["cores"] >= 1
+    assert "M=2" in r["sample"]
