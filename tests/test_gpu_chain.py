@@ -101,14 +101,16 @@ def check_chain(ch, ws, x0, layers, Y, Yb, M):
 @pytest.mark.parametrize("M,flags", [(1, 0), (2, 0), (5, 0), (16, 0), (33, 0), (64, 0), (1, sg.F_FORCE_MFMA),
                                      (5, sg.F_FORCE_DOT2), (9, sg.F_FORCE_DOT2), (15, sg.F_FORCE_DOT2),
                                      (1, sg.F_SCHEDULER), (5, sg.F_SCHEDULER), (16, sg.F_SCHEDULER),
-                                     (64, sg.F_SCHEDULER)])
+                                     (33, sg.F_SCHEDULER), (64, sg.F_SCHEDULER),
+                                     (2, sg.F_SCHEDULER | sg.F_LAUNCH_PER_STAGE),
+                                     (16, sg.F_SCHEDULER | sg.F_LAUNCH_PER_STAGE)])
 def test_chain_small_parity(cuda_device, M, flags):
     """dot2 stages at M <= 2 and when forced below 16, MFMA otherwise; also
     under the per-XCD scheduler runtime (31 workers per XCD)."""
     L, d, q, dff = 3, 256, 128, 384
     x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x1000 + M, cuda_device)
     ch = sg.LayerChain(M, L, d, q, dff, flags=flags)
-    dot2 = flags == sg.F_FORCE_DOT2 or (M <= 2 and flags in (0, sg.F_SCHEDULER))
+    dot2 = flags == sg.F_FORCE_DOT2 or (M <= 2 and not flags & (sg.F_FORCE_DOT2 | sg.F_FORCE_MFMA))
     assert {s["path"] for s in ch.describe()["stages"]} == {"dot2" if dot2 else "mfma"}
     rc, Y, Yb, ws = run_chain(ch, X0, dl)
     assert rc == sg.OK, sg.status_string(rc)
