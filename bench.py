@@ -16,6 +16,13 @@ launch stream, next to the attainable rate of a plain streaming read of the
 same weight buffers (sgemm_read_probe); ``cpu_baseline`` is the CPU oracle on
 the same step.
 
+Unless ``--no-extra`` is given, the line also carries ``configs``: every
+other configuration timed in the same run with HIP events on the launch
+stream (the single GEMM at M = 1, 8, 16, 32, 64 on the four projection shapes,
+the K = 7168 grid at M = 1..16, 1 x 1024 x 1024, each on weights rotating over
+a 4.5 GiB pool; the 36-layer chain at M = 64, 16 and 1), each with its
+fraction of 8 TB/s.
+
 ``--workload chain``: the 36-layer persistent chain at M = 64 (``--chain-m``
 selects another row count; Q 4096x4096,
 O 4096x4096, gate_up 4096x24576 with SiLU gate, down 12288x4096 per layer;
@@ -64,6 +71,20 @@ def load_traffic(name: str):
     return t.get("bytes_per_launch")
 
 
+def host_cpu():
+    """CPU model name and the host's logical CPU count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def cpu_baseline_proj(x_bits, w_host):
     import oracle
 
@@ -78,10 +99,10 @@ def cpu_baseline_proj(x_bits, w_host):
         if time.perf_counter() - t0 > 10.0 or reps >= 2000:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "%d full steps (%.1f s): all four projections, every output column, M=1, double "
-                      "accumulation" % (reps, dt)}
+    return dict({"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+                 "kind": "oracle",
+                 "sample": "%d full steps (%.1f s): all four projections, every output column, M=1, double "
+                           "accumulation" % (reps, dt)}, **host_cpu())
 
 
 def cpu_baseline_chain(M, x_bits, layer_w):
@@ -100,10 +121,11 @@ def cpu_baseline_chain(M, x_bits, layer_w):
         if time.perf_counter() - t0 > 10.0 or reps >= 2000:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "%d chain layers (%.1f s) on layer 0's weights and input: Q, O, gate_up with SiLU "
-                      "gate, down, every output column, M=%d, double accumulation" % (reps, dt, M)}
+    return dict({"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+                 "kind": "oracle",
+                 "sample": "%d chain layers (%.1f s) on layer 0's weights and input: Q, O, gate_up with SiLU "
+                           "gate, down, every output column, M=%d, double accumulation" % (reps, dt, M)},
+                **host_cpu())
 
 
 def bench_proj(args):
@@ -205,6 +227,7 @@ def bench_proj(args):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.steps
         attain[key] = round(W[0][di].numel() * 2 / (us * 1e-6) / 1e9, 1)
+    w_host = [synth.from_torch_bf16(W[0][i]) for i in range(len(PROJ))] if not args.no_cpu else None
     ms_step = wall / args.steps * 1e3
     value = wbytes_step / (wall / args.steps) / 1e9
     K, N = per[dom]["K"], per[dom]["N"]
@@ -229,10 +252,117 @@ def bench_proj(args):
         "plans": {k: {kk: d["plan"][kk] for kk in ("path", "waves", "TN", "ksl", "S", "KS", "items")}
                   for k, d in per.items()},
     }
+    if not args.no_extra:
+        # The other configurations, each timed on the same box in this run:
+        # every single-GEMM shape (M = 1..64 on the decode projections, the
+        # K = 7168 grid, 1 x 1024 x 1024) and the 36-layer chain at M = 64 and 1.
+        del W, ptrs
+        torch.cuda.empty_cache()
+        out["configs"] = {"gemm": timed_gemm_table(dev, max(args.steps, 20), args.warmup)}
+        wl = chain_weights(dev)
+        out["configs"]["chain36"] = [timed_chain(dev, wl, m, 10, 2) for m in (64, 16, 1)]
+        del wl
+        torch.cuda.empty_cache()
     if not args.no_cpu:
-        w_host = [synth.from_torch_bf16(W[0][i]) for i in range(len(PROJ))]
         out["cpu_baseline"] = cpu_baseline_proj(x_bits, w_host)
     return out
+
+
+GEMM_TABLE = ([(1, 1024, 1024)] +
+              [(M, K, N) for M in (1, 8, 16, 32, 64) for _, K, N in PROJ] +
+              [(M, 7168, N) for M in (1, 2, 4, 8, 16) for N in (1536, 4096, 18432)])
+
+
+def timed_gemm_table(dev, steps, warmup):
+    """Every single-GEMM configuration shape: kernel time per launch from HIP
+    events around `steps` back-to-back launches on the launch stream, the
+    weights rotating over views of a >= 4 GiB pool so each launch reads them
+    from HBM."""
+    import torch
+
+    import chiplet_aware_persistent_amd as sg
+
+    pool = torch.empty((9 << 30) // 4, dtype=torch.bfloat16, device=dev)   # 4.5 GiB
+    pool.uniform_(-0.01, 0.01)
+    stream = torch.cuda.current_stream()
+    lib, h = sg.library(), int(stream.cuda_stream)
+    rows = []
+    for M, K, N in GEMM_TABLE:
+        g = sg.Gemm(M, K, N)
+        ws = g.new_workspace()
+        X = torch.randn((M, K), device=dev).to(torch.bfloat16)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        span = -(-N * K // 256) * 256
+        copies = min(pool.numel() // span, 4096)
+        ptr = [pool.data_ptr() + c * span * 2 for c in range(copies)]
+        a = (g.handle, X.data_ptr(), 0, Y.data_ptr(), ws.data_ptr(), h)
+        for s_ in range(warmup):
+            lib.sgemm_run(a[0], a[1], ptr[s_ % copies], a[3], a[4], h)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s_ in range(steps):
+            rc = lib.sgemm_run(a[0], a[1], ptr[(warmup + s_) % copies], a[3], a[4], h)
+            if rc:
+                raise sg.SgemmError(rc, "sgemm_run")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rc = g.status(ws)
+        if rc:
+            raise sg.SgemmError(rc, "status")
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        st = g.describe()["stage"]
+        rows.append({"M": M, "K": K, "N": N, "us_avg": round(us, 3),
+                     "weight_GBps": round(2 * K * N / (us * 1e-6) / 1e9, 1),
+                     "frac_of_8TBps": round(2 * K * N / (us * 1e-6) / 1e12 / 8.0, 4),
+                     "plan": "%s ta=%d tb=%d wpi=%d ksl=%d S=%d" % (st["path"], st["ta"], st["tb"], st["wpi"],
+                                                                   st["ksl"], st["S"])})
+        log("table %dx%dx%d: %.2f us" % (M, K, N, us))
+    del pool
+    torch.cuda.empty_cache()
+    return rows
+
+
+def chain_weights(dev, L=36, d=4096, q=4096, dff=12288):
+    import synth
+
+    return [[synth.uniform_bf16_torch(synth.seed_for(5, l, 1), q, d, synth.weight_scale(d), dev),
+             synth.uniform_bf16_torch(synth.seed_for(5, l, 2), d, q, synth.weight_scale(q), dev),
+             synth.uniform_bf16_torch(synth.seed_for(5, l, 3), 2 * dff, d, synth.weight_scale(d), dev),
+             synth.uniform_bf16_torch(synth.seed_for(5, l, 4), d, dff, synth.weight_scale(dff), dev)]
+            for l in range(L)]
+
+
+def timed_chain(dev, wl, M, steps, warmup):
+    """The 36-layer chain at M rows: per-launch time from HIP event pairs."""
+    import torch
+
+    import chiplet_aware_persistent_amd as sg
+    import synth
+
+    L, d, q, dff = len(wl), wl[0][0].shape[1], wl[0][0].shape[0], wl[0][3].shape[1]
+    X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(5, 0, 0), M, d), dev)
+    ch = sg.LayerChain(M, L, d, q, dff)
+    ws = ch.new_workspace()
+    Y = torch.empty((M, d), dtype=torch.float32, device=dev)
+    cols = [[w[i] for w in wl] for i in range(4)]
+    for _ in range(warmup):
+        ch(X0, *cols, Y, ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s_ in range(steps):
+        ev[s_][0].record()
+        ch(X0, *cols, Y, ws)
+        ev[s_][1].record()
+    torch.cuda.synchronize()
+    rc = ch.status(ws)
+    if rc:
+        raise sg.SgemmError(rc, "chain status")
+    ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    wbytes = L * 2 * (q * d + d * q + 2 * dff * d + d * dff)
+    avg = sum(ts) / len(ts)
+    return {"M": M, "layers": L, "us_avg": round(avg, 2), "us_median": round(ts[len(ts) // 2], 2),
+            "weight_GBps": round(wbytes / (avg * 1e-6) / 1e9, 1),
+            "frac_of_8TBps": round(wbytes / (avg * 1e-6) / 1e12 / 8.0, 4), "weight_bytes": wbytes,
+            "plan": [{k: st[k] for k in ("path", "ta", "tb", "wpi", "ksl", "S")} for st in ch.describe()["stages"]]}
 
 
 def bench_chain(args):
@@ -243,12 +373,7 @@ def bench_chain(args):
 
     dev = torch.device("cuda:0")
     M, L, d, q, dff = args.chain_m, 36, 4096, 4096, 12288
-    wl = []
-    for l in range(L):
-        wl.append([synth.uniform_bf16_torch(synth.seed_for(5, l, 1), q, d, synth.weight_scale(d), dev),
-                   synth.uniform_bf16_torch(synth.seed_for(5, l, 2), d, q, synth.weight_scale(q), dev),
-                   synth.uniform_bf16_torch(synth.seed_for(5, l, 3), 2 * dff, d, synth.weight_scale(d), dev),
-                   synth.uniform_bf16_torch(synth.seed_for(5, l, 4), d, dff, synth.weight_scale(dff), dev)])
+    wl = chain_weights(dev, L, d, q, dff)
     X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(5, 0, 0), M, d), dev)
     ch = sg.LayerChain(M, L, d, q, dff)
     ws = ch.new_workspace()
@@ -308,6 +433,8 @@ def main():
     ap.add_argument("--workload", choices=["proj", "chain"], default="proj")
     ap.add_argument("--chain-m", type=int, default=64, help="rows of the chain workload (1-64)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the per-configuration table (all GEMM shapes, the 36-layer chain)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (counter calibration for --pmc runs)")
     args = ap.parse_args()

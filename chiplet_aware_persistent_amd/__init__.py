@@ -78,9 +78,10 @@ def library() -> ctypes.CDLL:
         lib.sgemm_plan_describe.argtypes = [vp, ctypes.c_char_p, sz]
         lib.sgemm_topology_probe.argtypes = [vp, ctypes.c_int, vp]
         lib.sgemm_read_probe.argtypes = [vp, sz, ctypes.c_int, vp, ctypes.c_int, vp]
+        lib.sgemm_device_check.argtypes = [ctypes.c_int]
         for f in ("sgemm_plan_create", "sgemm_plan_destroy", "sgemm_workspace_init", "sgemm_run",
                   "layerchain_run", "sgemm_chain_buffer", "sgemm_query_status", "sgemm_plan_describe",
-                  "sgemm_topology_probe", "sgemm_read_probe"):
+                  "sgemm_topology_probe", "sgemm_read_probe", "sgemm_device_check"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -149,6 +150,10 @@ def sgemm_plan_describe(plan) -> dict:
     return json.loads(buf.value.decode())
 
 
+def sgemm_device_check(device: int = 0) -> int:
+    return library().sgemm_device_check(int(device))
+
+
 def sgemm_topology_probe(xcc_out: int, n_wg: int, stream: int = 0) -> int:
     return library().sgemm_topology_probe(xcc_out, n_wg, stream)
 
@@ -169,6 +174,25 @@ def _stream_handle(stream) -> int:
 def _check(rc: int, what: str):
     if rc != OK:
         raise SgemmError(rc, what)
+
+
+def _need(t, shape, dtype, name):
+    """Raise ValueError unless tensor t has this shape and dtype and is contiguous."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s: expected dtype %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s: must be contiguous" % name)
+
+
+def _need_workspace(ws, nbytes):
+    import torch
+
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace: expected a contiguous 1-D uint8 tensor")
+    if ws.numel() < nbytes:
+        raise ValueError("workspace: %d bytes, the plan needs %d" % (ws.numel(), nbytes))
 
 
 class _PlanBase:
@@ -210,12 +234,10 @@ class Gemm(_PlanBase):
     def __call__(self, X, W, Y, workspace, stream=None):
         import torch
 
-        assert X.dtype == torch.bfloat16 and W.dtype == torch.bfloat16
-        assert tuple(X.shape) == (self.M, self.K) and tuple(W.shape) == (self.N, self.K)
-        assert tuple(Y.shape) == (self.M, self.N)
-        assert Y.dtype == (torch.float32 if self.out_dtype == OUT_F32 else torch.bfloat16)
-        assert X.is_contiguous() and W.is_contiguous() and Y.is_contiguous()
-        assert workspace.numel() >= self.workspace_bytes
+        _need(X, (self.M, self.K), torch.bfloat16, "X")
+        _need(W, (self.N, self.K), torch.bfloat16, "W")
+        _need(Y, (self.M, self.N), torch.float32 if self.out_dtype == OUT_F32 else torch.bfloat16, "Y")
+        _need_workspace(workspace, self.workspace_bytes)
         _check(sgemm_run(self.handle, X.data_ptr(), W.data_ptr(), Y.data_ptr(), workspace.data_ptr(),
                          _stream_handle(stream)), "sgemm_run")
         return Y
@@ -235,14 +257,18 @@ class LayerChain(_PlanBase):
         import torch
 
         L = self.n_layers
-        assert len(Wq) == len(Wo) == len(Wgu) == len(Wdown) == L
+        if not (len(Wq) == len(Wo) == len(Wgu) == len(Wdown) == L):
+            raise ValueError("expected %d weight tensors per projection" % L)
         for l in range(L):
-            assert tuple(Wq[l].shape) == (self.q, self.d) and tuple(Wo[l].shape) == (self.d, self.q)
-            assert tuple(Wgu[l].shape) == (2 * self.dff, self.d) and tuple(Wdown[l].shape) == (self.d, self.dff)
-            for w in (Wq[l], Wo[l], Wgu[l], Wdown[l]):
-                assert w.dtype == torch.bfloat16 and w.is_contiguous()
-        assert tuple(X0.shape) == (self.M, self.d) and X0.dtype == torch.bfloat16
-        assert tuple(Y_f32.shape) == (self.M, self.d) and Y_f32.dtype == torch.float32
+            _need(Wq[l], (self.q, self.d), torch.bfloat16, "Wq[%d]" % l)
+            _need(Wo[l], (self.d, self.q), torch.bfloat16, "Wo[%d]" % l)
+            _need(Wgu[l], (2 * self.dff, self.d), torch.bfloat16, "Wgu[%d]" % l)
+            _need(Wdown[l], (self.d, self.dff), torch.bfloat16, "Wdown[%d]" % l)
+        _need(X0, (self.M, self.d), torch.bfloat16, "X0")
+        _need(Y_f32, (self.M, self.d), torch.float32, "Y_f32")
+        if Y_bf16 is not None:
+            _need(Y_bf16, (self.M, self.d), torch.bfloat16, "Y_bf16")
+        _need_workspace(workspace, self.workspace_bytes)
         _check(layerchain_run(self.handle, X0.data_ptr(), [w.data_ptr() for w in Wq],
                               [w.data_ptr() for w in Wo], [w.data_ptr() for w in Wgu],
                               [w.data_ptr() for w in Wdown], Y_f32.data_ptr(),

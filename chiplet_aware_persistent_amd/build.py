@@ -43,21 +43,37 @@ def _compile(src: str):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr[-6000:]))
+    static = {k: v for k, v in resource_usage(r.stderr, "LDS Size [bytes/block]").items()
+              if v > STATIC_LDS_RESERVE}
+    if static:
+        raise RuntimeError("kernels declare more static LDS than the planner reserves (%d B): %s"
+                           % (STATIC_LDS_RESERVE, static))
     return obj, scratch_usage(r.stderr)
 
 
-def scratch_usage(remarks: str) -> dict:
-    """Per-kernel private (scratch) bytes per lane from the compiler's resource-usage remarks."""
+def resource_usage(remarks: str, field: str) -> dict:
+    """Per-kernel value of one field of the compiler's resource-usage remarks."""
     out, name = {}, None
+    pat = re.compile(re.escape(field) + r": (\d+)")
     for line in remarks.splitlines():
         m = re.search(r"Function Name: (\S+)", line)
         if m:
             name = m.group(1)
             continue
-        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        m = pat.search(line)
         if m and name:
             out[name] = int(m.group(1))
     return out
+
+
+def scratch_usage(remarks: str) -> dict:
+    """Per-kernel private (scratch) bytes per lane."""
+    return resource_usage(remarks, "ScratchSize [bytes/lane]")
+
+
+# The planner keeps this much of the CU's 160 KB of LDS free for a kernel's
+# static LDS (api.hip, kStaticLdsReserve).
+STATIC_LDS_RESERVE = 256
 
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:

@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -18,7 +19,11 @@ using namespace sg;
 namespace {
 
 constexpr size_t kCtl = 256;            // control block: status word, done counter, slot claims
-constexpr int kLdsMax = 160 * 1024;     // LDS budget of one workgroup (one per CU; 160 KB/CU)
+constexpr int kLdsCu = 160 * 1024;      // LDS of one CU (one workgroup per CU)
+// Static LDS a kernel may declare besides the planned dynamic region (the
+// chain's two flags take 16 bytes); the build refuses a kernel with more.
+constexpr int kStaticLdsReserve = 256;
+constexpr int kLdsMax = kLdsCu - kStaticLdsReserve;  // dynamic LDS budget of a plan
 constexpr size_t kMaxOperand = (size_t)1 << 31;  // buffer extents are 31-bit here
 constexpr int kWgPerXcd = 32;           // one workgroup per CU, 32 CUs per XCD
 
@@ -237,6 +242,27 @@ struct sgemm_plan_s {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The kernels assume the device they run on: a gfx950 part with 8 XCDs of 32
+// CUs each visible as one device (the grid is one workgroup per CU and the
+// per-XCD partition is indexed by the hardware XCC id).  Checked once per
+// device on its first run; another architecture or partition mode is
+// refused with SGEMM_ERR_UNSUPPORTED instead of computing the wrong columns.
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 supported, else a status
+
+static int device_check(int device) {
+  if (device < 0 || device >= kMaxDevices) return SGEMM_ERR_INVALID_ARG;
+  const int st = g_device_state[device].load(std::memory_order_acquire);
+  if (st == 1) return SGEMM_OK;
+  if (st != 0) return st;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return SGEMM_ERR_HIP;  // not cached
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                  prop.multiProcessorCount == kXcds * kWgPerXcd;
+  g_device_state[device].store(ok ? 1 : SGEMM_ERR_UNSUPPORTED, std::memory_order_release);
+  return ok ? SGEMM_OK : SGEMM_ERR_UNSUPPORTED;
+}
+
 static int validate_gemm(const sgemm_problem& p) {
   if (p.M < 1 || p.K < 8 || p.N < 1) return SGEMM_ERR_INVALID_ARG;
   if (p.K % 8 != 0) return SGEMM_ERR_INVALID_ARG;
@@ -306,6 +332,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
     }
+    if (pl->geo.part_floats * 4 >= kMaxOperand) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     layout_stage_ws(cur, pl->geo, pl->off_ctr, pl->off_part);
   } else if (p.kind == SGEMM_KIND_LAYERCHAIN) {
     if (p.flags & (SGEMM_F_W_CACHED | SGEMM_F_W_SC1 | SGEMM_F_MTILE_ITEMS)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
@@ -316,7 +343,16 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
       { delete pl; return SGEMM_ERR_INVALID_ARG; }
     if (p.d_model % 8 || p.q_cols % 8 || p.d_ff % 8) { delete pl; return SGEMM_ERR_INVALID_ARG; }
     if (p.M > 64 || p.n_layers > kMaxLayers) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
-    if ((size_t)2 * p.d_ff * p.d_model * 2 >= kMaxOperand) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    // Every operand a stage addresses through a buffer descriptor must stay
+    // below the 31-bit extent: weights, X and Y of each stage, the fp32 copy
+    // of the last output.
+    {
+      const size_t M_ = (size_t)p.M, d_ = (size_t)p.d_model, q_ = (size_t)p.q_cols, f_ = (size_t)p.d_ff;
+      const size_t ext[] = {q_ * d_ * 2, d_ * q_ * 2, 2 * f_ * d_ * 2, d_ * f_ * 2,
+                            M_ * d_ * 4, M_ * q_ * 2, M_ * 2 * f_ * 2};
+      for (size_t e : ext)
+        if (e >= kMaxOperand) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    }
     // Stages: Q [d -> q], O [q -> d], gate_up paired [d -> dff], down [dff -> d].
     // One block size and one n-tile width for the unpaired stages per launch.
     const int Ks[4] = {p.d_model, p.q_cols, p.d_model, p.d_ff};
@@ -381,6 +417,8 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
       }
     }
     if (best < 0.0) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    for (int s = 0; s < kChainStages; ++s)
+      if (pl->cg[s].part_floats * 4 >= kMaxOperand) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     // Re-layout with the final geometries.
     cur = kCtl;
     for (int s = 0; s < kChainStages; ++s) layout_stage_ws(cur, pl->cg[s], pl->c_ctr[s], pl->c_part[s]);
@@ -465,6 +503,7 @@ int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* work
   d.w_bytes = (unsigned)((size_t)p.N * p.K * 2);
   d.y_bytes = (unsigned)((size_t)p.M * p.N * (p.out_dtype == SGEMM_OUT_F32 ? 4 : 2));
   d.y2_bytes = 0;
+  if (const int dc = device_check(plan->device); dc != SGEMM_OK) return dc;
   if (hipSetDevice(plan->device) != hipSuccess) return SGEMM_ERR_HIP;
   hipError_t e = launch_gemm(d, g.mtiles > 1 ? 2 : g.path, g.ta, g.tb, plan->grid, g.waves * 64, g.lds, (unsigned*)ws,
                              (hipStream_t)stream);
@@ -533,6 +572,7 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   a.nt_q = plan->cg[0].tb; a.nt_o = plan->cg[1].tb; a.nt_d = plan->cg[3].tb;
   int lds = 0;
   for (int s = 0; s < kChainStages; ++s) lds = std::max(lds, plan->cg[s].lds);
+  if (const int dc = device_check(plan->device); dc != SGEMM_OK) return dc;
   if (hipSetDevice(plan->device) != hipSuccess) return SGEMM_ERR_HIP;
   // One launch runs every event; the per-stage ablation launches once per event.
   const int events = 4 * p.n_layers;
@@ -626,6 +666,8 @@ int sgemm_plan_describe(sgemm_plan plan, char* buf, size_t len) {
   }
   return (int)s.size() + 1;
 }
+
+int sgemm_device_check(int device) { return device_check(device); }
 
 int sgemm_topology_probe(int* xcc_out, int n_wg, void* stream) {
   if (!xcc_out || n_wg < 1 || n_wg > 65536) return SGEMM_ERR_INVALID_ARG;

@@ -97,7 +97,13 @@ static __device__ bool wait_event(const ChainArgs& a, int e, int xcd, int slot, 
 }
 
 // Publish that this workgroup finished event e.
+// The workgroup's stores are acknowledged by its XCD's L2 before its bump of
+// L[x][e] (the fence keeps the compiler from moving them below the wait); the
+// XCD's last workgroup writes that L2 back with a device-scope release before
+// it bumps G[e], so the stores of all 32 workgroups reach memory before any
+// consumer, which acquires after seeing G[e] == 8, reads them.
 static __device__ void signal_event(const ChainArgs& a, int e, int xcd, int nslots) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   wait_vm0();  // this wave's stores are acknowledged by L2
   __syncthreads();
   if (threadIdx.x == 0) {

@@ -136,6 +136,39 @@ __device__ __forceinline__ int xcd_of_wg(unsigned* status) {
   return (int)(x & 7u);
 }
 
+// Placement check of a single launch.  Workgroup (XCD x, slot w) sets bit w
+// of the XCD's claim word (control block word kClaimWord + x) when it starts
+// and, once its work is done, checks the word's old value: a bit that was
+// already set means two workgroups ran as the same (XCD, slot) pair, so some
+// other pair's columns were never computed, and the topology bit is latched in
+// the status word.  The workgroup whose claim completes its XCD's mask (all
+// nslots bits) clears the word for the next launch; at that point every claim
+// of the XCD has been performed.  A broken dispatch never completes a mask,
+// so the error repeats on every later launch until the workspace is
+// re-initialised.  The fetch-or goes out before any weight load and its
+// result is only read after the stream, so no wait is added.
+constexpr int kClaimWord = 32;  // byte 128 of the workspace control block
+
+__device__ __forceinline__ unsigned claim_slot(unsigned* ctl, int xcd, int slot) {
+  unsigned old = 0;
+  if (threadIdx.x == 0)
+    old = __hip_atomic_fetch_or(ctl + kClaimWord + xcd, slot < 32 ? 1u << slot : 0u, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+  return old;
+}
+
+__device__ __forceinline__ void settle_claim(unsigned* ctl, int xcd, int slot, int nslots, unsigned old) {
+  if (threadIdx.x == 0) {
+    const unsigned bit = slot < 32 ? 1u << slot : 0u;
+    const unsigned full = nslots >= 32 ? 0xFFFFFFFFu : (1u << nslots) - 1u;
+    if (bit == 0u || (old & bit)) {
+      __hip_atomic_fetch_or(ctl, kStatusTopology, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if ((old | bit) == full) {
+      __hip_atomic_store(ctl + kClaimWord + xcd, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Reduce-scatter over the 64 lanes of a wave: v holds V (power of two <= 64)
 // per-lane partials; afterwards lane l holds the full sum of value l/(64/V).
 // Fixed exchange pattern, so the result is bitwise reproducible.  Stage ST
@@ -176,16 +209,26 @@ constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 
 // in issue order).  The wave whose arrival is the S-th (counter old value
 // S-1) owns the tile: it resets the counter and adds the S partials in split
 // order, so the sum does not depend on which split arrived last.
-//   SYNC_XCD: all S contributors run on the same XCD, so their partials meet
-//     in one L2: wait until our stores are acknowledged (vmcnt), bump the
-//     counter; the owner reads with device-coherent (sc1) loads that skip its
-//     L1.
-//   SYNC_AGENT: device-scope release (L2 write-back) and acquire (L1/L2
-//     invalidate), valid whatever the placement.
+//   SYNC_XCD: all S contributors run on the same XCD (a tile's counter and
+//     partials are indexed by the hardware XCD id), so their partials meet in
+//     that XCD's L2.  A contributor's stores go through the write-through
+//     vector L1 to the L2; s_waitcnt vmcnt(0) returns once the L2 has
+//     acknowledged them, and only then does the counter bump go out.  The
+//     owner's bump returns S-1 only after every contributor's bump was
+//     performed, and it then reads the partials with sc1 (agent-scope)
+//     loads, which miss its own L1 and are served by the same L2.  The
+//     workgroup-scope fences emit no instruction on gfx950; they keep the
+//     compiler from moving the partial stores below the wait or the owner's
+//     loads above its bump.  This is weaker than a device-scope release
+//     (an L2 write-back, buffer_wbl2 sc1) and acquire (buffer_inv sc1), which
+//     the partials do not need because they never leave the XCD.
+//   SYNC_AGENT: device-scope release and acquire, valid whatever the
+//     placement.
 __device__ __forceinline__ void splitk_release(int sync) {
   if (sync == SYNC_AGENT) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   } else {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     wait_vm0();
   }
 }
@@ -201,7 +244,11 @@ __device__ __forceinline__ bool splitk_own(unsigned* ctr, unsigned old_lane0, in
   const bool last = old == (unsigned)(S - 1);
   if (last) {
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (sync == SYNC_AGENT) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (sync == SYNC_AGENT) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    } else {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
   }
   return last;
 }

@@ -10,16 +10,23 @@ namespace sg {
 
 typedef void (*GemmKernel)(StageDesc, unsigned*);
 
+// ctl: the workspace control block (word 0 status, claim words at kClaimWord).
 template <int M, int G, int AUX>
-__global__ __launch_bounds__(512) void k_gemm_dot2(StageDesc d, unsigned* status) {
+__global__ __launch_bounds__(512) void k_gemm_dot2(StageDesc d, unsigned* ctl) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  dot2_stage<M, G, AUX>(d, lds, xcd_of_wg(status), blockIdx.x >> 3, gridDim.x >> 3);
+  const int xcd = xcd_of_wg(ctl), slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+  const unsigned claim = claim_slot(ctl, xcd, slot);
+  dot2_stage<M, G, AUX>(d, lds, xcd, slot, nslots);
+  settle_claim(ctl, xcd, slot, nslots, claim);
 }
 
 template <int MT, int NT, int AUX, bool MTI = false>
-__global__ __launch_bounds__(512) void k_gemm_mfma(StageDesc d, unsigned* status) {
+__global__ __launch_bounds__(512) void k_gemm_mfma(StageDesc d, unsigned* ctl) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  mfma_stage<MT, NT, false, AUX, false, NoHook, MTI>(d, lds, xcd_of_wg(status), blockIdx.x >> 3, gridDim.x >> 3);
+  const int xcd = xcd_of_wg(ctl), slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+  const unsigned claim = claim_slot(ctl, xcd, slot);
+  mfma_stage<MT, NT, false, AUX, false, NoHook, MTI>(d, lds, xcd, slot, nslots);
+  settle_claim(ctl, xcd, slot, nslots, claim);
 }
 
 // dot2: M = 1..15, G in {1, 2, 3, 4, 8} with G*M <= 64.  MFMA: MT = 1..4, NT = 1, 2.

@@ -167,7 +167,10 @@ int sgemm_workspace_init(sgemm_plan plan, void* workspace, void* stream);
 /*
  * Y = X . W (kind GEMM).  X [M][K] bf16, W [N][K] bf16, Y [M][N] (fp32 or bf16
  * as planned); all device pointers, 16-byte aligned.  Enqueues one kernel on
- * `stream` and returns.
+ * `stream` and returns.  SGEMM_ERR_UNSUPPORTED when the plan's device is not
+ * a 256-CU gfx950 (sgemm_device_check).  Each launch also checks on the device
+ * that its 256 workgroups covered every (XCD, slot) pair exactly once; a
+ * violation latches SGEMM_ERR_TOPOLOGY for sgemm_query_status.
  */
 int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* workspace,
               void* stream);
@@ -214,6 +217,20 @@ const char* sgemm_status_string(int status);
  * length needed.
  */
 int sgemm_plan_describe(sgemm_plan plan, char* buf, size_t len);
+
+/*
+ * Whether `device` (a HIP ordinal) is what the kernels are built for: a gfx950
+ * device exposing 256 CUs (8 XCDs of 32, one partition), the layout the
+ * per-XCD column partition and the one-workgroup-per-CU grid assume (Fleet
+ * reading note, section 3b: 8 XCDs of 32 CUs, each with its own L2; the
+ * news item on MI355X low-latency GEMM: gfx950 with 256 CUs).  Queries the
+ * device properties once and caches the answer.  sgemm_run and
+ * layerchain_run make the same check before their first launch on a device.
+ * Returns SGEMM_OK, SGEMM_ERR_UNSUPPORTED (another architecture or partition
+ * mode), SGEMM_ERR_INVALID_ARG (device < 0 or >= 64) or SGEMM_ERR_HIP (the
+ * query failed, e.g. no such device; not cached).
+ */
+int sgemm_device_check(int device);
 
 /*
  * Topology probe: launch n_wg workgroups of one wave; workgroup i writes the

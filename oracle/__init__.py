@@ -52,6 +52,9 @@ def _load():
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_num_threads.restype = ctypes.c_int
+        f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+        lib.oracle_silu_gate.argtypes = [ctypes.c_long, f32p, f32p, u16p]
+        lib.oracle_silu_gate.restype = None
         lib.oracle_layer.argtypes = [ctypes.c_int] * 4 + [u16p] * 5 + [ctypes.c_void_p] * 5
         lib.oracle_layer.restype = None
         _lib = lib
@@ -99,6 +102,18 @@ def bf16_to_f64(bits) -> np.ndarray:
 
 def silu(v: float) -> float:
     return float(_load().oracle_silu(float(v)))
+
+
+def silu_gate(g, u) -> np.ndarray:
+    """The chain's SiLU gate on fp32 gate and up values (same shape):
+    bf16 bits of f32(silu(g) * u), silu in double."""
+    g32 = np.ascontiguousarray(g, dtype=np.float32)
+    u32 = np.ascontiguousarray(u, dtype=np.float32)
+    if g32.shape != u32.shape:
+        raise ValueError("shape mismatch")
+    out = np.empty(g32.shape, dtype=np.uint16)
+    _load().oracle_silu_gate(g32.size, g32.ravel(), u32.ravel(), out.reshape(-1))
+    return out
 
 
 def layer(x_bits, wq, wo, wgu, wdown):

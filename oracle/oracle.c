@@ -91,6 +91,13 @@ void oracle_gemm(int M, int K, int N, const uint16_t* x, const uint16_t* w,
 
 double oracle_silu(double v) { return v / (1.0 + exp(-v)); }
 
+/* The SiLU gate of the chain on fp32 gate and up values: a = bf16(f32(silu(g) * u)),
+ * silu in double (n values each). */
+void oracle_silu_gate(long n, const float* g, const float* u, uint16_t* a) {
+  for (long i = 0; i < n; ++i)
+    a[i] = oracle_bf16_from_float((float)(oracle_silu((double)g[i]) * (double)u[i]));
+}
+
 /* One decoder-layer projection sequence (see the header).  All activations are
  * bf16 bits.  x_in [M][d], h1 [M][q], h2 [M][d], a [M][dff], x_out [M][d];
  * y_f32 [M][d] receives f32(a . Wdown^T) when not NULL.  The weights are
@@ -113,9 +120,9 @@ void oracle_layer(int M, int d, int q, int dff, const uint16_t* x_in,
   oracle_gemm(M, d, 2 * dff, h2, wgu, y, NULL);
   for (int m = 0; m < M; ++m)
     for (int j = 0; j < dff; ++j) {
-      double g = (double)(float)y[(size_t)m * 2 * dff + j];
-      double u = (double)(float)y[(size_t)m * 2 * dff + dff + j];
-      a[(size_t)m * dff + j] = oracle_bf16_from_float((float)(oracle_silu(g) * u));
+      float g = (float)y[(size_t)m * 2 * dff + j];
+      float u = (float)y[(size_t)m * 2 * dff + dff + j];
+      oracle_silu_gate(1, &g, &u, &a[(size_t)m * dff + j]);
     }
 
   oracle_gemm(M, dff, d, a, wdown, y, NULL);

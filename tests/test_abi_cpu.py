@@ -61,9 +61,115 @@ def _create(**kw):
     (dict(M=32, K=1024, N=1024, flags=sg.F_MTILE_ITEMS), sg.OK),
     (dict(kind=sg.KIND_LAYERCHAIN, M=32, L=2, d=64, q=64, dff=64, flags=sg.F_MTILE_ITEMS), sg.ERR_UNSUPPORTED),
     (dict(M=64, K=12288, N=4096), sg.OK),
+    # a chain stage whose weight extent would pass 2 GiB (q_cols x d_model x 2 bytes)
+    (dict(kind=sg.KIND_LAYERCHAIN, M=4, L=1, d=32768, q=32768, dff=64), sg.ERR_UNSUPPORTED),
+    (dict(kind=sg.KIND_LAYERCHAIN, M=4, L=1, d=64, q=64, dff=1 << 24), sg.ERR_UNSUPPORTED),
 ])
 def test_plan_create_validation(kw, code):
     assert _create(**kw) == code
+
+
+def test_forced_plans_of_the_gpu_parity_cases():
+    """The forced split, K-slice and m-tile-item combinations the GPU parity
+    tests run are accepted, and the ones they leave out are refused with
+    SGEMM_ERR_UNSUPPORTED (X window or K-slice buffers past the LDS, or an
+    empty slice), not silently replanned."""
+    from helpers import KSL_CASES, KSL_REFUSED, MTI_CASES, MTI_REFUSED, SPLITK_SHAPES
+
+    for M, K, N in SPLITK_SHAPES:
+        for s in (2, 5, 11):
+            assert sg.Gemm(M, K, N, splitk=s).describe()["stage"]["S"] > 1
+    for M, K, N, ksl, s in KSL_CASES:
+        assert sg.Gemm(M, K, N, kslices=ksl, splitk=s).describe()["stage"]["ksl"] == ksl
+    for M, K, N, s in MTI_CASES:
+        assert sg.Gemm(M, K, N, flags=sg.F_MTILE_ITEMS, splitk=s).describe()["stage"]["mtiles"] == -(-M // 16)
+    for M, K, N, ksl, s in KSL_REFUSED:
+        assert _create(M=M, K=K, N=N, ksl=ksl, splitk=s) == sg.ERR_UNSUPPORTED
+    for M, K, N, s in MTI_REFUSED:
+        assert _create(M=M, K=K, N=N, flags=sg.F_MTILE_ITEMS, splitk=s) == sg.ERR_UNSUPPORTED
+
+
+# Static LDS a kernel may declare next to its planned dynamic region (the
+# build refuses a kernel that declares more).
+STATIC_LDS_RESERVE = 256
+
+
+@pytest.mark.parametrize("d,q,dff", [(4096, 4096, 12288), (5120, 5120, 13824), (4096, 4096, 14336)])
+@pytest.mark.parametrize("flags", [0, sg.F_SCHEDULER])
+def test_chain_lds_fits_next_to_static_lds(d, q, dff, flags):
+    """Every chain plan for M = 1..64 keeps its dynamic LDS within 160 KB minus
+    the static-LDS reserve, so dynamic plus the kernel's own static LDS fits
+    a CU."""
+    for M in range(1, 65):
+        for st in sg.LayerChain(M, 2, d, q, dff, flags=flags).describe()["stages"]:
+            assert st["lds"] + STATIC_LDS_RESERVE <= 160 * 1024, (M, st)
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 33, 44, 52, 64])
+def test_gemm_lds_fits_next_to_static_lds(M):
+    for K, N in ((4096, 6144), (4096, 24576), (12288, 4096), (7168, 1536), (5120, 13824)):
+        st = sg.Gemm(M, K, N).describe()["stage"]
+        assert st["lds"] + STATIC_LDS_RESERVE <= 160 * 1024, (M, K, N, st)
+
+
+def test_build_refuses_kernels_with_more_static_lds():
+    from chiplet_aware_persistent_amd import build
+
+    assert build.STATIC_LDS_RESERVE == STATIC_LDS_RESERVE
+    remarks = ("x.hip:1:1: remark: Function Name: _Z1kv [-Rpass-analysis=kernel-resource-usage]\n"
+               "x.hip:1:1: remark:     LDS Size [bytes/block]: 16 [-Rpass-analysis=kernel-resource-usage]\n"
+               "x.hip:1:1: remark: Function Name: _Z1jv [-Rpass-analysis=kernel-resource-usage]\n"
+               "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 8 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert build.resource_usage(remarks, "LDS Size [bytes/block]") == {"_Z1kv": 16}
+    assert build.scratch_usage(remarks) == {"_Z1jv": 8}
+
+
+def test_device_check_without_a_device():
+    """sgemm_device_check: a bad ordinal is an argument error; here no device
+    can be queried (the call fails cleanly, nothing is cached); a run on a
+    plan fails the same way before launching."""
+    assert sg.sgemm_device_check(-1) == sg.ERR_INVALID_ARG
+    assert sg.sgemm_device_check(64) == sg.ERR_INVALID_ARG
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except ImportError:
+        has_gpu = False
+    if not has_gpu:
+        assert sg.sgemm_device_check(0) == sg.ERR_HIP
+        g = sg.Gemm(4, 256, 128)
+        assert sg.sgemm_run(g.handle, 16, 16, 16, 16) == sg.ERR_HIP
+
+
+def test_binding_rejects_mismatched_tensors():
+    torch = pytest.importorskip("torch")
+    g = sg.Gemm(4, 256, 128)
+    X = torch.zeros((4, 256), dtype=torch.bfloat16)
+    W = torch.zeros((128, 256), dtype=torch.bfloat16)
+    Y = torch.zeros((4, 128), dtype=torch.float32)
+    ws = torch.zeros(g.workspace_bytes, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        g(X, W, Y, ws[:-1])
+    with pytest.raises(ValueError):
+        g(X.float(), W, Y, ws)
+    with pytest.raises(ValueError):
+        g(X, W.t().contiguous().t(), Y, ws)
+    with pytest.raises(ValueError):
+        g(X, W, Y.to(torch.bfloat16), ws)
+    ch = sg.LayerChain(2, 1, 64, 64, 64)
+    Wq, Wo = torch.zeros((64, 64), dtype=torch.bfloat16), torch.zeros((64, 64), dtype=torch.bfloat16)
+    Wgu, Wd = torch.zeros((128, 64), dtype=torch.bfloat16), torch.zeros((64, 64), dtype=torch.bfloat16)
+    X0 = torch.zeros((2, 64), dtype=torch.bfloat16)
+    Yf = torch.zeros((2, 64), dtype=torch.float32)
+    cws = torch.zeros(ch.workspace_bytes, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        ch(X0, [Wq], [Wo], [Wgu], [Wd], Yf, cws, Y_bf16=torch.zeros((2, 64), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        ch(X0, [Wq], [Wo], [Wgu], [Wd], Yf, cws[:16])
+    with pytest.raises(ValueError):
+        ch(torch.zeros((2, 128), dtype=torch.bfloat16)[:, ::2], [Wq], [Wo], [Wgu], [Wd], Yf, cws)
+    with pytest.raises(ValueError):
+        ch(X0, [Wq, Wq], [Wo], [Wgu], [Wd], Yf, cws)
 
 
 def test_null_and_misaligned_arguments_rejected_before_launch():

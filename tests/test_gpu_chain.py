@@ -19,7 +19,7 @@ import pytest
 import chiplet_aware_persistent_amd as sg
 import oracle
 import synth
-from helpers import device_tensor_bf16, host_bits
+from helpers import device_tensor_bf16, host_bits, report
 
 pytestmark = pytest.mark.gpu
 
@@ -248,107 +248,130 @@ def test_chain_watchdog_times_out_and_workspace_recovers(cuda_device, mode):
     check_chain(good, ws, x0, layers, Y, Yb, M)
 
 
-@pytest.mark.parametrize("M", [64, 1])
-def test_chain_36_layers_full_size_every_stage_sampled(cuda_device, M):
-    """The benchmarked 36-layer chain: M = 64 (MFMA stages) and M = 1 (dot2
-    stages), d = q = 4096, d_ff = 12288,
-    distinct seeded weights per layer (drawn on the GPU, 13.3 GB), one launch in
-    the bench's plan.  Every one of the 144 stages is checked against the oracle
-    on sampled output columns, each with the GPU's own input to that stage (the
-    weight rows of the sampled columns are regenerated on the host from the same
-    counter-based generator), so the stated per-element bound applies as is.
-    The configured distributions make the activations collapse towards zero
-    within a few layers (bf16 keeps them representable for a while); the later
-    stages are still checked, against near-zero references."""
-    L, d, q, dff = 36, 4096, 4096, 12288
-    seeds = [[synth.seed_for(5, l, t) for t in (synth.T_WQ, synth.T_WO, synth.T_WGU, synth.T_WDOWN)]
+def _full_width_weights(L, dev, variant=0):
+    """The 36-layer chain's weights (d = q = 4096, d_ff = 12288), drawn on the
+    device by the counter-based generator, distinct per layer."""
+    d, q, dff = 4096, 4096, 12288
+    seeds = [[synth.seed_for(5, l, t, variant) for t in (synth.T_WQ, synth.T_WO, synth.T_WGU, synth.T_WDOWN)]
              for l in range(L)]
     shapes = [(q, d), (d, q), (2 * dff, d), (d, dff)]
-    dl = [[synth.uniform_bf16_torch(seeds[l][i], shapes[i][0], shapes[i][1], synth.weight_scale(shapes[i][1]),
-                                    cuda_device) for i in range(4)] for l in range(L)]
+    dl = [[synth.uniform_bf16_torch(seeds[l][i], shapes[i][0], shapes[i][1], synth.weight_scale(shapes[i][1]), dev)
+           for i in range(4)] for l in range(L)]
+    return seeds, shapes, dl
+
+
+def _host_layer(dl, seeds, shapes, l, scale_down=None):
+    """Host copies of layer l's weights; each tensor's first, middle and last
+    rows are checked against the host generator (down rows after dividing out
+    a power-of-two gain, which is exact)."""
+    out = []
+    for i in range(4):
+        w = host_bits(dl[l][i])
+        rows = np.array([0, w.shape[0] // 2, w.shape[0] - 1], dtype=np.int64)
+        ref = synth.uniform_bf16_rows(seeds[l][i], shapes[i][1], synth.weight_scale(shapes[i][1]), rows)
+        got = w[rows]
+        if i == 3 and scale_down is not None:
+            got = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(got) / np.float32(scale_down[l]))
+        assert np.array_equal(got, ref), (l, i)
+        out.append(w)
+    return out
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("M", [64, 1])
+def test_chain_36_layers_full_size_every_stage(cuda_device, M):
+    """The benchmarked 36-layer chain: M = 64 (MFMA stages) and M = 1 (dot2
+    stages), d = q = 4096, d_ff = 12288, distinct seeded weights per layer
+    (13.3 GB), one launch in the bench's plan.  Every output element of every
+    one of the 144 stages is compared with the oracle evaluated on the GPU's own
+    input to that stage, with the stated per-element bound.  The configured
+    distributions make the activations collapse towards zero within a few
+    layers, so from there on this checks near-zero outputs against near-zero
+    references; the gain-normalised test below keeps them of order one."""
+    L, d, q, dff = 36, 4096, 4096, 12288
+    seeds, shapes, dl = _full_width_weights(L, cuda_device)
     x0 = synth.normal_bf16(synth.seed_for(5, 0, synth.T_X), M, d)
     ch = sg.LayerChain(M, L, d, q, dff)
     rc, Y, Yb, ws = run_chain(ch, device_tensor_bf16(x0, cuda_device), dl)
     assert rc == sg.OK, sg.status_string(rc)
-
-    def rows(l, i, ids):
-        return synth.uniform_bf16_rows(seeds[l][i], shapes[i][1], synth.weight_scale(shapes[i][1]), ids)
-
-    def check_stage(x_in, w_rows, got, what):
-        y_ref, absdot = oracle.gemm(x_in, w_rows)
-        b = oracle.bound(absdot, y_ref=y_ref, bf16_out=True)
-        err = np.abs(f64(got) - y_ref)
-        assert np.all(err <= b), (what, float(np.max(err / b)))
-        return y_ref, absdot
-
-    cq, cd = sampled_cols(q, 1), sampled_cols(d, 2)
-    cf = sampled_cols(dff, 3)
-    x_in = x0
-    rms = []
-    for l in range(L):
-        got = [host_bits(ch.activation(ws, l, w)) for w in range(4)]
-        check_stage(x_in, rows(l, 0, cq), got[0][:, cq], (l, "h1"))
-        check_stage(got[0], rows(l, 1, cd), got[1][:, cd], (l, "h2"))
-        g_ref, g_abs = oracle.gemm(got[1], rows(l, 2, cf))
-        u_ref, u_abs = oracle.gemm(got[1], rows(l, 2, cf + dff))
-        g32, u32 = g_ref.astype(np.float32), u_ref.astype(np.float32)
-        a_ref = oracle.bf16_from_f32(np.array([[oracle.silu(float(g32[i, j])) * float(u32[i, j])
-                                                for j in range(len(cf))] for i in range(M)], np.float32))
-        bg, bu = oracle.bound(g_abs), oracle.bound(u_abs)
-        g64, u64, a64 = g32.astype(np.float64), u32.astype(np.float64), f64(a_ref)
-        ba = (1.1 * bg * (np.abs(u64) + bu) + (np.abs(g64 * special.expit(g64)) + 1.1 * bg) * bu
-              + 2.0 ** -20 * np.abs(a64) + oracle.bf16_ulp(a64))
-        err = np.abs(f64(got[2][:, cf]) - a64)
-        assert np.all(err <= ba), (l, "a", float(np.max(err / ba)))
-        y_ref, y_abs = check_stage(got[2], rows(l, 3, cd), got[3][:, cd], (l, "x_out"))
-        if l == L - 1:
-            b = oracle.bound(y_abs)
-            assert np.all(np.abs(Y.cpu().numpy()[:, cd].astype(np.float64) - y_ref) <= b)
-            assert np.array_equal(host_bits(Yb), got[3])
-        rms.append(float(np.sqrt(np.mean(f64(got[3]) ** 2))))
-        x_in = got[3]
+    rms, worst = check_chain_own_inputs(ch, ws, x0, lambda l: _host_layer(dl, seeds, shapes, l), Y, Yb,
+                                        name="chain36 m%d as configured" % M)
     assert all(math.isfinite(r) for r in rms)
     print("per-layer RMS of x':", ["%.3g" % r for r in rms])
 
 
-def sampled_cols(n, seed):
-    from helpers import sampled_columns
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("M", [64, 1])
+def test_chain_36_layers_full_width_gain_normalised(cuda_device, M):
+    """The same 36-layer shapes with activations kept of order one: the down
+    weights of layer l are scaled by the power of two 2^round(-log2 rms) of the
+    GPU's own x' of layer l, fixed one layer at a time (a power-of-two scale of
+    layer l's down weights scales exactly that layer's output and leaves the
+    earlier layers alone; the chain is bitwise deterministic).  Every output
+    element of all 144 stages is then compared with the oracle on the GPU's own
+    input to each stage."""
+    L, d, q, dff = 36, 4096, 4096, 12288
+    seeds, shapes, dl = _full_width_weights(L, cuda_device, variant=1)
+    x0 = synth.normal_bf16(synth.seed_for(5, 0, synth.T_X, 1), M, d)
+    X0 = device_tensor_bf16(x0, cuda_device)
+    ch = sg.LayerChain(M, L, d, q, dff)
+    ws = ch.new_workspace()
+    scale = []
+    for l in range(L):
+        rc, _, _, ws = run_chain(ch, X0, dl, ws)
+        assert rc == sg.OK, sg.status_string(rc)
+        xo = f64(host_bits(ch.activation(ws, l, 3)))
+        s = int(round(-math.log2(float(np.sqrt(np.mean(xo ** 2))))))
+        before = dl[l][3].clone()
+        dl[l][3].mul_(2.0 ** s)
+        assert torch.equal(dl[l][3].float() / 2.0 ** s, before.float())   # exact power-of-two scaling
+        scale.append(2.0 ** s)
+    rc, Y, Yb, ws = run_chain(ch, X0, dl, ws)
+    assert rc == sg.OK, sg.status_string(rc)
+    rms, worst = check_chain_own_inputs(ch, ws, x0, lambda l: _host_layer(dl, seeds, shapes, l, scale), Y, Yb,
+                                        name="chain36 m%d gain-normalised" % M)
+    assert all(0.25 < r < 4.0 for r in rms), rms
 
-    return sampled_columns(n, 40, seed=seed)
 
-
-def check_chain_own_inputs(ch, ws, x0, layers, Y, Yb):
+def check_chain_own_inputs(ch, ws, x0, layer_w, Y, Yb, name=None):
     """Every stage of every layer against the oracle evaluated on the GPU's own
     input to that stage (all output columns), with the stated per-element
-    bound; returns the per-layer RMS of the GPU's x'."""
+    bound.  layer_w(l) gives layer l's host weights (wq, wo, wgu, wdown).
+    Returns the per-layer RMS of the GPU's x' and the worst |delta|/bound per
+    stage."""
     dff = ch.dff
     x_in, rms = x0, []
-    for l, (wq, wo, wgu, wdown) in enumerate(layers):
+    worst = {"h1": 0.0, "h2": 0.0, "a": 0.0, "x_out": 0.0, "y_f32": 0.0}
+
+    def take(key, err, b, l):
+        r = float(np.max(err / b))
+        assert r <= 1.0, (l, key, r)
+        worst[key] = max(worst[key], r)
+
+    for l in range(ch.n_layers):
+        wq, wo, wgu, wdown = layer_w(l)
         got = [host_bits(ch.activation(ws, l, w)) for w in range(4)]
-        for src, w, out, name in ((x_in, wq, got[0], "h1"), (got[0], wo, got[1], "h2")):
+        for src, w, out, key in ((x_in, wq, got[0], "h1"), (got[0], wo, got[1], "h2")):
             y_ref, absdot = oracle.gemm(src, w)
-            b = oracle.bound(absdot, y_ref=y_ref, bf16_out=True)
-            err = np.abs(f64(out) - y_ref)
-            assert np.all(err <= b), (l, name, float(np.max(err / b)))
+            take(key, np.abs(f64(out) - y_ref), oracle.bound(absdot, y_ref=y_ref, bf16_out=True), l)
         gu_ref, gu_abs = oracle.gemm(got[1], wgu)
         g32, u32 = gu_ref[:, :dff].astype(np.float32), gu_ref[:, dff:].astype(np.float32)
-        silu = np.vectorize(oracle.silu, otypes=[np.float64])
-        a64 = f64(oracle.bf16_from_f32((silu(g32) * u32.astype(np.float64)).astype(np.float32)))
+        a64 = f64(oracle.silu_gate(g32, u32))
         bg, bu = oracle.bound(gu_abs[:, :dff]), oracle.bound(gu_abs[:, dff:])
         g64, u64 = g32.astype(np.float64), u32.astype(np.float64)
         ba = (1.1 * bg * (np.abs(u64) + bu) + (np.abs(g64 * special.expit(g64)) + 1.1 * bg) * bu
               + 2.0 ** -20 * np.abs(a64) + oracle.bf16_ulp(a64))
-        err = np.abs(f64(got[2]) - a64)
-        assert np.all(err <= ba), (l, "a", float(np.max(err / ba)))
+        take("a", np.abs(f64(got[2]) - a64), ba, l)
         y_ref, y_abs = oracle.gemm(got[2], wdown)
-        b = oracle.bound(y_abs, y_ref=y_ref, bf16_out=True)
-        assert np.all(np.abs(f64(got[3]) - y_ref) <= b), (l, "x_out")
-        if l == len(layers) - 1:
-            assert np.all(np.abs(Y.cpu().numpy().astype(np.float64) - y_ref) <= oracle.bound(y_abs))
+        take("x_out", np.abs(f64(got[3]) - y_ref), oracle.bound(y_abs, y_ref=y_ref, bf16_out=True), l)
+        if l == ch.n_layers - 1:
+            take("y_f32", np.abs(Y.cpu().numpy().astype(np.float64) - y_ref), oracle.bound(y_abs), l)
             assert np.array_equal(host_bits(Yb), got[3])
         rms.append(float(np.sqrt(np.mean(f64(got[3]) ** 2))))
         x_in = got[3]
-    return rms
+    if name:
+        report(name, max(worst.values()), per_stage=worst)
+    return rms, worst
 
 
 @pytest.mark.parametrize("M", [16, 64, 1])
@@ -386,5 +409,6 @@ def test_chain_gain_normalised_36_layers(cuda_device, M):
         dl[l][3] = device_tensor_bf16(layers[l][3], cuda_device)
     rc, Y, Yb, ws = run_chain(ch, X0, dl, ws)
     assert rc == sg.OK, sg.status_string(rc)
-    rms = check_chain_own_inputs(ch, ws, x0, layers, Y, Yb)
+    rms, _ = check_chain_own_inputs(ch, ws, x0, lambda l: layers[l], Y, Yb,
+                                    name="chain36 m%d d512 gain-normalised" % M)
     assert all(0.25 < r < 4.0 for r in rms), rms     # non-vanishing through all 36 layers

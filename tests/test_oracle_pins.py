@@ -183,6 +183,34 @@ def test_silu_identities():
     assert 0 > oracle.silu(-50.0) > -1e-19
 
 
+def test_silu_gate_array_matches_closed_forms():
+    """The array form of the chain's SiLU gate: zero gate or zero up gives 0,
+    silu(g) -> g for large g (so a = bf16(g u)), the odd-part identity
+    silu(g) - silu(-g) = g on paired inputs, and agreement with
+    g * expit(g) * u rounded through fp32 to bf16 (within one bf16 ulp, the
+    rounding-order difference)."""
+    special = pytest.importorskip("scipy.special")
+    g = np.array([0.0, 0.0, 3.0, 40.0, 60.0, -60.0, 1.5], np.float32)
+    u = np.array([5.0, -2.0, 0.0, 0.5, -3.0, 7.0, 1.0], np.float32)
+    a = synth.bf16_bits_to_f32(oracle.silu_gate(g, u)).astype(np.float64)
+    assert a[0] == 0.0 and a[1] == 0.0 and a[2] == 0.0
+    assert a[3] == 20.0 and a[4] == -180.0
+    tiny = -60.0 * math.exp(-60.0) / (1.0 + math.exp(-60.0)) * 7.0   # silu(-60) * 7, about -3.7e-24
+    assert abs(a[5] - tiny) <= oracle.bf16_ulp(tiny)
+    rng = np.random.default_rng(5)
+    gg = rng.normal(size=(7, 33)).astype(np.float32)
+    uu = rng.normal(size=(7, 33)).astype(np.float32)
+    got = synth.bf16_bits_to_f32(oracle.silu_gate(gg, uu)).astype(np.float64)
+    ones = np.ones_like(gg)
+    pos = synth.bf16_bits_to_f32(oracle.silu_gate(gg, ones)).astype(np.float64)
+    neg = synth.bf16_bits_to_f32(oracle.silu_gate(-gg, ones)).astype(np.float64)
+    assert np.all(np.abs(pos - neg - gg) <= oracle.bf16_ulp(pos) + oracle.bf16_ulp(neg))
+    g64 = gg.astype(np.float64)
+    ref = synth.bf16_bits_to_f32(_bits(g64 * special.expit(g64) * uu.astype(np.float64))).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= oracle.bf16_ulp(ref))
+    assert np.mean(got == ref) > 0.95
+
+
 # ------------------------------------------------------------------- chain
 def _bits(v):
     return synth.f32_to_bf16_bits(np.asarray(v, np.float32))
