@@ -36,6 +36,8 @@ F_POLL_LEADER = 1 << 8
 F_MTILE_ITEMS = 1 << 9
 F_LAUNCH_PER_STAGE = 1 << 10
 F_SCHEDULER = 1 << 11
+F_CHECK_PLACEMENT = 1 << 12
+F_KCHUNK = 1 << 13
 
 
 class SgemmError(RuntimeError):

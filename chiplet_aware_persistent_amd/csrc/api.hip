@@ -42,6 +42,7 @@ struct Geo {
   int ring = 0;    // ring depth (k-steps in flight per wave)
   int mtiles = 1;  // m-tile items (ablation): items per (split, column block), m-tile fastest
   int slots = 32;  // workgroups per XCD that share the items (31 with a scheduler workgroup)
+  int xbuf = 0;    // K-chunked path: bytes of one X chunk buffer
   size_t ctr_count = 0, part_floats = 0;
   double est_us = 0.0;
 };
@@ -222,6 +223,79 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
   return found;
 }
 
+// K-chunked MFMA path (kc_device.h): all eight waves of a workgroup work on
+// one item of NTW 16-column tiles over a K split, walking it in 512-wide K
+// chunks double-buffered through LDS.  Fill g for (MT, NTW, paired, S); false
+// when it does not fit.
+constexpr int kKcChunkK = 512;  // K values per chunk (8 waves x one 64-wide k-step)
+
+int kc_ring(int ntw) { return ntw >= 6 ? 1 : (ntw >= 4 ? 2 : 4); }
+
+bool kc_geo(Geo& g, int want_S, const Cost& cost) {
+  const int MT = g.ta, NTW = g.tb;
+  if (g.paired && NTW % 2) return false;
+  const int NP = g.paired ? NTW / 2 : NTW;
+  const int ring = kc_ring(NTW);
+  g.waves = 8; g.wpi = 8; g.ng = 1; g.ksl = 1;
+  g.TN = 16;
+  g.CB = NP * 16;
+  g.Nx = (int)round_up((size_t)ceil_div(g.N, kXcds), 16);
+  g.NB = ceil_div(g.Nx, g.CB);
+  // Splits: whole chunk groups (the chunk count of an item is a multiple of
+  // the ring depth, so refills of the last steps fall into the next item).
+  g.KS = (int)round_up((size_t)ceil_div(g.K, want_S), (size_t)kKcChunkK * ring);
+  g.S = ceil_div(g.K, g.KS);
+  g.kss = g.KS;
+  g.steps = g.KS / kKcChunkK;  // chunks per item
+  g.ring = ring;
+  g.items = g.NB * g.S;
+  g.mtiles = 1;
+  const int rows = std::min(16 * MT, g.M + 1);
+  g.win = kKcChunkK;
+  g.xrow = kKcChunkK + 8;
+  g.xbuf = (int)round_up((size_t)rows * g.xrow * 2, 1024);
+  const int red = 4 * NTW * MT * 1024;  // first round of the eight-wave tree
+  g.lds = std::max(2 * g.xbuf, red);
+  g.red_off = g.lds; g.stash_off = g.lds; g.stash_cap = 0;
+  if (g.lds > kLdsMax) return false;
+  g.ctr_count = (size_t)kXcds * g.NB;
+  g.part_floats = g.S > 1 ? g.ctr_count * (size_t)g.S * NTW * MT * 256 : 0;
+  // Cost (microseconds): a workgroup's weight bytes at its share of HBM, or
+  // its weight plus X bytes at the CU's L2 read rate if that is longer; per
+  // item the reduction, the first chunk's X and the ring drain; per chunk a
+  // workgroup barrier; for S > 1 the partials' round trip and the finalize.
+  const double wg_items = ceil_div(g.items, g.slots);
+  const double w_bytes = wg_items * NTW * 16.0 * g.steps * kKcChunkK * 2.0;
+  const double x_bytes = wg_items * rows * g.steps * (double)kKcChunkK * 2.0;
+  const double p_bytes = g.S > 1 ? wg_items * NTW * MT * 1024.0 * 2.0 : 0.0;
+  const double bw_cu = 8.0e12 * 0.85 / 256.0;
+  const double cu_rd = 110.0e9;
+  g.est_us = std::max(w_bytes / bw_cu, (w_bytes + x_bytes + p_bytes) / cu_rd) * 1e6 +
+             wg_items * (1.5 + rows * kKcChunkK * 2.0 / cost.x_bw * 1e6) + wg_items * g.steps * 0.05 +
+             (g.S > 1 ? cost.split_us + cost.fin_us_kb * g.S * NTW * MT : 0.0);
+  return true;
+}
+
+bool plan_kc(Geo& best, int M, int K, int N, int paired, int ntw_o, int s_o, const Cost& cost,
+             int slots = kWgPerXcd) {
+  bool found = false;
+  const int MT = (M + 15) / 16;
+  for (int ntw = 2; ntw <= 8; ntw += 2) {
+    if (ntw_o && ntw != ntw_o) continue;
+    if (ntw == 8 && MT > 2) continue;
+    const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : 16;
+    for (int s = s_lo; s <= s_hi; ++s) {
+      Geo c;
+      c.path = 3; c.M = M; c.K = K; c.N = N; c.ta = MT; c.tb = ntw; c.paired = paired; c.slots = slots;
+      if (!kc_geo(c, s, cost)) continue;
+      if (c.S != s && !s_o) continue;
+      if (!paired && !gemm_variant_exists(3, c.ta, c.tb)) continue;
+      if (!found || c.est_us < best.est_us - 1e-9) { best = c; found = true; }
+    }
+  }
+  return found;
+}
+
 }  // namespace
 
 struct sgemm_plan_s {
@@ -325,17 +399,35 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     int rc = validate_gemm(p);
     if (rc != SGEMM_OK) { delete pl; return rc; }
     const bool mti = (p.flags & SGEMM_F_MTILE_ITEMS) != 0;
-    if (mti && (p.flags & SGEMM_F_FORCE_DOT2)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+    const bool kc = (p.flags & SGEMM_F_KCHUNK) != 0;
+    if ((mti || kc) && (p.flags & SGEMM_F_FORCE_DOT2)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+    if (mti && kc) { delete pl; return SGEMM_ERR_INVALID_ARG; }
     const int path = mti ? 1 : choose_path(p);
-    if ((path == 0 || mti) && k_o > 1) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
-    if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, kCostGemm, 0, mti)) {
+    if ((path == 0 || mti || kc) && k_o > 1) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    if (kc) {
+      // tn (a multiple of 16) gives the tiles per item.
+      if (tn_o % 16 || w_o == 4) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+      if (!plan_kc(pl->geo, p.M, p.K, p.N, 0, tn_o / 16, s_o, kCostGemm)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    } else if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, kCostGemm, 0, mti)) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
+    } else if (path == 1 && !mti && !tn_o && !s_o && !w_o && !k_o && p.K >= 6144) {
+      // Long K with a wide output: the K-chunked path takes one item of six
+      // tiles over all of K per workgroup and needs no split-K, where the
+      // windowed MFMA path has to split K seven ways (16 x 7168 x 18432:
+      // 45.0 against 50.1 us, measured; elsewhere it measured no faster).
+      Geo kcg;
+      if (plan_kc(kcg, p.M, p.K, p.N, 0, 6, 1, kCostGemm) && kcg.items <= kWgPerXcd &&
+          kcg.items * 4 >= kWgPerXcd * 3 && pl->geo.S > 2)
+        pl->geo = kcg;
     }
     if (pl->geo.part_floats * 4 >= kMaxOperand) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     layout_stage_ws(cur, pl->geo, pl->off_ctr, pl->off_part);
   } else if (p.kind == SGEMM_KIND_LAYERCHAIN) {
-    if (p.flags & (SGEMM_F_W_CACHED | SGEMM_F_W_SC1 | SGEMM_F_MTILE_ITEMS)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    if (p.flags & (SGEMM_F_W_CACHED | SGEMM_F_W_SC1 | SGEMM_F_MTILE_ITEMS | SGEMM_F_CHECK_PLACEMENT)) {
+      delete pl;
+      return SGEMM_ERR_UNSUPPORTED;
+    }
     const bool sched = (p.flags & SGEMM_F_SCHEDULER) != 0;
     if (sched && (p.flags & (SGEMM_F_SYNC_FLAT | SGEMM_F_POLL_LEADER))) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     const int slots = sched ? kWgPerXcd - 1 : kWgPerXcd;  // the scheduler workgroup takes no items
@@ -475,6 +567,7 @@ static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
   d.pair_off = g.pair_off;
   d.mtiles = g.mtiles;
   d.interleave = g.mtiles > 1 ? 1 : 0;
+  d.xbuf = g.xbuf;
   d.w_aux = w_aux;
   d.sync = sync;
   return d;
@@ -496,6 +589,7 @@ int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* work
   d.ldx = p.K;
   d.ldy = p.N;
   d.mode = p.out_dtype == SGEMM_OUT_F32 ? OUT_F32 : OUT_BF16;
+  d.check = (p.flags & SGEMM_F_CHECK_PLACEMENT) ? 1 : 0;
   d.part = (float*)(ws + plan->off_part);
   d.part_bytes = (unsigned)(g.part_floats * 4);
   d.ctr = (unsigned*)(ws + plan->off_ctr);
@@ -636,9 +730,10 @@ static std::string geo_json(const Geo& g) {
                 "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,\"wpi\":%d,"
                 "\"ksl\":%d,\"kss\":%d,\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,"
                 "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
-                "\"ring\":%d,\"mtiles\":%d,\"slots\":%d,\"est_us\":%.3f}",
-                g.path == 0 ? "dot2" : "mfma", g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
-                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles, g.slots, g.est_us);
+                "\"ring\":%d,\"mtiles\":%d,\"slots\":%d,\"xbuf\":%d,\"est_us\":%.3f}",
+                g.path == 0 ? "dot2" : (g.path == 3 ? "kc" : "mfma"), g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
+                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles, g.slots,
+                g.xbuf, g.est_us);
   return b;
 }
 

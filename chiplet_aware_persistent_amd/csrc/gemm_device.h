@@ -136,31 +136,27 @@ __device__ __forceinline__ int xcd_of_wg(unsigned* status) {
   return (int)(x & 7u);
 }
 
-// Placement check of a single launch.  Workgroup (XCD x, slot w) sets bit w
-// of the XCD's claim word (control block word kClaimWord + x) when it starts
-// and, once its work is done, checks the word's old value: a bit that was
-// already set means two workgroups ran as the same (XCD, slot) pair, so some
-// other pair's columns were never computed, and the topology bit is latched in
-// the status word.  The workgroup whose claim completes its XCD's mask (all
+// Placement check of a single launch.  Once its work is done, workgroup (XCD
+// x, slot w) sets bit w of the XCD's claim word (control block word
+// kClaimWord + x) and looks at the word's old value: a bit that was already
+// set means two workgroups ran as the same (XCD, slot) pair, so some other
+// pair's columns were never computed, and the topology bit is latched in the
+// status word.  The workgroup whose claim completes its XCD's mask (all
 // nslots bits) clears the word for the next launch; at that point every claim
 // of the XCD has been performed.  A broken dispatch never completes a mask,
 // so the error repeats on every later launch until the workspace is
-// re-initialised.  The fetch-or goes out before any weight load and its
-// result is only read after the stream, so no wait is added.
+// re-initialised.  The claim goes out after the workgroup's last stores.  Its
+// device-scope round trip still ends the workgroup 1.5-3 us later on MI355X
+// (measured on the M = 1 decode projections), so the check is a plan option
+// (SGEMM_F_CHECK_PLACEMENT).
 constexpr int kClaimWord = 32;  // byte 128 of the workspace control block
 
-__device__ __forceinline__ unsigned claim_slot(unsigned* ctl, int xcd, int slot) {
-  unsigned old = 0;
-  if (threadIdx.x == 0)
-    old = __hip_atomic_fetch_or(ctl + kClaimWord + xcd, slot < 32 ? 1u << slot : 0u, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-  return old;
-}
-
-__device__ __forceinline__ void settle_claim(unsigned* ctl, int xcd, int slot, int nslots, unsigned old) {
+__device__ __forceinline__ void claim_and_check(unsigned* ctl, int xcd, int slot, int nslots) {
   if (threadIdx.x == 0) {
     const unsigned bit = slot < 32 ? 1u << slot : 0u;
     const unsigned full = nslots >= 32 ? 0xFFFFFFFFu : (1u << nslots) - 1u;
+    const unsigned old =
+        __hip_atomic_fetch_or(ctl + kClaimWord + xcd, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (bit == 0u || (old & bit)) {
       __hip_atomic_fetch_or(ctl, kStatusTopology, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else if ((old | bit) == full) {

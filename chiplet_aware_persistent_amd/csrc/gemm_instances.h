@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "gemm_device.h"
+#include "kc_device.h"
 
 namespace sg {
 
@@ -15,18 +16,51 @@ template <int M, int G, int AUX>
 __global__ __launch_bounds__(512) void k_gemm_dot2(StageDesc d, unsigned* ctl) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int xcd = xcd_of_wg(ctl), slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
-  const unsigned claim = claim_slot(ctl, xcd, slot);
   dot2_stage<M, G, AUX>(d, lds, xcd, slot, nslots);
-  settle_claim(ctl, xcd, slot, nslots, claim);
+  if (d.check) claim_and_check(ctl, xcd, slot, nslots);
 }
 
 template <int MT, int NT, int AUX, bool MTI = false>
 __global__ __launch_bounds__(512) void k_gemm_mfma(StageDesc d, unsigned* ctl) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int xcd = xcd_of_wg(ctl), slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
-  const unsigned claim = claim_slot(ctl, xcd, slot);
   mfma_stage<MT, NT, false, AUX, false, NoHook, MTI>(d, lds, xcd, slot, nslots);
-  settle_claim(ctl, xcd, slot, nslots, claim);
+  if (d.check) claim_and_check(ctl, xcd, slot, nslots);
+}
+
+template <int MT, int NTW, int AUX>
+__global__ __launch_bounds__(512) void k_gemm_kc(StageDesc d, unsigned* ctl) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int xcd = xcd_of_wg(ctl), slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+  mfma_kc_stage<MT, NTW, false, AUX>(d, lds, xcd, slot, nslots);
+  if (d.check) claim_and_check(ctl, xcd, slot, nslots);
+}
+
+// K-chunked MFMA path (path 3): MT = 1..4 m-tiles, NTW = 2, 4, 6 or 8 tiles per
+// item (8 only up to two m-tiles: its accumulators and loads would not fit
+// the registers next to four).  Weights nt only.
+inline bool kc_variant_ok(int mt, int ntw) {
+  return mt >= 1 && mt <= 4 && (ntw == 2 || ntw == 4 || ntw == 6 || (ntw == 8 && mt <= 2));
+}
+
+template <int AUX>
+GemmKernel gemm_kernel_kc(int a, int b) {
+  if constexpr (AUX != kAuxNt) {
+    return nullptr;
+  } else {
+#define SG_KC(mt)                                               \
+  case mt:                                                      \
+    if (b == 2) return k_gemm_kc<mt, 2, AUX>;                   \
+    if (b == 4) return k_gemm_kc<mt, 4, AUX>;                   \
+    if (b == 6) return k_gemm_kc<mt, 6, AUX>;                   \
+    if (b == 8 && mt <= 2) return k_gemm_kc<(mt <= 2 ? mt : 2), 8, AUX>; \
+    return nullptr;
+    switch (a) {
+      SG_KC(1) SG_KC(2) SG_KC(3) SG_KC(4)
+      default: return nullptr;
+    }
+#undef SG_KC
+  }
 }
 
 // dot2: M = 1..15, G in {1, 2, 3, 4, 8} with G*M <= 64.  MFMA: MT = 1..4, NT = 1, 2.
@@ -46,6 +80,7 @@ GemmKernel gemm_kernel_for(int path, int a, int b) {
     if (b == 1) return k_gemm_mfma<mt, 1, AUX>;     \
     if (b == 2) return k_gemm_mfma<mt, 2, AUX>;     \
     return nullptr;
+  if (path == 3) return gemm_kernel_kc<AUX>(a, b);
   if (path == 2) {
     if (a != 1) return nullptr;
     if (b == 1) return k_gemm_mfma<1, 1, AUX, true>;

@@ -65,6 +65,8 @@ struct StageDesc {
   int interleave;      // streams of a workgroup take every ng-th item of its range
   int mode;            // OutMode
   int sync;            // SyncMode of the split-K arrival
+  int check;           // single GEMM: claim (XCD, slot) at the end and latch a duplicate
+  int xbuf;            // K-chunked MFMA path: bytes of one X chunk buffer (multiple of 1 KB)
   unsigned w_aux;      // cache-policy bits of the weight loads
   unsigned x_bytes, w_bytes, y_bytes, y2_bytes;  // operand extents (buffer bounds)
   unsigned part_bytes;                           // extent of the partial buffer

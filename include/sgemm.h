@@ -86,6 +86,28 @@ enum {
                                     boundary is the barrier between stages and
                                     no weights are prefetched across it; the
                                     results are bitwise those of one launch     */
+  SGEMM_F_CHECK_PLACEMENT = 1u << 12, /* GEMM: every workgroup claims its (XCD,
+                                    slot) pair in the workspace after its work
+                                    and a pair claimed twice latches
+                                    SGEMM_ERR_TOPOLOGY (Fleet reading note,
+                                    section 3b: the runtime learns each
+                                    workgroup's XCD from the hardware id).
+                                    Costs 1.5-3 us per launch (a device-scope
+                                    atomic round trip at the end), so it is
+                                    opt-in; the chain always checks (once per
+                                    launch).  Refused for the chain
+                                    (SGEMM_ERR_UNSUPPORTED)                     */
+  SGEMM_F_KCHUNK = 1u << 13,     /* the K-chunked MFMA path: the eight waves of
+                                    a workgroup share one block of tiles over a
+                                    K split, X goes through LDS in 512-wide K
+                                    chunks, double-buffered, so the split no
+                                    longer has to fit the LDS (the news item on
+                                    MI355X low-latency GEMM, techniques 2 and
+                                    3; the Fleet reading note's missing
+                                    wave-level K split, Limitations).  tn, when
+                                    given, is 16 x the tiles per block (32, 64,
+                                    96 or 128); kslices must be 0 or 1 and waves
+                                    0 or 8                                      */
   SGEMM_F_SCHEDULER = 1u << 11   /* chain, ablation: the per-XCD scheduler
                                     runtime (Fleet reading note, sections 3b
                                     and 5, the runtime layout figure of
@@ -168,9 +190,10 @@ int sgemm_workspace_init(sgemm_plan plan, void* workspace, void* stream);
  * Y = X . W (kind GEMM).  X [M][K] bf16, W [N][K] bf16, Y [M][N] (fp32 or bf16
  * as planned); all device pointers, 16-byte aligned.  Enqueues one kernel on
  * `stream` and returns.  SGEMM_ERR_UNSUPPORTED when the plan's device is not
- * a 256-CU gfx950 (sgemm_device_check).  Each launch also checks on the device
- * that its 256 workgroups covered every (XCD, slot) pair exactly once; a
- * violation latches SGEMM_ERR_TOPOLOGY for sgemm_query_status.
+ * a 256-CU gfx950 (sgemm_device_check).  With SGEMM_F_CHECK_PLACEMENT each
+ * launch also checks on the device that its 256 workgroups covered every
+ * (XCD, slot) pair exactly once; a violation latches SGEMM_ERR_TOPOLOGY for
+ * sgemm_query_status.
  */
 int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* workspace,
               void* stream);

@@ -172,6 +172,42 @@ def test_binding_rejects_mismatched_tensors():
         ch(X0, [Wq, Wq], [Wo], [Wgu], [Wd], Yf, cws)
 
 
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 24576), (64, 4096, 24576), (64, 12288, 4096), (33, 2048, 1536),
+                                   (64, 8, 1), (5, 1032, 777), (20, 12288, 300), (64, 4104, 129)])
+@pytest.mark.parametrize("ntw,splitk", [(0, 0), (2, 3), (4, 0), (6, 2), (8, 0)])
+def test_kchunk_plan_covers_columns_and_k(M, K, N, ntw, splitk):
+    """K-chunked plans: blocks of 16 * tiles columns cover each XCD's columns,
+    splits cover K in whole 512-wide chunks (a multiple of the ring depth per
+    item), two X chunk buffers and the first round of the eight-wave
+    reduction fit the LDS next to the static reserve."""
+    MT = -(-M // 16)
+    if ntw == 8 and MT > 2:
+        assert _create(M=M, K=K, N=N, flags=sg.F_KCHUNK, tn=128, splitk=splitk) == sg.ERR_UNSUPPORTED
+        return
+    st = sg.Gemm(M, K, N, flags=sg.F_KCHUNK, tn=16 * ntw, splitk=splitk).describe()["stage"]
+    assert st["path"] == "kc" and st["ta"] == MT and (ntw == 0 or st["tb"] == ntw)
+    tiles = st["tb"]
+    ring = 1 if tiles >= 6 else (2 if tiles >= 4 else 4)
+    assert st["CB"] == 16 * tiles and st["NB"] * st["CB"] >= st["Nx"] and 8 * st["Nx"] >= N
+    assert st["KS"] % (512 * ring) == 0 and st["steps"] * 512 == st["KS"]
+    assert st["S"] * st["KS"] >= K and (st["S"] - 1) * st["KS"] < K
+    assert st["items"] == st["NB"] * st["S"]
+    rows = min(16 * MT, M + 1)
+    assert st["xbuf"] >= rows * 520 * 2 and st["xbuf"] % 1024 == 0
+    assert st["lds"] >= max(2 * st["xbuf"], 4 * tiles * MT * 1024)
+    assert st["lds"] + STATIC_LDS_RESERVE <= 160 * 1024
+
+
+def test_kchunk_flag_combinations():
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_FORCE_DOT2) == sg.ERR_INVALID_ARG
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_MTILE_ITEMS) == sg.ERR_INVALID_ARG
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, ksl=2) == sg.ERR_UNSUPPORTED
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, tn=40) == sg.ERR_UNSUPPORTED
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, tn=48) == sg.ERR_UNSUPPORTED
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, waves=4) == sg.ERR_UNSUPPORTED
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, tn=64) == sg.OK
+
+
 def test_null_and_misaligned_arguments_rejected_before_launch():
     lib = sg.library()
     assert lib.sgemm_plan_create(None, 0, None, None) == sg.ERR_INVALID_ARG
@@ -207,6 +243,9 @@ def test_planner_covers_every_column_and_k_once(M, K, N, splitk, flags):
         assert splitk and e.code == sg.ERR_UNSUPPORTED
         return
     st = g.describe()["stage"]
+    if st["path"] == "kc":   # long K, wide N: the K-chunked path (its own coverage test below)
+        assert M >= 16 and K >= 6144 and not flags and not splitk and st["S"] == 1
+        return
     assert st["path"] == ("dot2" if M < 16 else "mfma")
     mt = st["mtiles"]
     assert mt == (math.ceil(M / 16) if flags else 1) and (mt == 1 or st["ta"] == 1)

@@ -71,14 +71,14 @@ def test_device_check_accepts_this_gpu(cuda_device):
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 1536), (32, 2048, 1024)])
 def test_gemm_placement_claim_reports_a_duplicate_slot(cuda_device, M, K, N):
-    """The single GEMM checks that its workgroups covered every (XCD, slot)
-    pair once.  A claim bit set in the workspace before the launch looks, to
+    """With SGEMM_F_CHECK_PLACEMENT the single GEMM checks that its workgroups
+    covered every (XCD, slot) pair once.  A claim bit set in the workspace before the launch looks, to
     the workgroup that owns that pair, like a second workgroup on the same
     pair: the launch reports SGEMM_ERR_TOPOLOGY instead of passing silently.
     Its XCD's mask still completes and is cleared, so the next launch is
     clean, and the output of a normal launch is unaffected."""
     x, w, X, W = gemm_inputs(M, K, N, 41, 42, cuda_device)
-    g = sg.Gemm(M, K, N)
+    g = sg.Gemm(M, K, N, flags=sg.F_CHECK_PLACEMENT)
     ws = g.new_workspace()
     Y = torch.empty((M, N), dtype=torch.float32, device=cuda_device)
     claim = ws[128:160].view(torch.int32)
@@ -332,3 +332,79 @@ def test_parity_mtile_items(cuda_device, M, K, N, splitk):
     st = g.describe()["stage"]
     assert st["mtiles"] == -(-M // 16) and st["ta"] == 1
     check(run(g, X, W).cpu().numpy(), x, w)
+
+
+# ----------------------------------------------------- K-chunked MFMA path
+KC_SMALL = [(16, 1024, 2048, 0, 0), (17, 776, 530, 2, 0), (33, 2048, 1536, 4, 0), (48, 520, 64, 6, 0),
+            (64, 2048, 1536, 6, 0), (64, 1000, 1000, 4, 3), (5, 1032, 777, 2, 0), (64, 8, 1, 2, 0),
+            (32, 3000, 700, 8, 2), (20, 12288, 300, 4, 5), (64, 4104, 129, 6, 2), (1, 1024, 1024, 8, 0)]
+
+
+@pytest.mark.parametrize("M,K,N,ntw,splitk", KC_SMALL)
+def test_parity_kchunk_small(cuda_device, M, K, N, ntw, splitk):
+    """The K-chunked MFMA path (eight waves on one block of tiles, X double-
+    buffered through LDS in 512-wide K chunks): ragged M, K and N, forced tile
+    counts and split counts, every output element."""
+    x, w, X, W = gemm_inputs(M, K, N, 8100 + M, 8200 + K, cuda_device)
+    g = sg.Gemm(M, K, N, flags=sg.F_KCHUNK, tn=16 * ntw, splitk=splitk)
+    st = g.describe()["stage"]
+    assert st["path"] == "kc" and (ntw == 0 or st["tb"] == ntw)
+    check(run(g, X, W).cpu().numpy(), x, w)
+
+
+@pytest.mark.parametrize("M", [16, 32, 64])
+@pytest.mark.parametrize("K,N", [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)])
+def test_kchunk_decode_projections_full_size(cuda_device, M, K, N):
+    """The decode projections at M = 16, 32, 64 on the K-chunked path, every
+    output element against the oracle."""
+    seed_x = synth.seed_for(3, 0, synth.T_X, M)
+    seed_w = synth.seed_for(3, 0, synth.T_WQ, K % 251 + N % 241)
+    x, _, X, W = gemm_inputs(M, K, N, seed_x, seed_w, cuda_device, w_on_device=True)
+    g = sg.Gemm(M, K, N, flags=sg.F_KCHUNK)
+    assert g.describe()["stage"]["path"] == "kc"
+    Y = run(g, X, W).cpu().numpy()
+    w = device_weights_checked(W, seed_w, K)
+    report("kc gemm %dx%dx%d" % (M, K, N), check(Y, x, w), workload=3)
+
+
+@pytest.mark.parametrize("M,K,N,splitk", [(64, 4096, 24576, 0), (64, 12288, 4096, 2), (17, 7168, 1536, 3),
+                                          (48, 4096, 4096, 4)])
+def test_kchunk_integer_inputs_bitwise(cuda_device, M, K, N, splitk):
+    """Integer inputs: every partial sum is exact in fp32, so the K-chunked
+    path (eight-wave tree reduction, split-K partials) must equal the exact
+    product bitwise."""
+    xb, wb, X, W = _int_inputs(M, K, N, cuda_device)
+    g = sg.Gemm(M, K, N, flags=sg.F_KCHUNK, splitk=splitk)
+    Y = run(g, X, W).cpu().numpy()
+    ref = (synth.bf16_bits_to_f32(xb).astype(np.float64) @ synth.bf16_bits_to_f32(wb).astype(np.float64).T)
+    assert np.array_equal(Y, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("splitk", [1, 3])
+def test_kchunk_graph_replays_and_repeat(cuda_device, splitk):
+    """Repeated eager runs and HIP graph replays of the K-chunked path give
+    bitwise the same output (split-K counters reset by their owners)."""
+    M, K, N = 40, 4096, 2048
+    x, w, X, W = gemm_inputs(M, K, N, 8300, 8400, cuda_device)
+    g = sg.Gemm(M, K, N, flags=sg.F_KCHUNK, splitk=splitk)
+    ws = g.new_workspace()
+    Ye = run(g, X, W, ws)
+    assert torch.equal(run(g, X, W, ws), Ye)
+    Y = torch.empty_like(Ye)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g(X, W, Y, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g(X, W, Y, ws)
+    for r in range(3):
+        Y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert g.status(ws) == sg.OK, r
+        assert torch.equal(Y, Ye), r
+    check(Ye.cpu().numpy(), x, w)
