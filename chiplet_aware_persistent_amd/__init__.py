@@ -81,9 +81,10 @@ def library() -> ctypes.CDLL:
         lib.sgemm_topology_probe.argtypes = [vp, ctypes.c_int, vp]
         lib.sgemm_read_probe.argtypes = [vp, sz, ctypes.c_int, vp, ctypes.c_int, vp]
         lib.sgemm_device_check.argtypes = [ctypes.c_int]
+        lib.sgemm_run_noalloc.argtypes = [vp, vp, vp, vp, vp]
         for f in ("sgemm_plan_create", "sgemm_plan_destroy", "sgemm_workspace_init", "sgemm_run",
                   "layerchain_run", "sgemm_chain_buffer", "sgemm_query_status", "sgemm_plan_describe",
-                  "sgemm_topology_probe", "sgemm_read_probe", "sgemm_device_check"):
+                  "sgemm_topology_probe", "sgemm_read_probe", "sgemm_device_check", "sgemm_run_noalloc"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -121,6 +122,10 @@ def sgemm_workspace_init(plan, workspace: int, stream: int = 0) -> int:
 
 def sgemm_run(plan, X: int, W: int, Y: int, workspace: int, stream: int = 0) -> int:
     return library().sgemm_run(plan, X, W, Y, workspace, stream)
+
+
+def sgemm_run_noalloc(plan, X: int, W: int, Y: int, stream: int = 0) -> int:
+    return library().sgemm_run_noalloc(plan, X, W, Y, stream)
 
 
 def _ptr_array(ptrs):

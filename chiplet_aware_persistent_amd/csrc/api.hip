@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -573,15 +574,14 @@ static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
   return d;
 }
 
-int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* workspace, void* stream) {
-  if (!plan || !X || !W || !Y || !workspace) return SGEMM_ERR_INVALID_ARG;
-  if (plan->prob.kind != SGEMM_KIND_GEMM) return SGEMM_ERR_INVALID_ARG;
-  if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || !aligned16(workspace))
-    return SGEMM_ERR_INVALID_ARG;
+// One single-GEMM launch with the workspace's control block at ws, its split-K
+// counters at ws + off_ctr and its partials at ws + off_part (arguments
+// already checked).
+static int launch_plan_gemm(sgemm_plan plan, const void* X, const void* W, void* Y, char* ws, size_t off_ctr,
+                            size_t off_part, void* stream) {
   const sgemm_problem& p = plan->prob;
   const Geo& g = plan->geo;
   StageDesc d = stage_desc(g, plan->w_aux, plan->sync);
-  char* ws = (char*)workspace;
   d.X = (const uint16_t*)X;
   d.W = (const uint16_t*)W;
   d.Y = Y;
@@ -590,9 +590,9 @@ int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* work
   d.ldy = p.N;
   d.mode = p.out_dtype == SGEMM_OUT_F32 ? OUT_F32 : OUT_BF16;
   d.check = (p.flags & SGEMM_F_CHECK_PLACEMENT) ? 1 : 0;
-  d.part = (float*)(ws + plan->off_part);
+  d.part = (float*)(ws + off_part);
   d.part_bytes = (unsigned)(g.part_floats * 4);
-  d.ctr = (unsigned*)(ws + plan->off_ctr);
+  d.ctr = (unsigned*)(ws + off_ctr);
   d.x_bytes = (unsigned)((size_t)p.M * p.K * 2);
   d.w_bytes = (unsigned)((size_t)p.N * p.K * 2);
   d.y_bytes = (unsigned)((size_t)p.M * p.N * (p.out_dtype == SGEMM_OUT_F32 ? 4 : 2));
@@ -602,6 +602,65 @@ int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* work
   hipError_t e = launch_gemm(d, g.mtiles > 1 ? 2 : g.path, g.ta, g.tb, plan->grid, g.waves * 64, g.lds, (unsigned*)ws,
                              (hipStream_t)stream);
   return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
+}
+
+int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* workspace, void* stream) {
+  if (!plan || !X || !W || !Y || !workspace) return SGEMM_ERR_INVALID_ARG;
+  if (plan->prob.kind != SGEMM_KIND_GEMM) return SGEMM_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || !aligned16(workspace))
+    return SGEMM_ERR_INVALID_ARG;
+  return launch_plan_gemm(plan, X, W, Y, (char*)workspace, plan->off_ctr, plan->off_part, stream);
+}
+
+// ------------------------------------------------------------------------
+// The single GEMM over a library-owned device array instead of a caller's
+// workspace, for callers that cannot allocate.  Layout of the array, fixed
+// for every plan: the control block, then a counter region, then the
+// partials.  Every run leaves its split-K counters at zero (each is reset by
+// its tile's last arriver) and the array is zero when the code object is
+// loaded, so the counter region is all zeros before every run whatever plan
+// ran before; the partials need no initial value.  Each GPU holds its own
+// copy, found once per device with hipGetSymbolAddress.
+namespace {
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;  // per device, held until the process ends
+constexpr size_t kStaticCtrBytes = (size_t)1 << 20;       // split-K counters: 262144
+constexpr size_t kStaticPartBytes = kStaticScratchBytes - kCtl - kStaticCtrBytes;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// The device address of this device's copy of `scratch` (looked up on the
+// first call for the device, with the device current).
+static int scratch_of(int device, char** out) {
+  if (device < 0 || device >= kMaxDevices) return SGEMM_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return SGEMM_ERR_HIP;
+    if (hipSetDevice(device) != hipSuccess) return SGEMM_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (hipSetDevice(cur) != hipSuccess || e != hipSuccess || !ptr) return SGEMM_ERR_HIP;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = (char*)g_scratch_ptr[device];
+  return SGEMM_OK;
+}
+
+int sgemm_run_noalloc(sgemm_plan plan, const void* X, const void* W, void* Y, void* stream) {
+  if (!plan || !X || !W || !Y) return SGEMM_ERR_INVALID_ARG;
+  if (plan->prob.kind != SGEMM_KIND_GEMM) return SGEMM_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return SGEMM_ERR_INVALID_ARG;
+  // No status word is read back for the shared array.
+  if (plan->prob.flags & SGEMM_F_CHECK_PLACEMENT) return SGEMM_ERR_UNSUPPORTED;
+  if (plan->geo.ctr_count * 4 > kStaticCtrBytes || plan->geo.part_floats * 4 > kStaticPartBytes)
+    return SGEMM_ERR_WORKSPACE;
+  if (const int dc = device_check(plan->device); dc != SGEMM_OK) return dc;
+  char* ws = nullptr;
+  if (const int rc = scratch_of(plan->device, &ws); rc != SGEMM_OK) return rc;
+  return launch_plan_gemm(plan, X, W, Y, ws, kCtl, kCtl + kStaticCtrBytes, stream);
 }
 
 int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const void* const* Wo,

@@ -199,6 +199,27 @@ int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* work
               void* stream);
 
 /*
+ * sgemm_run without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The split-K counters and partials live in a 32 MiB
+ * array of the library's own (a static device array, one copy per GPU, held
+ * until the process ends; its address is looked up once per device).  Same
+ * kernels, plan and results as sgemm_run.
+ *   Limits: the plan's split-K counters must fit 1 MiB and its partials
+ *   32 MiB - 1 MiB - 256 B, else SGEMM_ERR_WORKSPACE (every decode shape at
+ *   M <= 64 fits; the largest, 64 x 4096 x 24576, needs 24 MiB).
+ *   SGEMM_F_CHECK_PLACEMENT plans are refused (SGEMM_ERR_UNSUPPORTED): no
+ *   status word is read back from the shared array.
+ *   Concurrency: every call on a GPU uses that GPU's one array, so calls
+ *   that can overlap in time on the same GPU (two streams, two threads) race
+ *   and give wrong results; serialise them.  Calls in stream order are safe:
+ *   each run leaves the counters at zero for the next.
+ *   Other errors as sgemm_run.  Allocates nothing (no hipMalloc, no
+ *   allocating library call).
+ */
+int sgemm_run_noalloc(sgemm_plan plan, const void* X, const void* W, void* Y, void* stream);
+
+/*
  * The whole layer chain in one persistent launch (kind LAYERCHAIN).
  * X0 [M][d_model] bf16 device pointer.  Wq, Wo, Wgu, Wdown are HOST arrays of
  * n_layers DEVICE pointers each (layouts above).  Y_f32 [M][d_model] receives
