@@ -38,6 +38,7 @@ F_LAUNCH_PER_STAGE = 1 << 10
 F_SCHEDULER = 1 << 11
 F_CHECK_PLACEMENT = 1 << 12
 F_KCHUNK = 1 << 13
+F_MSPLIT = 1 << 14
 
 
 class SgemmError(RuntimeError):
@@ -51,7 +52,7 @@ class Problem(ctypes.Structure):
                 ("out_dtype", ctypes.c_int), ("n_layers", ctypes.c_int), ("d_model", ctypes.c_int),
                 ("q_cols", ctypes.c_int), ("d_ff", ctypes.c_int), ("flags", ctypes.c_uint),
                 ("tn", ctypes.c_int), ("splitk", ctypes.c_int), ("waves", ctypes.c_int),
-                ("kslices", ctypes.c_int)]
+                ("kslices", ctypes.c_int), ("tm", ctypes.c_int)]
 
 
 _lib = None
@@ -233,8 +234,8 @@ class Gemm(_PlanBase):
     """Y[M,N] = X[M,K] . W^T with W stored [N][K] (K-major), bf16 in, fp32 (or bf16) out."""
 
     def __init__(self, M: int, K: int, N: int, out_dtype: int = OUT_F32, flags: int = 0, tn: int = 0,
-                 splitk: int = 0, waves: int = 0, kslices: int = 0, device: int = 0):
-        p = Problem(KIND_GEMM, M, K, N, out_dtype, 0, 0, 0, 0, flags, tn, splitk, waves, kslices)
+                 splitk: int = 0, waves: int = 0, kslices: int = 0, device: int = 0, tm: int = 0):
+        p = Problem(KIND_GEMM, M, K, N, out_dtype, 0, 0, 0, 0, flags, tn, splitk, waves, kslices, tm)
         super().__init__(p, device)
         self.M, self.K, self.N, self.out_dtype = M, K, N, out_dtype
 

@@ -44,6 +44,7 @@ struct Geo {
   int mtiles = 1;  // m-tile items (ablation): items per (split, column block), m-tile fastest
   int slots = 32;  // workgroups per XCD that share the items (31 with a scheduler workgroup)
   int xbuf = 0;    // K-chunked path: bytes of one X chunk buffer
+  int nfast = 0;   // m-tile items in the M-split order (column block fastest)
   size_t ctr_count = 0, part_floats = 0;
   double est_us = 0.0;
 };
@@ -178,7 +179,7 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
 }
 
 bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, int s_o, int waves_o,
-              int ksl_o, const Cost& cost, int wpi_o = 0, bool mtile_items = false, int slots = kWgPerXcd) {
+              int ksl_o, const Cost& cost, int wpi_o = 0, int mti_rows = 0, int slots = kWgPerXcd) {
   bool found = false;
   const int waves_opts[2] = {8, 4};
   for (int wi = 0; wi < 2; ++wi) {
@@ -202,10 +203,11 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
         if (paired && tb != 2) continue;
         if (tn_o && !paired && 16 * tb != tn_o) continue;
         g.ta = (M + 15) / 16; g.tb = tb;
-        if (mtile_items) {  // one 16-row m-tile per item, one wave per item
+        if (mti_rows) {  // one window of mti_rows rows (16, 32 or 64) per item, one wave per item
           if (wpi != 1 || ksl != 1) continue;
-          g.mtiles = g.ta;
-          g.ta = 1;
+          g.ta = mti_rows / 16;
+          g.mtiles = (M + mti_rows - 1) / mti_rows;
+          if (!gemm_variant_exists(2, g.ta, g.tb)) continue;
         }
       }
       // The model was fitted up to 16 splits.  With 31 worker slots a
@@ -399,8 +401,13 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     if (p.flags & SGEMM_F_SCHEDULER) { delete pl; return SGEMM_ERR_UNSUPPORTED; }  // a chain runtime
     int rc = validate_gemm(p);
     if (rc != SGEMM_OK) { delete pl; return rc; }
-    const bool mti = (p.flags & SGEMM_F_MTILE_ITEMS) != 0;
+    const bool msplit = (p.flags & SGEMM_F_MSPLIT) != 0;
+    const bool mti = (p.flags & SGEMM_F_MTILE_ITEMS) != 0 || msplit;
     const bool kc = (p.flags & SGEMM_F_KCHUNK) != 0;
+    // Rows per m-tile item (the window of the M-major traversal): 16 unless given.
+    const int mti_rows = !mti ? 0 : (p.tm ? p.tm : 16);
+    if (mti && mti_rows != 16 && mti_rows != 32 && mti_rows != 64) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+    if (!mti && p.tm) { delete pl; return SGEMM_ERR_INVALID_ARG; }
     if ((mti || kc) && (p.flags & SGEMM_F_FORCE_DOT2)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
     if (mti && kc) { delete pl; return SGEMM_ERR_INVALID_ARG; }
     const int path = mti ? 1 : choose_path(p);
@@ -409,7 +416,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
       // tn (a multiple of 16) gives the tiles per item.
       if (tn_o % 16 || w_o == 4) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
       if (!plan_kc(pl->geo, p.M, p.K, p.N, 0, tn_o / 16, s_o, kCostGemm)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
-    } else if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, kCostGemm, 0, mti)) {
+    } else if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, kCostGemm, 0, mti_rows)) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
     } else if (path == 1 && !mti && !tn_o && !s_o && !w_o && !k_o && p.K >= 6144) {
@@ -422,10 +429,12 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
           kcg.items * 4 >= kWgPerXcd * 3 && pl->geo.S > 2)
         pl->geo = kcg;
     }
+    pl->geo.nfast = msplit ? 1 : 0;
     if (pl->geo.part_floats * 4 >= kMaxOperand) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     layout_stage_ws(cur, pl->geo, pl->off_ctr, pl->off_part);
   } else if (p.kind == SGEMM_KIND_LAYERCHAIN) {
-    if (p.flags & (SGEMM_F_W_CACHED | SGEMM_F_W_SC1 | SGEMM_F_MTILE_ITEMS | SGEMM_F_CHECK_PLACEMENT)) {
+    if (p.tm || (p.flags & (SGEMM_F_W_CACHED | SGEMM_F_W_SC1 | SGEMM_F_MTILE_ITEMS | SGEMM_F_CHECK_PLACEMENT |
+                            SGEMM_F_MSPLIT | SGEMM_F_KCHUNK))) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
     }
@@ -568,6 +577,7 @@ static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
   d.pair_off = g.pair_off;
   d.mtiles = g.mtiles;
   d.interleave = g.mtiles > 1 ? 1 : 0;
+  d.nfast = g.nfast;
   d.xbuf = g.xbuf;
   d.w_aux = w_aux;
   d.sync = sync;
@@ -789,10 +799,10 @@ static std::string geo_json(const Geo& g) {
                 "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,\"wpi\":%d,"
                 "\"ksl\":%d,\"kss\":%d,\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,"
                 "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
-                "\"ring\":%d,\"mtiles\":%d,\"slots\":%d,\"xbuf\":%d,\"est_us\":%.3f}",
+                "\"ring\":%d,\"mtiles\":%d,\"nfast\":%d,\"slots\":%d,\"xbuf\":%d,\"est_us\":%.3f}",
                 g.path == 0 ? "dot2" : (g.path == 3 ? "kc" : "mfma"), g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
-                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles, g.slots,
-                g.xbuf, g.est_us);
+                g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles,
+                g.nfast, g.slots, g.xbuf, g.est_us);
   return b;
 }
 

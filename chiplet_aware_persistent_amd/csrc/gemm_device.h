@@ -377,7 +377,7 @@ struct NoHook {
 // the G/2 up rows pair_off further on; the wave owns G/2 output columns and
 // writes silu(gate) * up.
 template <int M, int G, int AUX, bool PAIRED = false, typename Hook = NoHook>
-__device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
+__device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                            Hook pre_x = Hook()) {
   constexpr int P = ring_depth_dot2(G);
   constexpr int V = pow2_at_least(G * M);
@@ -593,7 +593,7 @@ __device__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
 // reads row 16i + l'%16 (the zero row M where that passes M) at
 // k = 32h + 8(l'/16).
 template <int MT, int NT, bool PAIRED, int AUX, bool DEEP = false, typename Hook = NoHook, bool MTI = false>
-__device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
+__device__ __forceinline__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                            Hook pre_x = Hook()) {
   constexpr int P = ring_depth_mfma(NT, DEEP);
   constexpr int TW = PAIRED ? 16 : 16 * NT;  // distinct output columns per wave
@@ -603,8 +603,9 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
   // Items: (split, column block, m-tile), m-tile fastest.  MTI (the m-tile-
-  // item variant): d.mtiles items per (split, column block), one 16-row
-  // m-tile each; otherwise one item covers every row.  A stream runs the
+  // item variant): d.mtiles items per (split, column block), MT 16-row
+  // m-tiles each (a window of 16 MT rows); otherwise one item covers every
+  // row.  A stream runs the
   // items i0, i0 + istep, ... below i1: a contiguous range, or with
   // d.interleave every ng-th item of the workgroup's range.
   const int mtl = MTI ? d.mtiles : 1;
@@ -617,10 +618,21 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     my_items(d.items, slot, nslots, d.ng, wave / d.wpi, i0, i1);
   }
   const int nit = i0 < i1 ? (i1 - i0 + istep - 1) / istep : 0;  // items of this stream
+  // With d.nfast (the M-split order) the column block runs fastest instead:
+  // neighbouring items take different weights, so no two m-tiles of a block
+  // run at the same time and nothing is shared between them.
   const int per_split = d.NB * mtl;
+  const bool nfast = MTI && d.nfast;
   auto split_of = [&](int it) { return it / per_split; };
-  auto block_of = [&](int it) { return (it - split_of(it) * per_split) / mtl; };
-  auto mtile_of = [&](int it) { return it % mtl; };
+  auto block_of = [&](int it) {
+    const int r = it - split_of(it) * per_split;
+    return nfast ? r % d.NB : r / mtl;
+  };
+  auto mtile_of = [&](int it) {
+    if constexpr (!MTI) return 0;
+    const int r = it - split_of(it) * per_split;
+    return nfast ? r / d.NB : r % mtl;
+  };
   const int wv = wave % d.wpi;  // wave's place within its item
   const int CG = d.wpi / d.ksl; // column groups per item
   const int cg = wv % CG;       // this wave's column group
@@ -718,7 +730,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
     const int b = block_of(it);
     if (d.S == 1) {
       const int colb = xc0 + b * d.CB + wv * TW;
-      const int mt = mtile_of(it);
+      const int mt = MT * mtile_of(it);
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         if (PAIRED) {
@@ -750,7 +762,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
   const int xrows = min(16 * MT * mtl, d.M + 1);
   int xro[MT];
   auto set_rows = [&](int it) {  // A-operand row offsets of item it's m-tiles
-    const int m0 = 16 * (it < i1 ? mtile_of(it) : 0);
+    const int m0 = 16 * MT * (it < i1 ? mtile_of(it) : 0);
 #pragma unroll
     for (int i = 0; i < MT; ++i) xro[i] = min(m0 + 16 * i + r16, d.M) * d.xrow;
   };
@@ -902,7 +914,7 @@ __device__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, 
           sum_partials_f4<0, NT, MT>(pr, tile * d.S * TILE, TILE, d.S, lane, tot, d.part_bytes);
         }
         const int colb = xc0 + b * d.CB + wv * TW;
-        const int mt = mtile_of(it);
+        const int mt = MT * mtile_of(it);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
           if (PAIRED) {

@@ -74,13 +74,14 @@ enum {
                                     counter and raises a per-XCD flag that the
                                     XCD's other workgroups poll (default: every
                                     workgroup polls the global counter)         */
-  SGEMM_F_MTILE_ITEMS = 1u << 9, /* GEMM, ablation: one 16-row m-tile per item,
+  SGEMM_F_MTILE_ITEMS = 1u << 9, /* GEMM, ablation: one window of T_M rows
+                                    (problem field tm: 16, 32 or 64) per item,
                                     m-tile fastest, consecutive items on
-                                    neighbouring waves, so the m-tiles of a
+                                    neighbouring waves, so the windows of a
                                     column block share its weights through the
                                     caches (Fleet reading note, section 3f,
-                                    M-major window) instead of in registers;
-                                    MFMA path, no K slices                      */
+                                    M-major window, T_M) instead of in
+                                    registers; MFMA path, no K slices           */
   SGEMM_F_LAUNCH_PER_STAGE = 1u << 10, /* chain, ablation: one launch of the same
                                     kernel per projection stage, so the kernel
                                     boundary is the barrier between stages and
@@ -97,6 +98,14 @@ enum {
                                     opt-in; the chain always checks (once per
                                     launch).  Refused for the chain
                                     (SGEMM_ERR_UNSUPPORTED)                     */
+  SGEMM_F_MSPLIT = 1u << 14,     /* GEMM, ablation: the m-tile items of
+                                    SGEMM_F_MTILE_ITEMS in the M-split order --
+                                    column block fastest, so neighbouring
+                                    waves read different weights and no m-tile
+                                    of a block shares them with another in time
+                                    (Fleet reading note, section 7, Table 4 and
+                                    its key findings: M-tile against M-split;
+                                    section 3f, Eq.(1) with R = 1)              */
   SGEMM_F_KCHUNK = 1u << 13,     /* the K-chunked MFMA path: the eight waves of
                                     a workgroup share one block of tiles over a
                                     K split, X goes through LDS in 512-wide K
@@ -147,6 +156,8 @@ typedef struct {
   int n_layers, d_model, q_cols, d_ff;
   unsigned flags;
   int tn, splitk, waves, kslices;
+  int tm;  /* SGEMM_F_MTILE_ITEMS / SGEMM_F_MSPLIT: rows per item, T_M = 16, 32 or
+              64 (0: 16); must be 0 otherwise                                   */
 } sgemm_problem;
 
 /*

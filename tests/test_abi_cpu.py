@@ -28,7 +28,7 @@ def _create(**kw):
     p = sg.Problem(kw.get("kind", sg.KIND_GEMM), kw.get("M", 1), kw.get("K", 64), kw.get("N", 64),
                    kw.get("out", sg.OUT_F32), kw.get("L", 0), kw.get("d", 0), kw.get("q", 0), kw.get("dff", 0),
                    kw.get("flags", 0), kw.get("tn", 0), kw.get("splitk", 0), kw.get("waves", 0),
-                   kw.get("ksl", 0))
+                   kw.get("ksl", 0), kw.get("tm", 0))
     rc, h, ws = sg.sgemm_plan_create(p)
     if h:
         sg.sgemm_plan_destroy(h)
@@ -198,6 +198,31 @@ def test_kchunk_plan_covers_columns_and_k(M, K, N, ntw, splitk):
     assert st["lds"] + STATIC_LDS_RESERVE <= 160 * 1024
 
 
+@pytest.mark.parametrize("M,K,N", [(64, 4096, 24576), (48, 12288, 4096), (33, 2056, 900), (17, 776, 530),
+                                   (64, 4096, 1536)])
+@pytest.mark.parametrize("tm", [16, 32, 64])
+@pytest.mark.parametrize("msplit", [False, True])
+def test_mtile_window_and_msplit_plans(M, K, N, tm, msplit):
+    """M-major window ablations: T_M-row windows per item (ceil(M / T_M) items
+    per column block and split) in the m-tile-fastest order, and the M-split
+    order (column block fastest).  The item count and the window rows cover
+    every output row and column once."""
+    flags = sg.F_MSPLIT if msplit else sg.F_MTILE_ITEMS
+    st = sg.Gemm(M, K, N, flags=flags, tm=tm).describe()["stage"]
+    assert st["path"] == "mfma" and st["ta"] == tm // 16
+    assert st["mtiles"] == -(-M // tm) and st["nfast"] == (1 if msplit else 0)
+    assert st["items"] == st["NB"] * st["S"] * st["mtiles"]
+    assert st["mtiles"] * tm >= M and (st["mtiles"] - 1) * tm < M
+    assert st["lds"] + STATIC_LDS_RESERVE <= 160 * 1024
+
+
+def test_mtile_window_flag_combinations():
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_MTILE_ITEMS, tm=48) == sg.ERR_INVALID_ARG
+    assert _create(M=32, K=1024, N=1024, tm=32) == sg.ERR_INVALID_ARG             # tm without the ablation
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_MSPLIT, tm=32) == sg.OK
+    assert _create(kind=sg.KIND_LAYERCHAIN, M=32, L=2, d=64, q=64, dff=64, flags=sg.F_MSPLIT) == sg.ERR_UNSUPPORTED
+
+
 def test_kchunk_flag_combinations():
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_FORCE_DOT2) == sg.ERR_INVALID_ARG
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_MTILE_ITEMS) == sg.ERR_INVALID_ARG
@@ -206,6 +231,56 @@ def test_kchunk_flag_combinations():
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, tn=48) == sg.ERR_UNSUPPORTED
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, waves=4) == sg.ERR_UNSUPPORTED
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, tn=64) == sg.OK
+
+
+def _stage_items(st, slots=32):
+    """(slot, stream) -> item list of one chain/GEMM stage, as the kernels
+    assign them: workgroup slot w of 32 runs streams q < ng, each the
+    contiguous balanced range of the XCD's items (split-major)."""
+    items, ng = st["items"], st["waves"] // st["wpi"]
+    out = {}
+    for w in range(slots):
+        for q in range(ng):
+            nw, ww = slots * ng, w * ng + q
+            out[(w, q)] = list(range(items * ww // nw, items * (ww + 1) // nw))
+    return out
+
+
+@pytest.mark.parametrize("M,L,d,q,dff", [(2, 2, 256, 128, 200), (1, 36, 4096, 4096, 12288), (16, 3, 256, 128, 384),
+                                         (64, 36, 4096, 4096, 12288), (8, 4, 512, 256, 1536), (5, 3, 256, 128, 384)])
+def test_chain_stage_items_windows_and_shared_lines(M, L, d, q, dff):
+    """Host model of how each chain stage's items fall to workgroups: every
+    item runs exactly once; every K range a workgroup's items read lies in
+    the one X window it stages for the stage (the window starts at its first
+    item's split); and the per-XCD output columns of each stage tile the
+    output.  It also lists how many XCDs write into each 128-byte line of
+    each stage's output (the ragged 256-wide chain has two XCDs per line),
+    the case the repeat test on the GPU exercises."""
+    ch = sg.LayerChain(M, L, d, q, dff)
+    outs = {0: q, 1: d, 2: dff, 3: d}
+    for si, st in enumerate(ch.describe()["stages"]):
+        assign = _stage_items(st)
+        seen = sorted(i for v in assign.values() for i in v)
+        assert seen == list(range(st["items"]))
+        per_split = st["NB"] * st["mtiles"]
+        kstep = 512 if st["path"] == "dot2" else 64
+        for w in range(32):
+            its = [i for qq in range(st["waves"] // st["wpi"]) for i in assign[(w, qq)]]
+            if not its:
+                continue
+            s_first = min(its) // per_split
+            for i in its:
+                k0 = (i // per_split) * st["KS"]
+                lo = k0 - s_first * st["KS"]
+                hi = lo + (st["ksl"] - 1) * st["kss"] + st["steps"] * kstep
+                assert 0 <= lo and hi <= st["win"], (si, w, i)
+        # output columns: XCD x owns [x*Nx, (x+1)*Nx); count XCDs per 128-B line of a bf16 row
+        N, Nx = outs[si], st["Nx"]
+        owners = [min(c // Nx, 7) for c in range(N)]
+        assert sorted(set(owners)) == list(range(min(8, -(-N // Nx))))
+        per_line = [len(set(owners[c:c + 64])) for c in range(0, N, 64)]
+        if (M, d) == (2, 256) and si == 3:
+            assert max(per_line) == 2      # the down output x' of the ragged case: two XCDs per line
 
 
 def test_null_and_misaligned_arguments_rejected_before_launch():

@@ -412,3 +412,27 @@ def test_chain_gain_normalised_36_layers(cuda_device, M):
     rms, _ = check_chain_own_inputs(ch, ws, x0, lambda l: layers[l], Y, Yb,
                                     name="chain36 m%d d512 gain-normalised" % M)
     assert all(0.25 < r < 4.0 for r in rms), rms     # non-vanishing through all 36 layers
+
+
+@pytest.mark.parametrize("M,d,q,dff", [(2, 256, 128, 200), (1, 128, 128, 96), (5, 256, 128, 200)])
+def test_chain_shared_output_lines_repeatable(cuda_device, M, d, q, dff):
+    """Narrow chains in which two to four XCDs write into each 128-byte line of
+    a stage's output (each XCD owns Nx = 16 or 32 columns), so a consumer
+    stage reads lines whose parts came from other XCDs' L2s through the
+    two-level counters' release and acquire.  Twenty runs on one workspace
+    must give bitwise the same output and stages, and the first must match
+    the oracle stage by stage (the ragged shape is the one where a dropped
+    work-queue variant once failed)."""
+    L = 4
+    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x7000 + M + d, cuda_device)
+    ch = sg.LayerChain(M, L, d, q, dff)
+    rc, Y, Yb, ws = run_chain(ch, X0, dl)
+    assert rc == sg.OK, sg.status_string(rc)
+    check_chain(ch, ws, x0, layers, Y, Yb, M)
+    acts = [host_bits(ch.activation(ws, l, w)) for l in range(L) for w in range(4)]
+    for r in range(20):
+        rc, Y2, _, ws = run_chain(ch, X0, dl, ws)
+        assert rc == sg.OK, (r, sg.status_string(rc))
+        assert torch.equal(Y2, Y), r
+        assert all(np.array_equal(a, host_bits(ch.activation(ws, l, w)))
+                   for a, (l, w) in zip(acts, [(l, w) for l in range(L) for w in range(4)])), r

@@ -408,3 +408,15 @@ def test_kchunk_graph_replays_and_repeat(cuda_device, splitk):
         assert g.status(ws) == sg.OK, r
         assert torch.equal(Y, Ye), r
     check(Ye.cpu().numpy(), x, w)
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 4096, 1536), (48, 2056, 900), (33, 776, 530), (64, 12288, 300)])
+@pytest.mark.parametrize("tm,msplit", [(32, False), (64, False), (16, True), (32, True)])
+def test_parity_mtile_windows_and_msplit(cuda_device, M, K, N, tm, msplit):
+    """The M-major window ablation with 32- and 64-row windows, and the
+    M-split order (column block fastest), compute the same GEMM."""
+    x, w, X, W = gemm_inputs(M, K, N, 9960 + M, 9970 + K, cuda_device)
+    g = sg.Gemm(M, K, N, flags=sg.F_MSPLIT if msplit else sg.F_MTILE_ITEMS, tm=tm)
+    st = g.describe()["stage"]
+    assert st["mtiles"] == -(-M // tm) and st["nfast"] == int(msplit)
+    check(run(g, X, W).cpu().numpy(), x, w)
