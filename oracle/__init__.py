@@ -56,6 +56,12 @@ def _load():
         lib.oracle_silu_gate.argtypes = [ctypes.c_long, f32p, f32p, u16p]
         lib.oracle_silu_gate.restype = None
         lib.oracle_layer.argtypes = [ctypes.c_int] * 4 + [u16p] * 5 + [ctypes.c_void_p] * 5
+        lib.oracle_rmsnorm.argtypes = [ctypes.c_int, ctypes.c_int, u16p, u16p, ctypes.c_double, u16p]
+        lib.oracle_rmsnorm.restype = None
+        lib.oracle_gqa_decode.argtypes = [ctypes.c_int] * 5 + [u16p] * 5 + [u16p]
+        lib.oracle_gqa_decode.restype = None
+        lib.oracle_residual.argtypes = [ctypes.c_long, u16p, f64p, u16p]
+        lib.oracle_residual.restype = None
         lib.oracle_layer.restype = None
         _lib = lib
     return _lib
@@ -167,3 +173,73 @@ def timed_gemm(x_bits, w_bits):
     t0 = time.perf_counter()
     gemm(x_bits, w_bits, want_abs=False)
     return time.perf_counter() - t0, num_threads()
+
+
+RMS_EPS = 1e-6   # the RMSNorm epsilon of the decoder layer
+
+
+def rmsnorm(x_bits, w_bits, eps: float = RMS_EPS) -> np.ndarray:
+    """bf16(x / sqrt(mean(x^2) + eps) * w) per row of x [M][d], in double."""
+    x, w = _u16(x_bits), _u16(w_bits)
+    M, d = x.shape
+    if w.shape != (d,):
+        raise ValueError("weight shape")
+    out = np.empty((M, d), np.uint16)
+    _load().oracle_rmsnorm(M, d, x, w, float(eps), out)
+    return out
+
+
+def gqa_decode(q_bits, kc_bits, vc_bits, kn_bits, vn_bits, Hq: int, Hkv: int) -> np.ndarray:
+    """Grouped-query decode attention (see oracle.c): q [M][Hq*hd], caches
+    [M][Hkv][T][hd], new key/value [M][Hkv*hd]; returns bf16 bits [M][Hq*hd]."""
+    q, kc, vc = _u16(q_bits), _u16(kc_bits), _u16(vc_bits)
+    kn, vn = _u16(kn_bits), _u16(vn_bits)
+    M, Hkv_, T, hd = kc.shape
+    if Hkv_ != Hkv or q.shape != (M, Hq * hd) or vc.shape != kc.shape or kn.shape != (M, Hkv * hd) \
+            or vn.shape != kn.shape or Hq % Hkv:
+        raise ValueError("attention shapes")
+    out = np.empty((M, Hq * hd), np.uint16)
+    _load().oracle_gqa_decode(M, Hq, Hkv, hd, T, q, kc.reshape(-1), vc.reshape(-1), kn, vn, out)
+    return out
+
+
+def residual(x_bits, y) -> np.ndarray:
+    """bf16(f32(x + f32(y))) elementwise: x bf16 bits, y the projection's double result."""
+    x = _u16(x_bits)
+    yy = np.ascontiguousarray(y, dtype=np.float64)
+    if yy.shape != x.shape:
+        raise ValueError("shape mismatch")
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_residual(x.size, x.reshape(-1), yy.reshape(-1), out.reshape(-1))
+    return out
+
+
+def decoder_layer(x_bits, w_attn, wqkv, kc, vc, wo, w_mlp, wgu, wdown, Hq: int, Hkv: int,
+                  eps: float = RMS_EPS):
+    """One decoder layer (see oracle.c): returns dict of n1, qkv, o, x1, n2, a, x_out (bf16 bits)
+    and the pieces of qkv (q, k, v)."""
+    x = _u16(x_bits)
+    M, d = x.shape
+    hd = kc.shape[3]
+    qc, kvc = Hq * hd, Hkv * hd
+    n1 = rmsnorm(x, w_attn, eps)
+    y, _ = gemm(n1, wqkv, want_abs=False)
+    qkv = _bf16_of_f64(y)
+    q, k, v = qkv[:, :qc], qkv[:, qc:qc + kvc], qkv[:, qc + kvc:qc + 2 * kvc]
+    o = gqa_decode(q, kc, vc, k, v, Hq, Hkv)
+    yo, _ = gemm(o, wo, want_abs=False)
+    x1 = residual(x, yo)
+    n2 = rmsnorm(x1, w_mlp, eps)
+    ygu, _ = gemm(n2, wgu, want_abs=False)
+    dff = wgu.shape[0] // 2
+    a = silu_gate(ygu[:, :dff].astype(np.float32), ygu[:, dff:].astype(np.float32))
+    yd, _ = gemm(a, wdown, want_abs=False)
+    x_out = residual(x1, yd)
+    return {"n1": n1, "qkv": qkv, "q": q, "k": k, "v": v, "o": o, "x1": x1, "n2": n2, "a": a, "x_out": x_out}
+
+
+def _bf16_of_f64(y) -> np.ndarray:
+    """bf16 bits of f32(y) for a large array, by the oracle's own rounding rule
+    applied through residual() with a zero residual (bf16(f32(0 + f32(y))))."""
+    zero = np.zeros(np.shape(y), np.uint16)
+    return residual(zero, y)

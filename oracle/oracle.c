@@ -32,6 +32,22 @@
  *   x' = bf16(f32(a . Wdown^T))      the last layer also reports f32(a . Wdown^T)
  *
  * where f32() and bf16() round to nearest even.
+ *
+ * The whole decoder layer (Fleet reading note, TL;DR and Summary: about seven
+ * operators per layer of a Qwen3-8B-shaped decoder; section 1, system scope:
+ * grouped-query attention with 32 query and 8 key/value heads, RMSNorm,
+ * residual adds, the SiLU-gated MLP) is, per layer, on the residual stream x:
+ *
+ *   n1  = bf16(rmsnorm(x) * w_attn)               rmsnorm(v) = v / sqrt(mean(v^2) + eps)
+ *   qkv = bf16(f32(n1 . Wqkv^T))                  q: Hq heads, k and v: Hkv heads of hd values
+ *   o   = bf16(attention(q, K|k, V|v))            per query head h, key/value head h / (Hq/Hkv),
+ *                                                 over the T cached positions and the new one
+ *   x1  = bf16(f32(x + f32(o . Wo^T)))
+ *   n2  = bf16(rmsnorm(x1) * w_mlp)
+ *   a   = bf16(f32(silu(g) * u)),  [g|u] = f32(n2 . Wgu^T)
+ *   x'  = bf16(f32(x1 + f32(a . Wdown^T)))
+ *
+ * attention(q_h, K, V) = sum_t softmax_t(q_h . k_t / sqrt(hd)) v_t in double.
  */
 #include <math.h>
 #include <stddef.h>
@@ -131,4 +147,68 @@ void oracle_layer(int M, int d, int q, int dff, const uint16_t* x_in,
     if (y_f32) y_f32[i] = (float)y[i];
   }
   free(y);
+}
+
+
+/* RMSNorm of each row of x [M][d] (bf16), times the weight w [d] (bf16):
+ * out = bf16(f32(x / sqrt(mean(x^2) + eps) * w)), in double. */
+void oracle_rmsnorm(int M, int d, const uint16_t* x, const uint16_t* w, double eps, uint16_t* out) {
+  for (int m = 0; m < M; ++m) {
+    const uint16_t* xm = x + (size_t)m * d;
+    double ss = 0.0;
+    for (int k = 0; k < d; ++k) ss += bf16_value(xm[k]) * bf16_value(xm[k]);
+    const double inv = 1.0 / sqrt(ss / d + eps);
+    for (int k = 0; k < d; ++k)
+      out[(size_t)m * d + k] = oracle_bf16_from_float((float)(bf16_value(xm[k]) * inv * bf16_value(w[k])));
+  }
+}
+
+/* Grouped-query decode attention for M sequences, one new token each.
+ *   q       [M][Hq*hd]           the new token's queries (bf16)
+ *   kc, vc  [M][Hkv][T][hd]      the T cached keys and values of each sequence (bf16)
+ *   kn, vn  [M][Hkv*hd]          the new token's key and value (bf16), position T
+ *   out     [M][Hq*hd]           bf16 of sum_t p_t v_t, p = softmax over t of q.k_t / sqrt(hd)
+ * Query head h reads key/value head h / (Hq / Hkv).  Double throughout;
+ * the softmax subtracts the maximum score. */
+void oracle_gqa_decode(int M, int Hq, int Hkv, int hd, int T, const uint16_t* q, const uint16_t* kc,
+                       const uint16_t* vc, const uint16_t* kn, const uint16_t* vn, uint16_t* out) {
+  const int grp = Hq / Hkv;
+  const double scale = 1.0 / sqrt((double)hd);
+  double* s = (double*)malloc((size_t)(T + 1) * sizeof(double));
+  double* acc = (double*)malloc((size_t)hd * sizeof(double));
+  if (!s || !acc) abort();
+  for (int m = 0; m < M; ++m)
+    for (int h = 0; h < Hq; ++h) {
+      const int g = h / grp;
+      const uint16_t* qh = q + (size_t)m * Hq * hd + (size_t)h * hd;
+      double mx = -INFINITY;
+      for (int t = 0; t <= T; ++t) {
+        const uint16_t* kt = t < T ? kc + (((size_t)m * Hkv + g) * T + t) * hd : kn + (size_t)m * Hkv * hd + (size_t)g * hd;
+        double dot = 0.0;
+        for (int i = 0; i < hd; ++i) dot += bf16_value(qh[i]) * bf16_value(kt[i]);
+        s[t] = dot * scale;
+        if (s[t] > mx) mx = s[t];
+      }
+      double l = 0.0;
+      for (int t = 0; t <= T; ++t) {
+        s[t] = exp(s[t] - mx);
+        l += s[t];
+      }
+      for (int i = 0; i < hd; ++i) acc[i] = 0.0;
+      for (int t = 0; t <= T; ++t) {
+        const uint16_t* vt = t < T ? vc + (((size_t)m * Hkv + g) * T + t) * hd : vn + (size_t)m * Hkv * hd + (size_t)g * hd;
+        for (int i = 0; i < hd; ++i) acc[i] += s[t] * bf16_value(vt[i]);
+      }
+      for (int i = 0; i < hd; ++i)
+        out[(size_t)m * Hq * hd + (size_t)h * hd + i] = oracle_bf16_from_float((float)(acc[i] / l));
+    }
+  free(s);
+  free(acc);
+}
+
+/* Residual add: out = bf16(f32(x + f32(y))), x bf16, y a projection's exact
+ * (double) result; [n] elements. */
+void oracle_residual(long n, const uint16_t* x, const double* y, uint16_t* out) {
+  for (long i = 0; i < n; ++i)
+    out[i] = oracle_bf16_from_float((float)(bf16_value(x[i]) + (double)(float)y[i]));
 }

@@ -275,3 +275,166 @@ def test_tolerance_helpers():
     assert oracle.bf16_ulp(-3.0) == 2.0 ** -6
     b = oracle.bound(np.array([1.0]), y_ref=np.array([1.0]), bf16_out=True)
     assert math.isclose(b[0], 2e-3 + 1e-6 + 2 ** -7)
+
+
+# ------------------------------------------------------- decoder-layer pieces
+def _f(b):
+    return synth.bf16_bits_to_f32(b).astype(np.float64)
+
+
+def test_rmsnorm_constant_row_and_scale_invariance():
+    """A constant row c normalises to sign(c) (times the weight); scaling a
+    row by a power of two leaves the result unchanged (eps negligible)."""
+    d = 64
+    w = synth.f32_to_bf16_bits(np.linspace(0.5, 2.0, d).astype(np.float32))
+    x = synth.f32_to_bf16_bits(np.array([[3.0] * d, [-0.25] * d], np.float32))
+    out = _f(oracle.rmsnorm(x, w, eps=0.0))
+    assert np.array_equal(out[0], _f(w)) and np.array_equal(out[1], -_f(w))
+    r = synth.normal_bf16(21, 3, 1000)
+    w2 = synth.uniform_bf16(22, 1, 1000, 1.0)[0]
+    base = oracle.rmsnorm(r, w2, eps=1e-30)
+    for a in (-3, 5):
+        scaled = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(r) * np.float32(2.0 ** a))
+        assert np.array_equal(oracle.rmsnorm(scaled, w2, eps=1e-30), base)
+
+
+def test_rmsnorm_against_numpy():
+    x = synth.normal_bf16(23, 5, 4096)
+    w = synth.uniform_bf16(24, 1, 4096, 2.0)[0]
+    got = _f(oracle.rmsnorm(x, w))
+    xf = _f(x)
+    ref = xf / np.sqrt(np.mean(xf ** 2, axis=1, keepdims=True) + oracle.RMS_EPS) * _f(w)[None, :]
+    assert np.all(np.abs(got - ref) <= oracle.bf16_ulp(ref))
+
+
+def _attn_inputs(M, Hq, Hkv, hd, T, seed):
+    q = synth.normal_bf16(seed, M, Hq * hd)
+    kc = synth.normal_bf16(seed + 1, M * Hkv * T, hd).reshape(M, Hkv, T, hd)
+    vc = synth.normal_bf16(seed + 2, M * Hkv * T, hd).reshape(M, Hkv, T, hd)
+    kn = synth.normal_bf16(seed + 3, M, Hkv * hd)
+    vn = synth.normal_bf16(seed + 4, M, Hkv * hd)
+    return q, kc, vc, kn, vn
+
+
+def test_attention_equal_keys_give_the_mean_of_values():
+    """All keys equal (cached and new): uniform weights, the output is the mean
+    of the T + 1 values of the query's key/value head."""
+    M, Hq, Hkv, hd, T = 2, 8, 2, 16, 9
+    q, kc, vc, kn, vn = _attn_inputs(M, Hq, Hkv, hd, T, 31)
+    key = synth.normal_bf16(40, 1, hd)[0]
+    kc[:] = key
+    kn[:] = np.tile(key, Hkv)
+    out = _f(oracle.gqa_decode(q, kc, vc, kn, vn, Hq, Hkv)).reshape(M, Hq, hd)
+    for m in range(M):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            vals = np.concatenate([_f(vc[m, g]), _f(vn[m].reshape(Hkv, hd)[g])[None, :]])
+            ref = vals.mean(axis=0)
+            assert np.all(np.abs(out[m, h] - ref) <= oracle.bf16_ulp(ref)), (m, h)
+
+
+def test_attention_dominant_key_selects_its_value_and_head_groups():
+    """One key aligned with a large multiple of the query dominates the
+    softmax, so the output is that position's value; value heads filled with
+    a constant per key/value head show the grouping h -> h / (Hq / Hkv)."""
+    M, Hq, Hkv, hd, T = 1, 8, 4, 32, 6
+    q, kc, vc, kn, vn = _attn_inputs(M, Hq, Hkv, hd, T, 51)
+    qf = _f(q).reshape(Hq, hd)
+    kc[:] = 0
+    kn[:] = 0
+    for g in range(Hkv):
+        # position 3 of key head g: 64 x the first query of its group, others zero
+        kc[0, g, 3] = synth.f32_to_bf16_bits((qf[g * (Hq // Hkv)] * 64.0).astype(np.float32))
+    out = _f(oracle.gqa_decode(q, kc, vc, kn, vn, Hq, Hkv)).reshape(Hq, hd)
+    for g in range(Hkv):
+        h = g * (Hq // Hkv)
+        assert np.array_equal(out[h], _f(vc[0, g, 3])), h
+    vc2 = np.empty_like(vc)
+    vn2 = np.empty_like(vn)
+    for g in range(Hkv):
+        vc2[:, g] = synth.f32_to_bf16_bits(np.float32(0.5 * (g + 1)))
+        vn2.reshape(M, Hkv, hd)[:, g] = synth.f32_to_bf16_bits(np.float32(0.5 * (g + 1)))
+    out2 = _f(oracle.gqa_decode(q, kc, vc2, kn, vn2, Hq, Hkv)).reshape(Hq, hd)
+    for h in range(Hq):
+        assert np.all(out2[h] == 0.5 * (h // (Hq // Hkv) + 1)), h
+
+
+def test_attention_permutation_and_value_scaling():
+    """Permuting the cached positions (keys with their values) leaves the
+    output unchanged; doubling every value doubles it exactly."""
+    M, Hq, Hkv, hd, T = 2, 4, 2, 16, 11
+    q, kc, vc, kn, vn = _attn_inputs(M, Hq, Hkv, hd, T, 61)
+    base = oracle.gqa_decode(q, kc, vc, kn, vn, Hq, Hkv)
+    perm = np.random.default_rng(0).permutation(T)
+    got = oracle.gqa_decode(q, kc[:, :, perm], vc[:, :, perm], kn, vn, Hq, Hkv)
+    assert np.all(np.abs(_f(got) - _f(base)) <= oracle.bf16_ulp(_f(base)))
+    two = lambda b: synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(b) * np.float32(2.0))
+    assert np.array_equal(_f(oracle.gqa_decode(q, kc, two(vc), kn, two(vn), Hq, Hkv)), 2.0 * _f(base))
+
+
+def test_attention_against_numpy_softmax():
+    special = pytest.importorskip("scipy.special")
+    M, Hq, Hkv, hd, T = 3, 8, 2, 32, 20
+    q, kc, vc, kn, vn = _attn_inputs(M, Hq, Hkv, hd, T, 71)
+    got = _f(oracle.gqa_decode(q, kc, vc, kn, vn, Hq, Hkv)).reshape(M, Hq, hd)
+    K = np.concatenate([_f(kc), _f(kn).reshape(M, Hkv, 1, hd)], axis=2)
+    V = np.concatenate([_f(vc), _f(vn).reshape(M, Hkv, 1, hd)], axis=2)
+    Q = _f(q).reshape(M, Hq, hd)
+    for m in range(M):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            p = special.softmax(K[m, g] @ Q[m, h] / np.sqrt(hd))
+            ref = p @ V[m, g]
+            assert np.all(np.abs(got[m, h] - ref) <= oracle.bf16_ulp(ref) * 1.0001 + 1e-30), (m, h)
+
+
+def test_residual_identities():
+    x = synth.normal_bf16(81, 4, 50)
+    assert np.array_equal(oracle.residual(x, np.zeros((4, 50))), x)
+    y = np.random.default_rng(1).normal(size=(4, 50))
+    zero = np.zeros((4, 50), np.uint16)
+    assert np.array_equal(oracle.residual(zero, y), synth.f32_to_bf16_bits(y.astype(np.float32)))
+    # x + f32(y) is one fp32 rounding, then one bf16 rounding
+    ref = synth.f32_to_bf16_bits((_f(x) + y.astype(np.float32).astype(np.float64)).astype(np.float32))
+    assert np.array_equal(oracle.residual(x, y), ref)
+
+
+def test_decoder_layer_small_against_numpy_composition():
+    special = pytest.importorskip("scipy.special")
+    M, d, Hq, Hkv, hd, T, dff = 2, 64, 4, 2, 16, 5, 96
+    qc, kvc = Hq * hd, Hkv * hd
+    x = synth.normal_bf16(91, M, d)
+    w_attn = synth.uniform_bf16(92, 1, d, 2.0)[0]
+    w_mlp = synth.uniform_bf16(93, 1, d, 2.0)[0]
+    wqkv = synth.uniform_bf16(94, qc + 2 * kvc, d, synth.weight_scale(d))
+    wo = synth.uniform_bf16(95, d, qc, synth.weight_scale(qc))
+    wgu = synth.uniform_bf16(96, 2 * dff, d, synth.weight_scale(d))
+    wdown = synth.uniform_bf16(97, d, dff, synth.weight_scale(dff))
+    kc = synth.normal_bf16(98, M * Hkv * T, hd).reshape(M, Hkv, T, hd)
+    vc = synth.normal_bf16(99, M * Hkv * T, hd).reshape(M, Hkv, T, hd)
+    r = oracle.decoder_layer(x, w_attn, wqkv, kc, vc, wo, w_mlp, wgu, wdown, Hq, Hkv)
+    b = lambda v: _f(synth.f32_to_bf16_bits(np.asarray(v, np.float64).astype(np.float32)))
+    xf = _f(x)
+    n1 = b(xf / np.sqrt(np.mean(xf ** 2, 1, keepdims=True) + oracle.RMS_EPS) * _f(w_attn))
+    qkv = b(n1 @ _f(wqkv).T)
+    q, k, v = qkv[:, :qc], qkv[:, qc:qc + kvc], qkv[:, qc + kvc:]
+    K = np.concatenate([_f(kc), k.reshape(M, Hkv, 1, hd)], axis=2)
+    V = np.concatenate([_f(vc), v.reshape(M, Hkv, 1, hd)], axis=2)
+    o = np.zeros((M, qc))
+    for m in range(M):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            p = special.softmax(K[m, g] @ q[m, h * hd:(h + 1) * hd] / np.sqrt(hd))
+            o[m, h * hd:(h + 1) * hd] = p @ V[m, g]
+    o = b(o)
+    x1 = b(xf + (o @ _f(wo).T).astype(np.float32))
+    n2 = b(x1 / np.sqrt(np.mean(x1 ** 2, 1, keepdims=True) + oracle.RMS_EPS) * _f(w_mlp))
+    gu = (n2 @ _f(wgu).T).astype(np.float32).astype(np.float64)
+    a = b(gu[:, :dff] * special.expit(gu[:, :dff]) * gu[:, dff:])
+    xo = b(x1 + (a @ _f(wdown).T).astype(np.float32))
+    for name, ref in (("n1", n1), ("qkv", qkv), ("o", o), ("x1", x1), ("n2", n2), ("a", a), ("x_out", xo)):
+        got = _f(r[name])
+        # each stage is compared on the previous stage's oracle value, so a
+        # one-ulp rounding difference upstream may move a value by a few ulp
+        assert np.all(np.abs(got - ref) <= 4 * oracle.bf16_ulp(ref) + 1e-30), name
+        assert np.mean(got == ref) > 0.9, name
