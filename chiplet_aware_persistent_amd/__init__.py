@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libsgemm.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "sgemm.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_TIMEOUT, ERR_WORKSPACE, ERR_TOPOLOGY = 0, -1, -2, -3, -4, -5, -6
-KIND_GEMM, KIND_LAYERCHAIN = 0, 1
+KIND_GEMM, KIND_LAYERCHAIN, KIND_DECODER = 0, 1, 2
 OUT_F32, OUT_BF16 = 0, 1
 F_FORCE_DOT2 = 1 << 0
 F_FORCE_MFMA = 1 << 1
@@ -52,7 +52,8 @@ class Problem(ctypes.Structure):
                 ("out_dtype", ctypes.c_int), ("n_layers", ctypes.c_int), ("d_model", ctypes.c_int),
                 ("q_cols", ctypes.c_int), ("d_ff", ctypes.c_int), ("flags", ctypes.c_uint),
                 ("tn", ctypes.c_int), ("splitk", ctypes.c_int), ("waves", ctypes.c_int),
-                ("kslices", ctypes.c_int), ("tm", ctypes.c_int)]
+                ("kslices", ctypes.c_int), ("tm", ctypes.c_int), ("n_heads", ctypes.c_int),
+                ("n_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("ctx", ctypes.c_int)]
 
 
 _lib = None
@@ -83,9 +84,11 @@ def library() -> ctypes.CDLL:
         lib.sgemm_read_probe.argtypes = [vp, sz, ctypes.c_int, vp, ctypes.c_int, vp]
         lib.sgemm_device_check.argtypes = [ctypes.c_int]
         lib.sgemm_run_noalloc.argtypes = [vp, vp, vp, vp, vp]
+        lib.decoder_run.argtypes = [vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                    ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp]
         for f in ("sgemm_plan_create", "sgemm_plan_destroy", "sgemm_workspace_init", "sgemm_run",
                   "layerchain_run", "sgemm_chain_buffer", "sgemm_query_status", "sgemm_plan_describe",
-                  "sgemm_topology_probe", "sgemm_read_probe", "sgemm_device_check", "sgemm_run_noalloc"):
+                  "sgemm_topology_probe", "sgemm_read_probe", "sgemm_device_check", "sgemm_run_noalloc", "decoder_run"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -139,6 +142,13 @@ def layerchain_run(plan, X0: int, Wq, Wo, Wgu, Wdown, Y_f32: int, Y_bf16: int, w
     a = [_ptr_array(p) for p in (Wq, Wo, Wgu, Wdown)]
     return library().layerchain_run(plan, X0, a[0][0], a[1][0], a[2][0], a[3][0], Y_f32, Y_bf16 or None,
                                     workspace, stream)
+
+
+def decoder_run(plan, X0: int, w_norm: int, Wqkv, Wo, Wgu, Wdown, K_cache: int, V_cache: int, Y_f32: int,
+                Y_bf16: int, workspace: int, stream: int = 0) -> int:
+    a = [_ptr_array(p) for p in (Wqkv, Wo, Wgu, Wdown)]
+    return library().decoder_run(plan, X0, w_norm, a[0][0], a[1][0], a[2][0], a[3][0], K_cache or None,
+                                 V_cache or None, Y_f32, Y_bf16 or None, workspace, stream)
 
 
 def sgemm_chain_buffer(plan, layer: int, which: int):
@@ -316,3 +326,57 @@ def topology(n_wg: int = 256, device: int = 0):
     _check(sgemm_topology_probe(out.data_ptr(), n_wg, _stream_handle(None)), "sgemm_topology_probe")
     torch.cuda.synchronize()
     return out.cpu().tolist()
+
+
+class Decoder(_PlanBase):
+    """The whole decoder layer (RMSNorm, QKV, grouped-query decode attention,
+    O with residual, RMSNorm, gate_up with SiLU gate, down with residual), all
+    layers in one persistent launch."""
+
+    def __init__(self, M: int, n_layers: int, d_model: int, d_ff: int, n_heads: int, n_kv_heads: int,
+                 head_dim: int, ctx: int, flags: int = 0, tn: int = 0, splitk: int = 0, waves: int = 0,
+                 kslices: int = 0, device: int = 0):
+        p = Problem(KIND_DECODER, M, 0, 0, 0, n_layers, d_model, 0, d_ff, flags, tn, splitk, waves, kslices, 0,
+                    n_heads, n_kv_heads, head_dim, ctx)
+        super().__init__(p, device)
+        self.M, self.n_layers, self.d, self.dff = M, n_layers, d_model, d_ff
+        self.Hq, self.Hkv, self.hd, self.T = n_heads, n_kv_heads, head_dim, ctx
+        self.q, self.kv = n_heads * head_dim, n_kv_heads * head_dim
+
+    def __call__(self, X0, w_norm, Wqkv, Wo, Wgu, Wdown, K_cache, V_cache, Y_f32, workspace, Y_bf16=None,
+                 stream=None):
+        import torch
+
+        L = self.n_layers
+        if not (len(Wqkv) == len(Wo) == len(Wgu) == len(Wdown) == L):
+            raise ValueError("expected %d weight tensors per projection" % L)
+        for l in range(L):
+            _need(Wqkv[l], (self.q + 2 * self.kv, self.d), torch.bfloat16, "Wqkv[%d]" % l)
+            _need(Wo[l], (self.d, self.q), torch.bfloat16, "Wo[%d]" % l)
+            _need(Wgu[l], (2 * self.dff, self.d), torch.bfloat16, "Wgu[%d]" % l)
+            _need(Wdown[l], (self.d, self.dff), torch.bfloat16, "Wdown[%d]" % l)
+        _need(X0, (self.M, self.d), torch.bfloat16, "X0")
+        _need(w_norm, (L, 2, self.d), torch.bfloat16, "w_norm")
+        cache = (L, self.M, self.Hkv, self.T, self.hd)
+        _need(K_cache, cache, torch.bfloat16, "K_cache")
+        _need(V_cache, cache, torch.bfloat16, "V_cache")
+        _need(Y_f32, (self.M, self.d), torch.float32, "Y_f32")
+        if Y_bf16 is not None:
+            _need(Y_bf16, (self.M, self.d), torch.bfloat16, "Y_bf16")
+        _need_workspace(workspace, self.workspace_bytes)
+        _check(decoder_run(self.handle, X0.data_ptr(), w_norm.data_ptr(), [w.data_ptr() for w in Wqkv],
+                           [w.data_ptr() for w in Wo], [w.data_ptr() for w in Wgu], [w.data_ptr() for w in Wdown],
+                           K_cache.data_ptr() if self.T else 0, V_cache.data_ptr() if self.T else 0,
+                           Y_f32.data_ptr(), Y_bf16.data_ptr() if Y_bf16 is not None else 0, workspace.data_ptr(),
+                           _stream_handle(stream)), "decoder_run")
+        return Y_f32
+
+    def activation(self, workspace, layer: int, which: int):
+        """View of an intermediate kept in the workspace: which = 0 qkv, 1 o,
+        2 x1, 3 a, 4 x' (bf16 [M][cols])."""
+        import torch
+
+        rc, off, nb = sgemm_chain_buffer(self.handle, layer, which)
+        _check(rc, "sgemm_chain_buffer")
+        cols = nb // (2 * self.M)
+        return workspace[off:off + nb].view(torch.bfloat16).view(self.M, cols)

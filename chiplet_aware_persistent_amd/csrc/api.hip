@@ -74,6 +74,7 @@ struct Cost {
   double fin_us_kb;  // per kilobyte of partials an owner reads
   double ksl_us;     // per item with K slices (two workgroup barriers, LDS exchange)
   bool chain;        // a chain stage (up to two m-tiles it keeps the deeper MFMA ring)
+  int lds_reserve = 0;  // LDS bytes kept free after the stage's own (the decoder's norm factors)
 };
 constexpr Cost kCostGemm{1.0, 200.0e9, 6.0, 0.05, 0.0, false};
 // Chain constants fitted to whole-chain times of per-stage forced plans at
@@ -128,12 +129,13 @@ bool shape_geo(Geo& g, int want_S, const Cost& cost) {
   g.stash_off = g.red_off + red_bytes;
   const int owners = g.ksl > 1 ? g.wpi / g.ksl : g.waves;
   const int per_stream = ceil_div(g.items, g.slots * g.ng);
-  g.stash_cap = std::max(0, std::min(per_stream, (kLdsMax - g.stash_off) / (owners * tile_bytes)));
+  const int lds_cap = kLdsMax - cost.lds_reserve;
+  g.stash_cap = std::max(0, std::min(per_stream, (lds_cap - g.stash_off) / (owners * tile_bytes)));
   g.lds = g.stash_off + owners * g.stash_cap * tile_bytes;
   const int vals = g.path == 0 ? g.tb * g.M : g.tb * g.ta * 256;
   g.ctr_count = (size_t)kXcds * g.NB * g.wpi * g.mtiles;
   g.part_floats = g.S > 1 ? g.ctr_count * (size_t)g.S * vals : 0;
-  if (g.stash_off > kLdsMax) return false;
+  if (g.stash_off > lds_cap) return false;
   // MFMA with S == 1 emits Y only from the stash (no epilogue inside the
   // weight loop), so every item of a stream must fit it.
   if (g.path == 1 && g.S == 1 && g.stash_cap < per_stream) return false;
@@ -314,6 +316,9 @@ struct sgemm_plan_s {
   size_t c_ctr[kChainStages] = {0}, c_part[kChainStages] = {0};
   size_t off_lctr = 0, off_gctr = 0, off_xflag = 0, off_ready = 0, off_act = 0, off_stamps = 0;
   size_t act_layer_elems = 0, a_h1 = 0, a_h2 = 0, a_a = 0, a_x = 0;
+  // Decoder layer: activations qkv = a_h1, o = a_h2, x1, a = a_a, x' = a_x; attention partials and counters.
+  size_t a_x1 = 0, off_apart = 0, off_actr = 0;
+  int nchunk = 0, norm_off = 0, dec_lds = 0;
   long long spin_ticks = 0;
 };
 
@@ -362,6 +367,103 @@ static void layout_stage_ws(size_t& cursor, const Geo& g, size_t& off_ctr, size_
   cursor = round_up(cursor + g.ctr_count * 4, 256);
   off_part = cursor;
   cursor = round_up(cursor + g.part_floats * 4, 256);
+}
+
+// The whole decoder layer (kind DECODER): four GEMM stages planned as the
+// chain's (QKV [d -> q + 2 kv], O [q -> d], gate_up paired [d -> d_ff], down
+// [d_ff -> d]) with 256 B of LDS kept for the RMSNorm factors, the attention
+// stage's chunking, and the workspace layout.  Fills pl->ws_bytes.
+static int plan_decoder(sgemm_plan_s* pl, const sgemm_problem& p, int tn_o, int s_o, int w_o, int k_o) {
+  const unsigned refused = SGEMM_F_SYNC_FLAT | SGEMM_F_POLL_LEADER | SGEMM_F_SCHEDULER | SGEMM_F_LAUNCH_PER_STAGE |
+                           SGEMM_F_W_CACHED | SGEMM_F_W_SC1 | SGEMM_F_MTILE_ITEMS | SGEMM_F_MSPLIT | SGEMM_F_KCHUNK |
+                           SGEMM_F_CHECK_PLACEMENT;
+  if (p.flags & refused) return SGEMM_ERR_UNSUPPORTED;
+  if (p.tm) return SGEMM_ERR_INVALID_ARG;
+  if (p.M < 1 || p.n_layers < 1 || p.d_model < 8 || p.d_ff < 8 || p.n_heads < 1 || p.n_kv_heads < 1 ||
+      p.head_dim < 1 || p.ctx < 0)
+    return SGEMM_ERR_INVALID_ARG;
+  if (p.d_model % 8 || p.d_ff % 8 || p.n_heads % p.n_kv_heads) return SGEMM_ERR_INVALID_ARG;
+  // Built: four query heads per key/value head, head dimension 128, up to
+  // 64 attention chunks of 64 positions, M <= 64.
+  if (p.n_heads / p.n_kv_heads != 4 || p.head_dim != 128) return SGEMM_ERR_UNSUPPORTED;
+  if (p.M > 64 || p.n_layers > kMaxLayers || p.ctx + 1 > 64 * 64) return SGEMM_ERR_UNSUPPORTED;
+  if (p.q_cols && p.q_cols != p.n_heads * p.head_dim) return SGEMM_ERR_INVALID_ARG;
+  if ((p.flags & SGEMM_F_FORCE_DOT2) && p.M >= 16) return SGEMM_ERR_UNSUPPORTED;
+  const size_t M = p.M, d = p.d_model, dff = p.d_ff, q = (size_t)p.n_heads * p.head_dim,
+               kv = (size_t)p.n_kv_heads * p.head_dim;
+  const size_t ext[] = {(q + 2 * kv) * d * 2, d * q * 2, 2 * dff * d * 2, d * dff * 2, M * (q + 2 * kv) * 2,
+                        M * d * 4, M * 2 * dff * 2, M * kv * (size_t)p.ctx * 2, M * q * 2};
+  for (size_t e : ext)
+    if (e >= kMaxOperand) return SGEMM_ERR_UNSUPPORTED;
+  const int Ks[4] = {p.d_model, (int)q, p.d_model, p.d_ff};
+  const int Ns[4] = {(int)(q + 2 * kv), p.d_model, p.d_ff, p.d_model};
+  Cost cost = kCostChain;
+  cost.lds_reserve = 256;
+  const int path = (p.flags & SGEMM_F_FORCE_DOT2) ? 0 : (p.flags & SGEMM_F_FORCE_MFMA) ? 1 : (p.M <= 2 ? 0 : 1);
+  double best = -1.0;
+  for (int waves = 8; waves >= 4; waves -= 4) {
+    if (w_o && waves != w_o) continue;
+    for (int tb = 1; tb <= (path == 0 ? 4 : 2); ++tb) {
+      if (path == 0 && tb != 2 && tb != 4) continue;
+      if (tn_o && tn_o != (path == 0 ? tb : 16 * tb)) continue;
+      const int a = path == 0 ? p.M : (p.M + 15) / 16;
+      if (!decoder_variant_exists(path, a, tb)) continue;
+      Geo c[kChainStages];
+      double tot = 0.0;
+      bool ok = true;
+      for (int s = 0; s < kChainStages && ok; ++s) {
+        const int paired = s == 2;
+        const int tn = path == 0 ? tb : (paired ? 0 : 16 * tb);
+        if (path == 0 && k_o > 1) { ok = false; break; }
+        ok = plan_geo(c[s], p.M, Ks[s], Ns[s], path, paired, tn, s_o, waves, path == 0 ? 1 : k_o, cost);
+        if (ok && paired) c[s].pair_off = p.d_ff;
+        tot += ok ? c[s].est_us : 0.0;
+      }
+      if (ok && (best < 0.0 || tot < best)) {
+        best = tot;
+        for (int s = 0; s < kChainStages; ++s) pl->cg[s] = c[s];
+      }
+    }
+  }
+  if (best < 0.0) return SGEMM_ERR_UNSUPPORTED;
+  size_t cur = kCtl;
+  for (int s = 0; s < kChainStages; ++s) {
+    if (pl->cg[s].part_floats * 4 >= kMaxOperand) return SGEMM_ERR_UNSUPPORTED;
+    layout_stage_ws(cur, pl->cg[s], pl->c_ctr[s], pl->c_part[s]);
+  }
+  const int events = 5 * p.n_layers;
+  pl->off_lctr = cur;
+  cur = round_up(cur + (size_t)kXcds * events * 4, 256);
+  pl->off_gctr = cur;
+  cur = round_up(cur + (size_t)events * 4, 256);
+  pl->off_xflag = cur;
+  cur = round_up(cur + (size_t)kXcds * events * 4, 256);
+  pl->off_ready = cur;
+  cur = round_up(cur + (size_t)kXcds * kWgPerXcd * 4, 256);
+  pl->nchunk = ceil_div(p.ctx + 1, 64);
+  const size_t apart = M * p.n_kv_heads * (size_t)pl->nchunk * 4 * (p.head_dim + 2) * 4;
+  if (apart >= kMaxOperand) return SGEMM_ERR_UNSUPPORTED;
+  pl->off_apart = cur;
+  cur = round_up(cur + apart, 256);
+  pl->off_actr = cur;
+  cur = round_up(cur + M * p.n_kv_heads * 4, 256);
+  pl->a_h1 = 0;                                            // qkv [M][q + 2 kv]
+  pl->a_h2 = round_up(M * (q + 2 * kv), 128);             // o [M][q]
+  pl->a_x1 = pl->a_h2 + round_up(M * q, 128);             // x1 [M][d]
+  pl->a_a = pl->a_x1 + round_up(M * d, 128);              // a [M][d_ff]
+  pl->a_x = pl->a_a + round_up(M * dff, 128);             // x' [M][d]
+  pl->act_layer_elems = pl->a_x + round_up(M * d, 128);
+  pl->off_act = cur;
+  cur = round_up(cur + pl->act_layer_elems * 2 * p.n_layers, 256);
+  pl->off_stamps = cur;
+  if (p.flags & SGEMM_F_STAMPS) cur = round_up(cur + (size_t)pl->grid * events * 2 * 8, 256);
+  int lds = 16 * 1024;  // the attention stage: queries and weights, 2 KB per wave
+  for (int s = 0; s < kChainStages; ++s) lds = std::max(lds, pl->cg[s].lds);
+  pl->norm_off = (int)round_up((size_t)lds, 16);
+  pl->dec_lds = pl->norm_off + 256;
+  if (pl->dec_lds > kLdsMax) return SGEMM_ERR_UNSUPPORTED;
+  pl->ws_bytes = cur;
+  return SGEMM_OK;
 }
 
 extern "C" {
@@ -544,6 +646,11 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     pl->off_stamps = cur;
     if (p.flags & SGEMM_F_STAMPS) cur = round_up(cur + (size_t)pl->grid * events * 2 * 8, 256);
     pl->spin_ticks = (p.flags & SGEMM_F_WATCHDOG_TEST) ? 0 : (long long)(watchdog_s * 1.0e8);
+  } else if (p.kind == SGEMM_KIND_DECODER) {
+    const int rc = plan_decoder(pl, p, tn_o, s_o, w_o, k_o);
+    if (rc != SGEMM_OK) { delete pl; return rc; }
+    cur = pl->ws_bytes;
+    pl->spin_ticks = (p.flags & SGEMM_F_WATCHDOG_TEST) ? 0 : (long long)(watchdog_s * 1.0e8);
   } else {
     delete pl;
     return SGEMM_ERR_INVALID_ARG;
@@ -724,6 +831,7 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   a.ready = (unsigned*)(ws + plan->off_ready);
   a.stamps = (p.flags & SGEMM_F_STAMPS) ? (unsigned long long*)(ws + plan->off_stamps) : nullptr;
   a.n_layers = p.n_layers; a.M = p.M; a.d = p.d_model; a.q = p.q_cols; a.dff = p.d_ff;
+  a.spl = kChainStages;
   a.act_layer_elems = plan->act_layer_elems;
   a.off_h1 = plan->a_h1; a.off_h2 = plan->a_h2; a.off_a = plan->a_a; a.off_x = plan->a_x;
   a.flat_sync = (p.flags & SGEMM_F_SYNC_FLAT) ? 1 : 0;
@@ -754,9 +862,100 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
 }
 
-int sgemm_chain_buffer(sgemm_plan plan, int layer, int which, size_t* offset, size_t* bytes) {
-  if (!plan || !offset || !bytes || plan->prob.kind != SGEMM_KIND_LAYERCHAIN) return SGEMM_ERR_INVALID_ARG;
+int decoder_run(sgemm_plan plan, const void* X0, const void* w_norm, const void* const* Wqkv, const void* const* Wo,
+                const void* const* Wgu, const void* const* Wdown, const void* K_cache, const void* V_cache,
+                float* Y_f32, void* Y_bf16, void* workspace, void* stream) {
+  if (!plan || !X0 || !w_norm || !Wqkv || !Wo || !Wgu || !Wdown || !Y_f32 || !workspace) return SGEMM_ERR_INVALID_ARG;
   const sgemm_problem& p = plan->prob;
+  if (p.kind != SGEMM_KIND_DECODER) return SGEMM_ERR_INVALID_ARG;
+  if (p.ctx > 0 && (!K_cache || !V_cache)) return SGEMM_ERR_INVALID_ARG;
+  if (!aligned16(X0) || !aligned16(w_norm) || !aligned16(Y_f32) || !aligned16(workspace) ||
+      (Y_bf16 && !aligned16(Y_bf16)) || (K_cache && !aligned16(K_cache)) || (V_cache && !aligned16(V_cache)))
+    return SGEMM_ERR_INVALID_ARG;
+  ChainArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int l = 0; l < p.n_layers; ++l) {
+    if (!Wqkv[l] || !Wo[l] || !Wgu[l] || !Wdown[l]) return SGEMM_ERR_INVALID_ARG;
+    if (!aligned16(Wqkv[l]) || !aligned16(Wo[l]) || !aligned16(Wgu[l]) || !aligned16(Wdown[l]))
+      return SGEMM_ERR_INVALID_ARG;
+    a.wq[l] = (const uint16_t*)Wqkv[l];
+    a.wo[l] = (const uint16_t*)Wo[l];
+    a.wgu[l] = (const uint16_t*)Wgu[l];
+    a.wdown[l] = (const uint16_t*)Wdown[l];
+  }
+  char* ws = (char*)workspace;
+  const int q = p.n_heads * p.head_dim, kv = p.n_kv_heads * p.head_dim;
+  const int Ks[4] = {p.d_model, q, p.d_model, p.d_ff};
+  const int Ns[4] = {q + 2 * kv, p.d_model, p.d_ff, p.d_model};
+  const int Wrows[4] = {q + 2 * kv, p.d_model, 2 * p.d_ff, p.d_model};
+  for (int s = 0; s < kChainStages; ++s) {
+    StageDesc d = stage_desc(plan->cg[s], plan->w_aux, plan->sync);
+    d.part = (float*)(ws + plan->c_part[s]);
+    d.part_bytes = (unsigned)(plan->cg[s].part_floats * 4);
+    d.ctr = (unsigned*)(ws + plan->c_ctr[s]);
+    d.ldx = Ks[s];
+    d.ldy = Ns[s];
+    d.x_bytes = (unsigned)((size_t)p.M * Ks[s] * 2);
+    d.w_bytes = (unsigned)((size_t)Wrows[s] * Ks[s] * 2);
+    d.y_bytes = (unsigned)((size_t)p.M * Ns[s] * 2);
+    d.r_bytes = (unsigned)((size_t)p.M * Ns[s] * 2);
+    d.mode = s == 2 ? OUT_SILU_BF16 : OUT_BF16;
+    d.y2_bytes = s == 3 ? (unsigned)((size_t)p.M * p.d_model * 4) : 0u;
+    a.st[s] = d;
+  }
+  a.x0 = (const uint16_t*)X0;
+  a.act = (uint16_t*)(ws + plan->off_act);
+  a.y_f32 = Y_f32;
+  a.y_bf16 = (uint16_t*)Y_bf16;
+  a.status = (unsigned*)ws;
+  a.done = (unsigned*)(ws + 64);
+  a.claim = (unsigned*)(ws + 128);
+  a.lctr = (unsigned*)(ws + plan->off_lctr);
+  a.gctr = (unsigned*)(ws + plan->off_gctr);
+  a.xflag = (unsigned*)(ws + plan->off_xflag);
+  a.ready = (unsigned*)(ws + plan->off_ready);
+  a.stamps = (p.flags & SGEMM_F_STAMPS) ? (unsigned long long*)(ws + plan->off_stamps) : nullptr;
+  a.n_layers = p.n_layers; a.M = p.M; a.d = p.d_model; a.q = q; a.dff = p.d_ff;
+  a.spl = 5;
+  a.act_layer_elems = plan->act_layer_elems;
+  a.off_qkv = plan->a_h1; a.off_o = plan->a_h2; a.off_x1 = plan->a_x1; a.off_a = plan->a_a; a.off_x = plan->a_x;
+  a.wnorm = (const uint16_t*)w_norm;
+  a.kc = (const uint16_t*)K_cache;
+  a.vc = (const uint16_t*)V_cache;
+  a.apart = (float*)(ws + plan->off_apart);
+  a.actr = (unsigned*)(ws + plan->off_actr);
+  a.Hq = p.n_heads; a.Hkv = p.n_kv_heads; a.hd = p.head_dim; a.T = p.ctx; a.pc = 64; a.nchunk = plan->nchunk;
+  a.eps = 1e-6f;
+  a.norm_off = plan->norm_off;
+  a.spin_ticks = plan->spin_ticks;
+  a.path = plan->cg[0].path;
+  a.mt = plan->cg[0].ta;
+  a.nt_q = plan->cg[0].tb; a.nt_o = plan->cg[1].tb; a.nt_d = plan->cg[3].tb;
+  a.e_begin = 0;
+  a.e_end = 5 * p.n_layers;
+  if (const int dc = device_check(plan->device); dc != SGEMM_OK) return dc;
+  if (hipSetDevice(plan->device) != hipSuccess) return SGEMM_ERR_HIP;
+  hipError_t e = launch_decoder(a, plan->grid, plan->cg[0].waves * 64, plan->dec_lds, (hipStream_t)stream);
+  if (e == hipSuccess && Y_bf16) {
+    const size_t off = plan->off_act + ((size_t)(p.n_layers - 1) * plan->act_layer_elems + plan->a_x) * 2;
+    e = hipMemcpyAsync(Y_bf16, ws + off, (size_t)p.M * p.d_model * 2, hipMemcpyDeviceToDevice, (hipStream_t)stream);
+  }
+  return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
+}
+
+int sgemm_chain_buffer(sgemm_plan plan, int layer, int which, size_t* offset, size_t* bytes) {
+  if (!plan || !offset || !bytes) return SGEMM_ERR_INVALID_ARG;
+  const sgemm_problem& p = plan->prob;
+  if (p.kind == SGEMM_KIND_DECODER) {
+    if (layer < 0 || layer >= p.n_layers || which < 0 || which > 4) return SGEMM_ERR_INVALID_ARG;
+    const size_t q = (size_t)p.n_heads * p.head_dim, kv = (size_t)p.n_kv_heads * p.head_dim;
+    const size_t offs[5] = {plan->a_h1, plan->a_h2, plan->a_x1, plan->a_a, plan->a_x};
+    const size_t cols[5] = {q + 2 * kv, q, (size_t)p.d_model, (size_t)p.d_ff, (size_t)p.d_model};
+    *offset = plan->off_act + ((size_t)layer * plan->act_layer_elems + offs[which]) * 2;
+    *bytes = (size_t)p.M * cols[which] * 2;
+    return SGEMM_OK;
+  }
+  if (p.kind != SGEMM_KIND_LAYERCHAIN) return SGEMM_ERR_INVALID_ARG;
   if (layer < 0 || layer >= p.n_layers || which < 0 || which > 3) return SGEMM_ERR_INVALID_ARG;
   const size_t offs[4] = {plan->a_h1, plan->a_h2, plan->a_a, plan->a_x};
   const size_t cols[4] = {(size_t)p.q_cols, (size_t)p.d_model, (size_t)p.d_ff, (size_t)p.d_model};
@@ -809,7 +1008,7 @@ static std::string geo_json(const Geo& g) {
 int sgemm_plan_describe(sgemm_plan plan, char* buf, size_t len) {
   if (!plan) return SGEMM_ERR_INVALID_ARG;
   std::string s = "{\"kind\":";
-  s += plan->prob.kind == SGEMM_KIND_GEMM ? "\"gemm\"" : "\"layerchain\"";
+  s += plan->prob.kind == SGEMM_KIND_GEMM ? "\"gemm\"" : (plan->prob.kind == SGEMM_KIND_DECODER ? "\"decoder\"" : "\"layerchain\"");
   char b[256];
   std::snprintf(b, sizeof b,
                 ",\"grid\":%d,\"workspace\":%zu,\"w_aux\":%u,\"sync\":\"%s\",\"stamps_offset\":%zu,",

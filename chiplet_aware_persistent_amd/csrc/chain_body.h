@@ -55,9 +55,9 @@ static __device__ __forceinline__ unsigned long long now_ticks() { return wall_c
 // sections 2a and 3b, without a dedicated workgroup): fewer pollers share the
 // counter's address, but the extra hop costs about a microsecond per stage
 // on MI355X, more than the contention of 256 pollers does.
-static __device__ bool wait_event(const ChainArgs& a, int e, int xcd, int slot, int* sh_alive) {
+static __device__ __forceinline__ bool wait_event(const ChainArgs& a, int e, int xcd, int slot, int* sh_alive) {
   if (threadIdx.x == 0) {
-    const int events = 4 * a.n_layers;
+    const int events = a.spl * a.n_layers;
     unsigned* flag = a.xflag + xcd * events + e;
     const unsigned target = a.flat_sync ? gridDim.x : (unsigned)kXcds;
     const bool leader = slot == 0 || a.flat_sync || !a.poll_leader;
@@ -102,7 +102,7 @@ static __device__ bool wait_event(const ChainArgs& a, int e, int xcd, int slot, 
 // XCD's last workgroup writes that L2 back with a device-scope release before
 // it bumps G[e], so the stores of all 32 workgroups reach memory before any
 // consumer, which acquires after seeing G[e] == 8, reads them.
-static __device__ void signal_event(const ChainArgs& a, int e, int xcd, int nslots) {
+static __device__ __forceinline__ void signal_event(const ChainArgs& a, int e, int xcd, int nslots) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   wait_vm0();  // this wave's stores are acknowledged by L2
   __syncthreads();
@@ -111,7 +111,7 @@ static __device__ void signal_event(const ChainArgs& a, int e, int xcd, int nslo
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __hip_atomic_fetch_add(a.gctr + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      const int events = 4 * a.n_layers;
+      const int events = a.spl * a.n_layers;
       const unsigned old =
           __hip_atomic_fetch_add(a.lctr + xcd * events + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (old == (unsigned)(nslots - 1)) {
@@ -128,7 +128,7 @@ static __device__ void signal_event(const ChainArgs& a, int e, int xcd, int nslo
 // 128-byte line, lanes 1..nslots-1 at once).  The acquire-release fence
 // between the two makes the producers' writes visible to a worker that
 // acquires after reading its word.  Returns false if a wait timed out.
-static __device__ bool run_scheduler(const ChainArgs& a, int xcd, int nslots) {
+static __device__ __forceinline__ bool run_scheduler(const ChainArgs& a, int xcd, int nslots) {
   const int lane = threadIdx.x & 63;
   for (int e = a.e_begin; e + 1 < a.e_end; ++e) {
     int ok = 1;
@@ -153,9 +153,9 @@ static __device__ bool run_scheduler(const ChainArgs& a, int xcd, int nslots) {
   return true;
 }
 
-static __device__ void stamp(const ChainArgs& a, int e, int which) {
+static __device__ __forceinline__ void stamp(const ChainArgs& a, int e, int which) {
   if (a.stamps && threadIdx.x == 0) {
-    const int events = 4 * a.n_layers;
+    const int events = a.spl * a.n_layers;
     a.stamps[((size_t)blockIdx.x * events + e) * 2 + which] = now_ticks();
   }
 }
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
   if (sh_last) {
     // Only this launch's events [e_begin, e_end) and their stages touched
     // counters; every other event's counters are still zero.
-    const int events = 4 * a.n_layers;
+    const int events = a.spl * a.n_layers;
     const int ne = a.e_end - a.e_begin;
     for (int i = threadIdx.x; i < ne; i += blockDim.x) a.gctr[a.e_begin + i] = 0u;
     for (int i = threadIdx.x; i < kXcds * ne; i += blockDim.x) {

@@ -350,6 +350,11 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void store_out(const StageDesc& d, Rsrc yr, Rsrc y2r, bool ok, int m,
                                           int col, float v) {
   const unsigned e = (unsigned)m * (unsigned)d.ldy + (unsigned)col;
+  if (d.R) {  // residual stream: y = x + projection, added in fp32 before the rounding
+    const Rsrc rr = make_rsrc(d.R, d.r_bytes);
+    const unsigned short x = (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rr, (int)(ok ? e * 2u : d.r_bytes), 0, 0);
+    v += __builtin_bit_cast(float, (unsigned)x << 16);
+  }
   if (d.mode == OUT_F32) {
     st_f32<kAuxNt>(yr, ok ? e * 4u : d.y_bytes, v);
   } else {
@@ -361,6 +366,15 @@ __device__ __forceinline__ void store_out(const StageDesc& d, Rsrc yr, Rsrc y2r,
 // ------------------------------------------------------------------ stages
 struct NoHook {
   __device__ bool operator()() const { return true; }
+};
+
+// Transform of the staged X window, called after the window's loads are
+// issued and before they are waited for: it may issue loads of its own, and it
+// must leave the window ready (all its loads and its LDS writes complete and
+// a workgroup barrier passed).  The default only waits.
+struct NoNorm {
+  static constexpr bool active = false;
+  __device__ void operator()(uint16_t*, int, int, int, int) const {}
 };
 
 // Per item: stage X for the item's split (only when it changes), stream the
@@ -376,9 +390,9 @@ struct NoHook {
 // PAIRED (the chain's gate_up stage): the wave's G rows are G/2 gate rows and
 // the G/2 up rows pair_off further on; the wave owns G/2 output columns and
 // writes silu(gate) * up.
-template <int M, int G, int AUX, bool PAIRED = false, typename Hook = NoHook>
+template <int M, int G, int AUX, bool PAIRED = false, typename Hook = NoHook, typename XNorm = NoNorm>
 __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
-                           Hook pre_x = Hook()) {
+                           Hook pre_x = Hook(), XNorm xnorm = XNorm()) {
   constexpr int P = ring_depth_dot2(G);
   constexpr int V = pow2_at_least(G * M);
   static_assert(V <= 64, "G*M must fit one wave");
@@ -482,6 +496,7 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
     wait_vm<P * G>();
   } else {
     stage_x_lds(d, xs, M, s_first * d.KS, d.K, xr);
+    if constexpr (XNorm::active) xnorm(xs, M, d.xrow, s_first * d.KS, d.win);
     wait_vm0();
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -592,9 +607,10 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
 // The A operand (X, from LDS) uses the same k slots: for m-tile i lane l'
 // reads row 16i + l'%16 (the zero row M where that passes M) at
 // k = 32h + 8(l'/16).
-template <int MT, int NT, bool PAIRED, int AUX, bool DEEP = false, typename Hook = NoHook, bool MTI = false>
+template <int MT, int NT, bool PAIRED, int AUX, bool DEEP = false, typename Hook = NoHook, bool MTI = false,
+          typename XNorm = NoNorm>
 __device__ __forceinline__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
-                           Hook pre_x = Hook()) {
+                           Hook pre_x = Hook(), XNorm xnorm = XNorm()) {
   constexpr int P = ring_depth_mfma(NT, DEEP);
   constexpr int TW = PAIRED ? 16 : 16 * NT;  // distinct output columns per wave
   constexpr unsigned TILE = NT * MT * 256;   // floats of one wave tile
@@ -777,6 +793,7 @@ __device__ __forceinline__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int
     wait_vm<P * NT * 2>();
   } else {
     stage_x_lds(d, xs, xrows, s_first * d.KS, d.K, xr);
+    if constexpr (XNorm::active) xnorm(xs, d.M, d.xrow, s_first * d.KS, d.win);
     wait_vm0();
   }
   __builtin_amdgcn_sched_barrier(0);

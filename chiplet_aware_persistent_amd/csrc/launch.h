@@ -37,6 +37,18 @@ struct ChainArgs {
   int path;                            // 1: MFMA stages, 0: dot2 stages (M < 16)
   int mt, nt_q, nt_o, nt_d;            // template parameters: MFMA (MT, NT); dot2 (M in mt, G in nt_*)
   int e_begin, e_end;                  // events this launch runs: [e_begin, e_end)
+  int spl;                             // stages (events) per layer: 4 (chain), 5 (decoder)
+  // Decoder layer only (5 stages: QKV with the attention norm, attention,
+  // O with the residual, gate_up with the MLP norm, down with the residual).
+  const uint16_t* wnorm;               // [layers][2][d] bf16: attention and MLP RMSNorm weights
+  const uint16_t* kc;                  // [layers][M][Hkv][T][hd] bf16 cached keys
+  const uint16_t* vc;                  // same, values
+  float* apart;                        // attention chunk partials [M][Hkv][chunks][grp][hd + 2]
+  unsigned* actr;                      // attention combine counters [M][Hkv]
+  int Hq, Hkv, hd, T, pc, nchunk;      // heads, head dim, cached positions, positions per chunk, chunks
+  float eps;                           // RMSNorm epsilon
+  int norm_off;                        // LDS byte offset of the RMSNorm factors (M floats)
+  size_t off_qkv, off_o, off_x1;       // decoder: element offsets of qkv, o and x1 in a layer's block
 };
 
 bool gemm_variant_exists(int path, int a, int b);
@@ -49,5 +61,7 @@ hipError_t launch_stream_read(const void* src, size_t bytes, int pattern, unsign
 
 bool chain_variant_exists(int path, int a, int b);  // MFMA (MT, NT) or dot2 (M, G)
 hipError_t launch_chain(const ChainArgs& a, int grid, int block, int lds, hipStream_t stream);
+bool decoder_variant_exists(int path, int a, int b);
+hipError_t launch_decoder(const ChainArgs& a, int grid, int block, int lds, hipStream_t stream);
 
 }  // namespace sg

@@ -68,6 +68,8 @@ struct StageDesc {
   int sync;            // SyncMode of the split-K arrival
   int check;           // single GEMM: claim (XCD, slot) at the end and latch a duplicate
   int xbuf;            // K-chunked MFMA path: bytes of one X chunk buffer (multiple of 1 KB)
+  const uint16_t* R;   // residual added to every output before its rounding (null: none), [M][ldy] bf16
+  unsigned r_bytes;    // extent of R
   unsigned w_aux;      // cache-policy bits of the weight loads
   unsigned x_bytes, w_bytes, y_bytes, y2_bytes;  // operand extents (buffer bounds)
   unsigned part_bytes;                           // extent of the partial buffer

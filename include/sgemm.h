@@ -54,7 +54,7 @@ typedef enum {
                                  round-robin from some starting XCD          */
 } sgemm_status;
 
-enum { SGEMM_KIND_GEMM = 0, SGEMM_KIND_LAYERCHAIN = 1 };
+enum { SGEMM_KIND_GEMM = 0, SGEMM_KIND_LAYERCHAIN = 1, SGEMM_KIND_DECODER = 2 };
 enum { SGEMM_OUT_F32 = 0, SGEMM_OUT_BF16 = 1 };
 
 /* Plan flags (bitwise OR). */
@@ -158,6 +158,11 @@ typedef struct {
   int tn, splitk, waves, kslices;
   int tm;  /* SGEMM_F_MTILE_ITEMS / SGEMM_F_MSPLIT: rows per item, T_M = 16, 32 or
               64 (0: 16); must be 0 otherwise                                   */
+  /* kind = SGEMM_KIND_DECODER: M, n_layers, d_model, d_ff and these (q_cols is
+     0 or n_heads * head_dim).  Built: n_heads = 4 n_kv_heads, head_dim = 128,
+     ctx + 1 <= 4096 (64 chunks of 64 positions), M <= 64. */
+  int n_heads, n_kv_heads, head_dim; /* query heads, key/value heads, head dim */
+  int ctx;                           /* cached positions T per sequence          */
 } sgemm_problem;
 
 /*
@@ -251,9 +256,42 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq,
                    float* Y_f32, void* Y_bf16, void* workspace, void* stream);
 
 /*
+ * The whole decoder layer, all layers in one persistent launch (kind DECODER;
+ * Fleet reading note, TL;DR and Summary: about seven operators per layer of
+ * a Qwen3-8B-shaped decoder, all inside one megakernel; section 1: grouped-
+ * query attention with 32 query and 8 key/value heads).  Per layer l, on the
+ * residual stream x (X0 for layer 0):
+ *   n1 = bf16(rmsnorm(x) * w_attn)            rmsnorm(v) = v / sqrt(mean(v^2) + 1e-6)
+ *   [q|k|v] = bf16(n1 . Wqkv^T)               q: n_heads x head_dim, k, v: n_kv_heads x head_dim
+ *   o  = bf16(attention)                       query head h reads key/value head h / 4 over the
+ *                                              ctx cached positions and the new k, v (position ctx):
+ *                                              sum_t softmax_t(q_h . k_t / sqrt(head_dim)) v_t
+ *   x1 = bf16(x + o . Wo^T)
+ *   a  = bf16(silu(g) * u), [g|u] = bf16(rmsnorm(x1) * w_mlp) . Wgu^T
+ *   x' = bf16(x1 + a . Wdown^T)               (the last layer's also in fp32, Y_f32)
+ * Pointers (device, 16-byte aligned):
+ *   X0 [M][d_model] bf16; w_norm [n_layers][2][d_model] bf16 (w_attn, w_mlp);
+ *   Wqkv, Wo, Wgu, Wdown: HOST arrays of n_layers device pointers, K-major
+ *     [q + 2 kv][d_model], [d_model][q], [2 d_ff][d_model], [d_model][d_ff]
+ *     (q = n_heads head_dim, kv = n_kv_heads head_dim; rows of Wqkv: q, then k, then v);
+ *   K_cache, V_cache [n_layers][M][n_kv_heads][ctx][head_dim] bf16 (may be NULL when ctx = 0);
+ *   Y_f32 [M][d_model]; Y_bf16 [M][d_model] or NULL.
+ * The caches are read only: the new token's k and v of layer l are left in
+ * the workspace (sgemm_chain_buffer which = 0, columns q .. q + 2 kv) for
+ * the caller to append.  Intermediates: sgemm_chain_buffer which = 0 qkv,
+ * 1 o, 2 x1, 3 a, 4 x'.  Errors and residency as layerchain_run.
+ */
+int decoder_run(sgemm_plan plan, const void* X0, const void* w_norm, const void* const* Wqkv,
+                const void* const* Wo, const void* const* Wgu, const void* const* Wdown,
+                const void* K_cache, const void* V_cache, float* Y_f32, void* Y_bf16, void* workspace,
+                void* stream);
+
+/*
  * Where the chain keeps an intermediate activation in the workspace:
  * which = 0 h1 [M][q_cols], 1 h2 [M][d_model], 2 a [M][d_ff], 3 x' [M][d_model]
- * (all bf16, row-major) of layer `layer`.  Valid after the run has completed.
+ * (all bf16, row-major) of layer `layer`; for a decoder plan which = 0 qkv
+ * [M][q + 2 kv], 1 o [M][q], 2 x1 [M][d_model], 3 a [M][d_ff], 4 x' [M][d_model].
+ * Valid after the run has completed.
  */
 int sgemm_chain_buffer(sgemm_plan plan, int layer, int which, size_t* offset, size_t* bytes);
 

@@ -283,6 +283,57 @@ def test_chain_stage_items_windows_and_shared_lines(M, L, d, q, dff):
             assert max(per_line) == 2      # the down output x' of the ragged case: two XCDs per line
 
 
+def _dec_create(M=4, L=2, d=256, dff=384, Hq=8, Hkv=2, hd=128, T=100, flags=0, q=0):
+    p = sg.Problem(sg.KIND_DECODER, M, 0, 0, 0, L, d, q, dff, flags, 0, 0, 0, 0, 0, Hq, Hkv, hd, T)
+    rc, h, ws = sg.sgemm_plan_create(p)
+    if h:
+        sg.sgemm_plan_destroy(h)
+    return rc
+
+
+def test_decoder_plan_validation():
+    assert _dec_create() == sg.OK
+    assert _dec_create(M=64, d=4096, dff=12288, Hq=32, Hkv=8, T=1024) == sg.OK
+    assert _dec_create(Hq=6, Hkv=4) == sg.ERR_INVALID_ARG          # heads not a multiple
+    assert _dec_create(Hq=16, Hkv=2) == sg.ERR_UNSUPPORTED         # 8 query heads per key/value head
+    assert _dec_create(hd=64) == sg.ERR_UNSUPPORTED
+    assert _dec_create(T=4096) == sg.ERR_UNSUPPORTED              # more than 64 chunks of 64
+    assert _dec_create(T=4095) == sg.OK
+    assert _dec_create(M=65) == sg.ERR_UNSUPPORTED
+    assert _dec_create(d=100) == sg.ERR_INVALID_ARG
+    assert _dec_create(q=999) == sg.ERR_INVALID_ARG
+    assert _dec_create(q=1024) == sg.OK
+    for f in (sg.F_SCHEDULER, sg.F_SYNC_FLAT, sg.F_POLL_LEADER, sg.F_LAUNCH_PER_STAGE, sg.F_KCHUNK, sg.F_MSPLIT):
+        assert _dec_create(flags=f) == sg.ERR_UNSUPPORTED, f
+    assert _dec_create(M=16, flags=sg.F_FORCE_DOT2) == sg.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("M", [1, 2, 16, 64])
+def test_decoder_plan_and_buffers(M):
+    """Qwen3-8B-shaped decoder: QKV [4096 -> 6144], O [4096 -> 4096], paired
+    gate_up [4096 -> 12288], down [12288 -> 4096]; per-layer activations that
+    do not overlap; LDS within the CU next to the norm factors and the
+    attention stage's 16 KB."""
+    dec = sg.Decoder(M, 3, 4096, 12288, 32, 8, 128, 1024)
+    dd = dec.describe()
+    assert dd["kind"] == "decoder"
+    st = dd["stages"]
+    assert [(s["K"], s["N"]) for s in st] == [(4096, 6144), (4096, 4096), (4096, 12288), (12288, 4096)]
+    assert st[2]["paired"] == 1
+    assert {s["path"] for s in st} == {"dot2" if M <= 2 else "mfma"}
+    assert all(s["lds"] + 256 + STATIC_LDS_RESERVE <= 160 * 1024 for s in st)
+    spans = []
+    cols = [6144, 4096, 4096, 12288, 4096]
+    for l in range(3):
+        for w in range(5):
+            rc, off, nb = sg.sgemm_chain_buffer(dec.handle, l, w)
+            assert rc == 0 and nb == M * cols[w] * 2 and off + nb <= dec.workspace_bytes and off % 16 == 0
+            spans.append((off, off + nb))
+    spans.sort()
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    assert sg.sgemm_chain_buffer(dec.handle, 0, 5)[0] == sg.ERR_INVALID_ARG
+
+
 def test_null_and_misaligned_arguments_rejected_before_launch():
     lib = sg.library()
     assert lib.sgemm_plan_create(None, 0, None, None) == sg.ERR_INVALID_ARG
