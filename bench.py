@@ -26,7 +26,9 @@ fraction of 8 TB/s.
 ``--workload chain``: the 36-layer persistent chain at M = 64 (``--chain-m``
 selects another row count; Q 4096x4096,
 O 4096x4096, gate_up 4096x24576 with SiLU gate, down 12288x4096 per layer;
-13.29 GB of weights) in one launch per step.
+13.29 GB of weights) in one launch per step.  ``--chain-kchunk`` runs every
+chain stage on the K-chunked MFMA path and ``--chain-tn`` fixes the planner's
+tile width (ablations of the chain's stage kernels).
 
 Prints exactly one JSON line on stdout (progress goes to stderr).
 """
@@ -375,7 +377,7 @@ def bench_chain(args):
     M, L, d, q, dff = args.chain_m, 36, 4096, 4096, 12288
     wl = chain_weights(dev, L, d, q, dff)
     X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(5, 0, 0), M, d), dev)
-    ch = sg.LayerChain(M, L, d, q, dff)
+    ch = sg.LayerChain(M, L, d, q, dff, flags=sg.F_KCHUNK if args.chain_kchunk else 0, tn=args.chain_tn)
     ws = ch.new_workspace()
     Y = torch.empty((M, d), dtype=torch.float32, device=dev)
     wbytes = L * 2 * (q * d + d * q + 2 * dff * d + d * dff)
@@ -416,7 +418,7 @@ def bench_chain(args):
                      "traffic": load_traffic(f"chain_m{M}_36l"), "algorithmic_bytes_per_launch": wbytes,
                      "avg_launch_us": round(avg, 2)},
         "chain_us": {"median": round(ts[len(ts) // 2], 2), "min": round(ts[0], 2), "max": round(ts[-1], 2)},
-        "plan": [{k: st[k] for k in ("path", "waves", "TN", "ksl", "S", "KS", "items")}
+        "plan": [{k: st[k] for k in ("path", "ta", "tb", "waves", "TN", "ksl", "S", "KS", "items")}
                  for st in ch.describe()["stages"]],
     }
     if not args.no_cpu:
@@ -432,6 +434,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=["proj", "chain"], default="proj")
     ap.add_argument("--chain-m", type=int, default=64, help="rows of the chain workload (1-64)")
+    ap.add_argument("--chain-kchunk", action="store_true",
+                    help="chain workload with every stage on the K-chunked MFMA path (M > 16)")
+    ap.add_argument("--chain-tn", type=int, default=0, help="chain workload: tile width override (0 = planner)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the per-configuration table (all GEMM shapes, the 36-layer chain)")

@@ -33,7 +33,7 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Decomposition of one GEMM stage (see gemm_device.h for how it is executed).
 struct Geo {
-  int path = 0;        // 0 dot2, 1 MFMA
+  int path = 0;        // 0 dot2, 1 MFMA, 2 MFMA m-tile items, 3 K-chunked MFMA
   int M = 0, K = 0, N = 0;
   int ta = 0, tb = 0;  // template parameters: dot2 (M, G); MFMA (MT, NT)
   int waves = 8, wpi = 8, ng = 1, TN = 0, CB = 0, Nx = 0, NB = 0, S = 1, KS = 0, steps = 0, items = 0;
@@ -45,6 +45,7 @@ struct Geo {
   int slots = 32;  // workgroups per XCD that share the items (31 with a scheduler workgroup)
   int xbuf = 0;    // K-chunked path: bytes of one X chunk buffer
   int nfast = 0;   // m-tile items in the M-split order (column block fastest)
+  int kc_chain = 0;  // K-chunked path: a stage of the layer chain (its ring depth rule)
   size_t ctr_count = 0, part_floats = 0;
   double est_us = 0.0;
 };
@@ -234,13 +235,14 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
 // when it does not fit.
 constexpr int kKcChunkK = 512;  // K values per chunk (8 waves x one 64-wide k-step)
 
-int kc_ring(int ntw) { return ntw >= 6 ? 1 : (ntw >= 4 ? 2 : 4); }
+// Same rule as the kernel's ring depth (kc_device.h).
+int kc_ring(int ntw, int mt, bool chain) { return (chain && mt >= 4) || ntw >= 6 ? 1 : (ntw >= 4 ? 2 : 4); }
 
 bool kc_geo(Geo& g, int want_S, const Cost& cost) {
   const int MT = g.ta, NTW = g.tb;
   if (g.paired && NTW % 2) return false;
   const int NP = g.paired ? NTW / 2 : NTW;
-  const int ring = kc_ring(NTW);
+  const int ring = kc_ring(NTW, MT, g.kc_chain);
   g.waves = 8; g.wpi = 8; g.ng = 1; g.ksl = 1;
   g.TN = 16;
   g.CB = NP * 16;
@@ -282,7 +284,7 @@ bool kc_geo(Geo& g, int want_S, const Cost& cost) {
 }
 
 bool plan_kc(Geo& best, int M, int K, int N, int paired, int ntw_o, int s_o, const Cost& cost,
-             int slots = kWgPerXcd) {
+             int slots = kWgPerXcd, bool chain = false) {
   bool found = false;
   const int MT = (M + 15) / 16;
   for (int ntw = 2; ntw <= 8; ntw += 2) {
@@ -292,6 +294,7 @@ bool plan_kc(Geo& best, int M, int K, int N, int paired, int ntw_o, int s_o, con
     for (int s = s_lo; s <= s_hi; ++s) {
       Geo c;
       c.path = 3; c.M = M; c.K = K; c.N = N; c.ta = MT; c.tb = ntw; c.paired = paired; c.slots = slots;
+      c.kc_chain = chain;
       if (!kc_geo(c, s, cost)) continue;
       if (c.S != s && !s_o) continue;
       if (!paired && !gemm_variant_exists(3, c.ta, c.tb)) continue;
@@ -536,10 +539,13 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     layout_stage_ws(cur, pl->geo, pl->off_ctr, pl->off_part);
   } else if (p.kind == SGEMM_KIND_LAYERCHAIN) {
     if (p.tm || (p.flags & (SGEMM_F_W_CACHED | SGEMM_F_W_SC1 | SGEMM_F_MTILE_ITEMS | SGEMM_F_CHECK_PLACEMENT |
-                            SGEMM_F_MSPLIT | SGEMM_F_KCHUNK))) {
+                            SGEMM_F_MSPLIT))) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
     }
+    const bool kcf = (p.flags & SGEMM_F_KCHUNK) != 0;
+    if (kcf && ((p.flags & (SGEMM_F_FORCE_DOT2 | SGEMM_F_FORCE_MFMA)) || k_o > 1 || (w_o && w_o != 8)))
+      { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     const bool sched = (p.flags & SGEMM_F_SCHEDULER) != 0;
     if (sched && (p.flags & (SGEMM_F_SYNC_FLAT | SGEMM_F_POLL_LEADER))) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     const int slots = sched ? kWgPerXcd - 1 : kWgPerXcd;  // the scheduler workgroup takes no items
@@ -594,7 +600,30 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     if ((p.flags & SGEMM_F_FORCE_DOT2) && p.M >= 16) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     const int path = (p.flags & SGEMM_F_FORCE_DOT2) ? 0 : (p.flags & SGEMM_F_FORCE_MFMA) ? 1 : (p.M <= 2 ? 0 : 1);
     double best = -1.0;
-    for (int waves = 8; waves >= 4; waves -= 4) {
+    // SGEMM_F_KCHUNK: every stage on the K-chunked MFMA path, NTW_u tiles per
+    // item in the Q, O and down stages and NTW_p in gate_up (kernel code
+    // 10 NTW_u + NTW_p); a tile-width override fixes NTW_u = tn / 16.
+    const int MTk = (p.M + 15) / 16;
+    for (int nu = 2; kcf && nu <= 6; nu += 2) {
+      for (int np = 4; np <= 6; np += 2) {
+        if (tn_o && tn_o != 16 * nu) continue;
+        if (!chain_variant_exists(3, MTk, 10 * nu + np)) continue;
+        Geo c[kChainStages];
+        double tot = 0.0;
+        bool ok = true;
+        for (int s = 0; s < kChainStages && ok; ++s) {
+          const int paired = s == 2;
+          ok = plan_kc(c[s], p.M, Ks[s], Ns[s], paired, paired ? np : nu, s_st[s], cost, slots, true);
+          if (ok && paired) c[s].pair_off = p.d_ff;
+          tot += ok ? c[s].est_us : 0.0;
+        }
+        if (ok && (best < 0.0 || tot < best)) {
+          best = tot;
+          for (int s = 0; s < kChainStages; ++s) pl->cg[s] = c[s];
+        }
+      }
+    }
+    for (int waves = 8; !kcf && waves >= 4; waves -= 4) {
       if (w_o && waves != w_o) continue;
       for (int nt = 1; nt <= (path == 0 ? 4 : 2); ++nt) {
         // dot2: G = 2 or 4 rows per wave in every stage; MFMA: NT = 1 or 2.
@@ -686,6 +715,7 @@ static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
   d.interleave = g.mtiles > 1 ? 1 : 0;
   d.nfast = g.nfast;
   d.xbuf = g.xbuf;
+  d.nctr = (int)g.ctr_count;
   d.w_aux = w_aux;
   d.sync = sync;
   return d;
@@ -841,6 +871,7 @@ int layerchain_run(sgemm_plan plan, const void* X0, const void* const* Wq, const
   a.path = plan->cg[0].path;
   a.mt = plan->cg[0].ta;
   a.nt_q = plan->cg[0].tb; a.nt_o = plan->cg[1].tb; a.nt_d = plan->cg[3].tb;
+  if (a.path == 3) a.nt_q = 10 * plan->cg[0].tb + plan->cg[2].tb;  // K-chunked kernel code
   int lds = 0;
   for (int s = 0; s < kChainStages; ++s) lds = std::max(lds, plan->cg[s].lds);
   if (const int dc = device_check(plan->device); dc != SGEMM_OK) return dc;

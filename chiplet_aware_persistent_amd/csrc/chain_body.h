@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 
 #include "gemm_device.h"
+#include "kc_device.h"
 #include "launch.h"
 
 namespace sg {
@@ -162,7 +163,9 @@ static __device__ __forceinline__ void stamp(const ChainArgs& a, int e, int whic
 
 // PATH 1: MFMA stages with A = MT m-tiles and B = NT n-tiles (the paired
 // gate_up stage uses two).  PATH 0 (M < 16): dot2 stages with A = M rows and
-// B = G weight rows per wave (gate_up: G/2 gate and G/2 up rows).
+// B = G weight rows per wave (gate_up: G/2 gate and G/2 up rows).  PATH 3:
+// K-chunked MFMA stages (kc_device.h) with A = MT, B = 10 NTW_u + NTW_p tiles
+// per item in the unpaired and the paired (gate_up) stages.
 template <int PATH, int A, int B>
 __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -212,7 +215,13 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
         return ok;
       };
       // Every workgroup runs the hook (the wait), also one without items here.
-      if constexpr (PATH == 1) {
+      if constexpr (PATH == 3) {
+        if (s == 2) {
+          alive = mfma_kc_stage<A, B % 10, true, kAuxNt, decltype(hook), true>(d, lds, xcd, wslot, wn, hook);
+        } else {
+          alive = mfma_kc_stage<A, B / 10, false, kAuxNt, decltype(hook), true>(d, lds, xcd, wslot, wn, hook);
+        }
+      } else if constexpr (PATH == 1) {
         // Up to two m-tiles (M <= 32) keep the deeper ring: across the stage
         // barriers it measured faster there, the shallow one at M = 64.
         if (s == 2) {
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
       bool used = ne >= kChainStages;
       for (int e = a.e_begin; e < a.e_end && !used; ++e) used = (e & 3) == s;
       if (!used) continue;
-      const int n = kXcds * a.st[s].NB * a.st[s].wpi;
+      const int n = a.st[s].nctr;
       for (int i = threadIdx.x; i < n; i += blockDim.x) a.st[s].ctr[i] = 0u;
     }
     wait_vm0();
@@ -279,5 +288,7 @@ typedef void (*ChainKernel)(ChainArgs);
 
 // dot2 instantiations (M = 1..15, G = 2 or 4), null when absent.
 ChainKernel chain_kernel_dot2(int m, int g);
+// K-chunked instantiations (MT, 10 NTW_u + NTW_p), null when absent.
+ChainKernel chain_kernel_kc(int mt, int code);
 
 }  // namespace sg

@@ -8,6 +8,7 @@ namespace sg {
 
 static ChainKernel chain_kernel(int path, int a, int b) {
   if (path == 0) return chain_kernel_dot2(a, b);
+  if (path == 3) return chain_kernel_kc(a, b);
   switch (a * 4 + b) {
     case 1 * 4 + 1: return k_chain<1, 1, 1>;
     case 1 * 4 + 2: return k_chain<1, 1, 2>;

@@ -353,7 +353,7 @@ __global__ __launch_bounds__(512) void k_decoder(ChainArgs a) {
     }
     if (threadIdx.x < kXcds) a.claim[threadIdx.x] = 0u;
     for (int s = 0; s < kChainStages; ++s) {
-      const int n = kXcds * a.st[s].NB * a.st[s].wpi;
+      const int n = a.st[s].nctr;
       for (int i = threadIdx.x; i < n; i += blockDim.x) a.st[s].ctr[i] = 0u;
     }
     for (int i = threadIdx.x; i < a.M * a.Hkv; i += blockDim.x) a.actr[i] = 0u;

@@ -34,7 +34,11 @@ constexpr int kKcChunk = kKcWaves * kMfmaKStep;      // K values per chunk: one 
 constexpr int kKcRow = kKcChunk + 8;                 // LDS row stride of an X chunk (elements)
 
 // Weight steps (chunks) in flight per wave: NTW tiles x 2 loads per step.
-constexpr int kc_ring_depth(int ntw) { return ntw >= 6 ? 1 : (ntw >= 4 ? 2 : 4); }
+// Inside the layer chain, four m-tiles keep one step: the chain's own state
+// and four m-tiles' accumulators leave no registers for a second.
+constexpr int kc_ring_depth(int ntw, int mt, bool chain) {
+  return (chain && mt >= 4) || ntw >= 6 ? 1 : (ntw >= 4 ? 2 : 4);
+}
 
 // X chunk: rows [0, rows) x K values [k0, k0 + kKcChunk) of X into an LDS
 // buffer of xbuf bytes (row stride kKcRow), zero outside [0, M) x [k0, kend).
@@ -61,10 +65,10 @@ __device__ __forceinline__ void stage_x_chunk(const StageDesc& d, uint16_t* buf,
 // XCD x covers the output columns [x*Nx + b*CB, x*Nx + (b+1)*CB), CB = 16 NTW
 // (paired: 16 NTW/2, with the up rows pair_off rows further on).  d.steps is
 // the number of chunks per item (a multiple of the ring depth).
-template <int MT, int NTW, bool PAIRED, int AUX, typename Hook = NoHook>
+template <int MT, int NTW, bool PAIRED, int AUX, typename Hook = NoHook, bool CHAIN = false>
 __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                               Hook pre_x = Hook()) {
-  constexpr int P = kc_ring_depth(NTW);
+  constexpr int P = kc_ring_depth(NTW, MT, CHAIN);
   static_assert(!PAIRED || NTW % 2 == 0, "a paired block holds whole (gate, up) tile pairs");
   constexpr int NP = PAIRED ? NTW / 2 : NTW;  // 16-column output tiles of a block
   constexpr unsigned TILE = NTW * MT * 256;   // floats of one item's partial

@@ -35,7 +35,7 @@ struct ChainArgs {
   int sched;                           // slot 0 of each XCD schedules, slots 1..31 work
   long long spin_ticks;                // watchdog budget (wall-clock ticks, 100 MHz)
   int path;                            // 1: MFMA stages, 0: dot2 stages (M < 16)
-  int mt, nt_q, nt_o, nt_d;            // template parameters: MFMA (MT, NT); dot2 (M in mt, G in nt_*)
+  int mt, nt_q, nt_o, nt_d;            // template parameters: MFMA (MT, NT); dot2 (M in mt, G in nt_*); K-chunked: code in nt_q
   int e_begin, e_end;                  // events this launch runs: [e_begin, e_end)
   int spl;                             // stages (events) per layer: 4 (chain), 5 (decoder)
   // Decoder layer only (5 stages: QKV with the attention norm, attention,

@@ -68,6 +68,7 @@ struct StageDesc {
   int sync;            // SyncMode of the split-K arrival
   int check;           // single GEMM: claim (XCD, slot) at the end and latch a duplicate
   int xbuf;            // K-chunked MFMA path: bytes of one X chunk buffer (multiple of 1 KB)
+  int nctr;            // split-K arrival counters of this stage (reset by the chain's last workgroup)
   const uint16_t* R;   // residual added to every output before its rounding (null: none), [M][ldy] bf16
   unsigned r_bytes;    // extent of R
   unsigned w_aux;      // cache-policy bits of the weight loads
