@@ -377,8 +377,7 @@ def bench_chain(args):
     M, L, d, q, dff = args.chain_m, 36, 4096, 4096, 12288
     wl = chain_weights(dev, L, d, q, dff)
     X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(5, 0, 0), M, d), dev)
-    flags = (sg.F_KCHUNK if args.chain_kchunk else 0) | (sg.F_OWN_SLICE_FIRST if args.chain_own_first else 0)
-    ch = sg.LayerChain(M, L, d, q, dff, flags=flags, tn=args.chain_tn)
+    ch = sg.LayerChain(M, L, d, q, dff, flags=sg.F_KCHUNK if args.chain_kchunk else 0, tn=args.chain_tn)
     ws = ch.new_workspace()
     Y = torch.empty((M, d), dtype=torch.float32, device=dev)
     wbytes = L * 2 * (q * d + d * q + 2 * dff * d + d * dff)
@@ -419,7 +418,7 @@ def bench_chain(args):
                      "traffic": load_traffic(f"chain_m{M}_36l"), "algorithmic_bytes_per_launch": wbytes,
                      "avg_launch_us": round(avg, 2)},
         "chain_us": {"median": round(ts[len(ts) // 2], 2), "min": round(ts[0], 2), "max": round(ts[-1], 2)},
-        "plan": [{k: st[k] for k in ("path", "ta", "tb", "waves", "TN", "ksl", "S", "KS", "items", "own_steps")}
+        "plan": [{k: st[k] for k in ("path", "ta", "tb", "waves", "TN", "ksl", "S", "KS", "items")}
                  for st in ch.describe()["stages"]],
     }
     if not args.no_cpu:
@@ -438,8 +437,6 @@ def main():
     ap.add_argument("--chain-kchunk", action="store_true",
                     help="chain workload with every stage on the K-chunked MFMA path (M > 16)")
     ap.add_argument("--chain-tn", type=int, default=0, help="chain workload: tile width override (0 = planner)")
-    ap.add_argument("--chain-own-first", action="store_true",
-                    help="chain workload: dot2 stages start on their own XCD's K slice (M <= 2)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the per-configuration table (all GEMM shapes, the 36-layer chain)")

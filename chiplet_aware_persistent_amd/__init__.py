@@ -39,7 +39,6 @@ F_SCHEDULER = 1 << 11
 F_CHECK_PLACEMENT = 1 << 12
 F_KCHUNK = 1 << 13
 F_MSPLIT = 1 << 14
-F_OWN_SLICE_FIRST = 1 << 15
 
 
 class SgemmError(RuntimeError):

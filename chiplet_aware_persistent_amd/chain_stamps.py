@@ -1,9 +1,8 @@
 """Where the 36-layer chain's time goes, from its per-workgroup stage stamps.
 
 With SGEMM_F_STAMPS every workgroup records the wall clock (100 MHz) when
-it is released into a stage (after its wait; with own slice first, after
-the wait for its own XCD's producers) and when its last wave ends the
-stage.  For every stage after the first this prints, averaged over the
+it is released into a stage (after its wait) and when its last wave ends
+the stage.  For every stage after the first this prints, averaged over the
 36 layers per projection (Q, O, gate_up, down), in microseconds:
 
 - release: first start of the stage minus the last end of the stage before
@@ -60,8 +59,7 @@ def main():
     import chiplet_aware_persistent_amd as sg
     import synth
 
-    modes = {"default": 0, "scheduler": sg.F_SCHEDULER, "poll_leader": sg.F_POLL_LEADER,
-             "own_first": sg.F_OWN_SLICE_FIRST}
+    modes = {"default": 0, "scheduler": sg.F_SCHEDULER, "poll_leader": sg.F_POLL_LEADER}
     ap = argparse.ArgumentParser()
     ap.add_argument("--m", type=int, nargs="+", default=[1, 16, 64])
     ap.add_argument("--modes", nargs="+", default=["default", "scheduler"], choices=sorted(modes))

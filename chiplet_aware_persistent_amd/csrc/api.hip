@@ -46,7 +46,6 @@ struct Geo {
   int xbuf = 0;    // K-chunked path: bytes of one X chunk buffer
   int nfast = 0;   // m-tile items in the M-split order (column block fastest)
   int kc_chain = 0;  // K-chunked path: a stage of the layer chain (its ring depth rule)
-  int own_steps = 0, own_off = 0, own_cap = 0;  // chain dot2 stage, own slice first (0: off)
   size_t ctr_count = 0, part_floats = 0;
   double est_us = 0.0;
 };
@@ -380,7 +379,7 @@ static void layout_stage_ws(size_t& cursor, const Geo& g, size_t& off_ctr, size_
 static int plan_decoder(sgemm_plan_s* pl, const sgemm_problem& p, int tn_o, int s_o, int w_o, int k_o) {
   const unsigned refused = SGEMM_F_SYNC_FLAT | SGEMM_F_POLL_LEADER | SGEMM_F_SCHEDULER | SGEMM_F_LAUNCH_PER_STAGE |
                            SGEMM_F_W_CACHED | SGEMM_F_W_SC1 | SGEMM_F_MTILE_ITEMS | SGEMM_F_MSPLIT | SGEMM_F_KCHUNK |
-                           SGEMM_F_CHECK_PLACEMENT | SGEMM_F_OWN_SLICE_FIRST;
+                           SGEMM_F_CHECK_PLACEMENT;
   if (p.flags & refused) return SGEMM_ERR_UNSUPPORTED;
   if (p.tm) return SGEMM_ERR_INVALID_ARG;
   if (p.M < 1 || p.n_layers < 1 || p.d_model < 8 || p.d_ff < 8 || p.n_heads < 1 || p.n_kv_heads < 1 ||
@@ -504,7 +503,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
 
   size_t cur = kCtl;
   if (p.kind == SGEMM_KIND_GEMM) {
-    if (p.flags & (SGEMM_F_SCHEDULER | SGEMM_F_OWN_SLICE_FIRST)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }  // chain only
+    if (p.flags & SGEMM_F_SCHEDULER) { delete pl; return SGEMM_ERR_UNSUPPORTED; }  // a chain runtime
     int rc = validate_gemm(p);
     if (rc != SGEMM_OK) { delete pl; return rc; }
     const bool msplit = (p.flags & SGEMM_F_MSPLIT) != 0;
@@ -653,25 +652,6 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     if (best < 0.0) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     for (int s = 0; s < kChainStages; ++s)
       if (pl->cg[s].part_floats * 4 >= kMaxOperand) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
-    if (p.flags & SGEMM_F_OWN_SLICE_FIRST) {
-      if (sched || kcf || (p.flags & (SGEMM_F_SYNC_FLAT | SGEMM_F_POLL_LEADER)) || pl->cg[0].path != 0)
-        { delete pl; return SGEMM_ERR_UNSUPPORTED; }
-      // Stage s reads the output of stage s - 1 (the first stage: the previous
-      // layer's down projection), whose XCD x wrote columns [x Nx_p, (x+1) Nx_p).
-      for (int s = 0; s < kChainStages; ++s) {
-        Geo& g = pl->cg[s];
-        const int nxp = pl->cg[(s + kChainStages - 1) % kChainStages].Nx;
-        if (g.S != 1 || g.wpi != 1 || g.K % kDot2KStep || nxp % kDot2KStep || kXcds * nxp != g.K) continue;
-        const int cap = ceil_div(g.items, g.slots * g.ng);
-        const int off = (int)round_up((size_t)g.lds, 256);
-        const int need = off + g.waves * cap * g.tb * g.M * 64 * 4;  // parked sums: G*M floats per lane and item
-        if (need > kLdsMax) continue;
-        g.own_steps = nxp / kDot2KStep;
-        g.own_off = off;
-        g.own_cap = cap;
-        g.lds = need;
-      }
-    }
     // Re-layout with the final geometries.
     cur = kCtl;
     for (int s = 0; s < kChainStages; ++s) layout_stage_ws(cur, pl->cg[s], pl->c_ctr[s], pl->c_part[s]);
@@ -736,9 +716,6 @@ static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
   d.nfast = g.nfast;
   d.xbuf = g.xbuf;
   d.nctr = (int)g.ctr_count;
-  d.own_steps = g.own_steps;
-  d.own_off = g.own_off;
-  d.own_cap = g.own_cap;
   d.w_aux = w_aux;
   d.sync = sync;
   return d;
@@ -1052,11 +1029,10 @@ static std::string geo_json(const Geo& g) {
                 "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,\"wpi\":%d,"
                 "\"ksl\":%d,\"kss\":%d,\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,"
                 "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
-                "\"ring\":%d,\"mtiles\":%d,\"nfast\":%d,\"slots\":%d,\"xbuf\":%d,\"own_steps\":%d,"
-                "\"est_us\":%.3f}",
+                "\"ring\":%d,\"mtiles\":%d,\"nfast\":%d,\"slots\":%d,\"xbuf\":%d,\"est_us\":%.3f}",
                 g.path == 0 ? "dot2" : (g.path == 3 ? "kc" : "mfma"), g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
                 g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles,
-                g.nfast, g.slots, g.xbuf, g.own_steps, g.est_us);
+                g.nfast, g.slots, g.xbuf, g.est_us);
   return b;
 }
 

@@ -42,7 +42,6 @@
 #include "gemm_device.h"
 #include "kc_device.h"
 #include "launch.h"
-#include "xready_device.h"
 
 namespace sg {
 
@@ -92,31 +91,6 @@ static __device__ __forceinline__ bool wait_event(const ChainArgs& a, int e, int
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (leader && ok && !a.flat_sync && a.poll_leader && !a.sched)
       __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *sh_alive = ok;
-  }
-  __syncthreads();
-  return *sh_alive != 0;
-}
-
-// Wait until this XCD's workgroups have all finished event e (its counter
-// L[x][e] is complete); workgroup-wide, returns false on time-out.  No
-// acquire: the producers' stores are in this XCD's L2 (each producer waited
-// for them before its bump) and the reads that follow bypass the CU's L1.
-static __device__ __forceinline__ bool wait_local(const ChainArgs& a, int e, int xcd, int nslots, int* sh_alive) {
-  if (threadIdx.x == 0) {
-    const int events = a.spl * a.n_layers;
-    const unsigned* ctr = a.lctr + xcd * events + e;
-    int ok = 1;
-    const unsigned long long t0 = now_ticks();
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)nslots) {
-      if ((long long)(now_ticks() - t0) > a.spin_ticks ||
-          (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout)) {
-        __hip_atomic_fetch_or(a.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
     *sh_alive = ok;
   }
   __syncthreads();
@@ -254,19 +228,6 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
           alive = mfma_stage<A, 2, true, kAuxNt, (A <= 2)>(d, lds, xcd, wslot, wn, hook);
         } else {
           alive = mfma_stage<A, B, false, kAuxNt, (A <= 2)>(d, lds, xcd, wslot, wn, hook);
-        }
-      } else if (d.own_steps > 0 && e != a.e_begin) {
-        // Own slice first: phase 1 after this XCD's producers, phase 2 after all.
-        auto wl = [&]() -> bool {
-          const bool ok = wait_local(a, e - 1, xcd, wn, &sh_alive);
-          stamp(a, e, 0);
-          return ok;
-        };
-        auto wg = [&]() -> bool { return wait_event(a, e - 1, xcd, slot, &sh_alive); };
-        if (s == 2) {
-          alive = dot2_stage_own_first<A, B, kAuxNt, true>(d, lds, xcd, wslot, wn, wl, wg);
-        } else {
-          alive = dot2_stage_own_first<A, B, kAuxNt, false>(d, lds, xcd, wslot, wn, wl, wg);
         }
       } else {
         if (s == 2) {

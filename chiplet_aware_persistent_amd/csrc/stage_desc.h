@@ -69,9 +69,6 @@ struct StageDesc {
   int check;           // single GEMM: claim (XCD, slot) at the end and latch a duplicate
   int xbuf;            // K-chunked MFMA path: bytes of one X chunk buffer (multiple of 1 KB)
   int nctr;            // split-K arrival counters of this stage (reset by the chain's last workgroup)
-  int own_steps;       // chain, own slice first: k-steps of one producer XCD's slice of X (0: off)
-  int own_off;         // LDS byte offset of the parked own-slice sums
-  int own_cap;         // items per stream with room there
   const uint16_t* R;   // residual added to every output before its rounding (null: none), [M][ldy] bf16
   unsigned r_bytes;    // extent of R
   unsigned w_aux;      // cache-policy bits of the weight loads

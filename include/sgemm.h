@@ -116,24 +116,7 @@ enum {
                                     wave-level K split, Limitations).  tn, when
                                     given, is 16 x the tiles per block (32, 64,
                                     96 or 128); kslices must be 0 or 1 and waves
-                                    0 or 8.  In the chain (M > 16): every stage
-                                    on this path, the gate_up stage with whole
-                                    (gate, up) tile pairs; tn fixes the tiles
-                                    of the unpaired stages                      */
-  SGEMM_F_OWN_SLICE_FIRST = 1u << 15, /* chain, dot2 stages (M <= 2 or forced):
-                                    every stage after the launch's first starts
-                                    on the K range its own XCD produced, as soon
-                                    as that XCD's workgroups are done (XCD-local
-                                    counter, no write-back needed: one L2), and
-                                    runs the other seven slices after the
-                                    global event (Fleet reading note, section 2
-                                    flowchart (b), section 4 runtime layout).
-                                    Stages whose K is not eight whole 512-wide
-                                    slices run as usual.  Not combined with
-                                    SGEMM_F_SCHEDULER, SGEMM_F_SYNC_FLAT or
-                                    SGEMM_F_POLL_LEADER, and refused when the
-                                    plan's stages are not dot2
-                                    (SGEMM_ERR_UNSUPPORTED)                     */
+                                    0 or 8                                      */
   SGEMM_F_SCHEDULER = 1u << 11   /* chain, ablation: the per-XCD scheduler
                                     runtime (Fleet reading note, sections 3b
                                     and 5, the runtime layout figure of

@@ -268,33 +268,6 @@ def test_chain_kchunk_flag_combinations():
     assert _create(M=64, flags=sg.F_KCHUNK, tn=96, **chain) == sg.ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("M,d,q,dff", [(1, 4096, 4096, 12288), (2, 4096, 4096, 12288), (1, 4096, 2048, 8192),
-                                       (1, 1024, 1024, 3072), (5, 4096, 4096, 4096)])
-def test_chain_own_slice_first_plans(M, d, q, dff):
-    """Own slice first: a dot2 stage takes it when its K is eight whole
-    512-wide slices, one per producer XCD (the previous stage's Nx), with S = 1
-    and one wave per item stream; its parked sums fit the LDS."""
-    flags = sg.F_OWN_SLICE_FIRST | (sg.F_FORCE_DOT2 if M > 2 else 0)
-    st = sg.LayerChain(M, 2, d, q, dff, flags=flags).describe()["stages"]
-    for s, (K, prev) in zip(st, ((d, 3), (q, 0), (d, 1), (dff, 2))):
-        nxp = st[prev]["Nx"]
-        ok = K == 8 * nxp and nxp % 512 == 0 and s["S"] == 1 and s["wpi"] == 1
-        assert s["own_steps"] == (nxp // 512 if ok else 0)
-        assert s["lds"] + STATIC_LDS_RESERVE <= 160 * 1024
-    plain = sg.LayerChain(M, 2, d, q, dff, flags=flags & ~sg.F_OWN_SLICE_FIRST).describe()["stages"]
-    assert all(p_["own_steps"] == 0 for p_ in plain)
-
-
-def test_chain_own_slice_first_flag_combinations():
-    chain = dict(kind=sg.KIND_LAYERCHAIN, L=2, d=4096, q=4096, dff=4096)
-    assert _create(M=1, flags=sg.F_OWN_SLICE_FIRST, **chain) == sg.OK
-    for f in (sg.F_SCHEDULER, sg.F_SYNC_FLAT, sg.F_POLL_LEADER, sg.F_FORCE_MFMA):
-        assert _create(M=1, flags=sg.F_OWN_SLICE_FIRST | f, **chain) == sg.ERR_UNSUPPORTED, f
-    assert _create(M=16, flags=sg.F_OWN_SLICE_FIRST, **chain) == sg.ERR_UNSUPPORTED   # MFMA stages
-    assert _create(M=33, flags=sg.F_OWN_SLICE_FIRST | sg.F_KCHUNK, **chain) == sg.ERR_UNSUPPORTED
-    assert _create(M=1, K=4096, N=4096, flags=sg.F_OWN_SLICE_FIRST) == sg.ERR_UNSUPPORTED  # a chain option
-
-
 def _stage_items(st, slots=32):
     """(slot, stream) -> item list of one chain/GEMM stage, as the kernels
     assign them: workgroup slot w of 32 runs streams q < ng, each the

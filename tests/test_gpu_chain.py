@@ -148,32 +148,6 @@ def test_chain_kchunk_parity(cuda_device, M, L, d, q, dff, flags, splitk):
     report("chain kc M=%d L=%d %dx%dx%d S=%s flags=%#x" % (M, L, d, q, dff, [s["S"] for s in st], flags), worst)
 
 
-@pytest.mark.parametrize("M,L,d,q,dff,flags", [
-    (1, 3, 4096, 4096, 4096, 0), (2, 2, 4096, 4096, 12288, 0), (1, 2, 4096, 2048, 8192, 0),
-    (5, 2, 4096, 4096, 4096, sg.F_FORCE_DOT2), (1, 2, 4096, 4096, 12288, sg.F_STAMPS)])
-def test_chain_own_slice_first_parity(cuda_device, M, L, d, q, dff, flags):
-    """dot2 stages that start on their own XCD's K slice as soon as that XCD's
-    producers are done, and run the other slices after the global event; a
-    stage whose K is not eight whole 512-wide slices (q = 2048: O) runs as
-    usual in the same launch.  Bitwise repeatable over launches."""
-    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x2600 + M + L + q, cuda_device)
-    ch = sg.LayerChain(M, L, d, q, dff, flags=sg.F_OWN_SLICE_FIRST | flags)
-    st = ch.describe()["stages"]
-    want = [(K // 8 // 512 if K == 8 * nxp and nxp % 512 == 0 and s_["S"] == 1 and s_["wpi"] == 1 else 0)
-            for s_, (K, nxp) in zip(st, ((d, st[3]["Nx"]), (q, st[0]["Nx"]), (d, st[1]["Nx"]), (dff, st[2]["Nx"])))]
-    assert [s["own_steps"] for s in st] == want and any(want)
-    rc, Y, Yb, ws = run_chain(ch, X0, dl)
-    assert rc == sg.OK, sg.status_string(rc)
-    worst = check_chain(ch, ws, x0, layers, Y, Yb, M)
-    report("chain own-slice-first M=%d L=%d %dx%dx%d" % (M, L, d, q, dff), worst)
-    first = [host_bits(ch.activation(ws, l, w)).copy() for l in range(L) for w in range(4)]
-    for _ in range(2):
-        rc2, _, _, _ = run_chain(ch, X0, dl, ws=ws)
-        assert rc2 == sg.OK
-        again = [host_bits(ch.activation(ws, l, w)) for l in range(L) for w in range(4)]
-        assert all(np.array_equal(a, b) for a, b in zip(first, again))
-
-
 @pytest.mark.parametrize("M,L,d,q,dff", [(64, 1, 4096, 4096, 12288), (1, 1, 4096, 4096, 12288),
                                          (8, 4, 512, 256, 1536), (2, 2, 256, 128, 200)])
 def test_chain_scheduler_parity(cuda_device, M, L, d, q, dff):
