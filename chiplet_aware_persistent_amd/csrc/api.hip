@@ -46,6 +46,7 @@ struct Geo {
   int xbuf = 0;    // K-chunked path: bytes of one X chunk buffer
   int nfast = 0;   // m-tile items in the M-split order (column block fastest)
   int kc_chain = 0;  // K-chunked path: a stage of the layer chain (its ring depth rule)
+  int wpf = 0, wpf_off = 0;  // chain dot2 stage: first-item steps whose weights go to LDS before the wait
   size_t ctr_count = 0, part_floats = 0;
   double est_us = 0.0;
 };
@@ -281,6 +282,22 @@ bool kc_geo(Geo& g, int want_S, const Cost& cost) {
              wg_items * (1.5 + rows * kKcChunkK * 2.0 / cost.x_bw * 1e6) + wg_items * g.steps * 0.05 +
              (g.S > 1 ? cost.split_us + cost.fin_us_kb * g.S * NTW * MT : 0.0);
   return true;
+}
+
+// Chain dot2 stage: the weights of the first steps of each wave's first item
+// are loaded into LDS before the wait for the stage's X, so that the latency
+// of the stage boundary streams weights.  As many whole ring groups as fit
+// next to the stage's other LDS, at most the item's steps and max_steps.
+void plan_wpf(Geo& g, int lds_cap, int max_steps) {
+  if (g.path != 0) return;
+  const int off = (int)round_up((size_t)g.lds, 1024);
+  const int per_step = g.waves * g.tb * 1024;  // one 1 KB load per weight row and wave
+  int q = std::min(std::min(g.steps, max_steps), (lds_cap - off) / per_step);
+  q -= q % g.ring;
+  if (q < g.ring) return;
+  g.wpf = q;
+  g.wpf_off = off;
+  g.lds = off + q * per_step;
 }
 
 bool plan_kc(Geo& best, int M, int K, int N, int paired, int ntw_o, int s_o, const Cost& cost,
@@ -652,6 +669,14 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     if (best < 0.0) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     for (int s = 0; s < kChainStages; ++s)
       if (pl->cg[s].part_floats * 4 >= kMaxOperand) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    // Ablation: SGEMM_CHAIN_WPF = n loads up to n weight steps into LDS
+    // ahead of each dot2 stage's wait (default 0, none).  The extra traffic at
+    // the stage boundary slows the counters' round trips and the X loads by
+    // more than it saves: the 36-layer chain at M = 1 and 2 measured 0-6%
+    // slower with 4 or 8 steps.
+    int wpf_max = 0;
+    if (!env_int("SGEMM_CHAIN_WPF", 0, &wpf_max) || wpf_max < 0) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+    for (int s = 0; s < kChainStages; ++s) plan_wpf(pl->cg[s], kLdsMax, wpf_max);
     // Re-layout with the final geometries.
     cur = kCtl;
     for (int s = 0; s < kChainStages; ++s) layout_stage_ws(cur, pl->cg[s], pl->c_ctr[s], pl->c_part[s]);
@@ -716,6 +741,8 @@ static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
   d.nfast = g.nfast;
   d.xbuf = g.xbuf;
   d.nctr = (int)g.ctr_count;
+  d.wpf = g.wpf;
+  d.wpf_off = g.wpf_off;
   d.w_aux = w_aux;
   d.sync = sync;
   return d;
@@ -1024,15 +1051,16 @@ const char* sgemm_status_string(int status) {
 }
 
 static std::string geo_json(const Geo& g) {
-  char b[512];
+  char b[1024];
   std::snprintf(b, sizeof b,
                 "{\"path\":\"%s\",\"M\":%d,\"K\":%d,\"N\":%d,\"ta\":%d,\"tb\":%d,\"waves\":%d,\"wpi\":%d,"
                 "\"ksl\":%d,\"kss\":%d,\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,"
                 "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
-                "\"ring\":%d,\"mtiles\":%d,\"nfast\":%d,\"slots\":%d,\"xbuf\":%d,\"est_us\":%.3f}",
+                "\"ring\":%d,\"mtiles\":%d,\"nfast\":%d,\"slots\":%d,\"xbuf\":%d,\"wpf\":%d,"
+                "\"est_us\":%.3f}",
                 g.path == 0 ? "dot2" : (g.path == 3 ? "kc" : "mfma"), g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
                 g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles,
-                g.nfast, g.slots, g.xbuf, g.est_us);
+                g.nfast, g.slots, g.xbuf, g.wpf, g.est_us);
   return b;
 }
 

@@ -488,8 +488,34 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
   const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
   if constexpr (early) stage_x_lds(d, xs, M, s_first * d.KS, d.K, xr);
   Src sc = src_of(i0), sn = src_of(i0 + 1);
+  // Chain: the first q0 steps of the wave's first item are loaded into LDS
+  // (buffer-to-LDS, no registers) before the wait for X, so the stage
+  // boundary's latency streams weights; the ring then starts at step q0.
+  int q0 = 0;
+  const uint16_t* wl = nullptr;
+  if constexpr (!early) {
+    q0 = i0 < i1 ? d.wpf : 0;
+    uint16_t* wdst = (uint16_t*)((char*)xs + d.wpf_off) + (size_t)wave * d.wpf * G * 512;
+    wl = wdst;
+    for (int t = 0; t < q0; ++t) {
+      const bool kin = t * kDot2KStep + lane * 8 < sc.klim;
 #pragma unroll
-  for (int p = 0; p < P; ++p) issue(ring[p], sc, p);
+      for (int c = 0; c < G; ++c) {
+        const bool valid = kin && (PAIRED ? c % GO : c) < sc.cols;
+        const unsigned off = sc.base + row_of(c) * (unsigned)d.K * 2u + (unsigned)t * (kDot2KStep * 2u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (__attribute__((address_space(3))) void*)(wdst + (t * G + c) * 512), 16,
+            valid ? off : d.w_bytes, 0, 0, AUX);
+      }
+    }
+  }
+  {
+    const bool whole = q0 > 0 && q0 == spad;  // the ring starts on the next item
+    const Src& rs = whole ? sn : sc;
+    const int rt = whole ? 0 : q0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue(ring[p], rs, rt + p);
+  }
   if (!pre_x()) return false;
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (early) {
@@ -509,7 +535,51 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
     for (int m = 0; m < M; ++m) acc[c][m] = 0.f;
   int it = i0, t0 = 0;
   int xoff = (i0 / d.NB - s_first) * d.KS;  // LDS column of the current item's k0
-  const int total = (i1 - i0) * spad;
+  // Item complete: reduce the lanes' sums, then stash or store the result.
+  auto finish_item = [&]() {
+    float v[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < G; ++c)
+#pragma unroll
+      for (int m = 0; m < M; ++m) v[c * M + m] = acc[c][m];
+    const float r = wave_reduce_scatter<V>(v, lane);
+    const int li = it - i0;
+    if (li < d.stash_cap) {
+      stash[(wave * d.stash_cap + li) * 64 + lane] = r;
+    } else {
+      out_item(it, r);
+    }
+#pragma unroll
+    for (int c = 0; c < G; ++c)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[c][m] = 0.f;
+    ++it;
+    t0 = 0;
+    sc = sn;
+    sn = src_of(it + 1);
+    xoff = (it / d.NB - s_first) * d.KS;
+  };
+  if constexpr (!early) {
+    if (q0 > 0) {  // the first item's LDS steps
+      const uint16_t* xb = xs + xoff + lane * 8;
+      for (int t = 0; t < q0; ++t) {
+        u4 xv[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xv[m] = *(const u4*)(xb + m * d.xrow + t * kDot2KStep);
+#pragma unroll
+        for (int c = 0; c < G; ++c) {
+          const u4 w = *(const u4*)(wl + (t * G + c) * 512 + lane * 8);
+#pragma unroll
+          for (int m = 0; m < M; ++m) acc[c][m] = dot8(w, xv[m], acc[c][m]);
+        }
+      }
+      t0 = q0;
+      if (q0 == spad) finish_item();
+    }
+  }
+  const int total = (i1 - i0) * spad - q0;
   for (int T = 0; T < total; T += P) {
     const bool here = t0 + P < spad;
     const Src& sr = here ? sc : sn;
@@ -531,31 +601,7 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
       __builtin_amdgcn_sched_barrier(0);
     }
     t0 += P;
-    if (t0 == spad) {  // item complete
-      float v[V];
-#pragma unroll
-      for (int i = 0; i < V; ++i) v[i] = 0.f;
-#pragma unroll
-      for (int c = 0; c < G; ++c)
-#pragma unroll
-        for (int m = 0; m < M; ++m) v[c * M + m] = acc[c][m];
-      const float r = wave_reduce_scatter<V>(v, lane);
-      const int li = it - i0;
-      if (li < d.stash_cap) {
-        stash[(wave * d.stash_cap + li) * 64 + lane] = r;
-      } else {
-        out_item(it, r);
-      }
-#pragma unroll
-      for (int c = 0; c < G; ++c)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[c][m] = 0.f;
-      ++it;
-      t0 = 0;
-      sc = sn;
-      sn = src_of(it + 1);
-      xoff = (it / d.NB - s_first) * d.KS;
-    }
+    if (t0 == spad) finish_item();
   }
 
   // Stored items: results of the stream, written after its last load.

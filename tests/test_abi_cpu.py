@@ -268,6 +268,32 @@ def test_chain_kchunk_flag_combinations():
     assert _create(M=64, flags=sg.F_KCHUNK, tn=96, **chain) == sg.ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("M,d,q,dff", [(1, 4096, 4096, 12288), (2, 4096, 4096, 12288), (2, 1024, 1032, 3000),
+                                       (1, 256, 128, 384)])
+def test_chain_lds_weight_prefetch_plans(M, d, q, dff, monkeypatch):
+    """Ablation SGEMM_CHAIN_WPF: dot2 chain stages take whole ring groups of
+    their first item's steps into LDS ahead of the wait, as many as fit next
+    to the window and stash (eight waves x G kilobytes per step) up to the
+    cap; off by default."""
+    assert all(s["wpf"] == 0 for s in sg.LayerChain(M, 2, d, q, dff).describe()["stages"])  # off by default
+    monkeypatch.setenv("SGEMM_CHAIN_WPF", "1000")
+    st = sg.LayerChain(M, 2, d, q, dff).describe()["stages"]
+    for s in st:
+        assert s["path"] == "dot2" and s["wpf"] % s["ring"] == 0 and 0 < s["wpf"] <= s["steps"]
+        assert s["lds"] + STATIC_LDS_RESERVE <= 160 * 1024
+    if M == 1 and d == 4096:
+        assert [s["wpf"] for s in st] == [8, 8, 8, 8]
+    monkeypatch.setenv("SGEMM_CHAIN_WPF", "0")
+    assert all(s["wpf"] == 0 for s in sg.LayerChain(M, 2, d, q, dff).describe()["stages"])
+    monkeypatch.setenv("SGEMM_CHAIN_WPF", "-1")
+    with pytest.raises(sg.SgemmError):
+        sg.LayerChain(M, 2, d, q, dff)
+    monkeypatch.delenv("SGEMM_CHAIN_WPF")
+    monkeypatch.setenv("SGEMM_CHAIN_WPF", "1000")
+    mf = sg.LayerChain(16, 2, d, q, dff).describe()["stages"]
+    assert all(s["wpf"] == 0 for s in mf)  # MFMA stages: not used
+
+
 def _stage_items(st, slots=32):
     """(slot, stream) -> item list of one chain/GEMM stage, as the kernels
     assign them: workgroup slot w of 32 runs streams q < ng, each the

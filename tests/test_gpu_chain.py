@@ -148,6 +148,39 @@ def test_chain_kchunk_parity(cuda_device, M, L, d, q, dff, flags, splitk):
     report("chain kc M=%d L=%d %dx%dx%d S=%s flags=%#x" % (M, L, d, q, dff, [s["S"] for s in st], flags), worst)
 
 
+@pytest.mark.parametrize("M,L,d,q,dff,flags", [(1, 2, 4096, 4096, 12288, 0), (2, 2, 1024, 1032, 3000, 0),
+                                               (5, 2, 2048, 1024, 4096, sg.F_FORCE_DOT2)])
+def test_chain_lds_weight_prefetch_bitwise(cuda_device, monkeypatch, M, L, d, q, dff, flags):
+    """Ablation SGEMM_CHAIN_WPF: dot2 stages load the first steps of each
+    wave's first item into LDS before waiting for X.  The steps are the same
+    and are summed in the same order, so the output must be bitwise that of
+    the chain without it, whole first items (the ring starts on the next
+    item) and partial ones alike; the result is also checked against the
+    oracle."""
+    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x2700 + M + d, cuda_device)
+    outs = {}
+    for cap in ("0", "4", "1000"):
+        monkeypatch.setenv("SGEMM_CHAIN_WPF", cap)
+        ch = sg.LayerChain(M, L, d, q, dff, flags=flags)
+        wpf = [s["wpf"] for s in ch.describe()["stages"]]
+        if cap == "0":
+            assert wpf == [0, 0, 0, 0]
+        elif cap == "4":
+            assert all(w == 4 for w in wpf)
+        else:
+            assert all(w >= 4 for w in wpf)
+        rc, Y, Yb, ws = run_chain(ch, X0, dl)
+        assert rc == sg.OK, sg.status_string(rc)
+        outs[cap] = ([host_bits(ch.activation(ws, l, w)).copy() for l in range(L) for w in range(4)],
+                     Y.cpu().numpy().copy())
+        if cap == "1000":
+            worst = check_chain(ch, ws, x0, layers, Y, Yb, M)
+            report("chain lds weight prefetch M=%d %dx%dx%d wpf=%s" % (M, d, q, dff, wpf), worst)
+    for cap in ("4", "1000"):
+        assert all(np.array_equal(a, b) for a, b in zip(outs["0"][0], outs[cap][0])), cap
+        assert np.array_equal(outs["0"][1].view(np.uint32), outs[cap][1].view(np.uint32)), cap
+
+
 @pytest.mark.parametrize("M,L,d,q,dff", [(64, 1, 4096, 4096, 12288), (1, 1, 4096, 4096, 12288),
                                          (8, 4, 512, 256, 1536), (2, 2, 256, 128, 200)])
 def test_chain_scheduler_parity(cuda_device, M, L, d, q, dff):
