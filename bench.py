@@ -435,7 +435,7 @@ def main():
     ap.add_argument("--workload", choices=["proj", "chain"], default="proj")
     ap.add_argument("--chain-m", type=int, default=64, help="rows of the chain workload (1-64)")
     ap.add_argument("--chain-kchunk", action="store_true",
-                    help="chain workload with every stage on the K-chunked MFMA path (M > 16)")
+                    help="chain workload with every stage on the K-chunked MFMA path (M = 17-32)")
     ap.add_argument("--chain-tn", type=int, default=0, help="chain workload: tile width override (0 = planner)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true",

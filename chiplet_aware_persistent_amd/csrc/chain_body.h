@@ -19,8 +19,11 @@
 // XCD's counter L[x][e] (the 32 workgroups of an XCD share one L2, so no
 // write-back is needed between them); the workgroup that brings L[x][e] to 32
 // writes the XCD's L2 back (device-scope release) and bumps the global G[e].
-// Consumers wait for G[e] == 8.  With SGEMM_F_SYNC_FLAT every workgroup does
-// the release and bumps G[e] (target = grid), flowchart (a).
+// G[e] has one copy per consumer XCD, all eight bumped by one instruction
+// of the releasing wave, so each copy is polled by 32 workgroups instead of
+// one address by 256.  Consumers wait for their copy of G[e] to reach 8.  With
+// SGEMM_F_SYNC_FLAT every workgroup does the release and bumps G[e] (target
+// = grid), flowchart (a).
 //
 // With SGEMM_F_SCHEDULER (the per-XCD scheduler runtime of the Fleet reading
 // note, sections 3b and 5 and the runtime layout figure of section 4) slot 0
@@ -49,19 +52,20 @@ static __device__ __forceinline__ unsigned long long now_ticks() { return wall_c
 
 // Wait until event e is complete (all producers published).  Executed by the
 // whole workgroup; returns false when the wait timed out (here or elsewhere).
-// Thread 0 of every workgroup polls the global counter with device-coherent
-// loads.  With poll_leader, one leader per XCD (slot 0) polls it instead and,
+// Thread 0 of every workgroup polls its XCD's copy of the global counter with
+// device-coherent loads.  With poll_leader, one leader per XCD (slot 0) polls it instead and,
 // once it is complete, raises the XCD's flag, which the other 31 workgroups
 // of the XCD poll (the per-XCD scheduler's polling role in the Fleet note,
 // sections 2a and 3b, without a dedicated workgroup): fewer pollers share the
 // counter's address, but the extra hop costs about a microsecond per stage
 // on MI355X, more than the contention of 256 pollers does.
 static __device__ __forceinline__ bool wait_event(const ChainArgs& a, int e, int xcd, int slot, int* sh_alive) {
+  const int events = a.spl * a.n_layers;
+  const unsigned* gc = a.gctr + (a.gcopies > 1 ? xcd * events : 0) + e;  // this XCD's copy
+  const unsigned target = a.flat_sync ? gridDim.x : (unsigned)kXcds;
+  const bool leader = slot == 0 || a.flat_sync || !a.poll_leader;
   if (threadIdx.x == 0) {
-    const int events = a.spl * a.n_layers;
     unsigned* flag = a.xflag + xcd * events + e;
-    const unsigned target = a.flat_sync ? gridDim.x : (unsigned)kXcds;
-    const bool leader = slot == 0 || a.flat_sync || !a.poll_leader;
     int ok = 1;
     const unsigned long long t0 = now_ticks();
     for (;;) {
@@ -71,7 +75,7 @@ static __device__ __forceinline__ bool wait_event(const ChainArgs& a, int e, int
         done = __hip_atomic_load(a.ready + xcd * 32 + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
                (unsigned)(e + 1);
       } else if (leader) {
-        done = __hip_atomic_load(a.gctr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
+        done = __hip_atomic_load(gc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
       } else {
         // Device-scope read (it skips the CU's L1, which could hold a stale 0).
         done = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
@@ -107,18 +111,17 @@ static __device__ __forceinline__ void signal_event(const ChainArgs& a, int e, i
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   wait_vm0();  // this wave's stores are acknowledged by L2
   __syncthreads();
-  if (threadIdx.x == 0) {
-    if (a.flat_sync) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_fetch_add(a.gctr + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const int events = a.spl * a.n_layers;
-      const unsigned old =
-          __hip_atomic_fetch_add(a.lctr + xcd * events + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == (unsigned)(nslots - 1)) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // write this XCD's L2 back
-        __hip_atomic_fetch_add(a.gctr + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+  if (threadIdx.x < 64) {
+    // Wave 0: lane 0 counts the workgroup in; lane c < gcopies bumps copy c.
+    const int lane = threadIdx.x;
+    const int events = a.spl * a.n_layers;
+    unsigned old = 0;
+    if (!a.flat_sync && lane == 0)
+      old = __hip_atomic_fetch_add(a.lctr + xcd * events + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.flat_sync || __builtin_amdgcn_readfirstlane(old) == (unsigned)(nslots - 1)) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // write this XCD's L2 back
+      if (lane < a.gcopies)
+        __hip_atomic_fetch_add(a.gctr + lane * events + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -136,7 +139,8 @@ static __device__ __forceinline__ bool run_scheduler(const ChainArgs& a, int xcd
     if (lane == 0) {
       const unsigned long long t0 = now_ticks();
       for (;;) {
-        if (__hip_atomic_load(a.gctr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)kXcds) break;
+        const unsigned* gc = a.gctr + (a.gcopies > 1 ? xcd * a.spl * a.n_layers : 0) + e;
+        if (__hip_atomic_load(gc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)kXcds) break;
         if ((long long)(now_ticks() - t0) > a.spin_ticks ||
             (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout)) {
           __hip_atomic_fetch_or(a.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -262,7 +266,10 @@ __global__ __launch_bounds__(512) void k_chain(ChainArgs a) {
     // counters; every other event's counters are still zero.
     const int events = a.spl * a.n_layers;
     const int ne = a.e_end - a.e_begin;
-    for (int i = threadIdx.x; i < ne; i += blockDim.x) a.gctr[a.e_begin + i] = 0u;
+    for (int i = threadIdx.x; i < a.gcopies * ne; i += blockDim.x) {
+      const int c = i / ne;
+      a.gctr[c * events + a.e_begin + (i - c * ne)] = 0u;
+    }
     for (int i = threadIdx.x; i < kXcds * ne; i += blockDim.x) {
       const int x = i / ne;
       const int e = a.e_begin + (i - x * ne);

@@ -1,7 +1,8 @@
-// Persistent layer chain with K-chunked MFMA stages: the instantiations for
-// MT = 2 and 3 m-tiles with (unpaired, paired) tiles per item of (4, 6) and
-// (2, 6), and (4, 4) at four m-tiles, where six paired tiles would not fit
-// the register file (the kernel is in chain_body.h).
+// Persistent layer chain with K-chunked MFMA stages (an ablation: slower than
+// the default stage kernels): the instantiations for MT = 2 m-tiles (M = 17
+// to 32) with (unpaired, paired) tiles per item of (4, 6) and (2, 6).  Three
+// and four m-tiles do not fit the register file next to the chain's state
+// (the kernel is in chain_body.h).
 #include <hip/hip_runtime.h>
 
 #include "chain_body.h"
@@ -12,9 +13,6 @@ ChainKernel chain_kernel_kc(int mt, int code) {
   switch (mt * 100 + code) {
     case 2 * 100 + 46: return k_chain<3, 2, 46>;
     case 2 * 100 + 26: return k_chain<3, 2, 26>;
-    case 3 * 100 + 46: return k_chain<3, 3, 46>;
-    case 3 * 100 + 26: return k_chain<3, 3, 26>;
-    case 4 * 100 + 44: return k_chain<3, 4, 44>;
     default: return nullptr;
   }
 }

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(512) void k_decoder(ChainArgs a) {
   __syncthreads();
   if (sh_last) {
     const int events = kSpl * a.n_layers;
-    for (int i = threadIdx.x; i < events; i += blockDim.x) a.gctr[i] = 0u;
+    for (int i = threadIdx.x; i < a.gcopies * events; i += blockDim.x) a.gctr[i] = 0u;
     for (int i = threadIdx.x; i < kXcds * events; i += blockDim.x) {
       a.lctr[i] = 0u;
       a.xflag[i] = 0u;

@@ -21,7 +21,7 @@ struct ChainArgs {
   uint16_t* y_bf16;                    // its bf16 rounding (may be null)
   unsigned* status;                    // workspace word 0
   unsigned* lctr;                      // [kXcds][events] intra-XCD event counters
-  unsigned* gctr;                      // [events] global event counters
+  unsigned* gctr;                      // [gcopies][events] global event counters (copy x polled by XCD x)
   unsigned* xflag;                     // [kXcds][events] per-XCD 'event seen' flags
   unsigned* done;                      // workgroups finished (reset by the last one)
   unsigned* claim;                     // [kXcds] slots claimed per XCD (reset by the last one)
@@ -34,6 +34,7 @@ struct ChainArgs {
   int poll_leader;                     // one workgroup per XCD polls and raises the XCD's flag
   int sched;                           // slot 0 of each XCD schedules, slots 1..31 work
   long long spin_ticks;                // watchdog budget (wall-clock ticks, 100 MHz)
+  int gcopies;                         // copies of each global counter: 8 (one per consumer XCD) or 1
   int path;                            // 1: MFMA stages, 0: dot2 stages (M < 16)
   int mt, nt_q, nt_o, nt_d;            // template parameters: MFMA (MT, NT); dot2 (M in mt, G in nt_*); K-chunked: code in nt_q
   int e_begin, e_end;                  // events this launch runs: [e_begin, e_end)

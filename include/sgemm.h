@@ -116,7 +116,11 @@ enum {
                                     wave-level K split, Limitations).  tn, when
                                     given, is 16 x the tiles per block (32, 64,
                                     96 or 128); kslices must be 0 or 1 and waves
-                                    0 or 8                                      */
+                                    0 or 8.  In the chain (an ablation, built
+                                    for M = 17-32, else SGEMM_ERR_UNSUPPORTED):
+                                    every stage on this path, the gate_up stage
+                                    with whole (gate, up) tile pairs; tn fixes
+                                    the tiles of the unpaired stages            */
   SGEMM_F_SCHEDULER = 1u << 11   /* chain, ablation: the per-XCD scheduler
                                     runtime (Fleet reading note, sections 3b
                                     and 5, the runtime layout figure of

@@ -233,27 +233,29 @@ def test_kchunk_flag_combinations():
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, tn=64) == sg.OK
 
 
-@pytest.mark.parametrize("M", [17, 32, 33, 48, 64])
+@pytest.mark.parametrize("M", [17, 24, 32, 33, 64])
 @pytest.mark.parametrize("d,q,dff", [(4096, 4096, 12288), (256, 128, 384), (1032, 520, 1000)])
 def test_chain_kchunk_plans(M, d, q, dff):
-    """K-chunked chain stages: every stage on the path with one tile count for
-    the unpaired stages, whole chunk groups per split, and inside the chain
-    a single weight step in flight at four m-tiles (the chain's state leaves
-    no registers for a second)."""
-    st = sg.LayerChain(M, 2, d, q, dff, flags=sg.F_KCHUNK).describe()["stages"]
+    """K-chunked chain stages (M = 17-32, two m-tiles): every stage on the
+    path with one tile count for the unpaired stages, whole chunk groups per
+    split; more m-tiles are refused (their kernels would not fit the
+    registers next to the chain's state)."""
     MT = -(-M // 16)
+    if MT != 2:
+        assert _create(kind=sg.KIND_LAYERCHAIN, M=M, L=2, d=d, q=q, dff=dff, flags=sg.F_KCHUNK) == \
+            sg.ERR_UNSUPPORTED
+        return
+    st = sg.LayerChain(M, 2, d, q, dff, flags=sg.F_KCHUNK).describe()["stages"]
     assert [s["path"] for s in st] == ["kc"] * 4 and all(s["ta"] == MT for s in st)
     assert st[0]["tb"] == st[1]["tb"] == st[3]["tb"] and st[2]["paired"] == 1 and st[2]["tb"] % 2 == 0
     for s, (K, N) in zip(st, ((d, q), (q, d), (d, dff), (dff, d))):
         tiles = s["tb"]
-        ring = 1 if tiles >= 6 or MT >= 4 else (2 if tiles >= 4 else 4)
+        ring = 1 if tiles >= 6 else (2 if tiles >= 4 else 4)
         assert s["ring"] == ring and s["KS"] % (512 * ring) == 0
         assert s["S"] * s["KS"] >= K and (s["S"] - 1) * s["KS"] < K
         np_ = tiles // 2 if s["paired"] else tiles
         assert s["CB"] == 16 * np_ and s["NB"] * s["CB"] >= s["Nx"] and 8 * s["Nx"] >= N
         assert s["lds"] + STATIC_LDS_RESERVE <= 160 * 1024
-    if MT == 4:
-        assert (st[0]["tb"], st[2]["tb"]) == (4, 4)
 
 
 def test_chain_kchunk_flag_combinations():
@@ -261,11 +263,12 @@ def test_chain_kchunk_flag_combinations():
     assert _create(M=32, flags=sg.F_KCHUNK, **chain) == sg.OK
     assert _create(M=32, flags=sg.F_KCHUNK | sg.F_SCHEDULER, **chain) == sg.OK
     assert _create(M=16, flags=sg.F_KCHUNK, **chain) == sg.ERR_UNSUPPORTED     # one m-tile: not built
+    assert _create(M=33, flags=sg.F_KCHUNK, **chain) == sg.ERR_UNSUPPORTED     # three: not built
     assert _create(M=32, flags=sg.F_KCHUNK | sg.F_FORCE_MFMA, **chain) == sg.ERR_UNSUPPORTED
     assert _create(M=32, flags=sg.F_KCHUNK, ksl=2, **chain) == sg.ERR_UNSUPPORTED
     assert _create(M=32, flags=sg.F_KCHUNK, waves=4, **chain) == sg.ERR_UNSUPPORTED
     assert _create(M=32, flags=sg.F_KCHUNK, tn=64, **chain) == sg.OK            # four tiles per item
-    assert _create(M=64, flags=sg.F_KCHUNK, tn=96, **chain) == sg.ERR_UNSUPPORTED
+    assert _create(M=32, flags=sg.F_KCHUNK, tn=96, **chain) == sg.ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("M,d,q,dff", [(1, 4096, 4096, 12288), (2, 4096, 4096, 12288), (2, 1024, 1032, 3000),
