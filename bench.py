@@ -26,7 +26,11 @@ fraction of 8 TB/s.
 ``--workload chain``: the 36-layer persistent chain at M = 64 (``--chain-m``
 selects another row count; Q 4096x4096,
 O 4096x4096, gate_up 4096x24576 with SiLU gate, down 12288x4096 per layer;
-13.29 GB of weights) in one launch per step.  ``--chain-kchunk`` runs every
+13.29 GB of weights) in one launch per step.  ``--workload decoder``: the
+whole decoder layer (RMSNorm, QKV 4096x6144, grouped-query decode attention
+over a synthetic KV cache of ``--decoder-ctx`` positions with 32 query and 8
+key/value heads of 128, O with residual, RMSNorm, gate_up with SiLU gate, down
+with residual), 36 layers in one launch, at M = ``--chain-m`` rows.  ``--chain-kchunk`` runs every
 chain stage on the K-chunked MFMA path and ``--chain-tn`` fixes the planner's
 tile width (ablations of the chain's stage kernels).
 
@@ -377,7 +381,8 @@ def bench_chain(args):
     M, L, d, q, dff = args.chain_m, 36, 4096, 4096, 12288
     wl = chain_weights(dev, L, d, q, dff)
     X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(5, 0, 0), M, d), dev)
-    ch = sg.LayerChain(M, L, d, q, dff, flags=sg.F_KCHUNK if args.chain_kchunk else 0, tn=args.chain_tn)
+    flags = (sg.F_KCHUNK if args.chain_kchunk else 0) | (sg.F_LAUNCH_PER_STAGE if args.chain_per_stage else 0)
+    ch = sg.LayerChain(M, L, d, q, dff, flags=flags, tn=args.chain_tn)
     ws = ch.new_workspace()
     Y = torch.empty((M, d), dtype=torch.float32, device=dev)
     wbytes = L * 2 * (q * d + d * q + 2 * dff * d + d * dff)
@@ -427,13 +432,114 @@ def bench_chain(args):
     return out
 
 
+def cpu_baseline_decoder(M, x_bits, wn, layer_w, kc, vc, Hq, Hkv):
+    """The oracle's decoder layer (RMSNorm, QKV, grouped-query decode
+    attention, O with residual, RMSNorm, gate_up with SiLU gate, down with
+    residual) on the host cores, repeated on layer 0 for about 10 s."""
+    import oracle
+
+    t0 = time.perf_counter()
+    reps = 0
+    nbytes = 0
+    step_bytes = sum(2 * w.size for w in layer_w) + 2 * kc.size + 2 * vc.size
+    while True:
+        oracle.decoder_layer(x_bits, wn[0], layer_w[0], kc, vc, layer_w[1], wn[1], layer_w[2], layer_w[3], Hq, Hkv)
+        nbytes += step_bytes
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 2000:
+            break
+    dt = time.perf_counter() - t0
+    return dict({"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+                 "kind": "oracle",
+                 "sample": "%d decoder layers (%.1f s) on layer 0's weights, norms, KV cache and input: every "
+                           "output, M=%d, double accumulation" % (reps, dt, M)}, **host_cpu())
+
+
+def bench_decoder(args):
+    import math
+
+    import torch
+
+    import chiplet_aware_persistent_amd as sg
+    import synth
+
+    dev = torch.device("cuda:0")
+    M, L, d, dff, Hq, Hkv, hd, T = args.chain_m, 36, 4096, 12288, 32, 8, 128, args.decoder_ctx
+    q, kv = Hq * hd, Hkv * hd
+    shapes = [(q + 2 * kv, d), (d, q), (2 * dff, d), (d, dff)]
+    wl = [[synth.uniform_bf16_torch(synth.seed_for(6, l, 1 + i), r, c, synth.weight_scale(c), dev)
+           for i, (r, c) in enumerate(shapes)] for l in range(L)]
+    wn_bits = synth.f32_to_bf16_bits(1.0 + synth.bf16_bits_to_f32(
+        synth.uniform_bf16(synth.seed_for(6, 0, 7), L * 2, d, 0.25))).reshape(L, 2, d)
+    Wn = synth.to_torch_bf16(wn_bits, dev)
+    n = L * M * Hkv * T
+    Kc = synth.uniform_bf16_torch(synth.seed_for(6, 0, 8), n, hd, math.sqrt(3.0), dev).view(L, M, Hkv, T, hd)
+    Vc = synth.uniform_bf16_torch(synth.seed_for(6, 0, 9), n, hd, math.sqrt(3.0), dev).view(L, M, Hkv, T, hd)
+    X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(6, 0, synth.T_X), M, d), dev)
+    dec = sg.Decoder(M, L, d, dff, Hq, Hkv, hd, T)
+    ws = dec.new_workspace()
+    Y = torch.empty((M, d), dtype=torch.float32, device=dev)
+    cols = [[w[i] for w in wl] for i in range(4)]
+    wbytes = L * sum(2 * r * c for r, c in shapes)
+    kvbytes = 2 * 2 * n * hd
+    nbytes = wbytes + kvbytes
+    if args.copy_calibration:
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        dec(X0, Wn, *cols, Kc, Vc, Y, ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        dec(X0, Wn, *cols, Kc, Vc, Y, ws)
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rc = dec.status(ws)
+    if rc:
+        raise sg.SgemmError(rc, "decoder status")
+    ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    avg = sum(ts) / len(ts)
+    achieved = nbytes / (avg * 1e-6) / 1e9
+    out = {
+        "metric": "achieved HBM GB/s (weight and KV-cache bytes), whole decoder layer chain, bf16",
+        "value": round(nbytes / (wall / args.steps) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decoder_36_layers_m{M}_ctx{T}", "M": M, "layers": L, "d_model": d, "d_ff": dff,
+                   "heads": Hq, "kv_heads": Hkv, "head_dim": hd, "ctx": T, "weight_bytes_per_step": wbytes,
+                   "kv_cache_bytes_per_step": kvbytes, "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "kernel": "k_decoder", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic(f"decoder_m{M}_ctx{T}_36l"), "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(avg, 2)},
+        "decoder_us": {"median": round(ts[len(ts) // 2], 2), "min": round(ts[0], 2), "max": round(ts[-1], 2)},
+        "plan": [{k: st[k] for k in ("path", "ta", "tb", "waves", "TN", "ksl", "S", "KS", "items")}
+                 for st in dec.describe()["stages"]],
+    }
+    if not args.no_cpu:
+        lw = [synth.from_torch_bf16(wl[0][i]) for i in range(4)]
+        kc0 = synth.from_torch_bf16(Kc[0].reshape(-1, hd)).reshape(M, Hkv, T, hd)
+        vc0 = synth.from_torch_bf16(Vc[0].reshape(-1, hd)).reshape(M, Hkv, T, hd)
+        out["cpu_baseline"] = cpu_baseline_decoder(M, synth.from_torch_bf16(X0), wn_bits[0], lw, kc0, vc0, Hq, Hkv)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["proj", "chain"], default="proj")
-    ap.add_argument("--chain-m", type=int, default=64, help="rows of the chain workload (1-64)")
+    ap.add_argument("--workload", choices=["proj", "chain", "decoder"], default="proj")
+    ap.add_argument("--chain-m", type=int, default=64, help="rows of the chain and decoder workloads (1-64)")
+    ap.add_argument("--decoder-ctx", type=int, default=1024, help="decoder workload: cached positions per sequence")
+    ap.add_argument("--chain-per-stage", action="store_true",
+                    help="chain workload: one launch per projection stage (for per-stage counters)")
     ap.add_argument("--chain-kchunk", action="store_true",
                     help="chain workload with every stage on the K-chunked MFMA path (M = 17-32)")
     ap.add_argument("--chain-tn", type=int, default=0, help="chain workload: tile width override (0 = planner)")
@@ -453,7 +559,7 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    out = bench_proj(args) if args.workload == "proj" else bench_chain(args)
+    out = {"proj": bench_proj, "chain": bench_chain, "decoder": bench_decoder}[args.workload](args)
     print(json.dumps(out), flush=True)
 
 

@@ -14,6 +14,7 @@ the stage.  For every stage after the first this prints, averaged over the
 - span: last end minus first start.
 
     python -m chiplet_aware_persistent_amd.chain_stamps [--m 1 16 64] [--modes default scheduler]
+    python -m chiplet_aware_persistent_amd.chain_stamps --m 1 64 --decoder-ctx 1024
 
 Weights and input as in the chain benchmark (distinct seeded
 U(-1/sqrt(K), 1/sqrt(K)) bf16 per layer, d = q = 4096, d_ff = 12288).  Each
@@ -37,17 +38,20 @@ D_MODEL, Q_COLS, D_FF, LAYERS = 4096, 4096, 12288, 36
 STAGES = ("Q", "O", "gate_up", "down")
 
 
-def stage_breakdown(st):
+DECODER_STAGES = ("QKV", "attention", "O", "gate_up", "down")
+
+
+def stage_breakdown(st, stages=STAGES):
     """st: [workgroups][events][2] start/end stamps in microseconds.  Returns
-    {projection: [release, skew, med_start, work_med, tail, span]} averaged
-    over the events of that projection (the first event excluded)."""
+    {stage: [release, skew, med_start, work_med, tail, span]} averaged over
+    the events of that stage (the first event excluded)."""
     import numpy as np
 
-    acc = {n: [] for n in STAGES}
+    acc = {n: [] for n in stages}
     for e in range(1, st.shape[1]):
         prev_end = st[:, e - 1, 1]
         s0, s1 = st[:, e, 0], st[:, e, 1]
-        acc[STAGES[e % 4]].append([s0.min() - prev_end.max(), s0.max() - s0.min(), np.median(s0) - s0.min(),
+        acc[stages[e % len(stages)]].append([s0.min() - prev_end.max(), s0.max() - s0.min(), np.median(s0) - s0.min(),
                                    np.median(s1 - s0), s1.max() - np.median(s1), s1.max() - s0.min()])
     return {n: np.mean(np.array(v), axis=0).tolist() for n, v in acc.items() if v}
 
@@ -63,7 +67,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--m", type=int, nargs="+", default=[1, 16, 64])
     ap.add_argument("--modes", nargs="+", default=["default", "scheduler"], choices=sorted(modes))
+    ap.add_argument("--decoder-ctx", type=int, default=-1,
+                    help="time the whole decoder layer instead (cached positions; 5 stages per layer)")
     a = ap.parse_args()
+    if a.decoder_ctx >= 0:
+        return decoder_main(a)
     dev = torch.device("cuda:0")
     d, q, dff = D_MODEL, Q_COLS, D_FF
     wl = []
@@ -102,6 +110,60 @@ def main():
                                   "release": round(v[0], 2), "skew": round(v[1], 2), "med_start": round(v[2], 2),
                                   "work_med": round(v[3], 2), "tail": round(v[4], 2), "span": round(v[5], 2)}),
                       flush=True)
+
+
+def decoder_main(a):
+    """Stage stamps of the decoder layer (QKV with the attention norm,
+    attention, O with the residual, gate_up with the MLP norm, down with the
+    residual), 36 layers, weights and KV cache as in the decoder benchmark."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import chiplet_aware_persistent_amd as sg
+    import synth
+
+    dev = torch.device("cuda:0")
+    L, d, dff, Hq, Hkv, hd, T = LAYERS, D_MODEL, D_FF, 32, 8, 128, a.decoder_ctx
+    q, kv = Hq * hd, Hkv * hd
+    shapes = [(q + 2 * kv, d), (d, q), (2 * dff, d), (d, dff)]
+    wl = [[synth.uniform_bf16_torch(synth.seed_for(6, l, 1 + i), r, c, synth.weight_scale(c), dev)
+           for i, (r, c) in enumerate(shapes)] for l in range(L)]
+    cols = [[w[i] for w in wl] for i in range(4)]
+    wn = synth.f32_to_bf16_bits(1.0 + synth.bf16_bits_to_f32(
+        synth.uniform_bf16(synth.seed_for(6, 0, 7), L * 2, d, 0.25))).reshape(L, 2, d)
+    Wn = synth.to_torch_bf16(wn, dev)
+    for M in a.m:
+        n = L * M * Hkv * max(T, 1)
+        Kc = synth.uniform_bf16_torch(synth.seed_for(6, 0, 8), n, hd, math.sqrt(3.0), dev)
+        Vc = synth.uniform_bf16_torch(synth.seed_for(6, 0, 9), n, hd, math.sqrt(3.0), dev)
+        Kc = Kc[: L * M * Hkv * T].view(L, M, Hkv, T, hd)
+        Vc = Vc[: L * M * Hkv * T].view(L, M, Hkv, T, hd)
+        X0 = synth.to_torch_bf16(synth.normal_bf16(synth.seed_for(6, 0, synth.T_X), M, d), dev)
+        dec = sg.Decoder(M, L, d, dff, Hq, Hkv, hd, T, flags=sg.F_STAMPS)
+        ws = dec.new_workspace()
+        Y = torch.empty((M, d), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            dec(X0, Wn, *cols, Kc, Vc, Y, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dec(X0, Wn, *cols, Kc, Vc, Y, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        rc = dec.status(ws)
+        if rc != sg.OK:
+            raise RuntimeError("decoder status %s (M=%d)" % (sg.status_string(rc), M))
+        info = dec.describe()
+        E, G, off = 5 * L, info["grid"], info["stamps_offset"]
+        st = ws[off:off + G * E * 16].view(torch.int64).view(G, E, 2).cpu().numpy().astype(np.float64) / 100.0
+        us = e0.elapsed_time(e1) * 1e3
+        for stage, v in stage_breakdown(st, DECODER_STAGES).items():
+            print(json.dumps({"M": M, "mode": "decoder", "ctx": T, "decoder_us": round(us, 1), "stage": stage,
+                              "release": round(v[0], 2), "skew": round(v[1], 2), "med_start": round(v[2], 2),
+                              "work_med": round(v[3], 2), "tail": round(v[4], 2), "span": round(v[5], 2)}),
+                  flush=True)
 
 
 if __name__ == "__main__":

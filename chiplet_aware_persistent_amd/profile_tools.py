@@ -5,6 +5,7 @@
         <write_counter_collection.csv> [--roles a,b,c] [--skip N]
     python -m chiplet_aware_persistent_amd.profile_tools sweep <config_sweep stdout> <kernel_trace.csv>
     python -m chiplet_aware_persistent_amd.profile_tools tcc <config_sweep stdout> <counter_collection.csv>
+    python -m chiplet_aware_persistent_amd.profile_tools counters <config_sweep stdout> <counter_collection.csv>
     python -m chiplet_aware_persistent_amd.profile_tools read <read_probe stdout> <kernel_trace.csv>
 
 ``trace``: per-role kernel durations.  The decode projections launch the same
@@ -31,7 +32,7 @@ import statistics
 
 
 def _ours(name: str) -> bool:
-    return "sg::k_gemm" in name or "sg::k_chain" in name
+    return "sg::k_gemm" in name or "sg::k_chain" in name or "sg::k_decoder" in name
 
 
 def role_sequence(n: int, roles, skip: int = 0, bench=None):
@@ -151,6 +152,27 @@ def sweep_tcc(sweep_log: str, counter_csv: str, warmup: int = 1):
     return out
 
 
+def sweep_counters(sweep_log: str, counter_csv: str, warmup: int = 1):
+    """Every counter of a --pmc run of config_sweep, summed over the
+    dispatch's instances and averaged over the shape's timed launches."""
+    disp = collections.OrderedDict()
+    for r in csv.DictReader(open(counter_csv)):
+        if not _ours(r["Kernel_Name"]):
+            continue
+        d = disp.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    rows = [disp[k] for k in sorted(disp)]
+    shapes, per = _sweep_groups(sweep_log, rows)
+    out = []
+    for i, sh in enumerate(shapes):
+        g = rows[i * per + warmup:(i + 1) * per]
+        r = {"M": sh["M"], "K": sh["K"], "N": sh["N"], "plan": sh["plan"], "launches": len(g)}
+        for name in sorted(g[0]) if g else []:
+            r[name] = round(statistics.mean(x[name] for x in g), 1)
+        out.append(r)
+    return out
+
+
 def read_durations(probe_log: str, trace_csv: str, warmup: int = 3):
     """Kernel durations of the read probe (k_stream_read) per (bytes, pattern)
     line of the read_probe driver's output, warm-up launches dropped."""
@@ -190,6 +212,10 @@ def main():
     h.add_argument("log")
     h.add_argument("csv")
     h.add_argument("--warmup", type=int, default=1)
+    k = sub.add_parser("counters")
+    k.add_argument("log")
+    k.add_argument("csv")
+    k.add_argument("--warmup", type=int, default=1)
     q = sub.add_parser("read")
     q.add_argument("log")
     q.add_argument("csv")
@@ -199,6 +225,8 @@ def main():
         print(json.dumps(read_durations(a.log, a.csv, a.warmup), indent=1))
     elif a.cmd == "sweep":
         print(json.dumps(sweep_durations(a.log, a.csv, a.warmup), indent=1))
+    elif a.cmd == "counters":
+        print(json.dumps(sweep_counters(a.log, a.csv, a.warmup), indent=1))
     elif a.cmd == "tcc":
         print(json.dumps(sweep_tcc(a.log, a.csv, a.warmup), indent=1))
     elif a.cmd == "trace":
