@@ -478,7 +478,7 @@ static int plan_decoder(sgemm_plan_s* pl, const sgemm_problem& p, int tn_o, int 
   cur = round_up(cur + pl->act_layer_elems * 2 * p.n_layers, 256);
   pl->off_stamps = cur;
   if (p.flags & SGEMM_F_STAMPS) cur = round_up(cur + (size_t)pl->grid * events * 2 * 8, 256);
-  int lds = 16 * 1024;  // the attention stage: queries and weights, 2 KB per wave
+  int lds = 8 * 18 * 1024;  // the attention stage: queries, weights and value rows, 18 KB per wave
   for (int s = 0; s < kChainStages; ++s) lds = std::max(lds, pl->cg[s].lds);
   pl->norm_off = (int)round_up((size_t)lds, 16);
   pl->dec_lds = pl->norm_off + 256;
@@ -1086,6 +1086,10 @@ int sgemm_plan_describe(sgemm_plan plan, char* buf, size_t len) {
                 plan->grid, plan->ws_bytes, plan->w_aux, plan->sync == SYNC_XCD ? "xcd" : "agent",
                 plan->off_stamps);
   s += b;
+  if (plan->prob.kind == SGEMM_KIND_DECODER) {
+    std::snprintf(b, sizeof b, "\"lds\":%d,\"chunks\":%d,", plan->dec_lds, plan->nchunk);
+    s += b;
+  }
   if (plan->prob.kind == SGEMM_KIND_GEMM) {
     s += "\"stage\":" + geo_json(plan->geo);
   } else {
