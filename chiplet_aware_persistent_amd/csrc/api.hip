@@ -339,6 +339,7 @@ struct sgemm_plan_s {
   // Decoder layer: activations qkv = a_h1, o = a_h2, x1, a = a_a, x' = a_x; attention partials and counters.
   size_t a_x1 = 0, off_apart = 0, off_actr = 0;
   int nchunk = 0, norm_off = 0, dec_lds = 0;
+  int attn_s = 1;  // decoder: attention slices (workgroups) per (sequence, head) pair
   long long spin_ticks = 0;
   int gcopies = kXcds;  // chain/decoder: copies of each global counter (see ChainArgs)
 };
@@ -462,7 +463,17 @@ static int plan_decoder(sgemm_plan_s* pl, const sgemm_problem& p, int tn_o, int 
   pl->off_ready = cur;
   cur = round_up(cur + (size_t)kXcds * kWgPerXcd * 4, 256);
   pl->nchunk = ceil_div(p.ctx + 1, 64);
-  const size_t apart = M * p.n_kv_heads * (size_t)pl->nchunk * 4 * (p.head_dim + 2) * 4;
+  // Attention: S workgroups (slices) per (sequence, key/value head) pair, so
+  // that an XCD's 32 workgroups are busy, at most 8 and at most the chunks.
+  // SGEMM_ATTN_SLICES overrides it (1..8).
+  {
+    const int pairs_per_xcd = ceil_div(p.n_kv_heads, kXcds) * p.M;
+    int sl = 1;
+    while (sl < 8 && 2 * sl * pairs_per_xcd <= kWgPerXcd && 2 * sl <= pl->nchunk) sl *= 2;
+    if (!env_int("SGEMM_ATTN_SLICES", sl, &sl) || sl < 1 || sl > 8) return SGEMM_ERR_INVALID_ARG;
+    pl->attn_s = sl;
+  }
+  const size_t apart = M * p.n_kv_heads * (size_t)pl->attn_s * 4 * (p.head_dim + 2) * 4;
   if (apart >= kMaxOperand) return SGEMM_ERR_UNSUPPORTED;
   pl->off_apart = cur;
   cur = round_up(cur + apart, 256);
@@ -994,6 +1005,7 @@ int decoder_run(sgemm_plan plan, const void* X0, const void* w_norm, const void*
   a.apart = (float*)(ws + plan->off_apart);
   a.actr = (unsigned*)(ws + plan->off_actr);
   a.Hq = p.n_heads; a.Hkv = p.n_kv_heads; a.hd = p.head_dim; a.T = p.ctx; a.pc = 64; a.nchunk = plan->nchunk;
+  a.attn_s = plan->attn_s;
   a.eps = 1e-6f;
   a.norm_off = plan->norm_off;
   a.spin_ticks = plan->spin_ticks;
@@ -1087,7 +1099,8 @@ int sgemm_plan_describe(sgemm_plan plan, char* buf, size_t len) {
                 plan->off_stamps);
   s += b;
   if (plan->prob.kind == SGEMM_KIND_DECODER) {
-    std::snprintf(b, sizeof b, "\"lds\":%d,\"chunks\":%d,", plan->dec_lds, plan->nchunk);
+    std::snprintf(b, sizeof b, "\"lds\":%d,\"chunks\":%d,\"attn_slices\":%d,", plan->dec_lds, plan->nchunk,
+                  plan->attn_s);
     s += b;
   }
   if (plan->prob.kind == SGEMM_KIND_GEMM) {

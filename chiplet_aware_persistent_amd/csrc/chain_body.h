@@ -113,7 +113,10 @@ static __device__ __forceinline__ void signal_event(const ChainArgs& a, int e, i
   __syncthreads();
   if (threadIdx.x < 64) {
     // Wave 0: lane 0 counts the workgroup in; lane c < gcopies bumps copy c.
-    const int lane = threadIdx.x;
+    // (The lane index is opaque here so that the copies' addresses are not
+    // hoisted out of the stage loop and kept in registers for the launch.)
+    int lane = threadIdx.x;
+    asm volatile("" : "+v"(lane));
     const int events = a.spl * a.n_layers;
     unsigned old = 0;
     if (!a.flat_sync && lane == 0)

@@ -101,32 +101,35 @@ struct RmsNormX {
 };
 
 // Grouped-query decode attention of layer l (event 5l+1).  Key/value head g
-// belongs to XCD g mod 8, so all the work on one head, and its combine,
-// stays in that XCD's L2.  A unit is one wave: sequence m, head g, positions
-// [64c, 64c + 64) of the T cached ones and the new one (position T, read from
-// the QKV output).  The unit issues all its loads at once, so it costs about
-// one memory round trip: lane i's key row 64c + i into registers, and the
-// 64 value rows into the wave's LDS with buffer-to-LDS loads (16 KB, no
-// registers).  Lane i scores its position against the GRP query heads of g
-// (v_dot2 over the head dimension against the queries staged in LDS), the
-// wave takes the softmax of its 64 scores per head, then sums p_t v_t from
-// LDS in two halves (lanes 0-31 positions 64c + r, lanes 32-63 positions
-// 64c + 32 + r, each lane four value dimensions) and adds the halves.  The
-// unit writes its (max, sum, accumulator) per head; the last of a (m, g)'s
-// units to arrive (arrival counter, old value nchunk - 1) combines them in
-// chunk order, so the result does not depend on timing, and writes bf16
-// o[m][(g GRP + j) HD + i].  The combine loads every chunk's max and sum of
-// all heads at once and keeps the next batch of accumulators in flight while
-// it adds the current one.
+// belongs to XCD g mod 8, so all the work on one head stays in that XCD's L2.
+// A (sequence m, head g) pair is split into S slices (S = 1 when an XCD has
+// enough pairs to keep its workgroups busy, up to 8 for few); slice s is one
+// workgroup and takes the chunks c = s, s + S, ... of 64 positions of the T
+// cached ones and the new one (position T, read from the QKV output).  Its
+// eight waves take those chunks in turn and each keeps a running softmax
+// (max, sum and accumulator, rescaled as the max grows).  A chunk costs one
+// memory round trip: the lane's key row 64c + lane into registers and the 64
+// value rows into the wave's LDS with buffer-to-LDS loads, all issued at
+// once; lane i scores its position against the GRP query heads of g (v_dot2
+// over the head dimension against the queries in LDS), and p_t v_t is summed
+// from LDS in two halves (lanes 0-31 positions 64c + r, lanes 32-63 positions
+// 64c + 32 + r, four value dimensions per lane).  The waves' results meet in
+// LDS and waves 0..GRP-1 add them in wave order, one head each.  With S > 1
+// the slice's result goes to memory and the slice whose arrival completes
+// the pair (XCD-local arrival counter, old value S - 1) adds the S results in
+// slice order.  Every sum runs in a fixed order, so the output does not
+// depend on timing.  Output: bf16 o[m][(g GRP + j) HD + i].
 template <int GRP, int HD, typename Hook>
 __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* lds, int xcd, int slot, int nslots,
                                           Hook pre) {
   static_assert(HD == 128, "four head dimensions per lane and half");
-  static_assert(GRP == 4 && GRP * HD * 2 == 1024, "one kilobyte of queries per unit");
+  static_assert(GRP == 4 && GRP * HD * 2 == 1024, "one kilobyte of queries per pair");
+  constexpr int RL = HD + 2;  // floats of one head's result: accumulator, max, sum
+  static_assert(GRP * RL * 4 <= kAttnPos * HD * 2, "a wave's result fits its value rows' LDS");
   if (!pre()) return false;
   const int wave = threadIdx.x >> 6;
   const int nwv = (int)(blockDim.x >> 6);
-  const int M = a.M, Hkv = a.Hkv, T = a.T, nch = a.nchunk;
+  const int M = a.M, Hkv = a.Hkv, T = a.T, nch = a.nchunk, S = a.attn_s;
   const int qcols = a.Hq * HD, ld = qcols + 2 * Hkv * HD;
   const uint16_t* qkv = a.act + (size_t)l * a.act_layer_elems + a.off_qkv;
   uint16_t* out = a.act + (size_t)l * a.act_layer_elems + a.off_o;
@@ -137,213 +140,207 @@ __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* l
   const unsigned qkv_bytes = (unsigned)((size_t)M * ld * 2);
   const Rsrc qr = make_rsrc(qkv, qkv_bytes);
   const Rsrc orr = make_rsrc(out, (unsigned)((size_t)M * qcols * 2));
-  constexpr int PL = GRP * (HD + 2);  // floats of one unit's partial
-  const unsigned pext = (unsigned)((size_t)M * Hkv * nch * PL * 4);
-  const Rsrc pr = make_rsrc(a.apart, pext);
+  const unsigned pext = (unsigned)((size_t)M * Hkv * S * GRP * RL * 4);
+  const Rsrc pr = make_rsrc(a.apart, pext);  // slice results [m][g][slice][head][RL]
   const float scale = 1.0f / __builtin_sqrtf((float)HD);
   constexpr float kLog2e = 1.4426950408889634f;
-  // Per wave (kAttnWaveLds bytes): the GRP query rows (GRP x HD bf16), the
-  // 64 x GRP weights and the 64 value rows (64 x HD bf16).
-  static_assert(kAttnWaveLds == GRP * HD * 2 + kAttnPos * GRP * 4 + kAttnPos * HD * 2, "attention LDS layout");
-  uint16_t* qs = (uint16_t*)((char*)lds + wave * kAttnWaveLds);
+  auto wave_lds = [&](int w) { return (char*)lds + w * kAttnWaveLds; };
+  uint16_t* qs = (uint16_t*)wave_lds(wave);
   float* ps = (float*)(qs + GRP * HD);
   uint16_t* vs = (uint16_t*)(ps + kAttnPos * GRP);
-  const int hpx = (Hkv + kXcds - 1) / kXcds;  // key/value heads per XCD
-  const int units = hpx * M * nch;
-  const int nwx = nslots * nwv;
-  for (int u = slot * nwv + wave; u < units; u += nwx) {
-    const int gi = u / (M * nch);
-    const int rem = u - gi * (M * nch);
-    const int m = rem / nch;
-    const int c = rem - m * nch;
+  const int vs_off = GRP * HD * 2 + kAttnPos * GRP * 4;  // byte offset of the value rows in a wave's LDS
+  const int hpx = (Hkv + kXcds - 1) / kXcds;
+  const int tasks = hpx * M * S;  // (pair, slice), slice fastest
+  for (int task = slot; task < tasks; task += nslots) {
+    const int pi = task / S;
+    const int sl = task - pi * S;
+    const int gi = pi / M;
+    const int m = pi - gi * M;
     const int g = xcd + kXcds * gi;
-    if (g >= Hkv) continue;  // uniform over the wave
-    // The lane index, opaque to the compiler inside the unit: otherwise it
-    // hoists the dozens of per-lane load offsets out of the layer loop and
-    // keeps them in registers through every stage of the launch.
+    if (g >= Hkv) continue;  // uniform over the workgroup
     int lane = threadIdx.x & 63;
-    asm volatile("" : "+v"(lane));
-    const int hf = lane >> 5;        // value half: positions [32 hf, 32 hf + 32) of the unit
-    const int dq = 4 * (lane & 31);  // the lane's first value dimension
-    const int t = c * kAttnPos + lane;
-    const unsigned hrow = ((unsigned)m * Hkv + g) * (unsigned)T;  // first cache row of (m, g)
-    const bool has_new = T >= c * kAttnPos && T < (c + 1) * kAttnPos;  // uniform: the chunk holding position T
-    // All loads of the unit, oldest first: queries, key rows (the cache for
-    // t < T, zeros past it; the new key for t == T only in the last chunk),
-    // value dimensions [dq, dq + 4) of the 32 positions of the lane's half
-    // (and of the new position).
-    const u4 qv = ld16<0>(qr, ((unsigned)m * ld + (unsigned)g * GRP * HD) * 2u + (unsigned)lane * 16u);
-    u4 kv[HD / 8];
-#pragma unroll
-    for (int i = 0; i < HD / 8; ++i) kv[i] = ld16<0>(kr, t < T ? (hrow + (unsigned)t) * HD * 2u + i * 16u : cext);
-    // Value rows to LDS: kilobyte i holds positions 64c + 4i .. 64c + 4i + 3
-    // (lane l: position 4i + l/16, dimensions 8 (l % 16) .. + 7).
-#pragma unroll
-    for (int i = 0; i < kAttnPos * HD * 2 / 1024; ++i) {
-      const int tt = c * kAttnPos + 4 * i + (lane >> 4);
-      const unsigned off = tt < T ? ((hrow + (unsigned)tt) * HD + 8u * (unsigned)(lane & 15)) * 2u : cext;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)((char*)vs + i * 1024),
-                                               16, off, 0, 0, 0);
-    }
-    U2 vnew = {0u, 0u};
-    if (has_new) {
-      const unsigned nkrow = ((unsigned)m * ld + (unsigned)qcols + (unsigned)g * HD) * 2u;
-      const unsigned nvrow = ((unsigned)m * ld + (unsigned)qcols + (unsigned)(Hkv + g) * HD) * 2u;
-#pragma unroll
-      for (int i = 0; i < HD / 8; ++i) kv[i] |= ld16<0>(qr, t == T ? nkrow + i * 16u : qkv_bytes);
-      vnew = ld8<0>(qr, hf == 0 ? nvrow + (unsigned)dq * 2u : qkv_bytes);
-    }
-    *(u4*)((char*)qs + lane * 16) = qv;
+    asm volatile("" : "+v"(lane));  // keeps the per-lane offsets inside the loop
+    const int hf = lane >> 5;
+    const int dq = 4 * (lane & 31);
+    const unsigned hrow = ((unsigned)m * Hkv + g) * (unsigned)T;
+    const unsigned nkrow = ((unsigned)m * ld + (unsigned)qcols + (unsigned)g * HD) * 2u;
+    const unsigned nvrow = ((unsigned)m * ld + (unsigned)qcols + (unsigned)(Hkv + g) * HD) * 2u;
+    *(u4*)((char*)qs + lane * 16) =
+        ld16<0>(qr, ((unsigned)m * ld + (unsigned)g * GRP * HD) * 2u + (unsigned)lane * 16u);
     __builtin_amdgcn_wave_barrier();
-    float s[GRP];
-#pragma unroll
-    for (int j = 0; j < GRP; ++j) s[j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < HD / 8; ++i) {
-      const bf16x8 kb = __builtin_bit_cast(bf16x8, kv[i]);
-#pragma unroll
-      for (int j = 0; j < GRP; ++j) {
-        const bf16x8 qb = *(const bf16x8*)(qs + j * HD + i * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2 kp = {kb[2 * e], kb[2 * e + 1]};
-          const bf16x2 qp = {qb[2 * e], qb[2 * e + 1]};
-          s[j] = __builtin_amdgcn_fdot2_f32_bf16(kp, qp, s[j], false);
-        }
-      }
-    }
-    const bool live = t <= T;
-    float mx[GRP], lsum[GRP];
-    f4 pl;
-#pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const float v = live ? s[j] * scale : -__builtin_huge_valf();
-      float mm = v;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
-      const float p = live ? __builtin_amdgcn_exp2f((v - mm) * kLog2e) : 0.f;
-      float sm = p;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
-      mx[j] = mm;
-      lsum[j] = sm;
-      pl[j] = p;
-    }
-    *(f4*)(ps + lane * GRP) = pl;
-    __builtin_amdgcn_wave_barrier();
-    // sum_t p_t v_t over the lane's half (zero weights past T), the new
-    // position's row (half 0), then the two halves added.
-    wait_vm0();  // the value rows are in LDS
+    float mrun[GRP], lrun[GRP];
     f4 acc[GRP];
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      const U2 vr2 = *(const U2*)(vs + (32 * hf + r) * HD + dq);
-      const f4 v = bf16x4_to_f4(vr2);
-      const f4 p4 = *(const f4*)(ps + (32 * hf + r) * GRP);
-#pragma unroll
-      for (int j = 0; j < GRP; ++j) acc[j] += p4[j] * v;
+    for (int j = 0; j < GRP; ++j) {
+      mrun[j] = -__builtin_huge_valf();
+      lrun[j] = 0.f;
+      acc[j] = f4{0.f, 0.f, 0.f, 0.f};
     }
-    if (has_new) {
-      const f4 v = bf16x4_to_f4(vnew);
-      const f4 p4 = *(const f4*)(ps + (T - c * kAttnPos) * GRP);
+    for (int c = sl + S * wave; c < nch; c += S * nwv) {
+      asm volatile("" : "+v"(lane));  // and inside the chunk loop
+      const int t = c * kAttnPos + lane;
+      const bool has_new = T >= c * kAttnPos && T < (c + 1) * kAttnPos;  // uniform
+      u4 kv[HD / 8];
 #pragma unroll
-      for (int j = 0; j < GRP; ++j) acc[j] += p4[j] * v;  // zero in half 1
+      for (int i = 0; i < HD / 8; ++i) kv[i] = ld16<0>(kr, t < T ? (hrow + (unsigned)t) * HD * 2u + i * 16u : cext);
+      // Value rows to LDS: kilobyte i holds positions 64c + 4i .. + 3 (lane
+      // l: position 4i + l/16, dimensions 8 (l % 16) .. + 7).
+#pragma unroll
+      for (int i = 0; i < kAttnPos * HD * 2 / 1024; ++i) {
+        const int tt = c * kAttnPos + 4 * i + (lane >> 4);
+        const unsigned off = tt < T ? ((hrow + (unsigned)tt) * HD + 8u * (unsigned)(lane & 15)) * 2u : cext;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)((char*)vs + i * 1024),
+                                                 16, off, 0, 0, 0);
+      }
+      U2 vnew = {0u, 0u};
+      if (has_new) {
+#pragma unroll
+        for (int i = 0; i < HD / 8; ++i) kv[i] |= ld16<0>(qr, t == T ? nkrow + i * 16u : qkv_bytes);
+        vnew = ld8<0>(qr, hf == 0 ? nvrow + (unsigned)dq * 2u : qkv_bytes);
+      }
+      float sc[GRP];
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) sc[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < HD / 8; ++i) {
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, kv[i]);
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) {
+          const bf16x8 qb = *(const bf16x8*)(qs + j * HD + i * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 kp = {kb[2 * e], kb[2 * e + 1]};
+            const bf16x2 qp = {qb[2 * e], qb[2 * e + 1]};
+            sc[j] = __builtin_amdgcn_fdot2_f32_bf16(kp, qp, sc[j], false);
+          }
+        }
+      }
+      const bool live = t <= T;
+      f4 pl;
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const float v = live ? sc[j] * scale : -__builtin_huge_valf();
+        float mm = v;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
+        const float nm = fmaxf(mrun[j], mm);  // finite: every chunk has a live position
+        const float so = __builtin_amdgcn_exp2f((mrun[j] - nm) * kLog2e);
+        const float p = live ? __builtin_amdgcn_exp2f((v - nm) * kLog2e) : 0.f;
+        float sm = p;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
+        lrun[j] = lrun[j] * so + sm;
+        mrun[j] = nm;
+        acc[j] *= so;
+        pl[j] = p;
+      }
+      *(f4*)(ps + lane * GRP) = pl;
+      __builtin_amdgcn_wave_barrier();
+      wait_vm0();  // the value rows are in LDS
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const f4 v = bf16x4_to_f4(*(const U2*)(vs + (32 * hf + r) * HD + dq));
+        const f4 p4 = *(const f4*)(ps + (32 * hf + r) * GRP);
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) acc[j] += p4[j] * v;
+      }
+      if (has_new) {
+        const f4 v = bf16x4_to_f4(vnew);
+        const f4 p4 = *(const f4*)(ps + (T - c * kAttnPos) * GRP);
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) acc[j] += p4[j] * v;  // zero in half 1
+      }
+      __builtin_amdgcn_wave_barrier();  // the LDS reads above before the next chunk's loads
     }
 #pragma unroll
     for (int j = 0; j < GRP; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[j][e] += __shfl_xor(acc[j][e], 32);
-    // The unit's partial: per head HD accumulator values, then max and sum.
-    const unsigned pbase = (unsigned)((((size_t)m * Hkv + g) * nch + c) * PL);
+    // The wave's result into its value-row LDS: per head RL floats.
+    float* res = (float*)vs;
 #pragma unroll
     for (int j = 0; j < GRP; ++j) {
-      const unsigned e = pbase + j * (HD + 2);
-      if (hf == 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st_f32<0>(pr, (e + dq + q) * 4u, acc[j][q]);
-      }
-      if (lane == 32) {
-        st_f32<0>(pr, (e + HD) * 4u, mx[j]);
-        st_f32<0>(pr, (e + HD + 1) * 4u, lsum[j]);
+      if (hf == 0) *(f4*)(res + j * RL + dq) = acc[j];
+      if (lane == 0) {
+        res[j * RL + HD] = mrun[j];
+        res[j * RL + HD + 1] = lrun[j];
       }
     }
-    // Arrival: the XCD-local split-K protocol (all units of (m, g) run on
-    // this XCD).  The owner adds the chunks in order.
-    splitk_release(SYNC_XCD);
-    unsigned* ctr = a.actr + m * Hkv + g;
-    const unsigned old = splitk_bump(ctr, lane);
-    if (!splitk_own(ctr, old, nch, SYNC_XCD, lane)) continue;
-    // Lane cc holds chunk cc's max and sum of every head (nch <= 64).
-    const unsigned base = (unsigned)(((size_t)m * Hkv + g) * nch * PL);
-    float mc[GRP], lc[GRP];
-#pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const unsigned ej = base + lane * PL + j * (HD + 2);
-      mc[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                            pr, (int)(lane < nch ? (ej + HD) * 4u : pext), 0, kAuxSc1));
-      lc[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                            pr, (int)(lane < nch ? (ej + HD + 1) * 4u : pext), 0, kAuxSc1));
+    __syncthreads();
+    // Waves 0..GRP-1, head j = wave: the waves' results added in wave order
+    // (lane: dimensions 2 lane, 2 lane + 1), giving the slice's max, sum and
+    // accumulator.
+    const int j = wave;
+    float gm = -__builtin_huge_valf(), L = 0.f, o0 = 0.f, o1 = 0.f;
+    if (wave < GRP) {
+      for (int w = 0; w < nwv; ++w) gm = fmaxf(gm, ((const float*)(wave_lds(w) + vs_off))[j * RL + HD]);
+      for (int w = 0; w < nwv; ++w) {
+        const float* rw = (const float*)(wave_lds(w) + vs_off) + j * RL;
+        const float f = __builtin_amdgcn_exp2f((rw[HD] - gm) * kLog2e);  // zero for a wave without chunks
+        L += rw[HD + 1] * f;
+        o0 += rw[2 * lane] * f;
+        o1 += rw[2 * lane + 1] * f;
+      }
     }
-    // Accumulators of head j, chunks [16 h, 16 h + 16): the lane's two values
-    // (dimensions 2 lane, 2 lane + 1) per chunk.  Batches in (head, chunk
-    // group) order alternate between two register sets; each is issued before
-    // the one ahead of it is added, and in-order returns leave it in flight.
-    auto issue = [&](U2(&dst)[16], int j, int h) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int cc = 16 * h + i;
-        const unsigned e = base + (unsigned)cc * PL + j * (HD + 2) + 2 * lane;
-        dst[i] = ld8<kAuxSc1>(pr, cc < nch ? e * 4u : pext);
+    const unsigned oc = ((unsigned)m * qcols + (unsigned)(g * GRP + j) * HD + 2u * lane) * 2u;
+    if (S == 1) {
+      if (wave < GRP) {
+        const unsigned pk = (unsigned)bf16_bits(o0 / L) | ((unsigned)bf16_bits(o1 / L) << 16);
+        __builtin_amdgcn_raw_buffer_store_b32(pk, orr, (int)oc, 0, kAuxNt);
       }
-    };
-    float o0[GRP], o1[GRP], L[GRP];
-    auto combine = [&](auto nbc) {
-      constexpr int NB = decltype(nbc)::value;  // chunk groups of 16 per head (nch <= 16 NB)
-      U2 buf[2][16];
-      issue(buf[0], 0, 0);
-      float f[GRP];
-#pragma unroll
-      for (int j = 0; j < GRP; ++j) {
-        float gm = lane < nch ? mc[j] : -__builtin_huge_valf();
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
-        f[j] = lane < nch ? __builtin_amdgcn_exp2f((mc[j] - gm) * kLog2e) : 0.f;
-        float sl = lc[j] * f[j];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) sl += __shfl_xor(sl, o);
-        L[j] = sl;
-        o0[j] = o1[j] = 0.f;
-      }
-#pragma unroll
-      for (int b = 0; b < NB * GRP; ++b) {
-        const int j = b / NB, h = b % NB;
-        if (b + 1 < NB * GRP) issue(buf[(b + 1) & 1], (b + 1) / NB, (b + 1) % NB);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float fi = __shfl(f[j], 16 * h + i);  // zero past nch
-          o0[j] += __builtin_bit_cast(float, buf[b & 1][i].x) * fi;
-          o1[j] += __builtin_bit_cast(float, buf[b & 1][i].y) * fi;
+    } else {
+      // The slice's result to memory, then the arrival: the XCD-local
+      // split-K protocol (all slices of (m, g) run on this XCD).
+      const unsigned pbase = (unsigned)(((size_t)m * Hkv + g) * S * GRP * RL);
+      if (wave < GRP) {
+        const unsigned e = pbase + (unsigned)(sl * GRP + j) * RL;
+        st_f32<0>(pr, (e + 2 * lane) * 4u, o0);
+        st_f32<0>(pr, (e + 2 * lane + 1) * 4u, o1);
+        if (lane == 0) {
+          st_f32<0>(pr, (e + HD) * 4u, gm);
+          st_f32<0>(pr, (e + HD + 1) * 4u, L);
         }
       }
-    };
-    const int ng = (nch + 15) / 16;
-    if (ng == 1) {
-      combine(std::integral_constant<int, 1>{});
-    } else if (ng == 2) {
-      combine(std::integral_constant<int, 2>{});
-    } else if (ng == 3) {
-      combine(std::integral_constant<int, 3>{});
-    } else {
-      combine(std::integral_constant<int, 4>{});
-    }
+      splitk_release(SYNC_XCD);
+      __syncthreads();
+      __shared__ int sh_own;
+      if (threadIdx.x < 64) {
+        unsigned* ctr = a.actr + m * Hkv + g;
+        const unsigned old = splitk_bump(ctr, lane);
+        const bool own = splitk_own(ctr, old, S, SYNC_XCD, lane);
+        if (lane == 0) sh_own = own ? 1 : 0;
+      }
+      __syncthreads();
+      if (sh_own && wave < GRP) {
+        // The S slices' results in slice order; lane s < S holds slice s's max.
+        const unsigned ej = pbase + (unsigned)j * RL;
+        const float ms = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                             pr, (int)(lane < S ? (ej + (unsigned)lane * GRP * RL + HD) * 4u : pext), 0, kAuxSc1));
+        const float ls = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                             pr, (int)(lane < S ? (ej + (unsigned)lane * GRP * RL + HD + 1) * 4u : pext), 0, kAuxSc1));
+        U2 av[8];
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const unsigned oc = ((unsigned)m * qcols + (unsigned)(g * GRP + j) * HD + 2u * lane) * 2u;
-      const unsigned pk = (unsigned)bf16_bits(o0[j] / L[j]) | ((unsigned)bf16_bits(o1[j] / L[j]) << 16);
-      __builtin_amdgcn_raw_buffer_store_b32(pk, orr, (int)oc, 0, kAuxNt);
+        for (int q = 0; q < 8; ++q)
+          av[q] = ld8<kAuxSc1>(pr, q < S ? (ej + (unsigned)q * GRP * RL + 2u * lane) * 4u : pext);
+        float M2 = lane < S ? ms : -__builtin_huge_valf();
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) M2 = fmaxf(M2, __shfl_xor(M2, o));
+        const float fs = lane < S ? __builtin_amdgcn_exp2f((ms - M2) * kLog2e) : 0.f;
+        float L2 = ls * fs;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) L2 += __shfl_xor(L2, o);
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float fq = __shfl(fs, q);  // zero past S
+          t0 += __builtin_bit_cast(float, av[q].x) * fq;
+          t1 += __builtin_bit_cast(float, av[q].y) * fq;
+        }
+        const unsigned pk = (unsigned)bf16_bits(t0 / L2) | ((unsigned)bf16_bits(t1 / L2) << 16);
+        __builtin_amdgcn_raw_buffer_store_b32(pk, orr, (int)oc, 0, kAuxNt);
+      }
     }
+    __syncthreads();  // LDS reuse by the next task
   }
   return true;
 }

@@ -44,9 +44,10 @@ struct ChainArgs {
   const uint16_t* wnorm;               // [layers][2][d] bf16: attention and MLP RMSNorm weights
   const uint16_t* kc;                  // [layers][M][Hkv][T][hd] bf16 cached keys
   const uint16_t* vc;                  // same, values
-  float* apart;                        // attention chunk partials [M][Hkv][chunks][grp][hd + 2]
-  unsigned* actr;                      // attention combine counters [M][Hkv]
+  float* apart;                        // attention slice results [M][Hkv][slices][grp][hd + 2]
+  unsigned* actr;                      // attention slice arrival counters [M][Hkv]
   int Hq, Hkv, hd, T, pc, nchunk;      // heads, head dim, cached positions, positions per chunk, chunks
+  int attn_s;                          // attention slices (workgroups) per (sequence, head) pair, 1..8
   float eps;                           // RMSNorm epsilon
   int norm_off;                        // LDS byte offset of the RMSNorm factors (M floats)
   size_t off_qkv, off_o, off_x1;       // decoder: element offsets of qkv, o and x1 in a layer's block

@@ -382,6 +382,8 @@ def test_decoder_plan_and_buffers(M):
     dec = sg.Decoder(M, 3, 4096, 12288, 32, 8, 128, 1024)
     dd = dec.describe()
     assert dd["kind"] == "decoder" and dd["chunks"] == 17
+    # attention slices per (sequence, head) pair: fill an XCD's 32 workgroups (one head per XCD here)
+    assert dd["attn_slices"] == {1: 8, 2: 8, 16: 2, 64: 1}[M]
     assert dd["lds"] >= 8 * 18 * 1024 + 256 and dd["lds"] + STATIC_LDS_RESERVE <= 160 * 1024
     st = dd["stages"]
     assert [(s["K"], s["N"]) for s in st] == [(4096, 6144), (4096, 4096), (4096, 12288), (12288, 4096)]
