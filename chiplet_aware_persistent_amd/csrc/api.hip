@@ -304,9 +304,10 @@ bool plan_kc(Geo& best, int M, int K, int N, int paired, int ntw_o, int s_o, con
              int slots = kWgPerXcd, bool chain = false) {
   bool found = false;
   const int MT = (M + 15) / 16;
-  for (int ntw = 2; ntw <= 8; ntw += 2) {
+  for (int ntw : {2, 3, 4, 6, 8}) {
     if (ntw_o && ntw != ntw_o) continue;
     if (ntw == 8 && MT > 2) continue;
+    if (paired && ntw % 2) continue;  // a paired block holds whole (gate, up) pairs
     const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : 16;
     for (int s = s_lo; s <= s_hi; ++s) {
       Geo c;
@@ -562,11 +563,13 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     } else if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, kCostGemm, 0, mti_rows)) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
-    } else if (path == 1 && !mti && !tn_o && !s_o && !w_o && !k_o && p.K >= 6144) {
-      // Long K with a wide output: the K-chunked path takes one item of six
-      // tiles over all of K per workgroup and needs no split-K, where the
-      // windowed MFMA path has to split K seven ways (16 x 7168 x 18432:
-      // 45.0 against 50.1 us, measured; elsewhere it measured no faster).
+    } else if (path == 1 && !mti && !tn_o && !s_o && !w_o && !k_o && (p.K >= 6144 || p.M > 48)) {
+      // Long K, or four full m-tiles, with a wide output: the K-chunked path
+      // takes one item of six tiles over all of K per workgroup and needs no
+      // split-K, where the windowed MFMA path has to split K four to seven
+      // ways (measured, back-to-back launches: 16 x 7168 x 18432 45.0 against
+      // 47.6 us, 64 x 4096 x 24576 49.5 against 54.0 us; at M = 32 and 48 and
+      // on the narrower outputs it measured no faster).
       Geo kcg;
       if (plan_kc(kcg, p.M, p.K, p.N, 0, 6, 1, kCostGemm) && kcg.items <= kWgPerXcd &&
           kcg.items * 4 >= kWgPerXcd * 3 && pl->geo.S > 2)

@@ -126,7 +126,6 @@ __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* l
   static_assert(GRP == 4 && GRP * HD * 2 == 1024, "one kilobyte of queries per pair");
   constexpr int RL = HD + 2;  // floats of one head's result: accumulator, max, sum
   static_assert(GRP * RL * 4 <= kAttnPos * HD * 2, "a wave's result fits its value rows' LDS");
-  if (!pre()) return false;
   const int wave = threadIdx.x >> 6;
   const int nwv = (int)(blockDim.x >> 6);
   const int M = a.M, Hkv = a.Hkv, T = a.T, nch = a.nchunk, S = a.attn_s;
@@ -151,6 +150,37 @@ __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* l
   const int vs_off = GRP * HD * 2 + kAttnPos * GRP * 4;  // byte offset of the value rows in a wave's LDS
   const int hpx = (Hkv + kXcds - 1) / kXcds;
   const int tasks = hpx * M * S;  // (pair, slice), slice fastest
+  // Value rows of a chunk to the wave's LDS: kilobyte i holds positions
+  // 64c + 4i .. + 3 (lane l: position 4i + l/16, dimensions 8 (l % 16) .. + 7).
+  auto issue_values = [&](int c, unsigned hrow, int ln) {
+#pragma unroll
+    for (int i = 0; i < kAttnPos * HD * 2 / 1024; ++i) {
+      const int tt = c * kAttnPos + 4 * i + (ln >> 4);
+      const unsigned off = tt < T ? ((hrow + (unsigned)tt) * HD + 8u * (unsigned)(ln & 15)) * 2u : cext;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)((char*)vs + i * 1024),
+                                               16, off, 0, 0, 0);
+    }
+  };
+  // The cache does not depend on the stage's input: the value rows of the
+  // first chunk of the wave's first task go to LDS before the wait (the LDS
+  // is free, every stage ends at a barrier), so their round trip overlaps
+  // the previous stage.  They take no registers across the wait.
+  bool vahead = false;
+  if (slot < tasks) {
+    const int pi = slot / S;
+    const int sl = slot - pi * S;
+    const int gi = pi / M;
+    const int m = pi - gi * M;
+    const int g = xcd + kXcds * gi;
+    const int c = sl + S * wave;
+    if (g < Hkv && c < nch) {
+      int ln = threadIdx.x & 63;
+      asm volatile("" : "+v"(ln));
+      issue_values(c, ((unsigned)m * Hkv + g) * (unsigned)T, ln);
+      vahead = true;
+    }
+  }
+  if (!pre()) return false;
   for (int task = slot; task < tasks; task += nslots) {
     const int pi = task / S;
     const int sl = task - pi * S;
@@ -165,9 +195,12 @@ __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* l
     const unsigned hrow = ((unsigned)m * Hkv + g) * (unsigned)T;
     const unsigned nkrow = ((unsigned)m * ld + (unsigned)qcols + (unsigned)g * HD) * 2u;
     const unsigned nvrow = ((unsigned)m * ld + (unsigned)qcols + (unsigned)(Hkv + g) * HD) * 2u;
-    *(u4*)((char*)qs + lane * 16) =
-        ld16<0>(qr, ((unsigned)m * ld + (unsigned)g * GRP * HD) * 2u + (unsigned)lane * 16u);
-    __builtin_amdgcn_wave_barrier();
+    // The queries (one kilobyte) go to LDS by a buffer-to-LDS load, so their
+    // round trip overlaps the first chunk's key loads.
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (__attribute__((address_space(3))) void*)qs, 16,
+                                             ((unsigned)m * ld + (unsigned)g * GRP * HD) * 2u + (unsigned)lane * 16u,
+                                             0, 0, 0);
+    bool qpend = true;
     float mrun[GRP], lrun[GRP];
     f4 acc[GRP];
 #pragma unroll
@@ -183,14 +216,13 @@ __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* l
       u4 kv[HD / 8];
 #pragma unroll
       for (int i = 0; i < HD / 8; ++i) kv[i] = ld16<0>(kr, t < T ? (hrow + (unsigned)t) * HD * 2u + i * 16u : cext);
-      // Value rows to LDS: kilobyte i holds positions 64c + 4i .. + 3 (lane
-      // l: position 4i + l/16, dimensions 8 (l % 16) .. + 7).
-#pragma unroll
-      for (int i = 0; i < kAttnPos * HD * 2 / 1024; ++i) {
-        const int tt = c * kAttnPos + 4 * i + (lane >> 4);
-        const unsigned off = tt < T ? ((hrow + (unsigned)tt) * HD + 8u * (unsigned)(lane & 15)) * 2u : cext;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)((char*)vs + i * 1024),
-                                                 16, off, 0, 0, 0);
+      if (!vahead) issue_values(c, hrow, lane);
+      vahead = false;
+      if (qpend) {
+        // At least the 16 key loads were issued after the queries' load.
+        wait_vm<HD / 8>();
+        __builtin_amdgcn_wave_barrier();
+        qpend = false;
       }
       U2 vnew = {0u, 0u};
       if (has_new) {

@@ -36,11 +36,11 @@ __global__ __launch_bounds__(512) void k_gemm_kc(StageDesc d, unsigned* ctl) {
   if (d.check) claim_and_check(ctl, xcd, slot, nslots);
 }
 
-// K-chunked MFMA path (path 3): MT = 1..4 m-tiles, NTW = 2, 4, 6 or 8 tiles per
+// K-chunked MFMA path (path 3): MT = 1..4 m-tiles, NTW = 2, 3, 4, 6 or 8 tiles per
 // item (8 only up to two m-tiles: its accumulators and loads would not fit
 // the registers next to four).  Weights nt only.
 inline bool kc_variant_ok(int mt, int ntw) {
-  return mt >= 1 && mt <= 4 && (ntw == 2 || ntw == 4 || ntw == 6 || (ntw == 8 && mt <= 2));
+  return mt >= 1 && mt <= 4 && (ntw == 2 || ntw == 3 || ntw == 4 || ntw == 6 || (ntw == 8 && mt <= 2));
 }
 
 template <int AUX>
@@ -51,6 +51,7 @@ GemmKernel gemm_kernel_kc(int a, int b) {
 #define SG_KC(mt)                                               \
   case mt:                                                      \
     if (b == 2) return k_gemm_kc<mt, 2, AUX>;                   \
+    if (b == 3) return k_gemm_kc<mt, 3, AUX>;                   \
     if (b == 4) return k_gemm_kc<mt, 4, AUX>;                   \
     if (b == 6) return k_gemm_kc<mt, 6, AUX>;                   \
     if (b == 8 && mt <= 2) return k_gemm_kc<(mt <= 2 ? mt : 2), 8, AUX>; \

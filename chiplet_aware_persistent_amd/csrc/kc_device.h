@@ -175,6 +175,7 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
   int xro[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) xro[i] = min(16 * i + r16, d.M) * kKcRow;
+  bf16x8 xa[2][MT];
 
   constexpr bool early = __is_same(Hook, NoHook);
   int k0, kend;
@@ -219,22 +220,24 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
       // Chunk t + 1 of this item into the other buffer (zeros after the last).
       stage_x_chunk(d, xbuf((t + 1) & 1), k0 + (t + 1) * kKcChunk, t + 1 < nc ? kend : 0, xr);
       const uint16_t* xb = xbuf(t & 1) + wave * kMfmaKStep + 8 * g4;
+      // Both halves' A fragments first; then tile by tile, both halves and
+      // the tile's reload right behind them, so each tile waits only for its
+      // own loads and the wave keeps the rest of the ring in flight.
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 xa[MT];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < MT; ++i) xa[i] = __builtin_bit_cast(bf16x8, *(const u4*)(xb + xro[i] + 32 * h));
+        for (int i = 0; i < MT; ++i) xa[h][i] = __builtin_bit_cast(bf16x8, *(const u4*)(xb + xro[i] + 32 * h));
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
+      for (int j = 0; j < NTW; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
           const bf16x8 wb = to_b(ring[p][j], h);
 #pragma unroll
           for (int i = 0; i < MT; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], wb, acc[j][i], 0, 0, 0);
-          if (h == 1) {
-            issue_tile(ring[p][j], sr, tn + p, j);
-            __builtin_amdgcn_sched_barrier(0);  // the reload right behind its last use
-          }
+            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[h][i], wb, acc[j][i], 0, 0, 0);
         }
+        issue_tile(ring[p][j], sr, tn + p, j);
+        __builtin_amdgcn_sched_barrier(0);  // the reload right behind its last use
       }
       // Only this step's refills may still be outstanding: chunk t + 1 is in
       // LDS for this wave's kilobytes; the barrier makes it whole, and frees

@@ -114,8 +114,8 @@ enum {
                                     MI355X low-latency GEMM, techniques 2 and
                                     3; the Fleet reading note's missing
                                     wave-level K split, Limitations).  tn, when
-                                    given, is 16 x the tiles per block (32, 64,
-                                    96 or 128); kslices must be 0 or 1 and waves
+                                    given, is 16 x the tiles per block (32, 48,
+                                    64, 96 or 128); kslices must be 0 or 1 and waves
                                     0 or 8.  In the chain (an ablation, built
                                     for M = 17-32, else SGEMM_ERR_UNSUPPORTED):
                                     every stage on this path, the gate_up stage

@@ -174,7 +174,7 @@ def test_binding_rejects_mismatched_tensors():
 
 @pytest.mark.parametrize("M,K,N", [(16, 4096, 24576), (64, 4096, 24576), (64, 12288, 4096), (33, 2048, 1536),
                                    (64, 8, 1), (5, 1032, 777), (20, 12288, 300), (64, 4104, 129)])
-@pytest.mark.parametrize("ntw,splitk", [(0, 0), (2, 3), (4, 0), (6, 2), (8, 0)])
+@pytest.mark.parametrize("ntw,splitk", [(0, 0), (2, 3), (3, 0), (4, 0), (6, 2), (8, 0)])
 def test_kchunk_plan_covers_columns_and_k(M, K, N, ntw, splitk):
     """K-chunked plans: blocks of 16 * tiles columns cover each XCD's columns,
     splits cover K in whole 512-wide chunks (a multiple of the ring depth per
@@ -228,7 +228,7 @@ def test_kchunk_flag_combinations():
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_MTILE_ITEMS) == sg.ERR_INVALID_ARG
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, ksl=2) == sg.ERR_UNSUPPORTED
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, tn=40) == sg.ERR_UNSUPPORTED
-    assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, tn=48) == sg.ERR_UNSUPPORTED
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, tn=80) == sg.ERR_UNSUPPORTED
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, waves=4) == sg.ERR_UNSUPPORTED
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK, tn=64) == sg.OK
 
@@ -421,7 +421,8 @@ def test_null_and_misaligned_arguments_rejected_before_launch():
 
 SHAPES = [(1, 1024, 1024), (1, 4096, 6144), (1, 4096, 4096), (1, 4096, 24576), (1, 12288, 4096),
           (8, 4096, 6144), (16, 4096, 4096), (32, 4096, 24576), (64, 12288, 4096), (1, 7168, 1536),
-          (2, 7168, 4096), (16, 7168, 18432), (3, 520, 1000), (17, 776, 530), (5, 8, 17), (64, 8, 1)]
+          (2, 7168, 4096), (16, 7168, 18432), (3, 520, 1000), (17, 776, 530), (5, 8, 17), (64, 8, 1),
+          (64, 4096, 24576), (48, 4096, 24576)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
@@ -437,8 +438,8 @@ def test_planner_covers_every_column_and_k_once(M, K, N, splitk, flags):
         assert splitk and e.code == sg.ERR_UNSUPPORTED
         return
     st = g.describe()["stage"]
-    if st["path"] == "kc":   # long K, wide N: the K-chunked path (its own coverage test below)
-        assert M >= 16 and K >= 6144 and not flags and not splitk and st["S"] == 1
+    if st["path"] == "kc":   # long K or M > 48, wide N: the K-chunked path (its own coverage test below)
+        assert M >= 16 and (K >= 6144 or M > 48) and not flags and not splitk and st["S"] == 1
         return
     assert st["path"] == ("dot2" if M < 16 else "mfma")
     mt = st["mtiles"]

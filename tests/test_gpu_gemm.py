@@ -337,7 +337,8 @@ def test_parity_mtile_items(cuda_device, M, K, N, splitk):
 # ----------------------------------------------------- K-chunked MFMA path
 KC_SMALL = [(16, 1024, 2048, 0, 0), (17, 776, 530, 2, 0), (33, 2048, 1536, 4, 0), (48, 520, 64, 6, 0),
             (64, 2048, 1536, 6, 0), (64, 1000, 1000, 4, 3), (5, 1032, 777, 2, 0), (64, 8, 1, 2, 0),
-            (32, 3000, 700, 8, 2), (20, 12288, 300, 4, 5), (64, 4104, 129, 6, 2), (1, 1024, 1024, 8, 0)]
+            (32, 3000, 700, 8, 2), (20, 12288, 300, 4, 5), (64, 4104, 129, 6, 2), (1, 1024, 1024, 8, 0),
+            (64, 4096, 1536, 3, 0), (40, 2056, 900, 3, 2)]
 
 
 @pytest.mark.parametrize("M,K,N,ntw,splitk", KC_SMALL)
