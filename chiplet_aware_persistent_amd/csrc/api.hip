@@ -490,7 +490,9 @@ static int plan_decoder(sgemm_plan_s* pl, const sgemm_problem& p, int tn_o, int 
   cur = round_up(cur + pl->act_layer_elems * 2 * p.n_layers, 256);
   pl->off_stamps = cur;
   if (p.flags & SGEMM_F_STAMPS) cur = round_up(cur + (size_t)pl->grid * events * 2 * 8, 256);
-  int lds = 8 * 18 * 1024;  // the attention stage: queries, weights and value rows, 18 KB per wave
+  // The attention stage: per wave queries, weights, value rows and the new
+  // position's key and value rows (18.5 KB).
+  int lds = 8 * (4 * 128 * 2 + 64 * 4 * 4 + 64 * 128 * 2 + 2 * 128 * 2);
   for (int s = 0; s < kChainStages; ++s) lds = std::max(lds, pl->cg[s].lds);
   pl->norm_off = (int)round_up((size_t)lds, 16);
   pl->dec_lds = pl->norm_off + 256;

@@ -20,7 +20,9 @@
 namespace sg {
 
 constexpr int kAttnPos = 64;  // positions per attention unit (one per lane)
-constexpr int kAttnWaveLds = 4 * 128 * 2 + kAttnPos * 4 * 4 + kAttnPos * 128 * 2;  // bytes of LDS per wave
+// Bytes of LDS per wave: queries, weights, value rows, and the new position's
+// key and value rows.
+constexpr int kAttnWaveLds = 4 * 128 * 2 + kAttnPos * 4 * 4 + kAttnPos * 128 * 2 + 2 * 128 * 2;
 
 // Two dwords.  A plain struct: an ext_vector_type(2) built from two adjacent
 // dword buffer loads compiled here to one dword load copied into both halves
@@ -148,6 +150,15 @@ __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* l
   float* ps = (float*)(qs + GRP * HD);
   uint16_t* vs = (uint16_t*)(ps + kAttnPos * GRP);
   const int vs_off = GRP * HD * 2 + kAttnPos * GRP * 4;  // byte offset of the value rows in a wave's LDS
+  uint16_t* nk = vs + kAttnPos * HD;  // the new position's key row, then its value row
+  uint16_t* nv = nk + HD;
+  // With T a multiple of 64 the new position would be a chunk of its own and
+  // cost its wave a third round trip.  Instead the wave that chunk falls to
+  // loads the new key and value rows into LDS with its first loads and adds
+  // the position after its cached chunks (the tail step below).
+  const bool newsep = T % kAttnPos == 0;
+  const int ncc = newsep ? nch - 1 : nch;  // chunks holding cached positions
+  const int c_new = T / kAttnPos;
   const int hpx = (Hkv + kXcds - 1) / kXcds;
   const int tasks = hpx * M * S;  // (pair, slice), slice fastest
   // Value rows of a chunk to the wave's LDS: kilobyte i holds positions
@@ -173,7 +184,7 @@ __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* l
     const int m = pi - gi * M;
     const int g = xcd + kXcds * gi;
     const int c = sl + S * wave;
-    if (g < Hkv && c < nch) {
+    if (g < Hkv && c < ncc) {
       int ln = threadIdx.x & 63;
       asm volatile("" : "+v"(ln));
       issue_values(c, ((unsigned)m * Hkv + g) * (unsigned)T, ln);
@@ -201,6 +212,13 @@ __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* l
                                              ((unsigned)m * ld + (unsigned)g * GRP * HD) * 2u + (unsigned)lane * 16u,
                                              0, 0, 0);
     bool qpend = true;
+    const bool tail = newsep && sl == c_new % S && wave == (c_new / S) % nwv;  // uniform
+    if (tail) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (__attribute__((address_space(3))) void*)nk, 4,
+                                               nkrow + (unsigned)lane * 4u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (__attribute__((address_space(3))) void*)nv, 4,
+                                               nvrow + (unsigned)lane * 4u, 0, 0, 0);
+    }
     float mrun[GRP], lrun[GRP];
     f4 acc[GRP];
 #pragma unroll
@@ -209,7 +227,7 @@ __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* l
       lrun[j] = 0.f;
       acc[j] = f4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int c = sl + S * wave; c < nch; c += S * nwv) {
+    for (int c = sl + S * wave; c < ncc; c += S * nwv) {
       asm volatile("" : "+v"(lane));  // and inside the chunk loop
       const int t = c * kAttnPos + lane;
       const bool has_new = T >= c * kAttnPos && T < (c + 1) * kAttnPos;  // uniform
@@ -283,6 +301,29 @@ __device__ __forceinline__ bool gqa_stage(const ChainArgs& a, int l, uint16_t* l
         for (int j = 0; j < GRP; ++j) acc[j] += p4[j] * v;  // zero in half 1
       }
       __builtin_amdgcn_wave_barrier();  // the LDS reads above before the next chunk's loads
+    }
+    if (tail) {
+      // The new position (a chunk of one): lane l scores dimensions 2l and
+      // 2l + 1, the wave adds the 64 partial sums, and the running softmax
+      // takes the one score.  Every load of the wave is complete here.
+      wait_vm0();
+      __builtin_amdgcn_wave_barrier();
+      const bf16x2 kp = *(const bf16x2*)(nk + 2 * lane);
+      const f4 vn = bf16x4_to_f4(*(const U2*)(nv + dq));
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        float sj = __builtin_amdgcn_fdot2_f32_bf16(kp, *(const bf16x2*)(qs + j * HD + 2 * lane), 0.f, false);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sj += __shfl_xor(sj, o);
+        const float v = sj * scale;
+        const float nm = fmaxf(mrun[j], v);
+        const float so = __builtin_amdgcn_exp2f((mrun[j] - nm) * kLog2e);
+        const float pn = __builtin_amdgcn_exp2f((v - nm) * kLog2e);
+        lrun[j] = lrun[j] * so + pn;
+        mrun[j] = nm;
+        acc[j] *= so;
+        if (hf == 0) acc[j] += pn * vn;
+      }
     }
 #pragma unroll
     for (int j = 0; j < GRP; ++j)
