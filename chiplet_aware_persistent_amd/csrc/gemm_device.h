@@ -400,8 +400,19 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
   constexpr int GO = PAIRED ? G / 2 : G;  // output columns per wave
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  int i0, i1;
-  my_items(d.items, slot, nslots, d.ng, wave / d.wpi, i0, i1);
+  // The stream's items: i0, i0 + istep, ... below i1.  With d.rr (single
+  // launches with one K split) stream w of the XCD's nslots * ng takes the
+  // items w, w + nslots * ng, ..., so the streams of an XCD read neighbouring
+  // weight rows at any one time; otherwise a contiguous balanced range.
+  int i0, i1, istep = 1;
+  if (__is_same(Hook, NoHook) && d.rr) {
+    i0 = slot * d.ng + wave / d.wpi;
+    i1 = d.items;
+    istep = nslots * d.ng;
+  } else {
+    my_items(d.items, slot, nslots, d.ng, wave / d.wpi, i0, i1);
+  }
+  const int nit = i0 < i1 ? (i1 - i0 + istep - 1) / istep : 0;
   const int wv = wave % d.wpi;  // wave's place within its item
   const int xc0 = xcd * d.Nx;
   const int xc1 = min(d.N, xc0 + d.Nx);
@@ -487,7 +498,7 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
   constexpr bool early = __is_same(Hook, NoHook);
   const int s_first = first_item_of_wg(d.items, slot, nslots) / d.NB;
   if constexpr (early) stage_x_lds(d, xs, M, s_first * d.KS, d.K, xr);
-  Src sc = src_of(i0), sn = src_of(i0 + 1);
+  Src sc = src_of(i0), sn = src_of(i0 + istep);
   // Chain: the first q0 steps of the wave's first item are loaded into LDS
   // (buffer-to-LDS, no registers) before the wait for X, so the stage
   // boundary's latency streams weights; the ring then starts at step q0.
@@ -545,7 +556,7 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
 #pragma unroll
       for (int m = 0; m < M; ++m) v[c * M + m] = acc[c][m];
     const float r = wave_reduce_scatter<V>(v, lane);
-    const int li = it - i0;
+    const int li = (it - i0) / istep;
     if (li < d.stash_cap) {
       stash[(wave * d.stash_cap + li) * 64 + lane] = r;
     } else {
@@ -555,10 +566,10 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
     for (int c = 0; c < G; ++c)
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[c][m] = 0.f;
-    ++it;
+    it += istep;
     t0 = 0;
     sc = sn;
-    sn = src_of(it + 1);
+    sn = src_of(it + istep);
     xoff = (it / d.NB - s_first) * d.KS;
   };
   if constexpr (!early) {
@@ -579,7 +590,7 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
       if (q0 == spad) finish_item();
     }
   }
-  const int total = (i1 - i0) * spad - q0;
+  const int total = nit * spad - q0;
   for (int T = 0; T < total; T += P) {
     const bool here = t0 + P < spad;
     const Src& sr = here ? sc : sn;
@@ -606,8 +617,8 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
 
   // Stored items: results of the stream, written after its last load.
   {
-    const int n = min(i1 - i0, d.stash_cap);
-    for (int li = 0; li < n; ++li) out_item(i0 + li, stash[(wave * d.stash_cap + li) * 64 + lane]);
+    const int n = min(nit, d.stash_cap);
+    for (int li = 0; li < n; ++li) out_item(i0 + li * istep, stash[(wave * d.stash_cap + li) * 64 + lane]);
   }
 
   if (d.S > 1 && i0 < i1) {

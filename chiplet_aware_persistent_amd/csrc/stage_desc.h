@@ -63,6 +63,7 @@ struct StageDesc {
   int pair_off;        // paired: weight row offset of the up half
   int mtiles;          // MFMA: items per (split, column block), one 16-row m-tile each (1: all rows)
   int interleave;      // streams of a workgroup take every ng-th item of its range
+  int rr;              // dot2, one K split: stream w of the XCD takes items w, w + streams, ...
   int nfast;           // m-tile items: column block fastest (the M-split order) instead of m-tile fastest
   int mode;            // OutMode
   int sync;            // SyncMode of the split-K arrival

@@ -426,6 +426,28 @@ SHAPES = [(1, 1024, 1024), (1, 4096, 6144), (1, 4096, 4096), (1, 4096, 24576), (
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
+def test_dot2_round_robin_items_cover_each_item_once(M, K, N, monkeypatch):
+    """Single-launch dot2 plans with one K split take their items round-robin
+    over the XCD's 32 x ng streams (rr = 1; SGEMM_DOT2_RR=0 gives contiguous
+    ranges, other paths and split plans always do): a host model of both
+    assignments runs every item exactly once, and the longest stream is no
+    longer than with contiguous ranges."""
+    for env in ("1", "0"):
+        monkeypatch.setenv("SGEMM_DOT2_RR", env)
+        st = sg.Gemm(M, K, N).describe()["stage"]
+        assert st["rr"] == (1 if env == "1" and st["path"] == "dot2" and st["S"] == 1 else 0)
+        items, ng = st["items"], st["waves"] // st["wpi"]
+        nw = 32 * ng
+        contiguous = [list(range(items * w // nw, items * (w + 1) // nw)) for w in range(nw)]
+        streams = [list(range(w, items, nw)) for w in range(nw)] if st["rr"] else contiguous
+        assert sorted(i for s_ in streams for i in s_) == list(range(items))
+        assert max(len(s_) for s_ in streams) <= max(len(s_) for s_ in contiguous)
+    with pytest.raises(sg.SgemmError):
+        monkeypatch.setenv("SGEMM_DOT2_RR", "x")
+        sg.Gemm(1, 1024, 1024)
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
 @pytest.mark.parametrize("splitk", [0, 3])
 @pytest.mark.parametrize("flags", [0, sg.F_MTILE_ITEMS])
 def test_planner_covers_every_column_and_k_once(M, K, N, splitk, flags):

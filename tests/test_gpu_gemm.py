@@ -112,6 +112,25 @@ def test_parity_small(cuda_device, M, K, N):
     check(Y, x, w)
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 6144), (3, 4104, 129), (8, 1024, 2048), (13, 16, 3000),
+                                   (1, 12288, 4096), (5, 8, 17)])
+def test_dot2_round_robin_order_bitwise(cuda_device, M, K, N, monkeypatch):
+    """The dot2 path's items round-robin over the XCD's streams (the default
+    for one K split) or in contiguous ranges (SGEMM_DOT2_RR=0): the same
+    products in the same order per output, so bitwise the same Y, and both
+    within the bound."""
+    x, w, X, W = gemm_inputs(M, K, N, 3000 + M, 4000 + K, cuda_device)
+    out = {}
+    for rr in ("1", "0"):
+        monkeypatch.setenv("SGEMM_DOT2_RR", rr)
+        g = sg.Gemm(M, K, N)
+        st = g.describe()["stage"]
+        assert st["path"] == "dot2" and st["S"] == 1 and st["rr"] == int(rr)
+        out[rr] = run(g, X, W)
+    assert torch.equal(out["1"], out["0"])
+    check(out["1"].cpu().numpy(), x, w)
+
+
 # One GPU's share of the Qwen3-8B decode projections under 8-way tensor parallelism:
 # QKV and gate_up split by output columns (N / 8), O and down by K (K / 8).
 TP8_SHARDS = [(4096, 768), (512, 4096), (4096, 3072), (1536, 4096)]
