@@ -390,6 +390,11 @@ struct NoNorm {
 // PAIRED (the chain's gate_up stage): the wave's G rows are G/2 gate rows and
 // the G/2 up rows pair_off further on; the wave owns G/2 output columns and
 // writes silu(gate) * up.
+// Inside the layer chain the round-robin item order is built only for waves
+// of at most this many (column, row) sums: with more, its two extra loop
+// registers push the chain kernel past the register file.
+constexpr int kRrChainMaxMG = 16;
+
 template <int M, int G, int AUX, bool PAIRED = false, typename Hook = NoHook, typename XNorm = NoNorm>
 __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                            Hook pre_x = Hook(), XNorm xnorm = XNorm()) {
@@ -405,7 +410,7 @@ __device__ __forceinline__ bool dot2_stage(const StageDesc& d, uint16_t* xs, int
   // items w, w + nslots * ng, ..., so the streams of an XCD read neighbouring
   // weight rows at any one time; otherwise a contiguous balanced range.
   int i0, i1, istep = 1;
-  if (__is_same(Hook, NoHook) && d.rr) {
+  if ((__is_same(Hook, NoHook) || M * G <= kRrChainMaxMG) && d.rr) {
     i0 = slot * d.ng + wave / d.wpi;
     i1 = d.items;
     istep = nslots * d.ng;

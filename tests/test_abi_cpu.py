@@ -297,6 +297,37 @@ def test_chain_lds_weight_prefetch_plans(M, d, q, dff, monkeypatch):
     assert all(s["wpf"] == 0 for s in mf)  # MFMA stages: not used
 
 
+@pytest.mark.parametrize("M,d,q,dff", [(1, 4096, 4096, 12288), (2, 1024, 1032, 3000), (2, 256, 128, 200),
+                                       (8, 1024, 1024, 3072)])
+def test_chain_and_decoder_round_robin_plans(M, d, q, dff, monkeypatch):
+    """Chain and decoder dot2 stages with one K split take their items
+    round-robin over the XCD's streams by default when a wave holds at most 16
+    (column, row) sums; SGEMM_CHAIN_RR=0, an LDS weight prefetch or the
+    scheduler mode keep contiguous ranges; a malformed value is refused."""
+    monkeypatch.delenv("SGEMM_CHAIN_RR", raising=False)
+
+    def want(s):
+        return int(s["path"] == "dot2" and s["S"] == 1 and s["wpf"] == 0 and M * s["tb"] <= 16)
+
+    st = sg.LayerChain(M, 2, d, q, dff, flags=sg.F_FORCE_DOT2).describe()["stages"]
+    assert [s["rr"] for s in st] == [want(s) for s in st]
+    if M == 1 and d == 4096:
+        assert all(s["rr"] == 1 for s in st)
+    if M <= 2:  # the decoder's dot2 stages are built for M <= 2
+        dec = sg.Decoder(M, 2, 1024, 3072, 8, 2, 128, 100).describe()["stages"]
+        assert [s["rr"] for s in dec] == [want(s) for s in dec] and any(s["rr"] for s in dec)
+    sch = sg.LayerChain(M, 2, d, q, dff, flags=sg.F_FORCE_DOT2 | sg.F_SCHEDULER).describe()["stages"]
+    assert all(s["rr"] == 0 for s in sch)
+    monkeypatch.setenv("SGEMM_CHAIN_WPF", "1000")
+    assert all(s["rr"] == 0 for s in sg.LayerChain(M, 2, d, q, dff, flags=sg.F_FORCE_DOT2).describe()["stages"])
+    monkeypatch.delenv("SGEMM_CHAIN_WPF")
+    monkeypatch.setenv("SGEMM_CHAIN_RR", "0")
+    assert all(s["rr"] == 0 for s in sg.LayerChain(M, 2, d, q, dff, flags=sg.F_FORCE_DOT2).describe()["stages"])
+    monkeypatch.setenv("SGEMM_CHAIN_RR", "1x")
+    with pytest.raises(sg.SgemmError):
+        sg.LayerChain(M, 2, d, q, dff)
+
+
 def _stage_items(st, slots=32):
     """(slot, stream) -> item list of one chain/GEMM stage, as the kernels
     assign them: workgroup slot w of 32 runs streams q < ng, each the

@@ -148,6 +148,29 @@ def test_chain_kchunk_parity(cuda_device, M, L, d, q, dff, flags, splitk):
     report("chain kc M=%d L=%d %dx%dx%d S=%s flags=%#x" % (M, L, d, q, dff, [s["S"] for s in st], flags), worst)
 
 
+@pytest.mark.parametrize("M,L,d,q,dff", [(1, 2, 4096, 4096, 12288), (2, 3, 1024, 1032, 3000), (2, 4, 256, 128, 200)])
+def test_chain_round_robin_bitwise(cuda_device, monkeypatch, M, L, d, q, dff):
+    """dot2 chain stages with items round-robin over the XCD's streams (the
+    default) and in contiguous ranges (SGEMM_CHAIN_RR=0): every item is the
+    same sum in the same order, so every stage and the output are bitwise
+    equal; the default is also checked against the oracle."""
+    x0, layers, X0, dl = make_chain(M, L, d, q, dff, 0x2900 + M + d, cuda_device)
+    outs = {}
+    for rr in ("1", "0"):
+        monkeypatch.setenv("SGEMM_CHAIN_RR", rr)
+        ch = sg.LayerChain(M, L, d, q, dff)
+        flags_rr = [s["rr"] for s in ch.describe()["stages"]]
+        assert (any(flags_rr) if rr == "1" else not any(flags_rr)), flags_rr
+        rc, Y, Yb, ws = run_chain(ch, X0, dl)
+        assert rc == sg.OK, sg.status_string(rc)
+        outs[rr] = ([host_bits(ch.activation(ws, l, w)).copy() for l in range(L) for w in range(4)],
+                    Y.cpu().numpy().copy())
+        if rr == "1":
+            check_chain(ch, ws, x0, layers, Y, Yb, M)
+    assert all(np.array_equal(a, b) for a, b in zip(outs["1"][0], outs["0"][0]))
+    assert np.array_equal(outs["1"][1].view(np.uint32), outs["0"][1].view(np.uint32))
+
+
 @pytest.mark.parametrize("M,L,d,q,dff,flags", [(1, 2, 4096, 4096, 12288, 0), (2, 2, 1024, 1032, 3000, 0),
                                                (5, 2, 2048, 1024, 4096, sg.F_FORCE_DOT2)])
 def test_chain_lds_weight_prefetch_bitwise(cuda_device, monkeypatch, M, L, d, q, dff, flags):
