@@ -237,17 +237,19 @@ bool plan_geo(Geo& best, int M, int K, int N, int path, int paired, int tn_o, in
 // when it does not fit.
 constexpr int kKcChunkK = 512;  // K values per chunk (8 waves x one 64-wide k-step)
 
-// Chain and decoder dot2 stages with one K split take their items
-// round-robin over the XCD's streams (as single launches do) when their waves
-// hold at most 16 (column, row) sums, the kernel's limit (gemm_device.h,
-// kRrChainMaxMG); SGEMM_CHAIN_RR=0 keeps contiguous ranges.  Measured on the
-// 36-layer chain: 1.7% faster at M = 1, 1.3% at M = 2, bitwise the same.
+// Chain and decoder stages with one K split take their items round-robin
+// over the XCD's streams (as single launches do): MFMA stages, and dot2
+// stages whose waves hold at most 16 (column, row) sums, the kernel's limit
+// (gemm_device.h, kRrChainMaxMG); SGEMM_CHAIN_RR=0 keeps contiguous ranges.
+// Measured on the 36-layer chain: 1.7% faster at M = 1, 1.3% at M = 2,
+// bitwise the same.
 bool set_chain_rr(Geo* cg, int n, bool scheduler) {
   int rr = 1;
   if (!env_int("SGEMM_CHAIN_RR", 1, &rr)) return false;
   for (int s = 0; s < n; ++s) {
     Geo& g = cg[s];
-    g.rr = rr && g.path == 0 && g.S == 1 && g.wpf == 0 && g.M * g.tb <= 16 && !scheduler ? 1 : 0;
+    const bool fits = g.path == 0 ? g.M * g.tb <= 16 : (g.path == 1 && g.mtiles == 1);
+    g.rr = rr && fits && g.S == 1 && g.wpf == 0 && !scheduler ? 1 : 0;
   }
   return true;
 }
@@ -595,12 +597,13 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
         pl->geo = kcg;
     }
     pl->geo.nfast = msplit ? 1 : 0;
-    if (pl->geo.path == 0 && pl->geo.S == 1) {
+    if ((pl->geo.path == 0 || (pl->geo.path == 1 && pl->geo.mtiles == 1)) && pl->geo.S == 1) {
       // Items round-robin over the XCD's streams (measured 0-3% faster than
-      // contiguous ranges on the decode shapes, bitwise the same results);
-      // SGEMM_DOT2_RR=0 keeps the contiguous ranges.
+      // contiguous ranges on the dot2 decode shapes, 2-5% on M = 16 MFMA
+      // ones with several items per workgroup; bitwise the same results);
+      // SGEMM_DOT2_RR=0 / SGEMM_MFMA_RR=0 keep the contiguous ranges.
       int rr = 1;
-      if (!env_int("SGEMM_DOT2_RR", 1, &rr)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+      if (!env_int(pl->geo.path == 0 ? "SGEMM_DOT2_RR" : "SGEMM_MFMA_RR", 1, &rr)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
       pl->geo.rr = rr ? 1 : 0;
     }
     if (pl->geo.part_floats * 4 >= kMaxOperand) { delete pl; return SGEMM_ERR_UNSUPPORTED; }

@@ -692,6 +692,12 @@ __device__ __forceinline__ bool mfma_stage(const StageDesc& d, uint16_t* xs, int
     i0 = first_item_of_wg(d.items, slot, nslots) + wave / d.wpi;
     i1 = first_item_of_wg(d.items, slot + 1, nslots);
     istep = d.ng;
+  } else if (!MTI && d.rr) {
+    // One K split: the items round-robin over the XCD's streams, as in the
+    // dot2 path.
+    i0 = slot * d.ng + wave / d.wpi;
+    i1 = d.items;
+    istep = nslots * d.ng;
   } else {
     my_items(d.items, slot, nslots, d.ng, wave / d.wpi, i0, i1);
   }

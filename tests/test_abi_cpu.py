@@ -307,7 +307,8 @@ def test_chain_and_decoder_round_robin_plans(M, d, q, dff, monkeypatch):
     monkeypatch.delenv("SGEMM_CHAIN_RR", raising=False)
 
     def want(s):
-        return int(s["path"] == "dot2" and s["S"] == 1 and s["wpf"] == 0 and M * s["tb"] <= 16)
+        fits = M * s["tb"] <= 16 if s["path"] == "dot2" else (s["path"] == "mfma" and s["mtiles"] == 1)
+        return int(fits and s["S"] == 1 and s["wpf"] == 0)
 
     st = sg.LayerChain(M, 2, d, q, dff, flags=sg.F_FORCE_DOT2).describe()["stages"]
     assert [s["rr"] for s in st] == [want(s) for s in st]
@@ -318,6 +319,8 @@ def test_chain_and_decoder_round_robin_plans(M, d, q, dff, monkeypatch):
         assert [s["rr"] for s in dec] == [want(s) for s in dec] and any(s["rr"] for s in dec)
     sch = sg.LayerChain(M, 2, d, q, dff, flags=sg.F_FORCE_DOT2 | sg.F_SCHEDULER).describe()["stages"]
     assert all(s["rr"] == 0 for s in sch)
+    mf = sg.LayerChain(16, 2, d, q, dff).describe()["stages"]
+    assert [s["rr"] for s in mf] == [int(s["path"] == "mfma" and s["mtiles"] == 1 and s["S"] == 1) for s in mf]
     monkeypatch.setenv("SGEMM_CHAIN_WPF", "1000")
     assert all(s["rr"] == 0 for s in sg.LayerChain(M, 2, d, q, dff, flags=sg.F_FORCE_DOT2).describe()["stages"])
     monkeypatch.delenv("SGEMM_CHAIN_WPF")
@@ -458,15 +461,18 @@ SHAPES = [(1, 1024, 1024), (1, 4096, 6144), (1, 4096, 4096), (1, 4096, 24576), (
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
 def test_dot2_round_robin_items_cover_each_item_once(M, K, N, monkeypatch):
-    """Single-launch dot2 plans with one K split take their items round-robin
-    over the XCD's 32 x ng streams (rr = 1; SGEMM_DOT2_RR=0 gives contiguous
-    ranges, other paths and split plans always do): a host model of both
+    """Single-launch dot2 and MFMA plans with one K split take their items
+    round-robin over the XCD's 32 x ng streams (rr = 1; SGEMM_DOT2_RR=0 and
+    SGEMM_MFMA_RR=0 give contiguous ranges, the K-chunked path, m-tile items
+    and split plans always do): a host model of both
     assignments runs every item exactly once, and the longest stream is no
     longer than with contiguous ranges."""
     for env in ("1", "0"):
         monkeypatch.setenv("SGEMM_DOT2_RR", env)
+        monkeypatch.setenv("SGEMM_MFMA_RR", env)
         st = sg.Gemm(M, K, N).describe()["stage"]
-        assert st["rr"] == (1 if env == "1" and st["path"] == "dot2" and st["S"] == 1 else 0)
+        rr_path = st["path"] == "dot2" or (st["path"] == "mfma" and st["mtiles"] == 1)
+        assert st["rr"] == (1 if env == "1" and rr_path and st["S"] == 1 else 0)
         items, ng = st["items"], st["waves"] // st["wpi"]
         nw = 32 * ng
         contiguous = [list(range(items * w // nw, items * (w + 1) // nw)) for w in range(nw)]

@@ -113,19 +113,21 @@ def test_parity_small(cuda_device, M, K, N):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 6144), (3, 4104, 129), (8, 1024, 2048), (13, 16, 3000),
-                                   (1, 12288, 4096), (5, 8, 17)])
-def test_dot2_round_robin_order_bitwise(cuda_device, M, K, N, monkeypatch):
-    """The dot2 path's items round-robin over the XCD's streams (the default
-    for one K split) or in contiguous ranges (SGEMM_DOT2_RR=0): the same
-    products in the same order per output, so bitwise the same Y, and both
-    within the bound."""
+                                   (1, 12288, 4096), (5, 8, 17), (16, 2048, 24576), (16, 1032, 3000),
+                                   (16, 520, 1000)])
+def test_round_robin_order_bitwise(cuda_device, M, K, N, monkeypatch):
+    """The dot2 and MFMA paths' items round-robin over the XCD's streams (the
+    default for one K split) or in contiguous ranges (SGEMM_DOT2_RR=0,
+    SGEMM_MFMA_RR=0): the same products in the same order per output, so
+    bitwise the same Y, and both within the bound."""
     x, w, X, W = gemm_inputs(M, K, N, 3000 + M, 4000 + K, cuda_device)
     out = {}
     for rr in ("1", "0"):
         monkeypatch.setenv("SGEMM_DOT2_RR", rr)
+        monkeypatch.setenv("SGEMM_MFMA_RR", rr)
         g = sg.Gemm(M, K, N)
         st = g.describe()["stage"]
-        assert st["path"] == "dot2" and st["S"] == 1 and st["rr"] == int(rr)
+        assert st["path"] == ("dot2" if M < 16 else "mfma") and st["S"] == 1 and st["rr"] == int(rr), st
         out[rr] = run(g, X, W)
     assert torch.equal(out["1"], out["0"])
     check(out["1"].cpu().numpy(), x, w)
