@@ -442,10 +442,17 @@ static int plan_decoder(sgemm_plan_s* pl, const sgemm_problem& p, int tn_o, int 
   cost.lds_reserve = 256;
   const int path = (p.flags & SGEMM_F_FORCE_DOT2) ? 0 : (p.flags & SGEMM_F_FORCE_MFMA) ? 1 : (p.M <= 2 ? 0 : 1);
   double best = -1.0;
+  // dot2 stages: four columns per wave unless that cannot be planned (or tn
+  // says otherwise).  Measured on the 36-layer decoder against two columns,
+  // which the cost model prefers: 3.145 against 3.237 ms at M = 1 with 1024
+  // positions, 3.507 against 3.565 with 4000, 3.264 against 3.333 at M = 2.
+  const int tb_pref = path == 0 && !tn_o ? 4 : 0;
+  for (int pass = 0; pass < 2 && best < 0.0; ++pass)
   for (int waves = 8; waves >= 4; waves -= 4) {
     if (w_o && waves != w_o) continue;
     for (int tb = 1; tb <= (path == 0 ? 4 : 2); ++tb) {
       if (path == 0 && tb != 2 && tb != 4) continue;
+      if (pass == 0 && tb_pref && tb != tb_pref) continue;
       if (tn_o && tn_o != (path == 0 ? tb : 16 * tb)) continue;
       const int a = path == 0 ? p.M : (p.M + 15) / 16;
       if (!decoder_variant_exists(path, a, tb)) continue;
