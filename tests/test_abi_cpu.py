@@ -331,6 +331,18 @@ def test_chain_and_decoder_round_robin_plans(M, d, q, dff, monkeypatch):
         sg.LayerChain(M, 2, d, q, dff)
 
 
+def test_decoder_dot2_stages_take_four_columns(monkeypatch):
+    """The decoder's dot2 stages (M <= 2) take four columns per wave unless
+    the tile width is given (two is still allowed)."""
+    monkeypatch.delenv("SGEMM_TN", raising=False)
+    for M in (1, 2):
+        st = sg.Decoder(M, 2, 4096, 12288, 32, 8, 128, 1024).describe()["stages"]
+        assert [s["path"] for s in st] == ["dot2"] * 4 and all(s["tb"] == 4 for s in st)
+    monkeypatch.setenv("SGEMM_TN", "2")
+    st = sg.Decoder(1, 2, 4096, 12288, 32, 8, 128, 1024).describe()["stages"]
+    assert all(s["tb"] == 2 for s in st)
+
+
 def _stage_items(st, slots=32):
     """(slot, stream) -> item list of one chain/GEMM stage, as the kernels
     assign them: workgroup slot w of 32 runs streams q < ng, each the
