@@ -42,7 +42,8 @@ def role_sequence(n: int, roles, skip: int = 0, bench=None):
     steps, warmup = bench
     seq = [roles[i % len(roles)] if i // len(roles) >= warmup else None
            for i in range((warmup + steps) * len(roles))]
-    seq += [None] * (steps * len(roles))  # solo back-to-back timing blocks
+    for r in roles:  # then the bench's back-to-back timing block of each role
+        seq += [r + "_solo"] * steps
     assert len(seq) == n, (len(seq), n)
     return seq
 
@@ -51,6 +52,8 @@ def kernel_durations(trace_csv: str, roles, skip: int = 0, bench=None):
     rows = [r for r in csv.DictReader(open(trace_csv)) if _ours(r["Kernel_Name"])]
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))  # the CSV is not in launch order
     per = collections.OrderedDict((r, []) for r in roles)
+    if bench is not None:
+        per.update((r + "_solo", []) for r in roles)
     names = {}
     for r, role in zip(rows, role_sequence(len(rows), roles, skip, bench)):
         if role is None:
