@@ -27,6 +27,7 @@ constexpr int kStaticLdsReserve = 256;
 constexpr int kLdsMax = kLdsCu - kStaticLdsReserve;  // dynamic LDS budget of a plan
 constexpr size_t kMaxOperand = (size_t)1 << 31;  // buffer extents are 31-bit here
 constexpr int kWgPerXcd = 32;           // one workgroup per CU, 32 CUs per XCD
+constexpr int kMaxM = 256;              // single GEMM rows (chain and decoder: 64)
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -46,6 +47,7 @@ struct Geo {
   int xbuf = 0;    // K-chunked path: bytes of one X chunk buffer
   int nfast = 0;   // m-tile items in the M-split order (column block fastest)
   int kc_chain = 0;  // K-chunked path: a stage of the layer chain (its ring depth rule)
+  int mb = 1;        // K-chunked path: m-blocks of 16 ta rows per (split, column block), M > 64
   int rr = 0;        // dot2 path, S = 1: items round-robin over the XCD's streams
   int wpf = 0, wpf_off = 0;  // chain dot2 stage: first-item steps whose weights go to LDS before the wait
   size_t ctr_count = 0, part_floats = 0;
@@ -274,8 +276,14 @@ bool kc_geo(Geo& g, int want_S, const Cost& cost) {
   g.kss = g.KS;
   g.steps = g.KS / kKcChunkK;  // chunks per item
   g.ring = ring;
-  g.items = g.NB * g.S;
+  // Beyond 16 MT rows, m-blocks of 16 MT rows: items (split, block, m-block),
+  // m-block fastest, taken round-robin so a block's m-blocks run together.
+  g.mb = ceil_div(g.M, 16 * MT);
+  g.items = g.NB * g.S * g.mb;
+  if (g.mb > 1) g.rr = 1;
   g.mtiles = 1;
+  // X rows of a chunk buffer: the m-block's, plus the zero row that the
+  // A-operand lanes past M read when the last m-block is partial.
   const int rows = std::min(16 * MT, g.M + 1);
   g.win = kKcChunkK;
   g.xrow = kKcChunkK + 8;
@@ -284,19 +292,28 @@ bool kc_geo(Geo& g, int want_S, const Cost& cost) {
   g.lds = std::max(2 * g.xbuf, red);
   g.red_off = g.lds; g.stash_off = g.lds; g.stash_cap = 0;
   if (g.lds > kLdsMax) return false;
-  g.ctr_count = (size_t)kXcds * g.NB;
+  g.ctr_count = (size_t)kXcds * g.NB * g.mb;
   g.part_floats = g.S > 1 ? g.ctr_count * (size_t)g.S * NTW * MT * 256 : 0;
   // Cost (microseconds): a workgroup's weight bytes at its share of HBM, or
   // its weight plus X bytes at the CU's L2 read rate if that is longer; per
   // item the reduction, the first chunk's X and the ring drain; per chunk a
   // workgroup barrier; for S > 1 the partials' round trip and the finalize.
+  // With m-blocks a weight byte comes from HBM once per block (the other
+  // m-blocks read it from L2), and the matrix cores' time is added.
   const double wg_items = ceil_div(g.items, g.slots);
   const double w_bytes = wg_items * NTW * 16.0 * g.steps * kKcChunkK * 2.0;
   const double x_bytes = wg_items * rows * g.steps * (double)kKcChunkK * 2.0;
   const double p_bytes = g.S > 1 ? wg_items * NTW * MT * 1024.0 * 2.0 : 0.0;
   const double bw_cu = 8.0e12 * 0.85 / 256.0;
   const double cu_rd = 110.0e9;
-  g.est_us = std::max(w_bytes / bw_cu, (w_bytes + x_bytes + p_bytes) / cu_rd) * 1e6 +
+  double mfma_us = 0.0;
+  if (g.mb > 1) {
+    // 16 MT x 16 NTW x KS multiply-adds per item at half the CU's dense
+    // bf16 rate (2.5 PFLOP/s over 256 CUs).
+    const double flops = wg_items * 2.0 * 16.0 * MT * 16.0 * NTW * g.steps * kKcChunkK;
+    mfma_us = flops / (2.5e15 / 256.0 * 0.5) * 1e6;
+  }
+  g.est_us = std::max(std::max(w_bytes / g.mb / bw_cu, (w_bytes + x_bytes + p_bytes) / cu_rd) * 1e6, mfma_us) +
              wg_items * (1.5 + rows * kKcChunkK * 2.0 / cost.x_bw * 1e6) + wg_items * g.steps * 0.05 +
              (g.S > 1 ? cost.split_us + cost.fin_us_kb * g.S * NTW * MT : 0.0);
   return true;
@@ -321,7 +338,7 @@ void plan_wpf(Geo& g, int lds_cap, int max_steps) {
 bool plan_kc(Geo& best, int M, int K, int N, int paired, int ntw_o, int s_o, const Cost& cost,
              int slots = kWgPerXcd, bool chain = false) {
   bool found = false;
-  const int MT = (M + 15) / 16;
+  const int MT = std::min(4, (M + 15) / 16);  // beyond 64 rows: m-blocks of 64 (kc_geo)
   for (int ntw : {2, 3, 4, 6, 8}) {
     if (ntw_o && ntw != ntw_o) continue;
     if (ntw == 8 && MT > 2) continue;
@@ -390,7 +407,10 @@ static int validate_gemm(const sgemm_problem& p) {
   if (p.M < 1 || p.K < 8 || p.N < 1) return SGEMM_ERR_INVALID_ARG;
   if (p.K % 8 != 0) return SGEMM_ERR_INVALID_ARG;
   if (p.out_dtype != SGEMM_OUT_F32 && p.out_dtype != SGEMM_OUT_BF16) return SGEMM_ERR_INVALID_ARG;
-  if (p.M > 64) return SGEMM_ERR_UNSUPPORTED;
+  if (p.M > kMaxM) return SGEMM_ERR_UNSUPPORTED;
+  // Beyond 64 rows only the K-chunked path (64-row m-blocks) is built.
+  if (p.M > 64 && (p.flags & (SGEMM_F_FORCE_DOT2 | SGEMM_F_FORCE_MFMA | SGEMM_F_MTILE_ITEMS | SGEMM_F_MSPLIT)))
+    return SGEMM_ERR_UNSUPPORTED;
   if ((size_t)p.N * p.K * 2 >= kMaxOperand || (size_t)p.M * p.K * 2 >= kMaxOperand ||
       (size_t)p.M * p.N * 4 >= kMaxOperand)
     return SGEMM_ERR_UNSUPPORTED;
@@ -575,7 +595,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     if (rc != SGEMM_OK) { delete pl; return rc; }
     const bool msplit = (p.flags & SGEMM_F_MSPLIT) != 0;
     const bool mti = (p.flags & SGEMM_F_MTILE_ITEMS) != 0 || msplit;
-    const bool kc = (p.flags & SGEMM_F_KCHUNK) != 0;
+    const bool kc = (p.flags & SGEMM_F_KCHUNK) != 0 || p.M > 64;
     // Rows per m-tile item (the window of the M-major traversal): 16 unless given.
     const int mti_rows = !mti ? 0 : (p.tm ? p.tm : 16);
     if (mti && mti_rows != 16 && mti_rows != 32 && mti_rows != 64) { delete pl; return SGEMM_ERR_INVALID_ARG; }
@@ -584,14 +604,16 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     if (mti && kc) { delete pl; return SGEMM_ERR_INVALID_ARG; }
     const int path = mti ? 1 : choose_path(p);
     if ((path == 0 || mti || kc) && k_o > 1) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    // The K-chunked kernels are built with nontemporal weight loads only.
+    const bool nt_w = pl->w_aux == 2u;
     if (kc) {
       // tn (a multiple of 16) gives the tiles per item.
-      if (tn_o % 16 || w_o == 4) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+      if (tn_o % 16 || w_o == 4 || !nt_w) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
       if (!plan_kc(pl->geo, p.M, p.K, p.N, 0, tn_o / 16, s_o, kCostGemm)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     } else if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, kCostGemm, 0, mti_rows)) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
-    } else if (path == 1 && !mti && !tn_o && !s_o && !w_o && !k_o && (p.K >= 6144 || p.M > 48)) {
+    } else if (path == 1 && !mti && nt_w && !tn_o && !s_o && !w_o && !k_o && (p.K >= 6144 || p.M > 48)) {
       // Long K, or four full m-tiles, with a wide output: the K-chunked path
       // takes one item of six tiles over all of K per workgroup and needs no
       // split-K, where the windowed MFMA path has to split K four to seven
@@ -806,6 +828,7 @@ static StageDesc stage_desc(const Geo& g, unsigned w_aux, int sync) {
   d.rr = g.rr;
   d.nfast = g.nfast;
   d.xbuf = g.xbuf;
+  d.mb = g.mb;
   d.nctr = (int)g.ctr_count;
   d.wpf = g.wpf;
   d.wpf_off = g.wpf_off;
@@ -1126,10 +1149,10 @@ static std::string geo_json(const Geo& g) {
                 "\"ksl\":%d,\"kss\":%d,\"TN\":%d,\"CB\":%d,\"Nx\":%d,\"NB\":%d,\"S\":%d,\"KS\":%d,"
                 "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
                 "\"ring\":%d,\"mtiles\":%d,\"nfast\":%d,\"slots\":%d,\"xbuf\":%d,\"wpf\":%d,"
-                "\"rr\":%d,\"est_us\":%.3f}",
+                "\"rr\":%d,\"mb\":%d,\"est_us\":%.3f}",
                 g.path == 0 ? "dot2" : (g.path == 3 ? "kc" : "mfma"), g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
                 g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles,
-                g.nfast, g.slots, g.xbuf, g.wpf, g.rr, g.est_us);
+                g.nfast, g.slots, g.xbuf, g.wpf, g.rr, g.mb, g.est_us);
   return b;
 }
 

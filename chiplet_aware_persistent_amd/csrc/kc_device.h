@@ -20,6 +20,15 @@
 // missing wave-level K split as why its megakernel falls behind at batch 64,
 // Limitations and open question 4).
 //
+// Beyond 64 rows (M up to 256) an item also names an m-block of 64 rows: the
+// items of one (split, column block) are its m-blocks, m-block fastest, and
+// the workgroups of an XCD take the items round-robin (workgroup w: items w,
+// w + 32, ...), so the m-blocks of a column block run at the same time on
+// neighbouring workgroups of one XCD and its weight lines are fetched from
+// HBM once and read from that XCD's L2 by the others: the M-major window of
+// the Fleet reading note (section 3f, Eq.(1): with R = 4 concurrent readers
+// of a line, a weight hit rate of 1 - 1/R), here at T_M = 64.
+//
 // At the end of an item the eight per-wave sums are added through LDS in a
 // fixed tree order (w + w+4, then + w+2, then + w+1), so the result does not
 // depend on timing; wave 0 then writes Y (or, with S > 1, the split's
@@ -40,31 +49,37 @@ constexpr int kc_ring_depth(int ntw, int mt, bool chain) {
   return (chain && mt >= 4) || ntw >= 6 ? 1 : (ntw >= 4 ? 2 : 4);
 }
 
-// X chunk: rows [0, rows) x K values [k0, k0 + kKcChunk) of X into an LDS
-// buffer of xbuf bytes (row stride kKcRow), zero outside [0, M) x [k0, kend).
-// One wave instruction fills one kilobyte; the waves take the kilobytes in
-// turn.  With kend <= k0 the whole buffer is written with zeros (the loads
-// are still issued, so every wave issues the same number of loads per step).
-__device__ __forceinline__ void stage_x_chunk(const StageDesc& d, uint16_t* buf, int k0, int kend, Rsrc xr) {
+// X chunk: rows [m0, m0 + mrows) x K values [k0, k0 + kKcChunk) of X into an
+// LDS buffer of xbuf bytes (buffer row r = X row m0 + r, row stride kKcRow),
+// zero outside those rows and [k0, kend) (so buffer row mrows, when the
+// buffer has it, is a zero row).  One wave instruction fills one kilobyte;
+// the waves take the kilobytes in turn.  With kend <= k0 the whole buffer is
+// written with zeros (the loads are still issued, so every wave issues the
+// same number of loads per step).
+__device__ __forceinline__ void stage_x_chunk(const StageDesc& d, uint16_t* buf, int k0, int kend, Rsrc xr,
+                                              int m0 = 0, int mrows = 1 << 30) {
   const int lane = threadIdx.x & 63;
   const int pieces = d.xbuf >> 10;
+  const int rows_ok = min(mrows, d.M - m0);
   for (int c = (int)(threadIdx.x >> 6); c < pieces; c += kKcWaves) {
     const int e = (c * 1024 + lane * 16) >> 1;
     const int row = e / kKcRow;
     const int col = e - row * kKcRow;
     const int k = k0 + col;
-    const bool valid = row < d.M && col < kKcChunk && k < kend;
-    const unsigned off = valid ? ((unsigned)row * (unsigned)d.ldx + (unsigned)k) * 2u : d.x_bytes;
+    const bool valid = row < rows_ok && col < kKcChunk && k < kend;
+    const unsigned off = valid ? ((unsigned)(m0 + row) * (unsigned)d.ldx + (unsigned)k) * 2u : d.x_bytes;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)((char*)buf + c * 1024),
                                              16, off, 0, 0, 0);
   }
 }
 
-// Items: (split s, block b), split-major; workgroup slot w of nslots takes the
-// contiguous range [first_item_of_wg(w), first_item_of_wg(w + 1)).  Block b of
-// XCD x covers the output columns [x*Nx + b*CB, x*Nx + (b+1)*CB), CB = 16 NTW
-// (paired: 16 NTW/2, with the up rows pair_off rows further on).  d.steps is
-// the number of chunks per item (a multiple of the ring depth).
+// Items: (split s, block b, m-block q), split-major, m-block fastest (d.mb
+// m-blocks of 16 MT rows; one when every row fits one item).  Workgroup slot
+// w of nslots takes the contiguous range [first_item_of_wg(w),
+// first_item_of_wg(w + 1)), or with d.rr the items w, w + nslots, ...  Block
+// b of XCD x covers the output columns [x*Nx + b*CB, x*Nx + (b+1)*CB), CB =
+// 16 NTW (paired: 16 NTW/2, with the up rows pair_off rows further on).
+// d.steps is the number of chunks per item (a multiple of the ring depth).
 template <int MT, int NTW, bool PAIRED, int AUX, typename Hook = NoHook, bool CHAIN = false>
 __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, int xcd, int slot, int nslots,
                               Hook pre_x = Hook()) {
@@ -76,10 +91,19 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
   const int wave = threadIdx.x >> 6;          // this wave's k-step within each chunk
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  const int i0 = first_item_of_wg(d.items, slot, nslots);
-  const int i1 = first_item_of_wg(d.items, slot + 1, nslots);
-  const int nit = i1 - i0;
+  int i0, i1, istep = 1;
+  if (d.rr) {
+    i0 = slot;
+    i1 = d.items;
+    istep = nslots;
+  } else {
+    i0 = first_item_of_wg(d.items, slot, nslots);
+    i1 = first_item_of_wg(d.items, slot + 1, nslots);
+  }
+  const int nit = i0 < i1 ? (i1 - i0 + istep - 1) / istep : 0;  // items of this workgroup
   const int nc = d.steps;
+  const int MB = d.mb > 1 ? d.mb : 1;
+  constexpr int TM = 16 * MT;  // rows of an m-block
   const int xc0 = xcd * d.Nx;
   const int xc1 = min(d.N, xc0 + d.Nx);
   const Rsrc wr = make_rsrc(d.W, d.w_bytes);
@@ -87,8 +111,12 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
   const Rsrc yr = make_rsrc(d.Y, d.y_bytes);
   const Rsrc y2r = make_rsrc(d.Y2, d.y2_bytes);
   const Rsrc pr = make_rsrc(d.part, d.part_bytes);
-  auto split_of = [&](int it) { return it / d.NB; };
-  auto block_of = [&](int it) { return it - (it / d.NB) * d.NB; };
+  const int per_split = d.NB * MB;
+  auto split_of = [&](int it) { return it / per_split; };
+  auto block_of = [&](int it) { return (it - (it / per_split) * per_split) / MB; };
+  auto mblk_of = [&](int it) { return it - (it / MB) * MB; };
+  // Split-K tile (counter and partial block) of item it.
+  auto tile_of = [&](int it) { return (unsigned)((xcd * d.NB + block_of(it)) * MB + mblk_of(it)); };
   auto xbuf = [&](int b) { return (uint16_t*)((char*)xs + b * d.xbuf); };
 
   // Weight stream: the full-line load layout of the MFMA path (load h gives
@@ -148,7 +176,7 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
     }
     return __builtin_bit_cast(bf16x8, o);
   };
-  auto emit = [&](int col0, const f4 (&v)[NTW][MT]) {
+  auto emit = [&](int col0, int m0, const f4 (&v)[NTW][MT]) {
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int col = col0 + 16 * j + r16;
@@ -156,7 +184,7 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = 16 * i + 4 * g4 + e;
+          const int m = m0 + 16 * i + 4 * g4 + e;
           const bool ok = m < d.M && col < xc1;
           if constexpr (PAIRED) {
             store_out(d, yr, y2r, ok, m, col, silu_mul(v[j][i][e], v[j + NP][i][e]));
@@ -166,24 +194,30 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
         }
     }
   };
-  auto item_k = [&](int it, int& k0, int& kend) {
+  // K range and first row of item it.
+  int k0, kend, m0;
+  auto item_k = [&](int it) {
     k0 = split_of(it) * d.KS;
     kend = min(d.K, k0 + d.KS);
+    m0 = TM * mblk_of(it);
   };
 
-  // A-operand rows: m-tile i, lane row 16i + r16 (row M, a zero row, past M).
+  // A-operand rows: m-tile i, lane row 16i + r16 of the item's m-block, or
+  // the buffer's zero row (row min(TM, M - m0)) past M.
   int xro[MT];
+  auto set_rows = [&]() {
 #pragma unroll
-  for (int i = 0; i < MT; ++i) xro[i] = min(16 * i + r16, d.M) * kKcRow;
+    for (int i = 0; i < MT; ++i) xro[i] = min(16 * i + r16, d.M - m0) * kKcRow;
+  };
   bf16x8 xa[2][MT];
 
   constexpr bool early = __is_same(Hook, NoHook);
-  int k0, kend;
-  item_k(i0 < i1 ? i0 : 0, k0, kend);
+  item_k(i0 < i1 ? i0 : 0);
   if (i0 >= i1) kend = 0;
-  if constexpr (early) stage_x_chunk(d, xbuf(0), k0, kend, xr);
+  set_rows();
+  if constexpr (early) stage_x_chunk(d, xbuf(0), k0, kend, xr, m0, TM);
   u4 ring[P][NTW][2];
-  Src sc = src_of(i0), sn = src_of(i0 + 1);
+  Src sc = src_of(i0), sn = src_of(i0 + istep);
 #pragma unroll
   for (int p = 0; p < P; ++p)
 #pragma unroll
@@ -193,7 +227,7 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
   if constexpr (early) {
     wait_vm<P * NTW * 2>();
   } else {
-    stage_x_chunk(d, xbuf(0), k0, kend, xr);
+    stage_x_chunk(d, xbuf(0), k0, kend, xr, m0, TM);
     wait_vm0();
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -218,7 +252,7 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
     for (int p = 0; p < P; ++p) {
       const int t = t0 + p;
       // Chunk t + 1 of this item into the other buffer (zeros after the last).
-      stage_x_chunk(d, xbuf((t + 1) & 1), k0 + (t + 1) * kKcChunk, t + 1 < nc ? kend : 0, xr);
+      stage_x_chunk(d, xbuf((t + 1) & 1), k0 + (t + 1) * kKcChunk, t + 1 < nc ? kend : 0, xr, m0, TM);
       const uint16_t* xb = xbuf(t & 1) + wave * kMfmaKStep + 8 * g4;
       // Both halves' A fragments first; then tile by tile, both halves and
       // the tile's reload right behind them, so each tile waits only for its
@@ -266,10 +300,9 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
       }
       if (wave == 0) {
         if (d.S == 1) {
-          emit(xc0 + block_of(it) * d.CB, acc);
+          emit(xc0 + block_of(it) * d.CB, m0, acc);
         } else {
-          const unsigned tile = (unsigned)(xcd * d.NB + block_of(it));
-          const unsigned base = (tile * d.S + split_of(it)) * TILE;
+          const unsigned base = (tile_of(it) * d.S + split_of(it)) * TILE;
 #pragma unroll
           for (int j = 0; j < NTW; ++j)
 #pragma unroll
@@ -281,16 +314,17 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
       for (int j = 0; j < NTW; ++j)
 #pragma unroll
         for (int i = 0; i < MT; ++i) acc[j][i] = f4{0.f, 0.f, 0.f, 0.f};
-      ++it;
+      it += istep;
       t0 = 0;
       sc = sn;
-      sn = src_of(it + 1);
+      sn = src_of(it + istep);
       if (it < i1) {
         // The next item's first chunk: the reduction used the buffers, so
         // its X is loaded only now, and waiting for it also waits for the
         // weights already in flight.
-        item_k(it, k0, kend);
-        stage_x_chunk(d, xbuf(0), k0, kend, xr);
+        item_k(it);
+        set_rows();
+        stage_x_chunk(d, xbuf(0), k0, kend, xr, m0, TM);
         wait_vm0();
         __syncthreads();
       }
@@ -299,16 +333,16 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
 
   if (d.S > 1 && nit > 0 && wave == 0) {
     splitk_release(d.sync);
-    for (int c0 = i0; c0 < i1; c0 += 4) {
+    for (int c0 = 0; c0 < nit; c0 += 4) {
       unsigned old[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        old[q] = c0 + q < i1 ? splitk_bump(d.ctr + xcd * d.NB + block_of(c0 + q), lane) : 0u;
+        old[q] = c0 + q < nit ? splitk_bump(d.ctr + tile_of(i0 + (c0 + q) * istep), lane) : 0u;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int itq = c0 + q;
-        if (itq >= i1) break;
-        const unsigned tile = (unsigned)(xcd * d.NB + block_of(itq));
+        if (c0 + q >= nit) break;
+        const int itq = i0 + (c0 + q) * istep;
+        const unsigned tile = tile_of(itq);
         if (!splitk_own(d.ctr + tile, old[q], d.S, d.sync, lane)) continue;
         f4 tot[NTW][MT];
 #pragma unroll
@@ -320,7 +354,7 @@ __device__ __forceinline__ bool mfma_kc_stage(const StageDesc& d, uint16_t* xs, 
         } else {
           sum_partials_f4<0, NTW, MT>(pr, tile * d.S * TILE, TILE, d.S, lane, tot, d.part_bytes);
         }
-        emit(xc0 + block_of(itq) * d.CB, tot);
+        emit(xc0 + block_of(itq) * d.CB, TM * mblk_of(itq), tot);
       }
     }
   }

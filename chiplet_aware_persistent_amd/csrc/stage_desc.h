@@ -70,6 +70,7 @@ struct StageDesc {
   int check;           // single GEMM: claim (XCD, slot) at the end and latch a duplicate
   int xbuf;            // K-chunked MFMA path: bytes of one X chunk buffer (multiple of 1 KB)
   int nctr;            // split-K arrival counters of this stage (reset by the chain's last workgroup)
+  int mb;              // K-chunked MFMA path: m-blocks of 16 MT rows per (split, column block) (0 or 1: one)
   int wpf;             // chain, dot2: steps of each wave's first item whose weights go to LDS before the wait
   int wpf_off;         // LDS byte offset of those weights (wave w: wpf * G kilobytes from wpf_off + w * that)
   const uint16_t* R;   // residual added to every output before its rounding (null: none), [M][ldy] bf16

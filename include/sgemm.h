@@ -174,9 +174,21 @@ typedef struct {
  * chooses the path (dot2 for M < 16, MFMA for M >= 16, unless forced), the
  * per-XCD column partition, tile widths, split-K count and workspace layout.
  * *workspace_bytes receives the size of the device workspace the runs need
- * (>= 4 KiB).  Shape rules: 1 <= M <= 64; K >= 8, K % 8 == 0; N >= 1; every
- * operand below 2 GiB.  Returns SGEMM_ERR_INVALID_ARG or
+ * (>= 4 KiB).  Shape rules: 1 <= M <= 256 for the single GEMM and
+ * 1 <= M <= 64 for the chain and the decoder; K >= 8, K % 8 == 0; N >= 1;
+ * every operand below 2 GiB.  Returns SGEMM_ERR_INVALID_ARG or
  * SGEMM_ERR_UNSUPPORTED without creating a plan when they are violated.
+ * A single GEMM with M = 65..256 (the compute-leaning regime: the scope of
+ * the FlyDSL news item's K-split and LDS pipeline, and the batch sizes at
+ * which the Fleet reading note reports its megakernel falling behind,
+ * Limitations) runs on the K-chunked MFMA path in 64-row m-blocks: the
+ * m-blocks of a column block are neighbouring items that an XCD's
+ * workgroups take round-robin, so they share the block's weight lines
+ * through that XCD's L2 (the M-major window, section 3f, Eq.(1)).  There
+ * SGEMM_F_FORCE_DOT2, SGEMM_F_FORCE_MFMA, SGEMM_F_MTILE_ITEMS,
+ * SGEMM_F_MSPLIT, SGEMM_F_W_CACHED and SGEMM_F_W_SC1 are refused with
+ * SGEMM_ERR_UNSUPPORTED (the K-chunked kernels load weights nontemporally
+ * only; so does SGEMM_F_KCHUNK at any M).
  *
  * Environment, read here (for experiments and calibration):
  *   SGEMM_TN, SGEMM_SPLITK, SGEMM_WAVES, SGEMM_KSLICES: used for the problem

@@ -6,6 +6,7 @@ import json
 import math
 import os
 
+import numpy as np
 import pytest
 
 import chiplet_aware_persistent_amd as sg
@@ -37,7 +38,7 @@ def _create(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(M=0), sg.ERR_INVALID_ARG),
-    (dict(M=65), sg.ERR_UNSUPPORTED),
+    (dict(M=257), sg.ERR_UNSUPPORTED),
     (dict(K=12), sg.ERR_INVALID_ARG),
     (dict(K=0), sg.ERR_INVALID_ARG),
     (dict(N=0), sg.ERR_INVALID_ARG),
@@ -741,3 +742,54 @@ def test_bench_cpu_baselines_report_the_contract_fields():
     r = bench.cpu_baseline_chain(2, x, ws)
     assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0 and r["cores"] >= 1
     assert "M=2" in r["sample"]
+
+
+@pytest.mark.parametrize("M", [65, 80, 100, 127, 128, 129, 192, 200, 255, 256])
+@pytest.mark.parametrize("K,N", [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096), (7168, 18432),
+                                 (1032, 777), (8, 1)])
+def test_large_m_plans_cover_rows_columns_and_k(M, K, N):
+    """M = 65..256: the K-chunked path in 64-row m-blocks, items (split,
+    block, m-block) taken round-robin.  A host walk of every (XCD, slot)
+    pair's items covers every (m-block, column block, split) exactly once;
+    the m-blocks cover the M rows, the blocks each XCD's columns and the
+    splits K; LDS fits next to the static reserve."""
+    st = sg.Gemm(M, K, N).describe()["stage"]
+    MB = -(-M // 64)
+    assert st["path"] == "kc" and st["ta"] == 4 and st["mb"] == MB and st["rr"] == 1
+    assert st["items"] == st["NB"] * st["S"] * MB
+    assert st["NB"] * st["CB"] >= st["Nx"] and 8 * st["Nx"] >= N
+    assert st["S"] * st["KS"] >= K and (st["S"] - 1) * st["KS"] < K
+    assert (MB - 1) * 64 < M <= MB * 64
+    assert st["xbuf"] >= 64 * 520 * 2 and st["lds"] + STATIC_LDS_RESERVE <= 160 * 1024
+    seen = np.zeros(st["items"], dtype=np.int64)
+    for slot in range(32):
+        for it in range(slot, st["items"], 32):
+            seen[it] += 1
+    assert np.all(seen == 1)
+    per_split = st["NB"] * MB
+    triples = {(it // per_split, (it % per_split) // MB, it % MB) for it in range(st["items"])}
+    assert len(triples) == st["items"]
+    # round-robin: the m-blocks of one (split, block) are consecutive items, so
+    # they land on consecutive slots of the XCD and run together
+    for it in range(0, st["items"], MB):
+        assert {(it + q) % MB for q in range(MB)} == set(range(MB))
+
+
+def test_large_m_refusals():
+    assert _create(M=257) == sg.ERR_UNSUPPORTED
+    for fl in (sg.F_FORCE_MFMA, sg.F_MTILE_ITEMS, sg.F_MSPLIT, sg.F_W_CACHED, sg.F_W_SC1, sg.F_FORCE_DOT2):
+        assert _create(M=65, K=1024, N=1024, flags=fl) == sg.ERR_UNSUPPORTED, fl
+    # the K-chunked kernels are built with nontemporal weight loads only
+    assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_W_CACHED) == sg.ERR_UNSUPPORTED
+    assert _create(M=64, K=4096, N=24576, flags=sg.F_W_CACHED) == sg.OK
+    assert sg.Gemm(64, 4096, 24576, flags=sg.F_W_CACHED).describe()["stage"]["path"] == "mfma"
+    assert sg.Gemm(64, 4096, 24576).describe()["stage"]["path"] == "kc"
+    assert _create(kind=sg.KIND_LAYERCHAIN, M=65, L=2, d=64, q=64, dff=64) == sg.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("M", [1, 16, 33, 64])
+def test_plans_up_to_64_rows_keep_one_m_block(M):
+    """Below 65 rows nothing changes: one m-block and, on the K-chunked path,
+    contiguous item ranges."""
+    st = sg.Gemm(M, 4096, 24576, flags=sg.F_KCHUNK).describe()["stage"]
+    assert st["mb"] == 1 and st["rr"] == 0 and st["items"] == st["NB"] * st["S"]

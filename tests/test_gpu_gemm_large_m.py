@@ -1,0 +1,126 @@
+"""GPU parity of the single GEMM beyond 64 rows (M = 65..256).
+
+Those shapes run on the K-chunked MFMA path in 64-row m-blocks, the m-blocks
+of a column block being neighbouring items that an XCD's workgroups take
+round-robin (so they share the block's weights through that XCD's L2).  Every
+output element is compared with the CPU oracle: ragged M, K and N that span
+several m-blocks, column blocks and splits, forced tile and split counts,
+bf16 output, integer inputs (bitwise), run-to-run and graph-replay
+determinism, and the decode projection shapes at M = 128 and 256 at full
+size.  Every call goes through the C ABI (ctypes) into libsgemm.so.
+"""
+import numpy as np
+import pytest
+
+import chiplet_aware_persistent_amd as sg
+import synth
+from helpers import check, device_tensor_bf16, device_weights_checked, gemm_inputs, report
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def run(g, X, W, ws=None):
+    Y = torch.empty((g.M, g.N), dtype=torch.float32 if g.out_dtype == sg.OUT_F32 else torch.bfloat16,
+                    device=X.device)
+    if ws is None:
+        ws = g.new_workspace()
+    g(X, W, Y, ws)
+    rc = g.status(ws)
+    assert rc == sg.OK, sg.status_string(rc)
+    return Y
+
+
+def _plan_checks(g, M):
+    st = g.describe()["stage"]
+    assert st["path"] == "kc" and st["ta"] == 4 and st["mb"] == -(-M // 64) and st["rr"] == 1, st
+    return st
+
+
+LARGE_SMALL = [(65, 1032, 777, 0, 0), (65, 1032, 777, 2, 3), (80, 520, 64, 0, 0), (100, 2048, 1536, 4, 0),
+               (100, 2048, 1536, 6, 2), (128, 1024, 4096, 0, 0), (129, 4104, 129, 3, 2), (144, 776, 530, 2, 0),
+               (200, 3000, 700, 0, 0), (200, 3000, 700, 4, 3), (255, 2056, 900, 6, 0), (256, 4096, 1024, 0, 0),
+               (256, 4096, 1024, 2, 4), (256, 8, 1, 0, 0), (192, 12288, 300, 0, 5)]
+
+
+@pytest.mark.parametrize("M,K,N,ntw,splitk", LARGE_SMALL)
+def test_parity_large_m_small(cuda_device, M, K, N, ntw, splitk):
+    x, w, X, W = gemm_inputs(M, K, N, 12100 + M, 12200 + K, cuda_device)
+    g = sg.Gemm(M, K, N, tn=16 * ntw, splitk=splitk)
+    st = _plan_checks(g, M)
+    assert ntw == 0 or st["tb"] == ntw
+    # forced splits are whole chunk groups, so a short K may take fewer
+    assert splitk == 0 or 1 <= st["S"] <= splitk
+    check(run(g, X, W).cpu().numpy(), x, w)
+
+
+@pytest.mark.parametrize("M", [65, 130])
+def test_large_m_bf16_output(cuda_device, M):
+    K, N = 2056, 1000
+    x, w, X, W = gemm_inputs(M, K, N, 12300 + M, 12301, cuda_device)
+    g = sg.Gemm(M, K, N, out_dtype=sg.OUT_BF16)
+    _plan_checks(g, M)
+    Y = run(g, X, W).float().cpu().numpy()
+    check(Y, x, w, bf16_out=True)
+
+
+@pytest.mark.parametrize("M,K,N,splitk", [(128, 4096, 24576, 0), (256, 12288, 4096, 0), (192, 4096, 6144, 2),
+                                          (97, 7168, 18432, 0)])
+def test_large_m_integer_inputs_bitwise(cuda_device, M, K, N, splitk):
+    """Integer inputs in [-3, 3]: every partial sum is an integer below 2**24,
+    exact in fp32 in any order, so every element equals the exact product."""
+    xb = synth.int_bf16(11, M, K, -3, 3)
+    wb = synth.int_bf16(12, N, K, -3, 3)
+    X, W = device_tensor_bf16(xb, cuda_device), device_tensor_bf16(wb, cuda_device)
+    g = sg.Gemm(M, K, N, splitk=splitk)
+    _plan_checks(g, M)
+    Y = run(g, X, W).cpu().numpy()
+    ref = synth.bf16_bits_to_f32(xb).astype(np.float64) @ synth.bf16_bits_to_f32(wb).astype(np.float64).T
+    assert np.array_equal(Y, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("splitk", [1, 3])
+def test_large_m_repeat_and_graph_replays(cuda_device, splitk):
+    """Repeated eager runs and replays of a captured HIP graph give bitwise
+    the same output (split-K counters reset by their owners)."""
+    M, K, N = 200, 4096, 2048
+    x, w, X, W = gemm_inputs(M, K, N, 12400, 12401, cuda_device)
+    g = sg.Gemm(M, K, N, splitk=splitk)
+    _plan_checks(g, M)
+    ws = g.new_workspace()
+    Ye = run(g, X, W, ws)
+    assert torch.equal(run(g, X, W, ws), Ye)
+    Y = torch.empty_like(Ye)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g(X, W, Y, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g(X, W, Y, ws)
+    for r in range(3):
+        Y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert g.status(ws) == sg.OK, r
+        assert torch.equal(Y, Ye), r
+    check(Ye.cpu().numpy(), x, w)
+
+
+@pytest.mark.parametrize("M", [128, 256])
+@pytest.mark.parametrize("K,N", [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)])
+def test_decode_projections_m128_m256_full_size(cuda_device, M, K, N):
+    """The four projection shapes at M = 128 and 256, every output element
+    against the oracle, in the plan the bench's large-M lines use."""
+    seed_x = synth.seed_for(3, 0, synth.T_X, M)
+    seed_w = synth.seed_for(3, 0, synth.T_WQ, K % 251 + N % 241)
+    x, _, X, W = gemm_inputs(M, K, N, seed_x, seed_w, cuda_device, w_on_device=True)
+    g = sg.Gemm(M, K, N)
+    _plan_checks(g, M)
+    Y = run(g, X, W).cpu().numpy()
+    w = device_weights_checked(W, seed_w, K)
+    report("gemm %dx%dx%d" % (M, K, N), check(Y, x, w), workload="large_m")
