@@ -18,10 +18,12 @@ the same step.
 
 Unless ``--no-extra`` is given, the line also carries ``configs``: every
 other configuration timed in the same run with HIP events on the launch
-stream (the single GEMM at M = 1, 8, 16, 32, 64 on the four projection shapes,
-the K = 7168 grid at M = 1..16, 1 x 1024 x 1024, each on weights rotating over
-a 4.5 GiB pool; the 36-layer chain at M = 64, 16 and 1), each with its
-fraction of 8 TB/s.
+stream (the single GEMM at M = 1, 8, 16, 32, 64, 128, 256 on the four
+projection shapes, the K = 7168 grid at M = 1..16 and at M = 256 x 18432,
+1 x 1024 x 1024, each on weights rotating over a 4.5 GiB pool; the 36-layer
+chain at M = 64, 16 and 1), each with its fraction of 8 TB/s (and, for the
+single GEMM, its TFLOP/s and its fraction of the roofline floor, the longer
+of the weight bytes at 8 TB/s and the flops at 2.5 PFLOP/s).
 
 ``--workload chain``: the 36-layer persistent chain at M = 64 (``--chain-m``
 selects another row count; Q 4096x4096,
@@ -275,8 +277,10 @@ def bench_proj(args):
 
 
 GEMM_TABLE = ([(1, 1024, 1024)] +
-              [(M, K, N) for M in (1, 8, 16, 32, 64) for _, K, N in PROJ] +
-              [(M, 7168, N) for M in (1, 2, 4, 8, 16) for N in (1536, 4096, 18432)])
+              [(M, K, N) for M in (1, 8, 16, 32, 64, 128, 256) for _, K, N in PROJ] +
+              [(M, 7168, N) for M in (1, 2, 4, 8, 16) for N in (1536, 4096, 18432)] +
+              [(256, 7168, 18432)])
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def timed_gemm_table(dev, steps, warmup):
@@ -317,9 +321,15 @@ def timed_gemm_table(dev, steps, warmup):
             raise sg.SgemmError(rc, "status")
         us = e0.elapsed_time(e1) * 1e3 / steps
         st = g.describe()["stage"]
+        # Roofline floor: the weight bytes at 8 TB/s or the 2 M K N flops at
+        # the dense bf16 matrix-core peak, whichever is longer (the latter
+        # only matters from M of about 300 up; M = 128 and 256 lean towards it).
+        floor_us = max(2 * K * N / (HBM_PEAK_GBPS * 1e3), 2.0 * M * K * N / (MFMA_BF16_PEAK_TFLOPS * 1e6))
         rows.append({"M": M, "K": K, "N": N, "us_avg": round(us, 3),
                      "weight_GBps": round(2 * K * N / (us * 1e-6) / 1e9, 1),
                      "frac_of_8TBps": round(2 * K * N / (us * 1e-6) / 1e12 / 8.0, 4),
+                     "tflops": round(2.0 * M * K * N / (us * 1e-6) / 1e12, 1),
+                     "frac_of_roofline": round(floor_us / us, 4),
                      "plan": "%s ta=%d tb=%d wpi=%d ksl=%d S=%d" % (st["path"], st["ta"], st["tb"], st["wpi"],
                                                                    st["ksl"], st["S"])})
         log("table %dx%dx%d: %.2f us" % (M, K, N, us))

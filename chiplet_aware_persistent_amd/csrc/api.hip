@@ -625,6 +625,13 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
           kcg.items * 4 >= kWgPerXcd * 3 && pl->geo.S > 2)
         pl->geo = kcg;
     }
+    if (pl->geo.path == 3 && pl->geo.mb > 1) {
+      // m-blocks round-robin over the XCD's workgroups (shared weights in
+      // L2); SGEMM_KC_RR=0 gives each workgroup a contiguous range instead.
+      int rr = 1;
+      if (!env_int("SGEMM_KC_RR", 1, &rr)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+      pl->geo.rr = rr ? 1 : 0;
+    }
     pl->geo.nfast = msplit ? 1 : 0;
     if ((pl->geo.path == 0 || (pl->geo.path == 1 && pl->geo.mtiles == 1)) && pl->geo.S == 1) {
       // Items round-robin over the XCD's streams (measured 0-3% faster than
