@@ -319,6 +319,72 @@ bool kc_geo(Geo& g, int want_S, const Cost& cost) {
   return true;
 }
 
+// Large-tile MFMA path (lt_device.h, path 5), single GEMM at M > 64: four
+// waves over a workgroup tile of 32 MW rows x 32 NW columns, 32-wide K steps
+// through a ring of LDS slots.  Fill g for (MW, NW, S); false when it does
+// not fit.
+bool lt_geo(Geo& g, int want_S) {
+  const int MW = g.ta, NW = g.tb;
+  g.path = 5;
+  g.waves = kLtWaves; g.wpi = kLtWaves; g.ng = 1; g.ksl = 1;
+  g.TN = 16;
+  g.CB = 32 * NW;
+  g.Nx = (int)round_up((size_t)ceil_div(g.N, kXcds), 16);
+  g.NB = ceil_div(g.Nx, g.CB);
+  // Splits start on whole 128-byte lines; every item runs the split's steps
+  // (the last split's extra steps read zeros).
+  g.KS = (int)round_up((size_t)ceil_div(g.K, want_S), 64);
+  g.S = ceil_div(g.K, g.KS);
+  g.kss = g.KS;
+  g.ring = lt_reg_steps(MW, NW);
+  g.steps = (int)round_up((size_t)(g.KS / kLtKStep), (size_t)g.ring);  // a multiple of the ring
+  g.mb = ceil_div(g.M, 32 * MW);
+  g.items = g.NB * g.S * g.mb;
+  g.rr = 1;
+  g.mtiles = 1;
+  g.lds = lt_lds_bytes(MW, NW);
+  g.win = 0; g.xrow = 0; g.xbuf = 0;
+  g.red_off = g.lds; g.stash_off = g.lds; g.stash_cap = 0;
+  if (g.lds > kLdsMax) return false;
+  g.ctr_count = (size_t)kXcds * g.NB * g.mb * kLtWaves;
+  g.part_floats = g.S > 1 ? g.ctr_count * (size_t)g.S * MW * NW * 256 : 0;
+  // Cost (microseconds): per workgroup the longest of its weight bytes from
+  // HBM (m-blocks of one block share them through L2), its weight and X
+  // bytes from L2, and its matrix-core work at 70% of the CU's dense bf16
+  // rate; plus a per-step barrier and, with splits, the partials' round
+  // trip and the finalize.
+  const double wg_items = ceil_div(g.items, g.slots);
+  const double ks = (double)g.steps * kLtKStep;
+  const double tm = 32.0 * MW, cb = 32.0 * NW;
+  const double w_bytes = wg_items * cb * ks * 2.0, x_bytes = wg_items * tm * ks * 2.0;
+  const double flops = wg_items * 2.0 * tm * cb * ks;
+  const double p_bytes = g.S > 1 ? wg_items * tm * cb * 4.0 * 2.0 : 0.0;
+  const double bw_cu = 8.0e12 * 0.85 / 256.0, cu_rd = 110.0e9, mfma_cu = 2.5e15 / 256.0 * 0.7;
+  g.est_us = std::max(std::max((w_bytes / g.mb + p_bytes) / bw_cu, (w_bytes + x_bytes) / cu_rd), flops / mfma_cu) * 1e6 +
+             wg_items * g.steps * 0.02 + (g.S > 1 ? 6.0 : 0.0);
+  return true;
+}
+
+bool plan_lt(Geo& best, int M, int K, int N, int mw_o, int nw_o, int s_o) {
+  bool found = false;
+  for (int mw : {2, 4, 8}) {
+    if (mw_o && mw != mw_o) continue;
+    for (int nw : {3, 6}) {
+      if (nw_o && nw != nw_o) continue;
+      const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : 8;
+      for (int s = s_lo; s <= s_hi; ++s) {
+        Geo c;
+        c.M = M; c.K = K; c.N = N; c.ta = mw; c.tb = nw; c.slots = kWgPerXcd;
+        if (!lt_geo(c, s)) continue;
+        if (c.S != s && !s_o) continue;
+        if (!gemm_variant_exists(5, mw, nw)) continue;
+        if (!found || c.est_us < best.est_us - 1e-9) { best = c; found = true; }
+      }
+    }
+  }
+  return found;
+}
+
 // Chain dot2 stage: the weights of the first steps of each wave's first item
 // are loaded into LDS before the wait for the stage's X, so that the latency
 // of the stage boundary streams weights.  As many whole ring groups as fit
@@ -595,18 +661,29 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     if (rc != SGEMM_OK) { delete pl; return rc; }
     const bool msplit = (p.flags & SGEMM_F_MSPLIT) != 0;
     const bool mti = (p.flags & SGEMM_F_MTILE_ITEMS) != 0 || msplit;
-    const bool kc = (p.flags & SGEMM_F_KCHUNK) != 0 || p.M > 64;
+    const bool kc = (p.flags & SGEMM_F_KCHUNK) != 0;
+    // Beyond 64 rows: the large-tile path unless the K-chunked one is asked
+    // for (SGEMM_LT=0 takes the K-chunked path there too).
+    int lt_env = 1;
+    if (!env_int("SGEMM_LT", 1, &lt_env)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+    const bool lt = p.M > 64 && !kc && lt_env;
+    const bool kcm = kc || (p.M > 64 && !lt);
     // Rows per m-tile item (the window of the M-major traversal): 16 unless given.
     const int mti_rows = !mti ? 0 : (p.tm ? p.tm : 16);
     if (mti && mti_rows != 16 && mti_rows != 32 && mti_rows != 64) { delete pl; return SGEMM_ERR_INVALID_ARG; }
-    if (!mti && p.tm) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+    if (!mti && p.tm && !(lt && (p.tm == 64 || p.tm == 128 || p.tm == 256))) { delete pl; return SGEMM_ERR_INVALID_ARG; }
     if ((mti || kc) && (p.flags & SGEMM_F_FORCE_DOT2)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
     if (mti && kc) { delete pl; return SGEMM_ERR_INVALID_ARG; }
     const int path = mti ? 1 : choose_path(p);
-    if ((path == 0 || mti || kc) && k_o > 1) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
-    // The K-chunked kernels are built with nontemporal weight loads only.
+    if ((path == 0 || mti || kcm || lt) && k_o > 1) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    // The K-chunked and large-tile kernels are built with nontemporal weight loads only.
     const bool nt_w = pl->w_aux == 2u;
-    if (kc) {
+    if (lt) {
+      // tn (a multiple of 32) gives the workgroup tile's columns; waves must be 0 or 4.
+      if (tn_o % 32 || (w_o && w_o != kLtWaves) || !nt_w) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+      // tm (64, 128 or 256) gives the tile's rows.
+      if (!plan_lt(pl->geo, p.M, p.K, p.N, p.tm / 32, tn_o / 32, s_o)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+    } else if (kcm) {
       // tn (a multiple of 16) gives the tiles per item.
       if (tn_o % 16 || w_o == 4 || !nt_w) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
       if (!plan_kc(pl->geo, p.M, p.K, p.N, 0, tn_o / 16, s_o, kCostGemm)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
@@ -625,7 +702,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
           kcg.items * 4 >= kWgPerXcd * 3 && pl->geo.S > 2)
         pl->geo = kcg;
     }
-    if (pl->geo.path == 3 && pl->geo.mb > 1) {
+    if ((pl->geo.path == 3 || pl->geo.path == 5) && pl->geo.mb > 1) {
       // m-blocks round-robin over the XCD's workgroups (shared weights in
       // L2); SGEMM_KC_RR=0 gives each workgroup a contiguous range instead.
       int rr = 1;
@@ -1157,7 +1234,7 @@ static std::string geo_json(const Geo& g) {
                 "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
                 "\"ring\":%d,\"mtiles\":%d,\"nfast\":%d,\"slots\":%d,\"xbuf\":%d,\"wpf\":%d,"
                 "\"rr\":%d,\"mb\":%d,\"est_us\":%.3f}",
-                g.path == 0 ? "dot2" : (g.path == 3 ? "kc" : "mfma"), g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
+                g.path == 0 ? "dot2" : (g.path == 3 ? "kc" : (g.path == 5 ? "lt" : "mfma")), g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
                 g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles,
                 g.nfast, g.slots, g.xbuf, g.wpf, g.rr, g.mb, g.est_us);
   return b;

@@ -1,0 +1,27 @@
+// Large-tile MFMA kernels of the single GEMM (lt_device.h), weights nt.
+// Four waves of one workgroup per CU, so each wave may hold the register file
+// of a whole SIMD (accumulators in the accumulation registers).
+#include "gemm_instances.h"
+#include "lt_device.h"
+
+namespace sg {
+
+template <int MW, int NW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_lt(StageDesc d,
+                                                                                              unsigned* ctl) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int xcd = xcd_of_wg(ctl), slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+  lt_stage<MW, NW, kAuxNt>(d, lds, xcd, slot, nslots);
+  if (d.check) claim_and_check(ctl, xcd, slot, nslots);
+}
+
+// (MW, NW): workgroup tiles of 32 MW rows x 32 NW columns.
+GemmKernel gemm_kernel_lt(int a, int b) {
+  if (a == 2 && b == 3) return k_gemm_lt<2, 3>;
+  if (a == 4 && b == 3) return k_gemm_lt<4, 3>;
+  if (a == 4 && b == 6) return k_gemm_lt<4, 6>;
+  if (a == 8 && b == 3) return k_gemm_lt<8, 3>;
+  return nullptr;
+}
+
+}  // namespace sg

@@ -161,7 +161,9 @@ typedef struct {
   unsigned flags;
   int tn, splitk, waves, kslices;
   int tm;  /* SGEMM_F_MTILE_ITEMS / SGEMM_F_MSPLIT: rows per item, T_M = 16, 32 or
-              64 (0: 16); must be 0 otherwise                                   */
+              64 (0: 16).  Single GEMM with M > 64 on the large-tile path:
+              rows of a workgroup tile, 64, 128 or 256 (0: the planner's);
+              tn there is the tile's columns, 96 or 192.  Must be 0 otherwise */
   /* kind = SGEMM_KIND_DECODER: M, n_layers, d_model, d_ff and these (q_cols is
      0 or n_heads * head_dim).  Built: n_heads = 4 n_kv_heads, head_dim = 128,
      ctx + 1 <= 4096 (64 chunks of 64 positions), M <= 64. */
@@ -179,16 +181,20 @@ typedef struct {
  * every operand below 2 GiB.  Returns SGEMM_ERR_INVALID_ARG or
  * SGEMM_ERR_UNSUPPORTED without creating a plan when they are violated.
  * A single GEMM with M = 65..256 (the compute-leaning regime: the scope of
- * the FlyDSL news item's K-split and LDS pipeline, and the batch sizes at
- * which the Fleet reading note reports its megakernel falling behind,
- * Limitations) runs on the K-chunked MFMA path in 64-row m-blocks: the
- * m-blocks of a column block are neighbouring items that an XCD's
- * workgroups take round-robin, so they share the block's weight lines
- * through that XCD's L2 (the M-major window, section 3f, Eq.(1)).  There
- * SGEMM_F_FORCE_DOT2, SGEMM_F_FORCE_MFMA, SGEMM_F_MTILE_ITEMS,
- * SGEMM_F_MSPLIT, SGEMM_F_W_CACHED and SGEMM_F_W_SC1 are refused with
- * SGEMM_ERR_UNSUPPORTED (the K-chunked kernels load weights nontemporally
- * only; so does SGEMM_F_KCHUNK at any M).
+ * the FlyDSL news item's K-split and multi-stage LDS pipeline, and the batch
+ * sizes at which the Fleet reading note reports its megakernel falling
+ * behind, Limitations) runs on the large-tile MFMA path: a workgroup of four
+ * waves owns a tile of up to 256 rows and 96 or 192 columns over a K split
+ * and stages each 32-wide K step's X and W fragments in LDS through a ring of
+ * slots.  With SGEMM_F_KCHUNK it runs on the K-chunked MFMA path in 64-row
+ * m-blocks instead.  On both, the m-blocks of a column block are
+ * neighbouring items that an XCD's workgroups take round-robin, so they
+ * share the block's weight lines through that XCD's L2 (the M-major window,
+ * section 3f, Eq.(1)).  There SGEMM_F_FORCE_DOT2, SGEMM_F_FORCE_MFMA,
+ * SGEMM_F_MTILE_ITEMS, SGEMM_F_MSPLIT, SGEMM_F_W_CACHED and SGEMM_F_W_SC1 are
+ * refused with SGEMM_ERR_UNSUPPORTED (both kernels load weights
+ * nontemporally only; so does SGEMM_F_KCHUNK at any M), and so are kslices
+ * above 1 and, on the large-tile path, waves other than 0 or 4.
  *
  * Environment, read here (for experiments and calibration):
  *   SGEMM_TN, SGEMM_SPLITK, SGEMM_WAVES, SGEMM_KSLICES: used for the problem

@@ -753,7 +753,7 @@ def test_large_m_plans_cover_rows_columns_and_k(M, K, N):
     pair's items covers every (m-block, column block, split) exactly once;
     the m-blocks cover the M rows, the blocks each XCD's columns and the
     splits K; LDS fits next to the static reserve."""
-    st = sg.Gemm(M, K, N).describe()["stage"]
+    st = sg.Gemm(M, K, N, flags=sg.F_KCHUNK).describe()["stage"]
     MB = -(-M // 64)
     assert st["path"] == "kc" and st["ta"] == 4 and st["mb"] == MB and st["rr"] == 1
     assert st["items"] == st["NB"] * st["S"] * MB
@@ -785,6 +785,36 @@ def test_large_m_refusals():
     assert sg.Gemm(64, 4096, 24576, flags=sg.F_W_CACHED).describe()["stage"]["path"] == "mfma"
     assert sg.Gemm(64, 4096, 24576).describe()["stage"]["path"] == "kc"
     assert _create(kind=sg.KIND_LAYERCHAIN, M=65, L=2, d=64, q=64, dff=64) == sg.ERR_UNSUPPORTED
+    # large-tile path: tile widths are multiples of 32 columns, four waves, no K slices
+    assert _create(M=65, K=1024, N=1024, tn=48) == sg.ERR_UNSUPPORTED
+    assert _create(M=65, K=1024, N=1024, waves=8) == sg.ERR_UNSUPPORTED
+    assert _create(M=65, K=1024, N=1024, ksl=2) == sg.ERR_UNSUPPORTED
+    assert _create(M=65, K=1024, N=1024, tn=96) == sg.OK
+
+
+@pytest.mark.parametrize("M", [65, 80, 100, 127, 128, 129, 192, 200, 255, 256])
+@pytest.mark.parametrize("K,N", [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096), (7168, 18432),
+                                 (1032, 777), (8, 1)])
+def test_large_tile_plans_cover_rows_columns_and_k(M, K, N):
+    """M = 65..256, default plans: the large-tile path (four waves, tiles of
+    32 MW rows x 32 NW columns), items (split, block, m-block) round-robin;
+    the m-blocks cover M, the blocks each XCD's columns, the splits K in
+    whole 32-wide steps, padded to the register ring depth; the two LDS
+    buffers fit next to the static reserve; the loads in flight fit vmcnt."""
+    st = sg.Gemm(M, K, N).describe()["stage"]
+    MW, NW = st["ta"], st["tb"]
+    assert st["path"] == "lt" and st["waves"] == 4 and st["rr"] == 1
+    TM = 32 * MW
+    assert st["mb"] == -(-M // TM) and (st["mb"] - 1) * TM < M
+    assert st["CB"] == 32 * NW and st["NB"] * st["CB"] >= st["Nx"] and 8 * st["Nx"] >= N
+    F = 2 * MW + 2 * NW          # two-kilobyte blocks per 64-wide K step
+    LPW = -(-2 * F // 4)         # 16-byte loads per lane and step (two per block)
+    D = max(2, min(8, (24 // LPW) // 2 * 2))  # steps in flight in registers (even)
+    assert st["ring"] == D and LPW * (D - 1) < 64
+    assert st["KS"] % 64 == 0 and st["steps"] % D == 0 and 0 <= st["steps"] * 64 - st["KS"] < 64 * D
+    assert st["S"] * st["KS"] >= K and (st["S"] - 1) * st["KS"] < K
+    assert st["items"] == st["NB"] * st["S"] * st["mb"]
+    assert st["lds"] == 2 * F * 2048 and st["lds"] + STATIC_LDS_RESERVE <= 160 * 1024
 
 
 @pytest.mark.parametrize("M", [1, 16, 33, 64])
