@@ -324,11 +324,11 @@ bool kc_geo(Geo& g, int want_S, const Cost& cost) {
 // through a ring of LDS slots.  Fill g for (MW, NW, S); false when it does
 // not fit.
 bool lt_geo(Geo& g, int want_S) {
-  const int MW = g.ta, NW = g.tb;
-  g.path = 5;
-  g.waves = kLtWaves; g.wpi = kLtWaves; g.ng = 1; g.ksl = 1;
+  const int MW = g.ta, NW = g.tb, WV = g.waves;  // WV = 4 or 8 waves (2 x WV/2 over the tile)
+  g.path = WV == 8 ? 6 : 5;
+  g.wpi = WV; g.ng = 1; g.ksl = 1;
   g.TN = 16;
-  g.CB = 32 * NW;
+  g.CB = 16 * NW * (WV / 2);
   g.Nx = (int)round_up((size_t)ceil_div(g.N, kXcds), 16);
   g.NB = ceil_div(g.Nx, g.CB);
   // Splits start on whole 128-byte lines; every item runs the split's steps
@@ -336,17 +336,17 @@ bool lt_geo(Geo& g, int want_S) {
   g.KS = (int)round_up((size_t)ceil_div(g.K, want_S), 64);
   g.S = ceil_div(g.K, g.KS);
   g.kss = g.KS;
-  g.ring = lt_reg_steps(MW, NW);
+  g.ring = lt_reg_steps(MW, NW, WV);
   g.steps = (int)round_up((size_t)(g.KS / kLtKStep), (size_t)g.ring);  // a multiple of the ring
   g.mb = ceil_div(g.M, 32 * MW);
   g.items = g.NB * g.S * g.mb;
   g.rr = 1;
   g.mtiles = 1;
-  g.lds = lt_lds_bytes(MW, NW);
+  g.lds = lt_lds_bytes(MW, NW, WV);
   g.win = 0; g.xrow = 0; g.xbuf = 0;
   g.red_off = g.lds; g.stash_off = g.lds; g.stash_cap = 0;
   if (g.lds > kLdsMax) return false;
-  g.ctr_count = (size_t)kXcds * g.NB * g.mb * kLtWaves;
+  g.ctr_count = (size_t)kXcds * g.NB * g.mb * WV;
   g.part_floats = g.S > 1 ? g.ctr_count * (size_t)g.S * MW * NW * 256 : 0;
   // Cost (microseconds): per workgroup the longest of its weight bytes from
   // HBM (m-blocks of one block share them through L2), its weight and X
@@ -355,7 +355,7 @@ bool lt_geo(Geo& g, int want_S) {
   // trip and the finalize.
   const double wg_items = ceil_div(g.items, g.slots);
   const double ks = (double)g.steps * kLtKStep;
-  const double tm = 32.0 * MW, cb = 32.0 * NW;
+  const double tm = 32.0 * MW, cb = (double)g.CB;
   const double w_bytes = wg_items * cb * ks * 2.0, x_bytes = wg_items * tm * ks * 2.0;
   const double flops = wg_items * 2.0 * tm * cb * ks;
   const double p_bytes = g.S > 1 ? wg_items * tm * cb * 4.0 * 2.0 : 0.0;
@@ -365,20 +365,33 @@ bool lt_geo(Geo& g, int want_S) {
   return true;
 }
 
-bool plan_lt(Geo& best, int M, int K, int N, int mw_o, int nw_o, int s_o) {
+// tm_o, tn_o, w_o: forced tile rows, tile columns and waves.  Unforced, the
+// tile is 128 x 192 with eight waves (64 x 48 per wave), the fastest or
+// within 10-18% of it on every projection shape at M = 128 and 256 measured
+// (cold HBM: 76.1 us at 256 x 4096 x 24576 against 93.8-98.7 us for the four-
+// wave tiles, 111.0 against 142.8 us at 256 x 7168 x 18432); the cost model
+// then only picks the split count.
+bool plan_lt(Geo& best, int M, int K, int N, int tm_o, int tn_o, int w_o, int s_o) {
   bool found = false;
-  for (int mw : {2, 4, 8}) {
-    if (mw_o && mw != mw_o) continue;
-    for (int nw : {3, 6}) {
-      if (nw_o && nw != nw_o) continue;
-      const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : 8;
-      for (int s = s_lo; s <= s_hi; ++s) {
-        Geo c;
-        c.M = M; c.K = K; c.N = N; c.ta = mw; c.tb = nw; c.slots = kWgPerXcd;
-        if (!lt_geo(c, s)) continue;
-        if (c.S != s && !s_o) continue;
-        if (!gemm_variant_exists(5, mw, nw)) continue;
-        if (!found || c.est_us < best.est_us - 1e-9) { best = c; found = true; }
+  const bool free_tile = !tm_o && !tn_o && !w_o;
+  for (int wv : {4, 8}) {
+    if (w_o && wv != w_o) continue;
+    if (free_tile && wv != 8) continue;
+    for (int mw : {2, 4, 8}) {
+      if (tm_o && 32 * mw != tm_o) continue;
+      if (free_tile && mw != 4) continue;
+      for (int nw : {3, 6}) {
+        if (tn_o && 16 * nw * (wv / 2) != tn_o) continue;
+        if (free_tile && nw != 3) continue;
+        if (!gemm_variant_exists(wv == 8 ? 6 : 5, mw, nw)) continue;
+        const int s_lo = s_o ? s_o : 1, s_hi = s_o ? s_o : 8;
+        for (int s = s_lo; s <= s_hi; ++s) {
+          Geo c;
+          c.M = M; c.K = K; c.N = N; c.ta = mw; c.tb = nw; c.waves = wv; c.slots = kWgPerXcd;
+          if (!lt_geo(c, s)) continue;
+          if (c.S != s && !s_o) continue;
+          if (!found || c.est_us < best.est_us - 1e-9) { best = c; found = true; }
+        }
       }
     }
   }
@@ -679,10 +692,10 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     // The K-chunked and large-tile kernels are built with nontemporal weight loads only.
     const bool nt_w = pl->w_aux == 2u;
     if (lt) {
-      // tn (a multiple of 32) gives the workgroup tile's columns; waves must be 0 or 4.
-      if (tn_o % 32 || (w_o && w_o != kLtWaves) || !nt_w) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
-      // tm (64, 128 or 256) gives the tile's rows.
-      if (!plan_lt(pl->geo, p.M, p.K, p.N, p.tm / 32, tn_o / 32, s_o)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+      // tn gives the workgroup tile's columns (96, 192 or 384), tm its rows
+      // (64, 128 or 256), waves 4 or 8.
+      if ((w_o && w_o != 4 && w_o != 8) || !nt_w) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+      if (!plan_lt(pl->geo, p.M, p.K, p.N, p.tm, tn_o, w_o, s_o)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
     } else if (kcm) {
       // tn (a multiple of 16) gives the tiles per item.
       if (tn_o % 16 || w_o == 4 || !nt_w) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
@@ -702,7 +715,7 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
           kcg.items * 4 >= kWgPerXcd * 3 && pl->geo.S > 2)
         pl->geo = kcg;
     }
-    if ((pl->geo.path == 3 || pl->geo.path == 5) && pl->geo.mb > 1) {
+    if ((pl->geo.path == 3 || pl->geo.path == 5 || pl->geo.path == 6) && pl->geo.mb > 1) {
       // m-blocks round-robin over the XCD's workgroups (shared weights in
       // L2); SGEMM_KC_RR=0 gives each workgroup a contiguous range instead.
       int rr = 1;
@@ -1234,7 +1247,7 @@ static std::string geo_json(const Geo& g) {
                 "\"steps\":%d,\"items\":%d,\"win\":%d,\"lds\":%d,\"stash_cap\":%d,\"paired\":%d,"
                 "\"ring\":%d,\"mtiles\":%d,\"nfast\":%d,\"slots\":%d,\"xbuf\":%d,\"wpf\":%d,"
                 "\"rr\":%d,\"mb\":%d,\"est_us\":%.3f}",
-                g.path == 0 ? "dot2" : (g.path == 3 ? "kc" : (g.path == 5 ? "lt" : "mfma")), g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
+                g.path == 0 ? "dot2" : (g.path == 3 ? "kc" : (g.path >= 5 ? "lt" : "mfma")), g.M, g.K, g.N, g.ta, g.tb, g.waves, g.wpi, g.ksl, g.kss, g.TN,
                 g.CB, g.Nx, g.NB, g.S, g.KS, g.steps, g.items, g.win, g.lds, g.stash_cap, g.paired, g.ring, g.mtiles,
                 g.nfast, g.slots, g.xbuf, g.wpf, g.rr, g.mb, g.est_us);
   return b;

@@ -64,7 +64,8 @@ GemmKernel gemm_kernel_kc(int a, int b) {
   }
 }
 
-GemmKernel gemm_kernel_lt(int a, int b);  // large-tile MFMA path (path 5, gemm_lt.hip), weights nt
+// Large-tile MFMA path (gemm_lt.hip), weights nt: path 5 four waves, path 6 eight.
+GemmKernel gemm_kernel_lt(int waves, int a, int b);
 
 // dot2: M = 1..15, G in {1, 2, 3, 4, 8} with G*M <= 64.  MFMA: MT = 1..4, NT = 1, 2.
 // Path 2: the MFMA m-tile-item variant (MT = 1, 2 with NT = 1, 2; MT = 4 with NT = 1).
@@ -84,7 +85,7 @@ GemmKernel gemm_kernel_for(int path, int a, int b) {
     if (b == 2) return k_gemm_mfma<mt, 2, AUX>;     \
     return nullptr;
   if (path == 3) return gemm_kernel_kc<AUX>(a, b);
-  if (path == 5) return AUX == kAuxNt ? gemm_kernel_lt(a, b) : nullptr;
+  if (path == 5 || path == 6) return AUX == kAuxNt ? gemm_kernel_lt(path == 6 ? 8 : 4, a, b) : nullptr;
   if (path == 2) {  // m-tile items with a window of 16, 32 or 64 rows
     if (a == 1) return b == 1 ? k_gemm_mfma<1, 1, AUX, true> : (b == 2 ? k_gemm_mfma<1, 2, AUX, true> : nullptr);
     if (a == 2) return b == 1 ? k_gemm_mfma<2, 1, AUX, true> : (b == 2 ? k_gemm_mfma<2, 2, AUX, true> : nullptr);

@@ -11,16 +11,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                                                               unsigned* ctl) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int xcd = xcd_of_wg(ctl), slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
-  lt_stage<MW, NW, kAuxNt>(d, lds, xcd, slot, nslots);
+  lt_stage<MW, NW, 4, kAuxNt>(d, lds, xcd, slot, nslots);
   if (d.check) claim_and_check(ctl, xcd, slot, nslots);
 }
 
-// (MW, NW): workgroup tiles of 32 MW rows x 32 NW columns.
-GemmKernel gemm_kernel_lt(int a, int b) {
-  if (a == 2 && b == 3) return k_gemm_lt<2, 3>;
-  if (a == 4 && b == 3) return k_gemm_lt<4, 3>;
-  if (a == 4 && b == 6) return k_gemm_lt<4, 6>;
-  if (a == 8 && b == 3) return k_gemm_lt<8, 3>;
+// Eight waves, two per SIMD: each keeps at most half a SIMD's registers.
+template <int MW, int NW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_lt8(StageDesc d,
+                                                                                               unsigned* ctl) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int xcd = xcd_of_wg(ctl), slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+  lt_stage<MW, NW, 8, kAuxNt>(d, lds, xcd, slot, nslots);
+  if (d.check) claim_and_check(ctl, xcd, slot, nslots);
+}
+
+// (MW, NW): MW x NW 16 x 16 tiles per wave; the workgroup tile is 32 MW rows
+// by 32 NW (four waves, path 5) or 64 NW (eight waves, path 6) columns.
+GemmKernel gemm_kernel_lt(int waves, int a, int b) {
+  if (waves == 4) {
+    if (a == 2 && b == 3) return k_gemm_lt<2, 3>;
+    if (a == 4 && b == 3) return k_gemm_lt<4, 3>;
+    if (a == 4 && b == 6) return k_gemm_lt<4, 6>;
+    if (a == 8 && b == 3) return k_gemm_lt<8, 3>;
+  } else if (waves == 8) {
+    if (a == 2 && b == 3) return k_gemm_lt8<2, 3>;
+    if (a == 4 && b == 3) return k_gemm_lt8<4, 3>;
+    if (a == 4 && b == 6) return k_gemm_lt8<4, 6>;
+    if (a == 8 && b == 3) return k_gemm_lt8<8, 3>;
+  }
   return nullptr;
 }
 

@@ -4,11 +4,11 @@
 // owns a K slice of the whole block tile, so its register tile stays small
 // and the m-blocks of a column block each load the block's weights again.
 //
-// Here a workgroup of four waves owns one output tile of TM = 32 MW rows by
-// TN = 32 NW columns (all of its rows: an m-block of up to 256) over one K
-// split, and the waves split the tile 2 x 2: wave (wm, wn) keeps the MW x NW
-// 16 x 16 accumulators of rows [16 MW wm, 16 MW (wm + 1)) and columns
-// [16 NW wn, 16 NW (wn + 1)).  Per 32-wide K step the workgroup stages the
+// Here a workgroup of four or eight waves owns one output tile of TM = 32 MW
+// rows by TN = 16 NW WN columns (all of its rows: an m-block of up to 256)
+// over one K split, and the waves split the tile 2 x WN (WN = 2 or 4): wave
+// (wm, wn) keeps the MW x NW 16 x 16 accumulators of rows [16 MW wm,
+// 16 MW (wm + 1)) and columns [16 NW wn, 16 NW (wn + 1)).  Per 32-wide K step the workgroup stages the
 // step's 2 MW fragments of X (A operand) and 2 NW fragments of W (B operand)
 // in LDS with buffer-to-LDS loads, each fragment one kilobyte laid out in the
 // lane order of v_mfma_f32_16x16x32_bf16 (lane l: row or column l % 16, K
@@ -36,11 +36,12 @@
 
 namespace sg {
 
-template <int MW, int NW, int AUX>
+template <int MW, int NW, int WAVES, int AUX>
 __device__ __forceinline__ void lt_stage(const StageDesc& d, uint16_t* lds, int xcd, int slot, int nslots) {
-  constexpr int FA = 2 * MW, FB = 2 * NW, F = FA + FB;
-  constexpr int LPW = lt_loads_per_wave(MW, NW);
-  constexpr int D = lt_reg_steps(MW, NW);  // steps in flight in registers
+  constexpr int WN = WAVES / 2;  // waves along the columns (two along the rows)
+  constexpr int FA = 2 * MW, FB = WN * NW, F = FA + FB;
+  constexpr int LPW = lt_loads_per_wave(MW, NW, WAVES);
+  constexpr int D = lt_reg_steps(MW, NW, WAVES);  // steps in flight in registers
   static_assert(LPW * (D - 1) < 64, "vmcnt is 6 bits");
   constexpr int TM = 16 * FA;
   constexpr unsigned WTILE = MW * NW * 256;  // floats of one wave's tile
@@ -67,7 +68,7 @@ __device__ __forceinline__ void lt_stage(const StageDesc& d, uint16_t* lds, int 
   auto mblk_of = [&](int it) { return it - (it / MB) * MB; };
   // Split-K tile of this wave in item it (one counter and partial block per wave tile).
   auto tile_of = [&](int it) {
-    return (unsigned)((((xcd * d.NB + block_of(it)) * MB + mblk_of(it)) * kLtWaves) + wave);
+    return (unsigned)((((xcd * d.NB + block_of(it)) * MB + mblk_of(it)) * WAVES) + wave);
   };
   const int xc0 = xcd * d.Nx;
   const int xc1 = min(d.N, xc0 + d.Nx);
@@ -107,7 +108,7 @@ __device__ __forceinline__ void lt_stage(const StageDesc& d, uint16_t* lds, int 
     const bool kok = k < c_kend;
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
-      const int u = q * kLtWaves + wave;  // wave-uniform
+      const int u = q * WAVES + wave;  // wave-uniform
       const int f = u >> 1, h = u & 1;
       const bool is_a = f < FA;
       const int row = c_row + 16 * f + 8 * h + lrow;
@@ -126,7 +127,7 @@ __device__ __forceinline__ void lt_stage(const StageDesc& d, uint16_t* lds, int 
     char* const base = (char*)lds + b * (F * 2048);
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
-      const int u = q * kLtWaves + wave;
+      const int u = q * WAVES + wave;
       const int f = u >> 1, h = u & 1;
       if (f < F) *(u4*)(base + f * 2048 + swz(8 * h + lrow, lch)) = src[q];
     }

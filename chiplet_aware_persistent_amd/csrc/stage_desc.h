@@ -29,18 +29,17 @@ constexpr int step_pad_mfma(int nt) { return kLoadsInFlight / (2 * nt) > 2 ? kLo
 // fetched into registers several steps ahead, two whole-line loads per
 // block, and written to one of two LDS buffers; the planner sizes the
 // kernel's LDS with the same functions.
-constexpr int kLtWaves = 4;                 // waves per workgroup (2 x 2 over the tile)
+// Waves: 4 (2 x 2 over the tile) or 8 (2 x 4); MW x NW 16 x 16 tiles per wave.
 constexpr int kLtKStep = 64;                // K values per step (two MFMA k-halves)
-constexpr int lt_frags(int mw, int nw) { return 2 * mw + 2 * nw; }  // 2 KB blocks per step
-constexpr int lt_loads_per_wave(int mw, int nw) { return (2 * lt_frags(mw, nw) + kLtWaves - 1) / kLtWaves; }
+constexpr int lt_frags(int mw, int nw, int wv) { return 2 * mw + (wv / 2) * nw; }  // 2 KB blocks per step
+constexpr int lt_loads_per_wave(int mw, int nw, int wv) { return (2 * lt_frags(mw, nw, wv) + wv - 1) / wv; }
 // Steps in flight in registers: about 24 16-byte loads per lane, an even
 // number from 2 to 8 (items are padded to a multiple of it).
-constexpr int lt_reg_steps(int mw, int nw) {
-  return (24 / lt_loads_per_wave(mw, nw)) / 2 * 2 < 2 ? 2
-         : ((24 / lt_loads_per_wave(mw, nw)) / 2 * 2 > 8 ? 8 : (24 / lt_loads_per_wave(mw, nw)) / 2 * 2);
+constexpr int lt_reg_steps(int mw, int nw, int wv) {
+  return (24 / lt_loads_per_wave(mw, nw, wv)) / 2 * 2 < 2 ? 2
+         : ((24 / lt_loads_per_wave(mw, nw, wv)) / 2 * 2 > 8 ? 8 : (24 / lt_loads_per_wave(mw, nw, wv)) / 2 * 2);
 }
-constexpr int lt_stages(int mw, int nw) { return lt_reg_steps(mw, nw); }
-constexpr int lt_lds_bytes(int mw, int nw) { return 2 * lt_frags(mw, nw) * 2048; }
+constexpr int lt_lds_bytes(int mw, int nw, int wv) { return 2 * lt_frags(mw, nw, wv) * 2048; }
 
 enum OutMode : int {
   OUT_F32 = 0,       // Y fp32

@@ -787,7 +787,9 @@ def test_large_m_refusals():
     assert _create(kind=sg.KIND_LAYERCHAIN, M=65, L=2, d=64, q=64, dff=64) == sg.ERR_UNSUPPORTED
     # large-tile path: tile widths are multiples of 32 columns, four waves, no K slices
     assert _create(M=65, K=1024, N=1024, tn=48) == sg.ERR_UNSUPPORTED
-    assert _create(M=65, K=1024, N=1024, waves=8) == sg.ERR_UNSUPPORTED
+    assert _create(M=65, K=1024, N=1024, waves=2) == sg.ERR_INVALID_ARG      # 4 or 8 waves only
+    assert _create(M=65, K=1024, N=1024, waves=8, tn=96) == sg.ERR_UNSUPPORTED   # 8 waves: 192 or 384
+    assert _create(M=65, K=1024, N=1024, waves=8, tn=192) == sg.OK
     assert _create(M=65, K=1024, N=1024, ksl=2) == sg.ERR_UNSUPPORTED
     assert _create(M=65, K=1024, N=1024, tn=96) == sg.OK
 
@@ -796,19 +798,24 @@ def test_large_m_refusals():
 @pytest.mark.parametrize("K,N", [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096), (7168, 18432),
                                  (1032, 777), (8, 1)])
 def test_large_tile_plans_cover_rows_columns_and_k(M, K, N):
-    """M = 65..256, default plans: the large-tile path (four waves, tiles of
-    32 MW rows x 32 NW columns), items (split, block, m-block) round-robin;
+    """M = 65..256, default plans and plans forced to four or eight waves: the
+    large-tile path (tiles of 32 MW rows x 16 NW x waves/2 columns), items
+    (split, block, m-block) round-robin;
     the m-blocks cover M, the blocks each XCD's columns, the splits K in
     whole 32-wide steps, padded to the register ring depth; the two LDS
     buffers fit next to the static reserve; the loads in flight fit vmcnt."""
-    st = sg.Gemm(M, K, N).describe()["stage"]
-    MW, NW = st["ta"], st["tb"]
-    assert st["path"] == "lt" and st["waves"] == 4 and st["rr"] == 1
+    for waves in (0, 4, 8):
+        _check_large_tile_plan(sg.Gemm(M, K, N, waves=waves).describe()["stage"], M, K, N, waves)
+
+
+def _check_large_tile_plan(st, M, K, N, waves):
+    MW, NW, WV = st["ta"], st["tb"], st["waves"]
+    assert st["path"] == "lt" and WV in (4, 8) and (waves == 0 or WV == waves) and st["rr"] == 1
     TM = 32 * MW
     assert st["mb"] == -(-M // TM) and (st["mb"] - 1) * TM < M
-    assert st["CB"] == 32 * NW and st["NB"] * st["CB"] >= st["Nx"] and 8 * st["Nx"] >= N
-    F = 2 * MW + 2 * NW          # two-kilobyte blocks per 64-wide K step
-    LPW = -(-2 * F // 4)         # 16-byte loads per lane and step (two per block)
+    assert st["CB"] == 16 * NW * (WV // 2) and st["NB"] * st["CB"] >= st["Nx"] and 8 * st["Nx"] >= N
+    F = 2 * MW + (WV // 2) * NW  # two-kilobyte blocks per 64-wide K step
+    LPW = -(-2 * F // WV)        # 16-byte loads per lane and step (two per block)
     D = max(2, min(8, (24 // LPW) // 2 * 2))  # steps in flight in registers (even)
     assert st["ring"] == D and LPW * (D - 1) < 64
     assert st["KS"] % 64 == 0 and st["steps"] % D == 0 and 0 <= st["steps"] * 64 - st["KS"] < 64 * D

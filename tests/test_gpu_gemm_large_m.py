@@ -73,12 +73,28 @@ LT_SMALL = [(65, 1032, 777, 0, 0), (65, 1032, 777, 96, 3), (80, 520, 64, 0, 0), 
             (256, 4096, 1024, 96, 4), (256, 8, 1, 0, 0), (192, 12288, 300, 0, 5), (96, 4104, 777, 192, 7)]
 
 
+LT8_SMALL = [(65, 1032, 777, 192, 0, 0), (100, 2048, 1536, 384, 128, 2), (129, 4104, 129, 192, 256, 2),
+             (200, 3000, 700, 192, 256, 3), (256, 4096, 1024, 384, 128, 0), (256, 8, 1, 192, 64, 0),
+             (144, 776, 530, 384, 0, 0), (192, 12288, 300, 192, 0, 5)]
+
+
+@pytest.mark.parametrize("M,K,N,tn,tm,splitk", LT8_SMALL)
+def test_parity_large_tile_eight_waves(cuda_device, M, K, N, tn, tm, splitk):
+    """Large-tile path with eight waves (2 x 4 over tiles of 192 or 384
+    columns): ragged shapes, forced tile sizes and splits."""
+    x, w, X, W = gemm_inputs(M, K, N, 12900 + M, 13000 + K, cuda_device)
+    g = sg.Gemm(M, K, N, waves=8, tn=tn, tm=tm, splitk=splitk)
+    st = _plan_checks(g, M)
+    assert st["path"] == "lt" and st["waves"] == 8 and st["CB"] == tn and (tm == 0 or 32 * st["ta"] == tm)
+    check(run(g, X, W).cpu().numpy(), x, w)
+
+
 @pytest.mark.parametrize("M,K,N,tn,splitk", LT_SMALL)
 def test_parity_large_tile_small(cuda_device, M, K, N, tn, splitk):
-    """Large-tile path: ragged M, K and N, forced tile widths (96 or 192
-    columns) and split counts, every element against the oracle."""
+    """Large-tile path, four waves: ragged M, K and N, forced tile widths (96
+    or 192 columns) and split counts, every element against the oracle."""
     x, w, X, W = gemm_inputs(M, K, N, 12700 + M, 12800 + K, cuda_device)
-    g = sg.Gemm(M, K, N, tn=tn, splitk=splitk)
+    g = sg.Gemm(M, K, N, waves=4, tn=tn, splitk=splitk)
     st = _plan_checks(g, M)
     assert st["path"] == "lt"
     assert tn == 0 or st["CB"] == tn
