@@ -677,9 +677,11 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     const bool kc = (p.flags & SGEMM_F_KCHUNK) != 0;
     // Beyond 64 rows: the large-tile path unless the K-chunked one is asked
     // for (SGEMM_LT=0 takes the K-chunked path there too).
-    int lt_env = 1;
-    if (!env_int("SGEMM_LT", 1, &lt_env)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
-    const bool lt = p.M > 64 && !kc && lt_env;
+    // SGEMM_LT_MIN_M: the fewest rows that take the large-tile path (65 by
+    // default; from 16 it replaces the MFMA paths too).
+    int lt_env = 1, lt_min = 65;
+    if (!env_int("SGEMM_LT", 1, &lt_env) || !env_int("SGEMM_LT_MIN_M", 65, &lt_min)) { delete pl; return SGEMM_ERR_INVALID_ARG; }
+    const bool lt = p.M >= std::max(lt_min, 16) && !kc && lt_env && !(p.flags & (SGEMM_F_FORCE_DOT2 | SGEMM_F_FORCE_MFMA | SGEMM_F_MTILE_ITEMS | SGEMM_F_MSPLIT));
     const bool kcm = kc || (p.M > 64 && !lt);
     // Rows per m-tile item (the window of the M-major traversal): 16 unless given.
     const int mti_rows = !mti ? 0 : (p.tm ? p.tm : 16);
@@ -703,6 +705,15 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     } else if (!plan_geo(pl->geo, p.M, p.K, p.N, path, 0, tn_o, s_o, w_o, k_o, kCostGemm, 0, mti_rows)) {
       delete pl;
       return SGEMM_ERR_UNSUPPORTED;
+    } else if (path == 1 && !mti && nt_w && !tn_o && !s_o && !w_o && !k_o && p.M > 48 &&
+               (p.N >= 12288 || p.K >= 12288)) {
+      // Four full m-tiles on the widest shapes: the large-tile path with a
+      // 64 x 96 tile and four waves (measured, cold HBM: 64 x 4096 x 24576
+      // 46.0 against 49.8 us on the K-chunked path, 64 x 12288 x 4096 32.7
+      // against 35.8 us on the split MFMA path; on the 4096-column shapes
+      // and at M = 32 it was slower).
+      Geo ltg;
+      if (plan_lt(ltg, p.M, p.K, p.N, 64, 96, 4, 0)) pl->geo = ltg;
     } else if (path == 1 && !mti && nt_w && !tn_o && !s_o && !w_o && !k_o && (p.K >= 6144 || p.M > 48)) {
       // Long K, or four full m-tiles, with a wide output: the K-chunked path
       // takes one item of six tiles over all of K per workgroup and needs no

@@ -485,7 +485,10 @@ def test_dot2_round_robin_items_cover_each_item_once(M, K, N, monkeypatch):
         monkeypatch.setenv("SGEMM_MFMA_RR", env)
         st = sg.Gemm(M, K, N).describe()["stage"]
         rr_path = st["path"] == "dot2" or (st["path"] == "mfma" and st["mtiles"] == 1)
-        assert st["rr"] == (1 if env == "1" and rr_path and st["S"] == 1 else 0)
+        if st["path"] == "lt":  # the large-tile path always takes its items round-robin
+            assert st["rr"] == 1
+        else:
+            assert st["rr"] == (1 if env == "1" and rr_path and st["S"] == 1 else 0)
         items, ng = st["items"], st["waves"] // st["wpi"]
         nw = 32 * ng
         contiguous = [list(range(items * w // nw, items * (w + 1) // nw)) for w in range(nw)]
@@ -512,6 +515,11 @@ def test_planner_covers_every_column_and_k_once(M, K, N, splitk, flags):
     st = g.describe()["stage"]
     if st["path"] == "kc":   # long K or M > 48, wide N: the K-chunked path (its own coverage test below)
         assert M >= 16 and (K >= 6144 or M > 48) and not flags and not splitk and st["S"] == 1
+        return
+    if st["path"] == "lt":   # M > 48 with N or K >= 12288: 64 x 96 large tiles (their own coverage test)
+        assert M > 48 and (N >= 12288 or K >= 12288) and not flags and not splitk
+        _check_large_tile_plan(st, M, K, N, 4)
+        assert 32 * st["ta"] == 64 and st["CB"] == 96
         return
     assert st["path"] == ("dot2" if M < 16 else "mfma")
     mt = st["mtiles"]
@@ -783,7 +791,10 @@ def test_large_m_refusals():
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_W_CACHED) == sg.ERR_UNSUPPORTED
     assert _create(M=64, K=4096, N=24576, flags=sg.F_W_CACHED) == sg.OK
     assert sg.Gemm(64, 4096, 24576, flags=sg.F_W_CACHED).describe()["stage"]["path"] == "mfma"
-    assert sg.Gemm(64, 4096, 24576).describe()["stage"]["path"] == "kc"
+    assert sg.Gemm(64, 4096, 24576).describe()["stage"]["path"] == "lt"
+    assert sg.Gemm(64, 12288, 4096).describe()["stage"]["path"] == "lt"
+    assert sg.Gemm(64, 4096, 4096).describe()["stage"]["path"] == "mfma"
+    assert sg.Gemm(48, 4096, 24576).describe()["stage"]["path"] == "mfma"
     assert _create(kind=sg.KIND_LAYERCHAIN, M=65, L=2, d=64, q=64, dff=64) == sg.ERR_UNSUPPORTED
     # large-tile path: tile widths are multiples of 32 columns, four waves, no K slices
     assert _create(M=65, K=1024, N=1024, tn=48) == sg.ERR_UNSUPPORTED
