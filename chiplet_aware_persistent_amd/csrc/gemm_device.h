@@ -141,26 +141,36 @@ __device__ __forceinline__ int xcd_of_wg(unsigned* status) {
 // kClaimWord + x) and looks at the word's old value: a bit that was already
 // set means two workgroups ran as the same (XCD, slot) pair, so some other
 // pair's columns were never computed, and the topology bit is latched in the
-// status word.  The workgroup whose claim completes its XCD's mask (all
-// nslots bits) clears the word for the next launch; at that point every claim
-// of the XCD has been performed.  A broken dispatch never completes a mask,
-// so the error repeats on every later launch until the workspace is
+// status word.  Only after its claim has returned does the workgroup count
+// itself in the XCD's arrival word (kClaimCount + x); the arrival that
+// brings the count to nslots comes after every claim of the XCD in this
+// launch, and it clears both words for the next launch.  (Clearing when the
+// mask looked complete instead would let a bit set before the launch
+// complete the mask early, so that its owner claimed a cleared word.)  A
+// broken dispatch leaves some XCD short of nslots arrivals, so its words stay
+// set and the error repeats on every later launch until the workspace is
 // re-initialised.  The claim goes out after the workgroup's last stores.  Its
-// device-scope round trip still ends the workgroup 1.5-3 us later on MI355X
+// device-scope round trips still end the workgroup 1.5-3 us later on MI355X
 // (measured on the M = 1 decode projections), so the check is a plan option
 // (SGEMM_F_CHECK_PLACEMENT).
-constexpr int kClaimWord = 32;  // byte 128 of the workspace control block
+constexpr int kClaimWord = 32;   // byte 128 of the workspace control block
+constexpr int kClaimCount = 40;  // byte 160: arrivals per XCD in the current launch
 
 __device__ __forceinline__ void claim_and_check(unsigned* ctl, int xcd, int slot, int nslots) {
   if (threadIdx.x == 0) {
     const unsigned bit = slot < 32 ? 1u << slot : 0u;
-    const unsigned full = nslots >= 32 ? 0xFFFFFFFFu : (1u << nslots) - 1u;
     const unsigned old =
         __hip_atomic_fetch_or(ctl + kClaimWord + xcd, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (bit == 0u || (old & bit)) {
+    if (bit == 0u || (old & bit))
       __hip_atomic_fetch_or(ctl, kStatusTopology, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if ((old | bit) == full) {
+    // The claim has returned (its value was used above; the wait and the
+    // clobber keep the arrival behind it).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const unsigned n =
+        __hip_atomic_fetch_add(ctl + kClaimCount + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n + 1u == (unsigned)nslots) {
       __hip_atomic_store(ctl + kClaimWord + xcd, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctl + kClaimCount + xcd, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

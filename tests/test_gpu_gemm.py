@@ -69,14 +69,15 @@ def test_device_check_accepts_this_gpu(cuda_device):
     assert sg.sgemm_device_check(0) == sg.OK
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 4096, 1536), (32, 2048, 1024)])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 1536), (32, 2048, 1024), (128, 2048, 1536)])
 def test_gemm_placement_claim_reports_a_duplicate_slot(cuda_device, M, K, N):
     """With SGEMM_F_CHECK_PLACEMENT the single GEMM checks that its workgroups
     covered every (XCD, slot) pair once.  A claim bit set in the workspace before the launch looks, to
     the workgroup that owns that pair, like a second workgroup on the same
-    pair: the launch reports SGEMM_ERR_TOPOLOGY instead of passing silently.
-    Its XCD's mask still completes and is cleared, so the next launch is
-    clean, and the output of a normal launch is unaffected."""
+    pair, whatever order the XCD's workgroups claim in: the launch reports
+    SGEMM_ERR_TOPOLOGY instead of passing silently.  Its XCD's 32 arrivals
+    still complete and clear the claim and arrival words, so the next launch
+    is clean, and the output of a normal launch is unaffected."""
     x, w, X, W = gemm_inputs(M, K, N, 41, 42, cuda_device)
     g = sg.Gemm(M, K, N, flags=sg.F_CHECK_PLACEMENT)
     ws = g.new_workspace()
@@ -85,7 +86,8 @@ def test_gemm_placement_claim_reports_a_duplicate_slot(cuda_device, M, K, N):
     claim[3] = 1 << 5                       # XCD 3, slot 5 already claimed
     g(X, W, Y, ws)
     assert g.status(ws) == sg.ERR_TOPOLOGY
-    assert int(claim.abs().sum()) == 0       # every XCD's mask completed and was cleared
+    assert int(claim.abs().sum()) == 0       # every XCD's claims were cleared by its last arrival
+    assert int(ws[160:192].view(torch.int32).abs().sum()) == 0   # and so were the arrival counts
     g(X, W, Y, ws)
     assert g.status(ws) == sg.OK
     check(Y.cpu().numpy(), x, w)
