@@ -175,3 +175,43 @@ def test_decode_projections_m128_m256_full_size(cuda_device, M, K, N, path, flag
     Y = run(g, X, W).cpu().numpy()
     w = device_weights_checked(W, seed_w, K)
     report("gemm %s %dx%dx%d" % (path, M, K, N), check(Y, x, w), workload="large_m")
+
+
+def _random_large_tile_cases(n=24, seed=20261204):
+    """Seeded random shapes and large-tile plans: M in 49..256, K a multiple
+    of 8 up to 8200 (ragged against the 64-wide steps), N up to 5000, the
+    tile (waves, rows, columns) and the split count drawn from what is
+    built."""
+    rng = np.random.default_rng(seed)
+    tiles = [(4, 64, 96), (4, 128, 96), (4, 128, 192), (4, 256, 96), (8, 64, 192), (8, 128, 192),
+             (8, 128, 384), (8, 256, 192)]
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(49, 257))
+        K = int(rng.integers(1, 1026)) * 8
+        N = int(rng.integers(1, 5001))
+        w, tm, tn = tiles[int(rng.integers(len(tiles)))]
+        S = int(rng.choice([0, 0, 1, 2, 3, 5, 8]))
+        out.append((M, K, N, w, tm, tn, S))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,waves,tm,tn,splitk", _random_large_tile_cases())
+def test_large_tile_random_shapes(cuda_device, M, K, N, waves, tm, tn, splitk):
+    """Seeded random shapes on forced large-tile plans (M = 49..64 included,
+    where the path is forced through the tile arguments), every element
+    against the oracle."""
+    x, w, X, W = gemm_inputs(M, K, N, 13100 + M + K % 97, 13200 + N, cuda_device)
+    import os
+    old = os.environ.get("SGEMM_LT_MIN_M")
+    os.environ["SGEMM_LT_MIN_M"] = "49"
+    try:
+        g = sg.Gemm(M, K, N, waves=waves, tm=tm, tn=tn, splitk=splitk)
+    finally:
+        if old is None:
+            del os.environ["SGEMM_LT_MIN_M"]
+        else:
+            os.environ["SGEMM_LT_MIN_M"] = old
+    st = g.describe()["stage"]
+    assert st["path"] == "lt" and st["waves"] == waves and 32 * st["ta"] == tm and st["CB"] == tn
+    check(run(g, X, W).cpu().numpy(), x, w)
