@@ -701,8 +701,15 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
     if (lt) {
       // tn gives the workgroup tile's columns (96, 192 or 384), tm its rows
       // (64, 128 or 256), waves 4 or 8.
-      if ((w_o && w_o != 4 && w_o != 8) || !nt_w) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+      // Weights nt or with the default policy (SGEMM_F_W_CACHED), not sc1.
+      if ((w_o && w_o != 4 && w_o != 8) || (p.flags & SGEMM_F_W_SC1)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
       if (!plan_lt(pl->geo, p.M, p.K, p.N, p.tm, tn_o, w_o, s_o)) { delete pl; return SGEMM_ERR_UNSUPPORTED; }
+      // Several m-blocks read each weight line (R >= 2 in Eq.(1) of the
+      // Fleet reading note, section 3f): the default cache policy keeps the
+      // lines in L2 for the later readers (measured: 256 x 4096 x 24576 67.1
+      // against 75.5 us, HBM fetch 1.09 against 1.25 x the weights;
+      // 256 x 12288 x 4096 52.3 against 60.4 us); one reader keeps nt.
+      if (pl->geo.mb > 1) pl->w_aux = 0u;
     } else if (kcm) {
       // tn (a multiple of 16) gives the tiles per item.
       if (tn_o % 16 || w_o == 4 || !nt_w) { delete pl; return SGEMM_ERR_UNSUPPORTED; }

@@ -64,8 +64,9 @@ GemmKernel gemm_kernel_kc(int a, int b) {
   }
 }
 
-// Large-tile MFMA path (gemm_lt.hip), weights nt: path 5 four waves, path 6 eight.
-GemmKernel gemm_kernel_lt(int waves, int a, int b);
+// Large-tile MFMA path (gemm_lt.hip): path 5 four waves, path 6 eight;
+// weights nt or, cached, with the default policy.
+GemmKernel gemm_kernel_lt(int waves, int a, int b, bool cached);
 
 // dot2: M = 1..15, G in {1, 2, 3, 4, 8} with G*M <= 64.  MFMA: MT = 1..4, NT = 1, 2.
 // Path 2: the MFMA m-tile-item variant (MT = 1, 2 with NT = 1, 2; MT = 4 with NT = 1).
@@ -85,7 +86,10 @@ GemmKernel gemm_kernel_for(int path, int a, int b) {
     if (b == 2) return k_gemm_mfma<mt, 2, AUX>;     \
     return nullptr;
   if (path == 3) return gemm_kernel_kc<AUX>(a, b);
-  if (path == 5 || path == 6) return AUX == kAuxNt ? gemm_kernel_lt(path == 6 ? 8 : 4, a, b) : nullptr;
+  if (path == 5 || path == 6) {
+    if (AUX != kAuxNt && AUX != 0) return nullptr;
+    return gemm_kernel_lt(path == 6 ? 8 : 4, a, b, AUX == 0);
+  }
   if (path == 2) {  // m-tile items with a window of 16, 32 or 64 rows
     if (a == 1) return b == 1 ? k_gemm_mfma<1, 1, AUX, true> : (b == 2 ? k_gemm_mfma<1, 2, AUX, true> : nullptr);
     if (a == 2) return b == 1 ? k_gemm_mfma<2, 1, AUX, true> : (b == 2 ? k_gemm_mfma<2, 2, AUX, true> : nullptr);

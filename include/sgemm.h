@@ -190,11 +190,14 @@ typedef struct {
  * m-blocks instead.  On both, the m-blocks of a column block are
  * neighbouring items that an XCD's workgroups take round-robin, so they
  * share the block's weight lines through that XCD's L2 (the M-major window,
- * section 3f, Eq.(1)).  There SGEMM_F_FORCE_DOT2, SGEMM_F_FORCE_MFMA,
- * SGEMM_F_MTILE_ITEMS, SGEMM_F_MSPLIT, SGEMM_F_W_CACHED and SGEMM_F_W_SC1 are
- * refused with SGEMM_ERR_UNSUPPORTED (both kernels load weights
- * nontemporally only; so does SGEMM_F_KCHUNK at any M), and so are kslices
- * above 1 and, on the large-tile path, waves other than 0 or 4.
+ * section 3f, Eq.(1)); on the large-tile path the weights are then loaded
+ * with the default cache policy (nontemporal with one m-block), which keeps
+ * the lines in L2 for the later readers.  There SGEMM_F_FORCE_DOT2,
+ * SGEMM_F_FORCE_MFMA, SGEMM_F_MTILE_ITEMS, SGEMM_F_MSPLIT and SGEMM_F_W_SC1
+ * are refused with SGEMM_ERR_UNSUPPORTED, SGEMM_F_W_CACHED too on the
+ * K-chunked path (its kernels load weights nontemporally only, at any M),
+ * and so are kslices above 1 and, on the large-tile path, waves other than
+ * 0, 4 or 8.
  *
  * Environment, read here (for experiments and calibration):
  *   SGEMM_TN, SGEMM_SPLITK, SGEMM_WAVES, SGEMM_KSLICES: used for the problem

@@ -785,8 +785,14 @@ def test_large_m_plans_cover_rows_columns_and_k(M, K, N):
 
 def test_large_m_refusals():
     assert _create(M=257) == sg.ERR_UNSUPPORTED
-    for fl in (sg.F_FORCE_MFMA, sg.F_MTILE_ITEMS, sg.F_MSPLIT, sg.F_W_CACHED, sg.F_W_SC1, sg.F_FORCE_DOT2):
+    for fl in (sg.F_FORCE_MFMA, sg.F_MTILE_ITEMS, sg.F_MSPLIT, sg.F_W_SC1, sg.F_FORCE_DOT2):
         assert _create(M=65, K=1024, N=1024, flags=fl) == sg.ERR_UNSUPPORTED, fl
+    # large tiles: nt weight loads with one m-block, the default policy when
+    # several m-blocks share the weights (or when asked for)
+    assert sg.Gemm(128, 4096, 24576).describe()["w_aux"] == 2
+    assert sg.Gemm(256, 4096, 24576).describe()["w_aux"] == 0
+    assert sg.Gemm(128, 4096, 24576, flags=sg.F_W_CACHED).describe()["w_aux"] == 0
+    assert _create(M=65, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_W_CACHED) == sg.ERR_UNSUPPORTED
     # the K-chunked kernels are built with nontemporal weight loads only
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_W_CACHED) == sg.ERR_UNSUPPORTED
     assert _create(M=64, K=4096, N=24576, flags=sg.F_W_CACHED) == sg.OK
