@@ -366,11 +366,11 @@ bool lt_geo(Geo& g, int want_S) {
 }
 
 // tm_o, tn_o, w_o: forced tile rows, tile columns and waves.  Unforced, the
-// tile is 128 x 192 with eight waves (64 x 48 per wave), the fastest or
-// within 10-18% of it on every projection shape at M = 128 and 256 measured
-// (cold HBM: 76.1 us at 256 x 4096 x 24576 against 93.8-98.7 us for the four-
-// wave tiles, 111.0 against 142.8 us at 256 x 7168 x 18432); the cost model
-// then only picks the split count.
+// tile is 128 (or 64, below) x 192 with eight waves, the fastest of the tiles
+// measured on every projection shape at M = 128 and 256 (cold HBM: 76.1 us at
+// 256 x 4096 x 24576 against 93.8-98.7 us for the four-wave tiles, 111.0
+// against 142.8 us at 256 x 7168 x 18432); the cost model then only picks
+// the split count.
 bool plan_lt(Geo& best, int M, int K, int N, int tm_o, int tn_o, int w_o, int s_o) {
   bool found = false;
   const bool free_tile = !tm_o && !tn_o && !w_o;
@@ -379,11 +379,12 @@ bool plan_lt(Geo& best, int M, int K, int N, int tm_o, int tn_o, int w_o, int s_
     if (free_tile && wv != 8) continue;
     for (int mw : {2, 4, 8}) {
       if (tm_o && 32 * mw != tm_o) continue;
-      // Unforced: 128-row tiles, or 64-row ones (two m-blocks sharing the
-      // weights through L2 instead of K splits) at M <= 128 on narrow shapes
-      // (128 x 4096 x 4096: 23.9 against 27.7 us; 128 x 4096 x 6144: 26.7
-      // against 29.4 us).
-      const int mw_free = M <= 128 && N <= 8192 && K <= 8192 ? 2 : 4;
+      // Unforced: 128-row tiles above 128 rows, 64-row ones up to 128 (two
+      // m-blocks sharing the weights through L2 instead of K splits or
+      // zero rows; measured: 65 x 4096 x 24576 50.4 against 53.2 us,
+      // 128 x 7168 x 18432 82.7 against 86.5, 128 x 12288 x 4096 42.5
+      // against 44.9, 128 x 4096 x 4096 23.9 against 27.7).
+      const int mw_free = M <= 128 ? 2 : 4;
       if (free_tile && mw != mw_free) continue;
       for (int nw : {3, 6}) {
         if (tn_o && 16 * nw * (wv / 2) != tn_o) continue;

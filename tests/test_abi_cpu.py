@@ -789,9 +789,10 @@ def test_large_m_refusals():
         assert _create(M=65, K=1024, N=1024, flags=fl) == sg.ERR_UNSUPPORTED, fl
     # large tiles: nt weight loads with one m-block, the default policy when
     # several m-blocks share the weights (or when asked for)
-    assert sg.Gemm(128, 4096, 24576).describe()["w_aux"] == 2
+    assert sg.Gemm(128, 4096, 24576, tm=128).describe()["w_aux"] == 2      # one 128-row m-block
+    assert sg.Gemm(128, 4096, 24576).describe()["w_aux"] == 0              # two 64-row m-blocks
     assert sg.Gemm(256, 4096, 24576).describe()["w_aux"] == 0
-    assert sg.Gemm(128, 4096, 24576, flags=sg.F_W_CACHED).describe()["w_aux"] == 0
+    assert sg.Gemm(128, 4096, 24576, tm=128, flags=sg.F_W_CACHED).describe()["w_aux"] == 0
     assert _create(M=65, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_W_CACHED) == sg.ERR_UNSUPPORTED
     # the K-chunked kernels are built with nontemporal weight loads only
     assert _create(M=32, K=1024, N=1024, flags=sg.F_KCHUNK | sg.F_W_CACHED) == sg.ERR_UNSUPPORTED
