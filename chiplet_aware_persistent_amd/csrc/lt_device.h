@@ -1,36 +1,38 @@
-// Large-tile MFMA stage ("lt"): the single GEMM from 65 to 256 rows, where a
+// Large-tile MFMA stage ("lt"): the single GEMM from 49 to 256 rows, where a
 // weight byte meets enough rows of X that operand traffic inside the CU, not
 // HBM, sets the time of the K-chunked path (kc_device.h): there every wave
 // owns a K slice of the whole block tile, so its register tile stays small
 // and the m-blocks of a column block each load the block's weights again.
 //
 // Here a workgroup of four or eight waves owns one output tile of TM = 32 MW
-// rows by TN = 16 NW WN columns (all of its rows: an m-block of up to 256)
-// over one K split, and the waves split the tile 2 x WN (WN = 2 or 4): wave
-// (wm, wn) keeps the MW x NW 16 x 16 accumulators of rows [16 MW wm,
-// 16 MW (wm + 1)) and columns [16 NW wn, 16 NW (wn + 1)).  Per 32-wide K step the workgroup stages the
-// step's 2 MW fragments of X (A operand) and 2 NW fragments of W (B operand)
-// in LDS with buffer-to-LDS loads, each fragment one kilobyte laid out in the
-// lane order of v_mfma_f32_16x16x32_bf16 (lane l: row or column l % 16, K
-// values 8 (l / 16) .. + 7), so a wave reads each of its fragments with one
-// conflict-free ds_read_b128 and feeds every A fragment to NW MFMAs and every
-// B fragment to MW.  Each weight byte is loaded once per workgroup, from
-// HBM, and each X byte once per column block, from L2.
+// rows by TN = 16 NW WN columns (an m-block of up to 256 rows) over one K
+// split, and the waves split the tile 2 x WN (WN = 2 or 4): wave (wm, wn)
+// keeps the MW x NW 16 x 16 accumulators of rows [16 MW wm, 16 MW (wm + 1))
+// and columns [16 NW wn, 16 NW (wn + 1)), and feeds every A fragment it reads
+// to NW MFMAs (v_mfma_f32_16x16x32_bf16) and every B fragment to MW.
 //
-// The fragments of the next D - 1 steps are in flight in registers (plain
-// 16-byte loads: buffer-to-LDS loads measured about 20 GB/s per CU here, a
-// fraction of what register loads reach), and each step's fragments go to
-// one of two LDS buffers with ds_write_b128 while the other is multiplied;
-// one workgroup barrier per step (the K-split, multi-stage pipeline of the
-// MI355X low-latency GEMM news item, techniques 2 and 3, at the batch sizes
-// where the Fleet reading note reports its megakernel falling behind,
-// Limitations and open question 4).
-// Every item runs the same padded number of steps; loads past the split or
-// past M or N read zeros through the buffer range check, so each wave issues
-// the same number of loads per step and the vmcnt arithmetic below is exact.
-// Items are (split, column block, m-block), taken round-robin by the XCD's
-// workgroups (kc_device.h).  With S > 1 each wave's accumulator tile is a
-// split-K tile of its own (gemm_device.h protocol).
+// Per 64-wide K step the tile's operand blocks (16 rows of X for A, 16 rows
+// of W for B, 64 K values each) are fetched with plain 16-byte loads, two
+// per block, so that every load instruction reads eight whole 128-byte
+// lines; the fetch runs D steps ahead in registers (buffer-to-LDS loads, and
+// loads of 64-byte halves of 16 rows, both measured about 20 GB/s per CU
+// here, well below whole-line register loads).  Each step's blocks are then
+// written to one of two LDS buffers in a row-swizzled layout, from which the
+// waves read their MFMA fragments without bank conflicts, while the other
+// buffer is multiplied; one workgroup barrier per step (the K-split,
+// multi-stage pipeline of the MI355X low-latency GEMM news item, techniques
+// 2 and 3, at the batch sizes where the Fleet reading note reports its
+// megakernel falling behind, Limitations and open question 4).  Each weight
+// byte is read once per workgroup and each X byte once per column block.
+//
+// Every item runs the same padded number of steps (a multiple of D); loads
+// past the split or past M or N read zeros through the buffer range check,
+// so each wave issues the same number of loads per step and the vmcnt
+// arithmetic below is exact.  Items are (split, column block, m-block),
+// taken round-robin by the XCD's workgroups (kc_device.h), so the m-blocks
+// of a block run together and share its weight lines through the XCD's L2.
+// With S > 1 each wave's accumulator tile is a split-K tile of its own
+// (gemm_device.h protocol).
 #pragma once
 #include "gemm_device.h"
 
@@ -79,9 +81,9 @@ __device__ __forceinline__ void lt_stage(const StageDesc& d, uint16_t* lds, int 
   const Rsrc pr = make_rsrc(d.part, d.part_bytes);
   const int steps = d.steps;
 
-  // Fetch coordinates of local item fl: its split's first K value (plus
-  // this lane's 8 g4), the split's end (0 past the last item: those steps
-  // load zeros), and this lane's first row and column.  The fetch runs D
+  // Fetch coordinates of local item fl: its split's first K value, the
+  // split's end (0 past the last item: those steps load zeros), and the
+  // item's first row (of X) and first column (row of W).  The fetch runs D
   // steps ahead of the multiply and items are a multiple of D steps long, so
   // the D fetches of one unrolled group all fall in one item.
   int c_k0 = 0, c_kend = 0, c_row = 0, c_col = 0;
@@ -97,8 +99,8 @@ __device__ __forceinline__ void lt_stage(const StageDesc& d, uint16_t* lds, int 
   // A step covers 64 K values: fragment block f (16 rows or columns x 64 K
   // values, two MFMA k-halves) is fetched by two loads, load h giving lane l
   // the 16 bytes at chunk l % 8 of row 8 h + l / 8, so that every load
-  // instruction reads eight whole 128-byte lines.  Load u = 4 q + wave of the
-  // step is (block u / 2, half u % 2); u >= 2 F is padding that reads zeros
+  // instruction reads eight whole 128-byte lines.  Load u = WAVES q + wave of
+  // the step is (block u / 2, half u % 2); u >= 2 F is padding that reads zeros
   // and is never written.  Operand and offset are selected without a branch,
   // so the compiler keeps exact counts of the loads in flight.
   u4 stg[D][LPW];  // fetched loads of the next D steps
