@@ -444,3 +444,27 @@ def test_parity_mtile_windows_and_msplit(cuda_device, M, K, N, tm, msplit):
     st = g.describe()["stage"]
     assert st["mtiles"] == -(-M // tm) and st["nfast"] == int(msplit)
     check(run(g, X, W).cpu().numpy(), x, w)
+
+
+def _random_default_cases(n=40, seed=20261205):
+    """Seeded random shapes for the planner's default plans: M in 1..256 (so
+    every path is drawn: dot2, MFMA, K-chunked, large tiles), K a multiple
+    of 8 up to 12288, N up to 6000, fp32 or bf16 output."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([int(rng.integers(1, 16)), int(rng.integers(16, 65)), int(rng.integers(65, 257))]))
+        K = int(rng.integers(1, 1537)) * 8
+        N = int(rng.integers(1, 6001))
+        out.append((M, K, N, int(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,bf16", _random_default_cases())
+def test_random_shapes_default_plans(cuda_device, M, K, N, bf16):
+    """Default plans on seeded random shapes, every element against the
+    oracle (bf16 outputs within one more bf16 ulp)."""
+    x, w, X, W = gemm_inputs(M, K, N, 14000 + M, 14100 + K % 1000, cuda_device)
+    g = sg.Gemm(M, K, N, out_dtype=sg.OUT_BF16 if bf16 else sg.OUT_F32)
+    Y = run(g, X, W).float().cpu().numpy()
+    check(Y, x, w, bf16_out=bool(bf16))
