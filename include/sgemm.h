@@ -163,7 +163,10 @@ typedef struct {
   int tm;  /* SGEMM_F_MTILE_ITEMS / SGEMM_F_MSPLIT: rows per item, T_M = 16, 32 or
               64 (0: 16).  Single GEMM with M > 64 on the large-tile path:
               rows of a workgroup tile, 64, 128 or 256 (0: the planner's);
-              tn there is the tile's columns, 96 or 192.  Must be 0 otherwise */
+              tn there is the tile's columns.  Tiles built (rows x columns):
+              64 x 96, 128 x 96, 128 x 192 and 256 x 96 with four waves,
+              twice the columns with eight; others are refused with
+              SGEMM_ERR_UNSUPPORTED.  Must be 0 otherwise */
   /* kind = SGEMM_KIND_DECODER: M, n_layers, d_model, d_ff and these (q_cols is
      0 or n_heads * head_dim).  Built: n_heads = 4 n_kv_heads, head_dim = 128,
      ctx + 1 <= 4096 (64 chunks of 64 positions), M <= 64. */
@@ -184,9 +187,13 @@ typedef struct {
  * the FlyDSL news item's K-split and multi-stage LDS pipeline, and the batch
  * sizes at which the Fleet reading note reports its megakernel falling
  * behind, Limitations) runs on the large-tile MFMA path: a workgroup of four
- * waves owns a tile of up to 256 rows and 96 or 192 columns over a K split
- * and stages each 32-wide K step's X and W fragments in LDS through a ring of
- * slots.  With SGEMM_F_KCHUNK it runs on the K-chunked MFMA path in 64-row
+ * or eight waves (2 x 2 or 2 x 4) owns a tile of 64-256 rows and 96-384
+ * columns over a K split; each 64-wide K step's X and W blocks are fetched a
+ * few steps ahead by whole-line register loads and written to one of two LDS
+ * buffers, from which every wave reads its MFMA fragments.  By default eight
+ * waves over 64 x 192 tiles up to 128 rows and 128 x 192 above; the same
+ * path, with four waves over 64 x 96 tiles, also takes M = 49..64 when N or
+ * K is at least 12288.  With SGEMM_F_KCHUNK it runs on the K-chunked MFMA path in 64-row
  * m-blocks instead.  On both, the m-blocks of a column block are
  * neighbouring items that an XCD's workgroups take round-robin, so they
  * share the block's weight lines through that XCD's L2 (the M-major window,
@@ -208,7 +215,21 @@ typedef struct {
  *   SGEMM_CHAIN_COST: "alpha,x_gbps,split_us,fin_us_kb,ksl_us", the chain
  *       planner's cost constants;
  *   SGEMM_WATCHDOG_S: seconds a chain stage may wait for its producer before
- *       the run stops with SGEMM_ERR_TIMEOUT (default 5, at most 3600).
+ *       the run stops with SGEMM_ERR_TIMEOUT (default 5, at most 3600);
+ *   SGEMM_LT (default 1): 0 runs M = 65..256 on the K-chunked path instead
+ *       of the large-tile one;
+ *   SGEMM_LT_MIN_M (default 65): the fewest rows (at least 16) that take the
+ *       large-tile path; below 65 it replaces the MFMA paths from that M on;
+ *   SGEMM_DOT2_RR, SGEMM_MFMA_RR, SGEMM_KC_RR, SGEMM_CHAIN_RR (default 1): 0
+ *       gives each workgroup a contiguous range of its XCD's items instead of
+ *       every 32nd item (single-GEMM dot2 and MFMA plans without splits,
+ *       K-chunked and large-tile plans with several m-blocks, chain stages);
+ *   SGEMM_CHAIN_WPF (default 0): weight steps that each chain dot2 stage
+ *       loads into LDS before its wait for X;
+ *   SGEMM_CHAIN_GCOPIES (8 or 1, default 8): copies of each chain and
+ *       decoder counter, one per XCD or one for all;
+ *   SGEMM_ATTN_SLICES (1..8): the decoder's attention workgroup slices per
+ *       (sequence, key/value head) pair (default: the planner's).
  * A malformed value makes the call return SGEMM_ERR_INVALID_ARG.
  */
 int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
