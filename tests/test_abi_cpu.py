@@ -848,3 +848,67 @@ def test_plans_up_to_64_rows_keep_one_m_block(M):
     contiguous item ranges."""
     st = sg.Gemm(M, 4096, 24576, flags=sg.F_KCHUNK).describe()["stage"]
     assert st["mb"] == 1 and st["rr"] == 0 and st["items"] == st["NB"] * st["S"]
+
+
+def _stage(M, K, N, **kw):
+    return sg.Gemm(M, K, N, **kw).describe()["stage"]
+
+
+def test_large_tile_environment_switches(monkeypatch):
+    """SGEMM_LT=0 sends M = 65..256 to the K-chunked path; SGEMM_LT_MIN_M
+    moves the fewest rows that take the large-tile path (never below 16);
+    SGEMM_KC_RR=0 gives m-block plans contiguous item ranges; a malformed
+    value of any of them is refused with SGEMM_ERR_INVALID_ARG."""
+    for var in ("SGEMM_LT", "SGEMM_LT_MIN_M", "SGEMM_KC_RR"):
+        monkeypatch.delenv(var, raising=False)
+    assert _stage(128, 4096, 24576)["path"] == "lt"
+    assert _stage(32, 4096, 4096)["path"] == "mfma"
+    monkeypatch.setenv("SGEMM_LT", "0")
+    st = _stage(128, 4096, 24576)
+    assert st["path"] == "kc" and st["mb"] == 2
+    monkeypatch.delenv("SGEMM_LT")
+    monkeypatch.setenv("SGEMM_LT_MIN_M", "16")
+    assert _stage(16, 4096, 4096)["path"] == "lt"
+    assert _stage(15, 4096, 4096)["path"] == "dot2"
+    monkeypatch.setenv("SGEMM_LT_MIN_M", "4")   # clamped to 16 rows
+    assert _stage(8, 4096, 4096)["path"] == "dot2"
+    monkeypatch.setenv("SGEMM_LT_MIN_M", "200")
+    assert _stage(128, 4096, 24576)["path"] == "kc"
+    assert _stage(200, 4096, 24576)["path"] == "lt"
+    monkeypatch.delenv("SGEMM_LT_MIN_M")
+    for kw in ({}, {"flags": sg.F_KCHUNK}):
+        assert _stage(256, 4096, 24576, **kw)["rr"] == 1
+    monkeypatch.setenv("SGEMM_KC_RR", "0")
+    for kw in ({}, {"flags": sg.F_KCHUNK}):
+        assert _stage(256, 4096, 24576, **kw)["rr"] == 0
+    monkeypatch.delenv("SGEMM_KC_RR")
+    for var in ("SGEMM_LT", "SGEMM_LT_MIN_M", "SGEMM_KC_RR"):
+        monkeypatch.setenv(var, "1x")
+        with pytest.raises(sg.SgemmError) as e:
+            sg.Gemm(256, 4096, 24576)
+        assert e.value.code == sg.ERR_INVALID_ARG, var
+        monkeypatch.delenv(var)
+
+
+def test_counter_copies_and_attention_slices_switches(monkeypatch):
+    """SGEMM_CHAIN_GCOPIES takes 8 (one counter copy per XCD) or 1;
+    SGEMM_ATTN_SLICES sets the decoder's attention slices (1..8); other
+    values are refused with SGEMM_ERR_INVALID_ARG."""
+    monkeypatch.delenv("SGEMM_CHAIN_GCOPIES", raising=False)
+    monkeypatch.delenv("SGEMM_ATTN_SLICES", raising=False)
+    for v, rc in (("8", sg.OK), ("1", sg.OK), ("2", sg.ERR_INVALID_ARG), ("x", sg.ERR_INVALID_ARG)):
+        monkeypatch.setenv("SGEMM_CHAIN_GCOPIES", v)
+        assert _dec_create() == rc, v
+        p = sg.Problem(sg.KIND_LAYERCHAIN, 2, 0, 0, 0, 2, 256, 128, 384, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+        prc, h, ws = sg.sgemm_plan_create(p)
+        if h:
+            sg.sgemm_plan_destroy(h)
+        assert prc == rc, v
+    monkeypatch.delenv("SGEMM_CHAIN_GCOPIES")
+    assert sg.Decoder(4, 2, 256, 384, 8, 2, 128, 100).describe()["attn_slices"] > 1
+    for v in ("1", "3", "8"):
+        monkeypatch.setenv("SGEMM_ATTN_SLICES", v)
+        assert sg.Decoder(4, 2, 256, 384, 8, 2, 128, 100).describe()["attn_slices"] == int(v)
+    for v in ("0", "9", "x"):
+        monkeypatch.setenv("SGEMM_ATTN_SLICES", v)
+        assert _dec_create() == sg.ERR_INVALID_ARG, v
