@@ -268,8 +268,9 @@ int sgemm_run(sgemm_plan plan, const void* X, const void* W, void* Y, void* work
  * until the process ends; its address is looked up once per device).  Same
  * kernels, plan and results as sgemm_run.
  *   Limits: the plan's split-K counters must fit 1 MiB and its partials
- *   32 MiB - 1 MiB - 256 B, else SGEMM_ERR_WORKSPACE (every decode shape at
- *   M <= 64 fits; the largest, 64 x 4096 x 24576, needs 24 MiB).
+ *   32 MiB - 1 MiB - 256 B, else SGEMM_ERR_WORKSPACE (every decode
+ *   projection shape up to M = 256 fits; the largest, 256 x 4096 x 6144 in
+ *   four splits, needs 24 MiB).
  *   SGEMM_F_CHECK_PLACEMENT plans are refused (SGEMM_ERR_UNSUPPORTED): no
  *   status word is read back from the shared array.
  *   Concurrency: every call on a GPU uses that GPU's one array, so calls

@@ -912,3 +912,13 @@ def test_counter_copies_and_attention_slices_switches(monkeypatch):
     for v in ("0", "9", "x"):
         monkeypatch.setenv("SGEMM_ATTN_SLICES", v)
         assert _dec_create() == sg.ERR_INVALID_ARG, v
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 128, 256])
+def test_decode_shapes_fit_the_no_alloc_array(M):
+    """Every decode projection shape up to M = 256 plans a workspace (split-K
+    counters, partials and control words together) below the 31 MiB that
+    sgemm_run_noalloc's static array leaves for partials."""
+    for K, N in [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096),
+                 (7168, 1536), (7168, 4096), (7168, 18432)]:
+        assert sg.Gemm(M, K, N).describe()["workspace"] < 31 * 2**20, (M, K, N)
