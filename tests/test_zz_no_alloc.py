@@ -33,7 +33,8 @@ def _no_alloc(g, X, W):
 @pytest.mark.parametrize("first,second", [((64, 4096, 24576, 4), (16, 2048, 3000, 3)),
                                           ((32, 12288, 4096, 8), (3, 1032, 777, 2)),
                                           ((64, 7168, 4096, 0), (1, 1024, 1024, 0)),
-                                          ((200, 4096, 6144, 3), (128, 2048, 1536, 0))])
+                                          ((200, 4096, 6144, 3), (128, 2048, 1536, 0)),
+                                          ((256, 4096, 6144, 0), (96, 4096, 4096, 0))])
 def test_no_alloc_matches_workspace_run_twice(cuda_device, first, second):
     for i, (M, K, N, S) in enumerate((first, second)):
         x, w, X, W = gemm_inputs(M, K, N, 700 + i, 800 + K, cuda_device)
