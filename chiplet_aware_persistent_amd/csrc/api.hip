@@ -738,6 +738,17 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
       if (plan_kc(kcg, p.M, p.K, p.N, 0, 6, 1, kCostGemm) && kcg.items <= kWgPerXcd &&
           kcg.items * 4 >= kWgPerXcd * 3 && pl->geo.S > 2)
         pl->geo = kcg;
+    } else if (path == 1 && !mti && nt_w && !tn_o && !s_o && !w_o && !k_o && p.M > 16 && p.M <= 32 &&
+               p.K > 3072 && p.K <= 4096 && p.N <= 4096 && pl->geo.S < 4) {
+      // Two m-tiles on a 4096-deep output of at most 4096 columns: four K
+      // splits instead of the cost model's one or two, so the X window each
+      // workgroup fills before its first step drops from 128-147 KB to 64 KB
+      // for 0.5-1 MB of partials (measured, cold HBM, best of 60 launches:
+      // 17 x 4096 x 4096 15.96 -> 14.24 us, 24 x 4096 x 4096 14.88 -> 14.32,
+      // 32 x 4096 x 4096 15.56 -> 14.60, 32 x 4096 x 2048 14.76 -> 12.88; at
+      // K = 3072 and on 6144-wide outputs within -9..+10%, so left alone).
+      Geo g4;
+      if (plan_geo(g4, p.M, p.K, p.N, path, 0, 0, 4, 0, 0, kCostGemm)) pl->geo = g4;
     }
     if ((pl->geo.path == 3 || pl->geo.path == 5 || pl->geo.path == 6) && pl->geo.mb > 1) {
       // m-blocks round-robin over the XCD's workgroups (shared weights in
