@@ -922,3 +922,18 @@ def test_decode_shapes_fit_the_no_alloc_array(M):
     for K, N in [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096),
                  (7168, 1536), (7168, 4096), (7168, 18432)]:
         assert sg.Gemm(M, K, N).describe()["workspace"] < 31 * 2**20, (M, K, N)
+
+
+def test_four_splits_at_two_m_tiles_on_4096_deep_narrow_outputs():
+    """M = 17-32 on K = 4096 with at most 4096 columns takes four K splits (a
+    64 KB X window per workgroup); M = 16, K = 3072, 6144 columns and forced
+    splits keep the cost model's or the caller's choice."""
+    for M in (17, 24, 32):
+        for N in (2048, 4096):
+            st = _stage(M, 4096, N)
+            assert st["path"] == "mfma" and st["S"] == 4 and st["KS"] == 1024, (M, N)
+    assert _stage(16, 4096, 4096)["S"] == 1
+    assert _stage(33, 4096, 4096)["S"] == 2
+    assert _stage(20, 3072, 4096)["S"] == 1
+    assert _stage(32, 4096, 6144)["S"] == 2
+    assert _stage(32, 4096, 4096, splitk=2)["S"] == 2
