@@ -738,17 +738,28 @@ int sgemm_plan_create(const sgemm_problem* problem, int device, sgemm_plan* out,
       if (plan_kc(kcg, p.M, p.K, p.N, 0, 6, 1, kCostGemm) && kcg.items <= kWgPerXcd &&
           kcg.items * 4 >= kWgPerXcd * 3 && pl->geo.S > 2)
         pl->geo = kcg;
-    } else if (path == 1 && !mti && nt_w && !tn_o && !s_o && !w_o && !k_o && p.M > 16 && p.M <= 32 &&
+    } else if (path == 1 && !mti && nt_w && !tn_o && !s_o && !w_o && !k_o && p.M > 16 && p.M <= 48 &&
                p.K > 3072 && p.K <= 4096 && p.N <= 4096 && pl->geo.S < 4) {
-      // Two m-tiles on a 4096-deep output of at most 4096 columns: four K
-      // splits instead of the cost model's one or two, so the X window each
-      // workgroup fills before its first step drops from 128-147 KB to 64 KB
-      // for 0.5-1 MB of partials (measured, cold HBM, best of 60 launches:
-      // 17 x 4096 x 4096 15.96 -> 14.24 us, 24 x 4096 x 4096 14.88 -> 14.32,
-      // 32 x 4096 x 4096 15.56 -> 14.60, 32 x 4096 x 2048 14.76 -> 12.88; at
-      // K = 3072 and on 6144-wide outputs within -9..+10%, so left alone).
+      // Two or three m-tiles on a 4096-deep output of at most 4096 columns:
+      // four K splits instead of the cost model's one or two, so the X window
+      // each workgroup fills before its first step drops from 128-147 KB to
+      // 64 KB for 0.5-1 MB of partials (measured, cold HBM, best of 60
+      // launches: 17 x 4096 x 4096 15.96 -> 14.24 us, 24 x 4096 x 4096
+      // 14.88 -> 14.32, 32 x 4096 x 4096 15.56 -> 14.60, 32 x 4096 x 2048
+      // 14.76 -> 12.88, 36 x 4096 x 2048 15.68 -> 13.40; at K = 3072 and on
+      // 6144-wide outputs within -9..+10%, so left alone).
       Geo g4;
       if (plan_geo(g4, p.M, p.K, p.N, path, 0, 0, 4, 0, 0, kCostGemm)) pl->geo = g4;
+    } else if (path == 0 && nt_w && !tn_o && !s_o && !w_o && !k_o && p.M >= 10 && p.M < 16 &&
+               p.K >= 6144 && p.K <= 8192 && p.N >= 3072 && p.N <= 4096 && pl->geo.S > 2) {
+      // dot2 at M = 10-15 where the X window over all of K does not fit:
+      // two K splits instead of the cost model's four (measured, cold HBM,
+      // best of 60 launches: 12 x 7168 x 4096 25.32 -> 22.40 us, 15 x 7168 x
+      // 4096 27.88 -> 24.84, 12 x 7168 x 3072 22.04 -> 19.44, 15 x 8192 x
+      // 4096 28.96 -> 27.48, 15 x 6144 x 4096 27.88 -> 25.08; on 1536-wide
+      // outputs and at M = 8 four splits measured as fast or faster).
+      Geo g2;
+      if (plan_geo(g2, p.M, p.K, p.N, path, 0, 0, 2, 0, 0, kCostGemm)) pl->geo = g2;
     }
     if ((pl->geo.path == 3 || pl->geo.path == 5 || pl->geo.path == 6) && pl->geo.mb > 1) {
       // m-blocks round-robin over the XCD's workgroups (shared weights in

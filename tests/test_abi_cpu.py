@@ -924,16 +924,23 @@ def test_decode_shapes_fit_the_no_alloc_array(M):
         assert sg.Gemm(M, K, N).describe()["workspace"] < 31 * 2**20, (M, K, N)
 
 
-def test_four_splits_at_two_m_tiles_on_4096_deep_narrow_outputs():
-    """M = 17-32 on K = 4096 with at most 4096 columns takes four K splits (a
-    64 KB X window per workgroup); M = 16, K = 3072, 6144 columns and forced
-    splits keep the cost model's or the caller's choice."""
-    for M in (17, 24, 32):
+def test_measured_split_rules():
+    """MFMA, M = 17-48 on K = 4096 with at most 4096 columns: four K splits (a
+    64 KB X window per workgroup).  dot2, M = 10-15, K = 6144-8192, 3072-4096
+    columns: two splits where the cost model takes more.  Neighbouring shapes
+    and forced splits keep the cost model's or the caller's choice."""
+    for M in (17, 24, 32, 33, 36, 48):
         for N in (2048, 4096):
             st = _stage(M, 4096, N)
             assert st["path"] == "mfma" and st["S"] == 4 and st["KS"] == 1024, (M, N)
     assert _stage(16, 4096, 4096)["S"] == 1
-    assert _stage(33, 4096, 4096)["S"] == 2
     assert _stage(20, 3072, 4096)["S"] == 1
     assert _stage(32, 4096, 6144)["S"] == 2
     assert _stage(32, 4096, 4096, splitk=2)["S"] == 2
+    for M, K, N in ((10, 7168, 3072), (12, 7168, 4096), (15, 7168, 4096), (15, 8192, 4096), (15, 6144, 4096)):
+        st = _stage(M, K, N)
+        assert st["path"] == "dot2" and st["S"] == 2, (M, K, N)
+    assert _stage(12, 6144, 4096)["S"] == 1
+    assert _stage(15, 7168, 1536)["S"] == 4
+    assert _stage(8, 12288, 4096)["S"] == 4
+    assert _stage(12, 7168, 4096, splitk=4)["S"] == 4
