@@ -468,3 +468,15 @@ def test_random_shapes_default_plans(cuda_device, M, K, N, bf16):
     g = sg.Gemm(M, K, N, out_dtype=sg.OUT_BF16 if bf16 else sg.OUT_F32)
     Y = run(g, X, W).float().cpu().numpy()
     check(Y, x, w, bf16_out=bool(bf16))
+
+
+@pytest.mark.parametrize("M,K,N,S", [(17, 4096, 4096, 4), (32, 4096, 2048, 4), (36, 4096, 2048, 4), (48, 4096, 3000, 4),
+                                     (10, 7168, 3072, 2), (12, 7168, 4096, 2), (15, 6144, 4096, 2), (15, 8192, 3500, 2)])
+def test_measured_split_rule_plans(cuda_device, M, K, N, S):
+    """The planner's measured split rules (four K splits at M = 17-48 on
+    4096-deep narrow outputs; two for dot2 at M = 10-15, K = 6144-8192):
+    the plan takes them, and every output element matches the oracle."""
+    g = sg.Gemm(M, K, N)
+    assert g.describe()["stage"]["S"] == S
+    x, w, X, W = gemm_inputs(M, K, N, 15000 + M, 15100 + N % 1000, cuda_device)
+    check(run(g, X, W).cpu().numpy(), x, w)
